@@ -1,0 +1,259 @@
+/*
+ * smla_oracle.c -- plain CPU oracle for sparse MLA forward over top-k indices.
+ *
+ * TEST INFRASTRUCTURE. This file exists to check the GPU library, not to be
+ * part of it. Only the test suite, the smoke check and the benchmark's CPU
+ * baseline may load it. The GPU path shares no code, header, table or helper
+ * with it, and it includes nothing from the GPU path.
+ *
+ * It is deliberately slow and literal: every step is the plain definition,
+ * computed in double precision, one query token per OpenMP iteration, no
+ * tiling, no fusion, no online softmax.
+ *
+ * Sources (the pages this build follows):
+ *   [P2] "vllm/v1/attention/backends/mla/flashmla_sparse.py" (the vLLM
+ *        FLASHMLA_SPARSE backend source, as shown in the vllm-cpu-avx512bf16
+ *        0.14.0 wheel diff):
+ *          - the module note on the fp8_ds_mla cache format (656-byte rows:
+ *            512 float8_e4m3, 4 float32 scales per 128 values, 64 bfloat16
+ *            RoPE values);
+ *          - triton_convert_req_index_to_global_index and its docstring
+ *            (logical top-k index -> physical cache slot through the block
+ *            table, -1 kept as -1, out-of-table blocks mapped to -1);
+ *          - FlashMLASparseImpl.forward (its note that both sparse kernels
+ *            run multi-query attention with 576-wide keys and 512-wide
+ *            values: every head of a token attends to the same rows, and the
+ *            value is the first 512 columns), _fp8_flash_mla_kernel (head_dim_v=512),
+ *            and the softmax_scale the backend passes to the kernels.
+ *   The OCP 8-bit floating point specification (the E4M3FN encoding) for the
+ *   value of an e4m3 byte.
+ *
+ * Readings where the pages are silent:
+ *   - the second kernel return value is the natural-log log-sum-exp of the
+ *     scaled logits;
+ *   - a token with no valid slot gets o = 0 and lse = -inf;
+ *   - a duplicated index counts once per occurrence (plain sum over the list);
+ *   - a request id outside [0, num_reqs) or a block-table entry outside
+ *     [0, num_blocks) yields slot -1 (the page's kernel would read out of
+ *     bounds there);
+ *   - the per-128 scales multiply the decoded e4m3 values.
+ *
+ * Parity pins for every function here live in the CPU test suite
+ * (tests/test_oracle_pins.py); none of them re-types these formulas.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORACLE_BLOCK 64   /* paged-cache block size (kernel supports 64 only) */
+#define ORACLE_DQK 576    /* 512 latent (NoPE) + 64 RoPE                     */
+#define ORACLE_DV 512     /* value width = latent part                       */
+#define ORACLE_FP8_ROW 656
+
+/* ---------------------------------------------------------------- values */
+
+/* OCP E4M3FN byte -> value. Sign bit, 4 exponent bits (bias 7), 3 mantissa
+ * bits; exponent field 0 is subnormal (m * 2^-9); S.1111.111 is NaN; there is
+ * no infinity. */
+double smla_oracle_e4m3fn(uint8_t code)
+{
+    int sign = (code >> 7) & 1;
+    int e = (code >> 3) & 0xF;
+    int m = code & 0x7;
+    double v;
+    if (e == 0xF && m == 0x7)
+        return NAN;
+    if (e == 0)
+        v = ldexp((double)m, -9);
+    else
+        v = ldexp(1.0 + (double)m / 8.0, e - 7);
+    return sign ? -v : v;
+}
+
+/* bfloat16 bit pattern -> value (the upper half of a float32). */
+double smla_oracle_bf16(uint16_t bits)
+{
+    uint32_t u = (uint32_t)bits << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+/* One 656-byte fp8_ds_mla row -> 576 values [P2, cache format note]:
+ * bytes 0..511 are e4m3 latent values, bytes 512..527 four little-endian
+ * float32 scales (scale i covers latent values 128*i .. 128*i+127), bytes
+ * 528..655 sixty-four bfloat16 RoPE values, not quantized. */
+void smla_oracle_decode_fp8_row(const uint8_t *row, double *out)
+{
+    float scale[4];
+    memcpy(scale, row + 512, sizeof scale);
+    for (int i = 0; i < 512; ++i)
+        out[i] = smla_oracle_e4m3fn(row[i]) * (double)scale[i / 128];
+    for (int r = 0; r < 64; ++r) {
+        uint16_t b;
+        memcpy(&b, row + 528 + 2 * r, sizeof b);
+        out[512 + r] = smla_oracle_bf16(b);
+    }
+}
+
+/* One bf16 cache row (576 values) -> values. */
+void smla_oracle_decode_bf16_row(const uint16_t *row, double *out)
+{
+    for (int i = 0; i < ORACLE_DQK; ++i)
+        out[i] = smla_oracle_bf16(row[i]);
+}
+
+/* --------------------------------------------------------- index convert */
+
+/* Logical per-request top-k index -> physical cache slot [P2,
+ * triton_convert_req_index_to_global_index docstring and kernel]:
+ *   slot = block_table[req, idx / 64] * 64 + idx % 64,
+ * with -1 for a negative index and for a block position outside the table
+ * width. Safety readings: bad request id or bad table entry -> -1. */
+int32_t smla_oracle_convert_one(int32_t req, int32_t idx, const int32_t *block_table,
+                                int64_t num_reqs, int64_t max_blocks_per_req,
+                                int64_t num_blocks)
+{
+    if (req < 0 || req >= num_reqs)
+        return -1;
+    if (idx < 0)
+        return -1;
+    int64_t blk = idx / ORACLE_BLOCK;
+    int64_t off = idx % ORACLE_BLOCK;
+    if (blk >= max_blocks_per_req)
+        return -1;
+    int64_t base = block_table[(int64_t)req * max_blocks_per_req + blk];
+    if (base < 0 || base >= num_blocks)
+        return -1;
+    return (int32_t)(base * ORACLE_BLOCK + off);
+}
+
+void smla_oracle_convert_indices(const int32_t *req_id_per_token, const int32_t *block_table,
+                                 const int32_t *topk_indices, int32_t *out, int64_t num_tokens,
+                                 int64_t topk, int64_t num_reqs, int64_t max_blocks_per_req,
+                                 int64_t num_blocks)
+{
+    for (int64_t t = 0; t < num_tokens; ++t)
+        for (int64_t j = 0; j < topk; ++j)
+            out[t * topk + j] = smla_oracle_convert_one(
+                req_id_per_token[t], topk_indices[t * topk + j], block_table, num_reqs,
+                max_blocks_per_req, num_blocks);
+}
+
+/* -------------------------------------------------------------- attention */
+
+/* Sparse MQA-576/512 attention for the listed query tokens [P2,
+ * FlashMLASparseImpl.forward and the two kernel wrappers]:
+ *   for token t, head h and valid slots j of t's list,
+ *     s_j      = sm_scale * <q[t,h,0:576], K_j>
+ *     lse[t,h] = ln sum_j exp(s_j)
+ *     p_j      = exp(s_j - lse[t,h])
+ *     o[t,h,:] = sum_j p_j * K_j[0:512]
+ *
+ * cache_format: 0 = bf16 rows [num_blocks, 64, 576] (uint16 bit patterns),
+ *               1 = 656-byte fp8_ds_mla rows [num_blocks, 64, 656].
+ * q: bf16 bit patterns [num_tokens, h_q, 576].
+ * tokens: which query tokens to compute (NULL = all, in order); output row i
+ *         belongs to token tokens[i].
+ * out: [n, h_q, 512]; lse: [n, h_q]; weights (nullable): [n, h_q, topk], the
+ *      softmax weight of every list position (0 for invalid positions).
+ * Returns 0, or -1 on a bad argument or allocation failure. */
+int smla_oracle_attention(int cache_format, const uint16_t *q, const void *cache,
+                          const int32_t *block_table, const int32_t *req_id_per_token,
+                          const int32_t *topk_indices, double sm_scale, int64_t num_tokens,
+                          int64_t h_q, int64_t topk, int64_t num_reqs,
+                          int64_t max_blocks_per_req, int64_t num_blocks,
+                          const int64_t *tokens, int64_t n, double *out, double *lse,
+                          double *weights)
+{
+    if (cache_format != 0 && cache_format != 1)
+        return -1;
+    if (tokens == NULL)
+        n = num_tokens;
+    int failed = 0;
+
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t i = 0; i < n; ++i) {
+        int64_t t = tokens ? tokens[i] : i;
+        double *rows = malloc(sizeof(double) * (size_t)(topk > 0 ? topk : 1) * ORACLE_DQK);
+        int32_t *slot = malloc(sizeof(int32_t) * (size_t)(topk > 0 ? topk : 1));
+        double *s = malloc(sizeof(double) * (size_t)(topk > 0 ? topk : 1));
+        double *qh = malloc(sizeof(double) * ORACLE_DQK);
+        if (!rows || !slot || !s || !qh || t < 0 || t >= num_tokens) {
+#pragma omp atomic write
+            failed = 1;
+            free(rows); free(slot); free(s); free(qh);
+            continue;
+        }
+
+        /* 1. every list position -> physical slot; decode the valid rows. */
+        for (int64_t j = 0; j < topk; ++j) {
+            slot[j] = smla_oracle_convert_one(req_id_per_token[t], topk_indices[t * topk + j],
+                                              block_table, num_reqs, max_blocks_per_req,
+                                              num_blocks);
+            if (slot[j] < 0)
+                continue;
+            if (cache_format == 1)
+                smla_oracle_decode_fp8_row((const uint8_t *)cache + (int64_t)slot[j] * ORACLE_FP8_ROW,
+                                           rows + j * ORACLE_DQK);
+            else
+                smla_oracle_decode_bf16_row((const uint16_t *)cache + (int64_t)slot[j] * ORACLE_DQK,
+                                            rows + j * ORACLE_DQK);
+        }
+
+        for (int64_t h = 0; h < h_q; ++h) {
+            const uint16_t *qrow = q + (t * h_q + h) * ORACLE_DQK;
+            double *o = out + (i * h_q + h) * ORACLE_DV;
+            double *w = weights ? weights + (i * h_q + h) * topk : NULL;
+            for (int d = 0; d < ORACLE_DQK; ++d)
+                qh[d] = smla_oracle_bf16(qrow[d]);
+
+            /* 2. logits of the valid positions, and their maximum. */
+            double m = -INFINITY;
+            int64_t nvalid = 0;
+            for (int64_t j = 0; j < topk; ++j) {
+                if (slot[j] < 0)
+                    continue;
+                double dot = 0.0;
+                for (int d = 0; d < ORACLE_DQK; ++d)
+                    dot += qh[d] * rows[j * ORACLE_DQK + d];
+                s[j] = sm_scale * dot;
+                if (s[j] > m)
+                    m = s[j];
+                ++nvalid;
+            }
+
+            for (int d = 0; d < ORACLE_DV; ++d)
+                o[d] = 0.0;
+            if (w)
+                for (int64_t j = 0; j < topk; ++j)
+                    w[j] = 0.0;
+            if (nvalid == 0) {
+                lse[i * h_q + h] = -INFINITY;
+                continue;
+            }
+
+            /* 3. softmax normaliser and log-sum-exp. */
+            double l = 0.0;
+            for (int64_t j = 0; j < topk; ++j)
+                if (slot[j] >= 0)
+                    l += exp(s[j] - m);
+            double lse_th = m + log(l);
+            lse[i * h_q + h] = lse_th;
+
+            /* 4. weighted sum of the latent (first 512) columns. */
+            for (int64_t j = 0; j < topk; ++j) {
+                if (slot[j] < 0)
+                    continue;
+                double p = exp(s[j] - lse_th);
+                if (w)
+                    w[j] = p;
+                for (int d = 0; d < ORACLE_DV; ++d)
+                    o[d] += p * rows[j * ORACLE_DQK + d];
+            }
+        }
+        free(rows); free(slot); free(s); free(qh);
+    }
+    return failed ? -1 : 0;
+}

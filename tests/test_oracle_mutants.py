@@ -1,0 +1,49 @@
+"""The oracle's pins must catch plausible mistakes.
+
+Each case copies oracle/smla_oracle.c, plants one mistake by text substitution,
+builds the copy with gcc in a temporary folder, and runs the pin suite against
+it in a subprocess. The suite has to fail for every mutant. Mistakes are only
+ever planted in a CPU copy of the oracle.
+"""
+
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "smla_oracle.c")
+
+MUTANTS = {
+    "scale_group_64": ("scale[i / 128]", "scale[i / 64]"),
+    "scale_offset": ("memcpy(scale, row + 512, sizeof scale);", "memcpy(scale, row + 508, sizeof scale);"),
+    "rope_offset": ("row + 528 + 2 * r", "row + 526 + 2 * r"),
+    "e4m3_bias": ("ldexp(1.0 + (double)m / 8.0, e - 7)", "ldexp(1.0 + (double)m / 8.0, e - 8)"),
+    "e4m3_subnormal": ("ldexp((double)m, -9)", "ldexp((double)m, -10)"),
+    "drop_rope_in_logits": ("for (int d = 0; d < ORACLE_DQK; ++d)\n                    dot +=",
+                            "for (int d = 0; d < ORACLE_DV; ++d)\n                    dot +="),
+    "no_softmax_scale": ("s[j] = sm_scale * dot;", "s[j] = dot;"),
+    "value_columns_shifted": ("o[d] += p * rows[j * ORACLE_DQK + d];", "o[d] += p * rows[j * ORACLE_DQK + d + 64];"),
+    "lse_log2": ("double lse_th = m + log(l);", "double lse_th = m + log2(l);"),
+    "table_width_off_by_one": ("if (blk >= max_blocks_per_req)", "if (blk > max_blocks_per_req)"),
+    "in_block_offset": ("return (int32_t)(base * ORACLE_BLOCK + off);", "return (int32_t)(base * ORACLE_BLOCK + off + 1);"),
+    "weights_unnormalised": ("double p = exp(s[j] - lse_th);", "double p = exp(s[j] - m);"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_reject_mutant(name, tmp_path):
+    old, new = MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation anchor for {name} not unique in the oracle"
+    mutant_c = tmp_path / "mutant.c"
+    mutant_c.write_text(src.replace(old, new))
+    so = tmp_path / "libmutant.so"
+    subprocess.run(["gcc", "-std=c11", "-O2", "-fPIC", "-shared", "-fopenmp", str(mutant_c),
+                    "-o", str(so), "-lm"], check=True)
+    env = dict(os.environ, SMLA_ORACLE_LIB=str(so))
+    r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider",
+                        os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+    assert r.returncode != 0, f"mutant {name} passed every pin:\n{r.stdout[-2000:]}"

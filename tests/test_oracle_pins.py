@@ -1,0 +1,320 @@
+"""Pins for the CPU oracle: each check ties it to something other than itself.
+
+- value decoding: hand-worked OCP E4M3 values, every code against torch's
+  float8_e4m3fn cast, bf16 widening against torch, a hand-worked fp8_ds_mla row,
+  and random rows against a torch library decode;
+- index conversion: hand-worked cases, and a paged-cache writer simulation that
+  places tokens by appending (never by dividing by the block size);
+- attention: the dense special case against torch's scaled_dot_product_attention
+  and logsumexp in float64, closed forms (one slot, q = 0, duplicates, no slot),
+  and the invariants (-1 slots add nothing, order does not matter, weights sum to
+  one, weights equal exp(s - lse), a split of the list merges back to the whole).
+
+The pages are the vLLM flashmla_sparse.py backend source (cache-format note,
+triton_convert_req_index_to_global_index, FlashMLASparseImpl.forward).
+"""
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from sparse_mla_attention_indices_amd import workloads as W
+from tests.paged_writer import PagedCache
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+# ------------------------------------------------------------ value decoding
+
+def test_e4m3_hand_worked_values():
+    g = _golden("e4m3_spec_values.json")
+    for code, want in g["cases"]:
+        got = oracle.e4m3fn(code)
+        if want == "nan":
+            assert math.isnan(got), code
+        else:
+            assert got == want, (code, got, want)
+            assert math.copysign(1.0, got) == math.copysign(1.0, want), code
+
+
+def test_e4m3_every_code_matches_torch():
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    ref = codes.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = np.array([oracle.e4m3fn(c) for c in range(256)])
+    nan = np.isnan(ref)
+    assert np.array_equal(nan, np.isnan(got))
+    assert np.array_equal(ref[~nan], got[~nan])
+    assert np.array_equal(np.signbit(ref[~nan]), np.signbit(got[~nan]))
+
+
+def test_bf16_widening_matches_torch():
+    rng = np.random.default_rng(1)
+    bits = rng.integers(0, 1 << 16, size=4096, dtype=np.uint16)
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    got = np.array([oracle.bf16(int(b)) for b in bits])
+    nan = np.isnan(ref)
+    assert np.array_equal(nan, np.isnan(got))
+    assert np.array_equal(ref[~nan], got[~nan])
+
+
+def test_fp8_row_hand_worked():
+    g = _golden("fp8_row_example.json")
+    row = np.zeros(656, dtype=np.uint8)
+    for grp, code in enumerate(g["latent_code_per_group"]):
+        row[128 * grp:128 * (grp + 1)] = code
+    row[512:528] = np.array(g["scales"], dtype="<f4").view(np.uint8)
+    rope = np.array(g["rope_bits_even_odd"] * 32, dtype="<u2")
+    row[528:656] = rope.view(np.uint8)
+    got = oracle.decode_fp8_rows(row[None])[0]
+    want = np.concatenate([np.repeat(g["expected_latent_per_group"], 128),
+                           np.array(g["expected_rope_even_odd"] * 32)])
+    assert np.array_equal(got, want)
+
+
+def torch_decode_fp8(rows: np.ndarray) -> np.ndarray:
+    """Library decode of fp8_ds_mla rows: torch's e4m3fn and bf16 views."""
+    rows = np.ascontiguousarray(rows, dtype=np.uint8).reshape(-1, 656)
+    t = torch.from_numpy(rows)
+    lat = t[:, :512].contiguous().view(torch.float8_e4m3fn).to(torch.float64)
+    scale = t[:, 512:528].contiguous().view(torch.float32).to(torch.float64)
+    rope = t[:, 528:].contiguous().view(torch.bfloat16).to(torch.float64)
+    return torch.cat([lat * scale.repeat_interleave(128, dim=1), rope], dim=1).numpy()
+
+
+def torch_decode_bf16(rows: np.ndarray) -> np.ndarray:
+    rows = np.ascontiguousarray(rows, dtype=np.uint16).reshape(-1, 576)
+    return torch.from_numpy(rows.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+
+
+def test_fp8_rows_match_torch_decode():
+    gen = W._tgen(7, 99)
+    lat = torch.randn((300, 512), generator=gen) * 3.0
+    rope = W.normal_bf16(gen, (300, 64))
+    rows = W.pack_fp8_rows(lat, rope, gen)
+    assert np.array_equal(oracle.decode_fp8_rows(rows), torch_decode_fp8(rows))
+
+
+def test_bf16_rows_match_torch_decode():
+    rows = W.normal_bf16(W._tgen(7, 98), (50, 576))
+    assert np.array_equal(oracle.decode_bf16_rows(rows), torch_decode_bf16(rows))
+
+
+# ---------------------------------------------------------- index conversion
+
+def test_convert_hand_worked_cases():
+    g = _golden("index_convert_cases.json")
+    got = oracle.convert_indices(np.array(g["req_id_per_token"]), np.array(g["block_table"]),
+                                 np.array(g["topk_indices"]), g["num_blocks"])
+    assert got.tolist() == g["expected"]
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_convert_finds_the_writers_slot(seed):
+    rng = np.random.default_rng(seed)
+    ctx = rng.integers(1, 700, size=5)
+    pc = PagedCache(rng, ctx, extra_blocks=3, max_blocks_per_req=int(max(-(-ctx // 64))) + 2)
+    # marker cache: every slot records which (request, position) the writer put there
+    marker = np.full((pc.num_blocks, 64, 2), -7, dtype=np.int64)
+    for (r, p), (b, off) in pc.where.items():
+        marker[b, off] = (r, p)
+    T, K = 12, 40
+    req = rng.integers(0, len(ctx), size=T).astype(np.int32)
+    idx = np.empty((T, K), dtype=np.int32)
+    for t in range(T):
+        idx[t] = rng.integers(0, ctx[req[t]], size=K)
+    idx[rng.random((T, K)) < 0.2] = -1
+    idx[0, 0] = pc.block_table.shape[1] * 64          # first block position past the table
+    idx[1, 1] = -64
+    slots = oracle.convert_indices(req, pc.block_table, idx, pc.num_blocks)
+    flat = marker.reshape(-1, 2)
+    for t in range(T):
+        for j in range(K):
+            if idx[t, j] < 0 or idx[t, j] >= pc.block_table.shape[1] * 64:
+                assert slots[t, j] == -1
+            else:
+                assert tuple(flat[slots[t, j]]) == (req[t], idx[t, j])
+
+
+# ----------------------------------------------------------------- attention
+
+def _small_problem(rng, fmt, ctx, H=4, T_per_req=2, topk=None, p_invalid=0.0, dense=False):
+    pc = PagedCache(rng, ctx, extra_blocks=2)
+    nb = pc.num_blocks
+    seed = int(rng.integers(1 << 30))
+    if fmt == oracle.BF16_CACHE:
+        cache = W.normal_bf16(W._tgen(seed, 1), (nb, 64, 576))
+    else:
+        gen = W._tgen(seed, 2)
+        lat = torch.randn((nb * 64, 512), generator=gen)
+        rope = W.normal_bf16(gen, (nb * 64, 64))
+        cache = W.pack_fp8_rows(lat, rope, gen).reshape(nb, 64, 656)
+    req = np.repeat(np.arange(len(ctx)), T_per_req).astype(np.int32)
+    T = len(req)
+    q = W.normal_bf16(W._tgen(seed, 3), (T, H, 576))
+    if dense:
+        K = max(ctx)
+        idx = np.full((T, K), -1, dtype=np.int32)
+        for t in range(T):
+            c = ctx[req[t]]
+            idx[t, :c] = rng.permutation(c)
+    else:
+        K = topk
+        idx = np.stack([rng.choice(ctx[r], size=K, replace=False) for r in req]).astype(np.int32)
+        idx[rng.random(idx.shape) < p_invalid] = -1
+    return pc, cache, q, req, idx
+
+
+def _logical_K(pc, cache, fmt, r, positions):
+    rows = pc.logical_rows(cache, r, positions)
+    return torch_decode_bf16(rows) if fmt == oracle.BF16_CACHE else torch_decode_fp8(rows)
+
+
+@pytest.mark.parametrize("fmt", [oracle.BF16_CACHE, oracle.FP8_CACHE])
+def test_dense_special_case_equals_sdpa(fmt):
+    """Top-k = every context position (any order) -> plain dense MQA attention."""
+    rng = np.random.default_rng(11 + fmt)
+    ctx = [150, 77, 64]
+    pc, cache, q, req, idx = _small_problem(rng, fmt, ctx, H=6, dense=True)
+    scale = 1.0 / math.sqrt(576.0)
+    o, lse = oracle.attention(fmt, q, cache, pc.block_table, req, idx, scale)
+    qf = torch_decode_bf16(q.reshape(-1, 576)).reshape(q.shape)
+    for t in range(len(req)):
+        Kt = torch.from_numpy(_logical_K(pc, cache, fmt, req[t], range(ctx[req[t]])))
+        qt = torch.from_numpy(qf[t])                               # [H, 576]
+        H = qt.shape[0]
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            qt[None, :, None, :], Kt[None, None].expand(1, H, -1, -1),
+            Kt[None, None, :, :512].expand(1, H, -1, -1), scale=scale)[0, :, 0]
+        ref_lse = torch.logsumexp(scale * (qt @ Kt.T), dim=1)
+        np.testing.assert_allclose(o[t], ref.numpy(), rtol=1e-9, atol=1e-12)
+        np.testing.assert_allclose(lse[t], ref_lse.numpy(), rtol=1e-12, atol=1e-12)
+
+
+@pytest.fixture(scope="module")
+def sparse_case():
+    rng = np.random.default_rng(5)
+    ctx = [300, 200, 129]
+    pc, cache, q, req, idx = _small_problem(rng, oracle.FP8_CACHE, ctx, H=5, T_per_req=3,
+                                            topk=48, p_invalid=0.15)
+    return rng, pc, cache, q, req, idx
+
+
+def test_invalid_slots_contribute_nothing(sparse_case):
+    rng, pc, cache, q, req, idx = sparse_case
+    o, lse = oracle.attention(1, q, cache, pc.block_table, req, idx, 0.05)
+    # insert extra -1 entries at random places: bit-identical result
+    T, K = idx.shape
+    wide = np.full((T, K + 17), -1, dtype=np.int32)
+    for t in range(T):
+        keep = np.sort(rng.choice(K + 17, size=K, replace=False))
+        wide[t, keep] = idx[t]
+    o2, lse2 = oracle.attention(1, q, cache, pc.block_table, req, wide, 0.05)
+    assert np.array_equal(o, o2) and np.array_equal(lse, lse2)
+
+
+def test_order_of_indices_does_not_matter(sparse_case):
+    rng, pc, cache, q, req, idx = sparse_case
+    o, lse = oracle.attention(1, q, cache, pc.block_table, req, idx, 0.05)
+    perm = np.stack([rng.permutation(row) for row in idx])
+    o2, lse2 = oracle.attention(1, q, cache, pc.block_table, req, perm, 0.05)
+    np.testing.assert_allclose(o2, o, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(lse2, lse, rtol=1e-13, atol=0)
+
+
+def test_weights_sum_to_one_and_match_exp_s_minus_lse(sparse_case):
+    rng, pc, cache, q, req, idx = sparse_case
+    scale = 0.05
+    o, lse, w = oracle.attention(1, q, cache, pc.block_table, req, idx, scale, want_weights=True)
+    np.testing.assert_allclose(w.sum(axis=2), 1.0, rtol=0, atol=1e-13)
+    qf = torch_decode_bf16(q.reshape(-1, 576)).reshape(q.shape)
+    for t in range(len(req)):
+        valid = idx[t] >= 0
+        Kt = _logical_K(pc, cache, 1, req[t], idx[t][valid])
+        s = scale * (qf[t] @ Kt.T)                                 # library matmul, float64
+        np.testing.assert_allclose(w[t][:, valid], np.exp(s - lse[t][:, None]), rtol=1e-11)
+        assert np.all(w[t][:, ~valid] == 0)
+        # and the output is the weighted sum of the latent columns
+        np.testing.assert_allclose(o[t], w[t][:, valid] @ Kt[:, :512], rtol=1e-10, atol=1e-13)
+
+
+@pytest.mark.parametrize("fmt", [oracle.BF16_CACHE, oracle.FP8_CACHE])
+def test_single_valid_slot_returns_that_row(fmt):
+    rng = np.random.default_rng(21)
+    pc, cache, q, req, idx = _small_problem(rng, fmt, [200, 90], H=3, topk=10)
+    idx[:, 1:] = -1
+    o, lse = oracle.attention(fmt, q, cache, pc.block_table, req, idx, 0.07)
+    qf = torch_decode_bf16(q.reshape(-1, 576)).reshape(q.shape)
+    for t in range(len(req)):
+        K1 = _logical_K(pc, cache, fmt, req[t], [idx[t, 0]])[0]
+        assert np.array_equal(o[t], np.broadcast_to(K1[:512], o[t].shape))
+        np.testing.assert_allclose(lse[t], 0.07 * (qf[t] @ K1), rtol=1e-13)
+
+
+def test_zero_query_gives_mean_of_rows_and_log_count(sparse_case):
+    rng, pc, cache, q, req, idx = sparse_case
+    qz = np.zeros_like(q)
+    o, lse = oracle.attention(1, qz, cache, pc.block_table, req, idx, 0.05)
+    for t in range(len(req)):
+        valid = idx[t] >= 0
+        Kt = _logical_K(pc, cache, 1, req[t], idx[t][valid])
+        np.testing.assert_allclose(o[t], np.broadcast_to(Kt[:, :512].mean(axis=0), o[t].shape),
+                                   rtol=1e-12, atol=1e-14)
+        np.testing.assert_allclose(lse[t], math.log(valid.sum()), rtol=1e-14)
+
+
+def test_duplicate_index_counts_per_occurrence():
+    rng = np.random.default_rng(3)
+    pc, cache, q, req, idx = _small_problem(rng, 0, [100], H=2, T_per_req=1, topk=3)
+    idx[0] = [17, 17, 40]
+    o, lse = oracle.attention(0, np.zeros_like(q), cache, pc.block_table, req, idx, 0.1)
+    K = _logical_K(pc, cache, 0, 0, [17, 40])
+    np.testing.assert_allclose(o[0], np.broadcast_to((2 * K[0, :512] + K[1, :512]) / 3, (2, 512)),
+                               rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(lse[0], math.log(3), rtol=1e-14)
+
+
+def test_no_valid_slot_gives_zero_and_minus_inf():
+    rng = np.random.default_rng(4)
+    pc, cache, q, req, idx = _small_problem(rng, 1, [100, 64], H=2, T_per_req=2, topk=5)
+    idx[0] = -1
+    idx[1] = pc.block_table.shape[1] * 64 + 3            # past the block table: all invalid
+    req = req.copy()
+    req[2] = 9                                            # request id outside the table
+    o, lse = oracle.attention(1, q, cache, pc.block_table, req, idx, 0.1)
+    for t in (0, 1, 2):
+        assert np.all(o[t] == 0) and np.all(np.isneginf(lse[t]))
+    assert np.all(np.isfinite(lse[3]))
+
+
+def test_split_halves_merge_to_whole(sparse_case):
+    """Two disjoint halves of a token's list, combined by log-sum-exp weights, give the whole."""
+    rng, pc, cache, q, req, idx = sparse_case
+    o, lse = oracle.attention(1, q, cache, pc.block_table, req, idx, 0.05)
+    K = idx.shape[1]
+    a = idx.copy(); a[:, K // 2:] = -1
+    b = idx.copy(); b[:, :K // 2] = -1
+    oa, la = oracle.attention(1, q, cache, pc.block_table, req, a, 0.05)
+    ob, lb = oracle.attention(1, q, cache, pc.block_table, req, b, 0.05)
+    m = np.maximum(la, lb)
+    wa, wb = np.exp(la - m), np.exp(lb - m)
+    merged = (wa[..., None] * oa + wb[..., None] * ob) / (wa + wb)[..., None]
+    np.testing.assert_allclose(merged, o, rtol=1e-11, atol=1e-14)
+    np.testing.assert_allclose(m + np.log(wa + wb), lse, rtol=1e-13)
+
+
+def test_token_subset_matches_full_run(sparse_case):
+    rng, pc, cache, q, req, idx = sparse_case
+    o, lse = oracle.attention(1, q, cache, pc.block_table, req, idx, 0.05)
+    pick = np.array([4, 0, 7])
+    o2, lse2 = oracle.attention(1, q, cache, pc.block_table, req, idx, 0.05, tokens=pick)
+    assert np.array_equal(o2, o[pick]) and np.array_equal(lse2, lse[pick])
