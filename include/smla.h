@@ -1,0 +1,166 @@
+/*
+ * smla.h -- C ABI of libsmla.so: sparse Multi-head Latent Attention (MLA)
+ * forward over per-token top-k KV indices, for AMD Instinct MI355X (gfx950).
+ *
+ * What it computes. For query token t, head h (h_q heads share ONE latent KV
+ * head), and every valid position j of t's top-k list:
+ *
+ *   slot_j   = block_table[req_id_per_token[t], idx[t,j] / 64] * 64 + idx[t,j] % 64
+ *   K_j      = the 576-wide cache row at slot_j   (512 latent + 64 RoPE values)
+ *   s_j      = sm_scale * <q[t,h,0:576], K_j>
+ *   out[t,h] = sum_j softmax(s)_j * K_j[0:512]    (value = the latent part)
+ *   lse[t,h] = ln sum_j exp(s_j)
+ *
+ * Sources: the vLLM page "vllm/v1/attention/backends/mla/flashmla_sparse.py"
+ * (FLASHMLA_SPARSE backend): triton_convert_req_index_to_global_index and its
+ * docstring (index conversion), the module note on the fp8_ds_mla format
+ * (656-byte rows), FlashMLASparseImpl.forward (both sparse kernels run
+ * multi-query attention with 576-wide keys and 512-wide values),
+ * _fp8_flash_mla_kernel and _bf16_flash_mla_kernel (shapes, head_dim_v 512,
+ * softmax_scale, the second returned value), FlashMLASparseBackend
+ * (block size 64, head size 576, output buffer supplied by the caller).
+ *
+ * Conventions shared by every entry point:
+ *   - All array arguments are DEVICE pointers to contiguous row-major memory
+ *     owned by the caller. The library never allocates, frees, or keeps a
+ *     pointer after the call returns. `options` and the output arguments of
+ *     the query functions (smla_plan, smla_workspace_size) are HOST pointers.
+ *   - Calls are asynchronous on `stream` (0 = the null stream). The library does
+ *     not synchronize and never reads device memory from the host.
+ *   - Every argument is validated before any HIP call; on an error nothing is
+ *     launched and nothing is written.
+ *   - A logical index < 0, a block position >= max_blocks_per_req, a request id
+ *     outside [0, num_reqs) and a block-table entry outside [0, num_blocks) all
+ *     mark the position invalid (slot -1); invalid positions contribute
+ *     nothing. A token/head with no valid position gets out = 0, lse = -inf.
+ *   - Duplicate positions in a list count once per occurrence.
+ *   - Block size is fixed at 64 tokens, q/key width at 576, value width at 512.
+ */
+#ifndef SMLA_H
+#define SMLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SMLA_ABI_VERSION 1
+#define SMLA_BLOCK_SIZE 64
+#define SMLA_HEAD_DIM_QK 576
+#define SMLA_HEAD_DIM_V 512
+#define SMLA_FP8_ROW_BYTES 656
+#define SMLA_MAX_TOPK (1 << 20)
+
+typedef enum smla_status {
+    SMLA_OK = 0,
+    SMLA_ERR_NULL = 1,      /* a required pointer is NULL                        */
+    SMLA_ERR_SHAPE = 2,     /* unsupported size (h_q, topk, counts, pool size)   */
+    SMLA_ERR_ALIGN = 3,     /* a pointer is not aligned as documented            */
+    SMLA_ERR_WORKSPACE = 4, /* workspace missing or smaller than required        */
+    SMLA_ERR_HIP = 5,       /* a HIP runtime call or kernel launch failed        */
+    SMLA_ERR_ARG = 6        /* invalid scalar argument or option                 */
+} smla_status;
+
+/* Tuning options (host struct, may be NULL for defaults). */
+typedef struct smla_options {
+    int32_t num_splits;     /* 0 = automatic; > 0 = split every token's top-k
+                               list into this many parts (capped at topk), each
+                               part computed by its own workgroups and merged by
+                               log-sum-exp weights. */
+    int32_t reserved[7];    /* must be zero */
+} smla_options;
+
+/* Human-readable name of a status code (static string). */
+const char *smla_status_string(smla_status status);
+
+/* SMLA_ABI_VERSION of the loaded library. */
+int32_t smla_abi_version(void);
+
+/* Split plan and workspace size for an attention call, by host arithmetic
+ * alone (no HIP call): num_cus is the device's compute-unit count (256 on
+ * MI355X). Writes the number of top-k splits per token and the workspace bytes
+ * an attention call with these sizes needs. Errors: SMLA_ERR_NULL,
+ * SMLA_ERR_SHAPE, SMLA_ERR_ARG as for the attention calls. */
+smla_status smla_plan(int32_t num_tokens, int32_t h_q, int32_t topk, int32_t num_cus,
+                      const smla_options *options, int32_t *num_splits,
+                      size_t *workspace_bytes);
+
+/* Workspace bytes an attention call with these sizes and options needs on the
+ * CURRENT device (its compute-unit count enters the split plan). Writes 0 when
+ * no top-k split is planned. Errors as for the attention calls; SMLA_ERR_HIP if
+ * the device cannot be queried. */
+smla_status smla_workspace_size(int32_t num_tokens, int32_t h_q, int32_t topk,
+                                const smla_options *options, size_t *workspace_bytes);
+
+/* Logical-to-physical index conversion alone [flashmla_sparse.py page,
+ * triton_convert_req_index_to_global_index and docstring]:
+ *   out[t,j] = block_table[req_id_per_token[t], topk_indices[t,j] / 64] * 64
+ *              + topk_indices[t,j] % 64,  or -1 for an invalid position.
+ * req_id_per_token int32 [num_tokens]; block_table int32 [num_reqs,
+ * max_blocks_per_req]; topk_indices int32 [num_tokens, topk]; out int32
+ * [num_tokens, topk]. All 4-byte aligned. num_blocks (the pool size in blocks)
+ * must satisfy num_blocks * 64 <= INT32_MAX. Any topk >= 1 (no multiple-of-128
+ * restriction). num_tokens == 0 is a no-op. */
+smla_status smla_convert_indices(const int32_t *req_id_per_token, const int32_t *block_table,
+                                 const int32_t *topk_indices, int32_t *out,
+                                 int32_t num_tokens, int32_t topk, int32_t num_reqs,
+                                 int32_t max_blocks_per_req, int64_t num_blocks,
+                                 hipStream_t stream);
+
+/* Sparse MLA forward over a bf16 paged cache [flashmla_sparse.py page,
+ * _bf16_flash_mla_kernel / flash_mla_sparse_prefill].
+ *
+ *   q                 bf16 [num_tokens, h_q, 576]   (absorbed latent 512 ++ RoPE 64), 16-B aligned
+ *   kv_cache          bf16 [num_blocks, 64, 576]    16-B aligned
+ *   block_table       int32 [num_reqs, max_blocks_per_req]
+ *   req_id_per_token  int32 [num_tokens]
+ *   topk_indices      int32 [num_tokens, topk], logical positions, -1 = invalid
+ *   sm_scale          softmax scale, finite and > 0 (e.g. 1/sqrt(576))
+ *   h_q               16, 32, 64 or 128
+ *   out               bf16 [num_tokens, h_q, 512], 16-B aligned, every element written
+ *   lse               fp32 [num_tokens, h_q] natural-log LSE of the scaled logits; may be NULL
+ *   phys_indices_out  int32 [num_tokens, topk] converted slots (-1 = invalid), bit-identical
+ *                     to smla_convert_indices; may be NULL
+ *   workspace         device scratch for the partial results of a top-k split,
+ *                     256-B aligned, contents need not be initialised; may be NULL when
+ *                     smla_workspace_size reports 0 bytes for these sizes
+ *   workspace_bytes   capacity of `workspace` in bytes (SMLA_ERR_WORKSPACE if too small)
+ *   options           host pointer or NULL; the same options must be given to
+ *                     smla_workspace_size
+ * Any mix of decode, speculative-decode and prefill tokens may share one call.
+ */
+smla_status smla_prefill_bf16(const void *q, const void *kv_cache, const int32_t *block_table,
+                              const int32_t *req_id_per_token, const int32_t *topk_indices,
+                              float sm_scale, int32_t num_tokens, int32_t h_q, int32_t topk,
+                              int32_t num_reqs, int32_t max_blocks_per_req, int64_t num_blocks,
+                              void *out, float *lse, int32_t *phys_indices_out,
+                              void *workspace, size_t workspace_bytes,
+                              const smla_options *options, hipStream_t stream);
+
+/* Sparse MLA forward over an fp8_ds_mla paged cache [flashmla_sparse.py page,
+ * module note on the 656-byte format, _fp8_flash_mla_kernel /
+ * flash_mla_with_kvcache with is_fp8_kvcache and indices].
+ *
+ *   kv_cache  uint8 [num_blocks, 64, 656], 16-B aligned; each row is 512 OCP E4M3FN latent
+ *             bytes, 4 little-endian fp32 scales (scale i multiplies latent values
+ *             128*i .. 128*i+127), 64 bf16 RoPE values.
+ * Every other argument as for smla_prefill_bf16. The rows are dequantised inside
+ * the kernel as they are gathered; no staging copy of the cache is made.
+ */
+smla_status smla_decode_fp8(const void *q, const void *kv_cache, const int32_t *block_table,
+                            const int32_t *req_id_per_token, const int32_t *topk_indices,
+                            float sm_scale, int32_t num_tokens, int32_t h_q, int32_t topk,
+                            int32_t num_reqs, int32_t max_blocks_per_req, int64_t num_blocks,
+                            void *out, float *lse, int32_t *phys_indices_out,
+                            void *workspace, size_t workspace_bytes,
+                            const smla_options *options, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SMLA_H */

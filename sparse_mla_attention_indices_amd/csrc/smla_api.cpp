@@ -1,0 +1,273 @@
+// smla_api.cpp -- the C ABI declared in include/smla.h: argument validation,
+// the split planner and the workspace contract. Every check runs before the
+// first HIP call, so invalid calls fail without touching a device.
+
+#include <math.h>
+#include <stdint.h>
+
+#include <algorithm>
+#include <mutex>
+
+#include "../../include/smla.h"
+#include "smla_internal.h"
+
+namespace smla {
+
+static size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+Plan make_plan(int num_tokens, int h_q, int topk, int num_cus, int forced_splits)
+{
+    Plan p{};
+    p.head_blocks = h_q >= kHeadsPerGroup ? h_q / kHeadsPerGroup : 1;
+    int splits = 1;
+    if (forced_splits > 0) {
+        splits = std::min(forced_splits, topk);
+    } else {
+        // One workgroup per (token, head block) when that fills the chip;
+        // otherwise cut each token's list so the grid covers every CU once.
+        const int64_t units = (int64_t)num_tokens * p.head_blocks;
+        const int64_t tiles = (topk + kBlock - 1) / kBlock;
+        if (units > 0 && units < num_cus)
+            splits = (int)std::min<int64_t>(tiles, (num_cus + units - 1) / units);
+        splits = std::max(splits, 1);
+    }
+    p.split_len = (topk + splits - 1) / splits;
+    p.num_splits = (topk + p.split_len - 1) / p.split_len;
+    if (p.num_splits > 1) {
+        const size_t rows = (size_t)num_tokens * p.num_splits * h_q;
+        p.part_o_off = 0;
+        p.part_lse_off = align_up(rows * kDv * sizeof(float), 256);
+        p.workspace = align_up(p.part_lse_off + rows * sizeof(float), 256);
+    }
+    return p;
+}
+
+namespace {
+
+bool aligned(const void *ptr, size_t a) { return ((uintptr_t)ptr % a) == 0; }
+
+smla_status check_options(const smla_options *o)
+{
+    if (o == nullptr)
+        return SMLA_OK;
+    if (o->num_splits < 0)
+        return SMLA_ERR_ARG;
+    for (int i = 0; i < 7; ++i)
+        if (o->reserved[i] != 0)
+            return SMLA_ERR_ARG;
+    return SMLA_OK;
+}
+
+smla_status check_sizes(int32_t num_tokens, int32_t h_q, int32_t topk)
+{
+    if (h_q != 16 && h_q != 32 && h_q != 64 && h_q != 128)
+        return SMLA_ERR_SHAPE;
+    if (num_tokens < 0 || topk < 1 || topk > SMLA_MAX_TOPK)
+        return SMLA_ERR_SHAPE;
+    return SMLA_OK;
+}
+
+smla_status check_pool(int32_t num_reqs, int32_t max_blocks_per_req, int64_t num_blocks)
+{
+    if (num_reqs < 1 || max_blocks_per_req < 1 || num_blocks < 1)
+        return SMLA_ERR_SHAPE;
+    if (num_blocks > (int64_t)INT32_MAX / kBlock)   // slots are int32
+        return SMLA_ERR_SHAPE;
+    return SMLA_OK;
+}
+
+// Compute units of the current device, cached per device id.
+smla_status device_cus(int *cus)
+{
+    static std::mutex mu;
+    static int cache[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0)
+        return SMLA_ERR_HIP;
+    std::lock_guard<std::mutex> lock(mu);
+    if (dev < 64 && cache[dev] > 0) {
+        *cus = cache[dev];
+        return SMLA_OK;
+    }
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+        return SMLA_ERR_HIP;
+    if (dev < 64)
+        cache[dev] = n;
+    *cus = n;
+    return SMLA_OK;
+}
+
+smla_status attention_entry(CacheFormat fmt, const void *q, const void *kv_cache,
+                            const int32_t *block_table, const int32_t *req_id_per_token,
+                            const int32_t *topk_indices, float sm_scale, int32_t num_tokens,
+                            int32_t h_q, int32_t topk, int32_t num_reqs,
+                            int32_t max_blocks_per_req, int64_t num_blocks, void *out, float *lse,
+                            int32_t *phys_indices_out, void *workspace, size_t workspace_bytes,
+                            const smla_options *options, hipStream_t stream)
+{
+    smla_status st = check_options(options);
+    if (st != SMLA_OK)
+        return st;
+    if (!(sm_scale > 0.f) || !isfinite(sm_scale))
+        return SMLA_ERR_ARG;
+    if ((st = check_sizes(num_tokens, h_q, topk)) != SMLA_OK)
+        return st;
+    if ((st = check_pool(num_reqs, max_blocks_per_req, num_blocks)) != SMLA_OK)
+        return st;
+    if (num_tokens == 0)
+        return SMLA_OK;
+    if (!q || !kv_cache || !block_table || !req_id_per_token || !topk_indices || !out)
+        return SMLA_ERR_NULL;
+    if (!aligned(q, 16) || !aligned(kv_cache, 16) || !aligned(out, 16))
+        return SMLA_ERR_ALIGN;
+    if (!aligned(block_table, 4) || !aligned(req_id_per_token, 4) || !aligned(topk_indices, 4) ||
+        !aligned(lse, 4) || !aligned(phys_indices_out, 4) || !aligned(workspace, 256))
+        return SMLA_ERR_ALIGN;
+    const int forced = options ? options->num_splits : 0;
+
+    int cus = 0;
+    if ((st = device_cus(&cus)) != SMLA_OK)
+        return st;
+    const Plan plan = make_plan(num_tokens, h_q, topk, cus, forced);
+    if (plan.workspace > 0 && (workspace == nullptr || workspace_bytes < plan.workspace))
+        return SMLA_ERR_WORKSPACE;
+
+    AttnArgs a;
+    a.q = q;
+    a.cache = kv_cache;
+    a.block_table = block_table;
+    a.req_id = req_id_per_token;
+    a.topk = topk_indices;
+    a.out = out;
+    a.lse = lse;
+    a.phys_out = phys_indices_out;
+    a.workspace = workspace;
+    a.sm_scale = sm_scale;
+    a.num_tokens = num_tokens;
+    a.h_q = h_q;
+    a.topk_len = topk;
+    a.num_reqs = num_reqs;
+    a.max_blocks = max_blocks_per_req;
+    a.num_blocks = num_blocks;
+    return launch_attention(fmt, a, plan, stream) == hipSuccess ? SMLA_OK : SMLA_ERR_HIP;
+}
+
+}  // namespace
+}  // namespace smla
+
+extern "C" {
+
+const char *smla_status_string(smla_status status)
+{
+    switch (status) {
+    case SMLA_OK: return "SMLA_OK";
+    case SMLA_ERR_NULL: return "SMLA_ERR_NULL: a required pointer is NULL";
+    case SMLA_ERR_SHAPE: return "SMLA_ERR_SHAPE: unsupported size";
+    case SMLA_ERR_ALIGN: return "SMLA_ERR_ALIGN: pointer not aligned as required";
+    case SMLA_ERR_WORKSPACE: return "SMLA_ERR_WORKSPACE: workspace too small";
+    case SMLA_ERR_HIP: return "SMLA_ERR_HIP: HIP runtime or launch failure";
+    case SMLA_ERR_ARG: return "SMLA_ERR_ARG: invalid scalar argument or option";
+    }
+    return "unknown smla_status";
+}
+
+int32_t smla_abi_version(void) { return SMLA_ABI_VERSION; }
+
+smla_status smla_plan(int32_t num_tokens, int32_t h_q, int32_t topk, int32_t num_cus,
+                      const smla_options *options, int32_t *num_splits, size_t *workspace_bytes)
+{
+    if (num_splits == nullptr || workspace_bytes == nullptr)
+        return SMLA_ERR_NULL;
+    smla_status st = smla::check_options(options);
+    if (st != SMLA_OK)
+        return st;
+    if ((st = smla::check_sizes(num_tokens, h_q, topk)) != SMLA_OK)
+        return st;
+    if (num_cus < 1)
+        return SMLA_ERR_ARG;
+    if (num_tokens == 0) {
+        *num_splits = 1;
+        *workspace_bytes = 0;
+        return SMLA_OK;
+    }
+    const smla::Plan p = smla::make_plan(num_tokens, h_q, topk, num_cus, options ? options->num_splits : 0);
+    *num_splits = p.num_splits;
+    *workspace_bytes = p.workspace;
+    return SMLA_OK;
+}
+
+smla_status smla_workspace_size(int32_t num_tokens, int32_t h_q, int32_t topk,
+                                const smla_options *options, size_t *workspace_bytes)
+{
+    if (workspace_bytes == nullptr)
+        return SMLA_ERR_NULL;
+    smla_status st = smla::check_options(options);
+    if (st != SMLA_OK)
+        return st;
+    if ((st = smla::check_sizes(num_tokens, h_q, topk)) != SMLA_OK)
+        return st;
+    if (num_tokens == 0) {
+        *workspace_bytes = 0;
+        return SMLA_OK;
+    }
+    int cus = 0;
+    if ((st = smla::device_cus(&cus)) != SMLA_OK)
+        return st;
+    *workspace_bytes =
+        smla::make_plan(num_tokens, h_q, topk, cus, options ? options->num_splits : 0).workspace;
+    return SMLA_OK;
+}
+
+smla_status smla_convert_indices(const int32_t *req_id_per_token, const int32_t *block_table,
+                                 const int32_t *topk_indices, int32_t *out, int32_t num_tokens,
+                                 int32_t topk, int32_t num_reqs, int32_t max_blocks_per_req,
+                                 int64_t num_blocks, hipStream_t stream)
+{
+    if (num_tokens < 0 || topk < 1 || topk > SMLA_MAX_TOPK)
+        return SMLA_ERR_SHAPE;
+    smla_status st = smla::check_pool(num_reqs, max_blocks_per_req, num_blocks);
+    if (st != SMLA_OK)
+        return st;
+    if (num_tokens == 0)
+        return SMLA_OK;
+    if (!req_id_per_token || !block_table || !topk_indices || !out)
+        return SMLA_ERR_NULL;
+    if (!smla::aligned(req_id_per_token, 4) || !smla::aligned(block_table, 4) ||
+        !smla::aligned(topk_indices, 4) || !smla::aligned(out, 4))
+        return SMLA_ERR_ALIGN;
+    return smla::launch_convert(req_id_per_token, block_table, topk_indices, out, num_tokens, topk,
+                                num_reqs, max_blocks_per_req, num_blocks, stream) == hipSuccess
+               ? SMLA_OK
+               : SMLA_ERR_HIP;
+}
+
+smla_status smla_prefill_bf16(const void *q, const void *kv_cache, const int32_t *block_table,
+                              const int32_t *req_id_per_token, const int32_t *topk_indices,
+                              float sm_scale, int32_t num_tokens, int32_t h_q, int32_t topk,
+                              int32_t num_reqs, int32_t max_blocks_per_req, int64_t num_blocks,
+                              void *out, float *lse, int32_t *phys_indices_out, void *workspace,
+                              size_t workspace_bytes, const smla_options *options,
+                              hipStream_t stream)
+{
+    return smla::attention_entry(smla::kCacheBf16, q, kv_cache, block_table, req_id_per_token,
+                                 topk_indices, sm_scale, num_tokens, h_q, topk, num_reqs,
+                                 max_blocks_per_req, num_blocks, out, lse, phys_indices_out,
+                                 workspace, workspace_bytes, options, stream);
+}
+
+smla_status smla_decode_fp8(const void *q, const void *kv_cache, const int32_t *block_table,
+                            const int32_t *req_id_per_token, const int32_t *topk_indices,
+                            float sm_scale, int32_t num_tokens, int32_t h_q, int32_t topk,
+                            int32_t num_reqs, int32_t max_blocks_per_req, int64_t num_blocks,
+                            void *out, float *lse, int32_t *phys_indices_out, void *workspace,
+                            size_t workspace_bytes, const smla_options *options,
+                            hipStream_t stream)
+{
+    return smla::attention_entry(smla::kCacheFp8, q, kv_cache, block_table, req_id_per_token,
+                                 topk_indices, sm_scale, num_tokens, h_q, topk, num_reqs,
+                                 max_blocks_per_req, num_blocks, out, lse, phys_indices_out,
+                                 workspace, workspace_bytes, options, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,60 @@
+// smla_internal.h -- shared between the C-ABI layer (smla_api.cpp) and the HIP
+// kernels (smla_kernels.hip). Not installed; the public interface is
+// include/smla.h.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+namespace smla {
+
+constexpr int kBlock = 64;        // paged-cache block size (tokens per block)
+constexpr int kDqk = 576;         // query/key width: 512 latent + 64 RoPE
+constexpr int kDv = 512;          // value width: the latent part of the row
+constexpr int kFp8RowBytes = 656; // 512 e4m3 + 4 fp32 scales + 64 bf16
+constexpr int kBf16RowBytes = kDqk * 2;
+
+enum CacheFormat { kCacheBf16 = 0, kCacheFp8 = 1 };
+
+// Heads one workgroup covers: 64 (as four waves of 16); h_q = 128 takes two
+// workgroups per token, h_q = 16 / 32 one workgroup whose spare waves split the
+// rows of each tile instead.
+constexpr int kHeadsPerGroup = 64;
+
+struct Plan {
+    int num_splits;      // top-k parts per token
+    int split_len;       // top-k positions per part (the last part may be shorter)
+    int head_blocks;     // workgroups per (token, part) along heads
+    size_t workspace;    // bytes of partial results needed (0 when num_splits == 1)
+    size_t part_o_off;   // byte offsets inside the workspace
+    size_t part_lse_off;
+};
+
+// Host arithmetic only.
+Plan make_plan(int num_tokens, int h_q, int topk, int num_cus, int forced_splits);
+
+struct AttnArgs {
+    const void *q;
+    const void *cache;
+    const int32_t *block_table;
+    const int32_t *req_id;
+    const int32_t *topk;
+    void *out;
+    float *lse;
+    int32_t *phys_out;
+    void *workspace;
+    float sm_scale;
+    int num_tokens, h_q, topk_len, num_reqs, max_blocks;
+    int64_t num_blocks;
+};
+
+// Kernel launchers (smla_kernels.hip). Return hipSuccess or the launch error.
+hipError_t launch_convert(const int32_t *req_id, const int32_t *block_table, const int32_t *topk,
+                          int32_t *out, int num_tokens, int topk_len, int num_reqs,
+                          int max_blocks, int64_t num_blocks, hipStream_t stream);
+
+hipError_t launch_attention(CacheFormat fmt, const AttnArgs &a, const Plan &p, hipStream_t stream);
+
+}  // namespace smla

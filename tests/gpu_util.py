@@ -1,0 +1,78 @@
+"""Helpers for the GPU parity tests: upload a workload, run an entry point,
+compare against the oracle with the tolerances the target states."""
+
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import oracle
+from sparse_mla_attention_indices_amd import smla
+
+# Tolerances, applied separately to o and to the finite lse values.
+TOL = {"bf16": dict(max_abs=1e-2, rel_l2=5e-3), "fp8": dict(max_abs=2e-2, rel_l2=1e-2)}
+
+
+def log(msg: str) -> None:
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def bf16_tensor(bits: np.ndarray, device="cuda") -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(device)
+
+
+class DeviceWorkload:
+    def __init__(self, w, device="cuda"):
+        self.w = w
+        self.q = bf16_tensor(w.q, device)
+        if w.cache_format == "bf16":
+            self.cache = bf16_tensor(w.cache, device)
+        else:
+            self.cache = torch.from_numpy(np.ascontiguousarray(w.cache)).to(device)
+        self.bt = torch.from_numpy(w.block_table).to(device)
+        self.req = torch.from_numpy(w.req_id_per_token).to(device)
+        self.idx = torch.from_numpy(w.topk_indices).to(device)
+
+    def run(self, num_splits=0, with_phys=False):
+        fn = smla.smla_prefill_bf16 if self.w.cache_format == "bf16" else smla.smla_decode_fp8
+        phys = torch.full_like(self.idx, -7) if with_phys else None
+        out, lse = fn(self.q, self.cache, self.bt, self.req, self.idx, self.w.sm_scale,
+                      phys_indices_out=phys, num_splits=num_splits)
+        torch.cuda.synchronize()
+        return out, lse, phys
+
+
+def oracle_run(w, tokens=None):
+    fmt = oracle.BF16_CACHE if w.cache_format == "bf16" else oracle.FP8_CACHE
+    return oracle.attention(fmt, w.q, w.cache, w.block_table, w.req_id_per_token, w.topk_indices,
+                            w.sm_scale, tokens=tokens)
+
+
+def errors(got: np.ndarray, ref: np.ndarray):
+    d = got.astype(np.float64) - ref
+    denom = np.linalg.norm(ref)
+    return float(np.abs(d).max(initial=0.0)), float(np.linalg.norm(d) / denom) if denom > 0 else float(np.linalg.norm(d))
+
+
+def assert_parity(w, out, lse, tokens=None, label=""):
+    """Compare GPU (out bf16 [T,H,512], lse fp32 [T,H]) with the oracle on `tokens`."""
+    o_ref, lse_ref = oracle_run(w, tokens)
+    sel = slice(None) if tokens is None else torch.as_tensor(np.asarray(tokens), device=out.device)
+    o_gpu = out[sel].float().cpu().numpy().astype(np.float64)
+    lse_gpu = lse[sel].cpu().numpy().astype(np.float64)
+    tol = TOL[w.cache_format]
+    assert np.all(np.isfinite(o_gpu)), f"{label}: non-finite output"
+    fin = np.isfinite(lse_ref)
+    assert np.array_equal(fin, np.isfinite(lse_gpu)), f"{label}: lse finiteness differs"
+    assert np.all(np.isneginf(lse_gpu[~fin])), f"{label}: empty rows must have lse = -inf"
+    assert np.all(o_gpu[~fin] == 0), f"{label}: empty rows must have o = 0"
+    o_max, o_rel = errors(o_gpu, o_ref)
+    l_max, l_rel = errors(lse_gpu[fin], lse_ref[fin])
+    log(f"[parity] {label}: o max_abs={o_max:.3e} rel_l2={o_rel:.3e}  "
+        f"lse max_abs={l_max:.3e} rel_l2={l_rel:.3e}")
+    assert o_max <= tol["max_abs"] and o_rel <= tol["rel_l2"], (label, o_max, o_rel)
+    assert l_max <= tol["max_abs"] and l_rel <= tol["rel_l2"], (label, l_max, l_rel)
+    return o_max, o_rel, l_max, l_rel

@@ -1,0 +1,148 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/smla.h declares, plans splits by host arithmetic, and rejects invalid
+arguments before making any HIP call (every call here fails validation, so no
+device is touched)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from sparse_mla_attention_indices_amd import smla
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "smla.h")
+
+A16 = 0x10000          # fake, 256-byte aligned addresses: never dereferenced
+A16B = 0x20000
+MIS = 0x10002          # misaligned
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(smla_\w+)\s*\(", text, re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(smla.LIB_PATH):
+        pytest.fail("libsmla.so not built (run __graft_entry__.build())")
+    return smla.library()
+
+
+def test_exports_every_declared_function(lib):
+    names = declared_functions()
+    assert set(names) == set(smla.EXPORTS), names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_abi_version(lib):
+    assert smla.smla_abi_version() == 1
+
+
+def test_status_strings(lib):
+    for code, name in smla.STATUS_NAMES.items():
+        assert lib.smla_status_string(code).decode().startswith(name)
+
+
+def test_plan_fills_the_chip_for_small_decode_batches(lib):
+    # 64 tokens x 64 heads: one workgroup per token -> 4 top-k splits on 256 CUs
+    s, ws = smla.smla_plan(64, 64, 2048, 256)
+    assert s == 4
+    rows = 64 * 4 * 64
+    lse_off = -(-rows * 512 * 4 // 256) * 256
+    assert ws == -(-(lse_off + rows * 4) // 256) * 256
+    # enough (token, head-block) units already: no split, no workspace
+    assert smla.smla_plan(256, 16, 2048, 256) == (1, 0)
+    assert smla.smla_plan(16384, 128, 2048, 256) == (1, 0)
+    # a split never exceeds the number of 64-row tiles of the list
+    assert smla.smla_plan(1, 64, 100, 256)[0] == 2
+    assert smla.smla_plan(1, 16, 64, 256)[0] == 1
+    # forced splits, capped at topk
+    assert smla.smla_plan(8, 16, 64, 256, num_splits=3)[0] == 3
+    assert smla.smla_plan(8, 16, 5, 256, num_splits=9)[0] == 5
+    assert smla.smla_plan(0, 16, 64, 256) == (1, 0)
+
+
+@pytest.mark.parametrize("args,code", [
+    ((8, 48, 64, 256), 2),     # h_q not supported
+    ((8, 16, 0, 256), 2),      # topk < 1
+    ((-1, 16, 64, 256), 2),    # negative token count
+    ((8, 16, 64, 0), 6),       # no compute units
+])
+def test_plan_rejects(lib, args, code):
+    with pytest.raises(smla.SmlaError) as e:
+        smla.smla_plan(*args)
+    assert e.value.status == code
+
+
+def test_plan_rejects_bad_options(lib):
+    o = smla.SmlaOptions()
+    o.reserved[3] = 1
+    s, b = ctypes.c_int32(), ctypes.c_size_t()
+    assert lib.smla_plan(8, 16, 64, 256, ctypes.byref(o), ctypes.byref(s), ctypes.byref(b)) == 6
+    o = smla.SmlaOptions()
+    o.num_splits = -2
+    assert lib.smla_plan(8, 16, 64, 256, ctypes.byref(o), ctypes.byref(s), ctypes.byref(b)) == 6
+    assert lib.smla_plan(8, 16, 64, 256, None, None, ctypes.byref(b)) == 1
+
+
+def _attn(lib, name="smla_decode_fp8", q=A16, kv=A16, bt=A16, req=A16, idx=A16, scale=0.04,
+          T=8, H=16, K=64, R=2, MB=4, NB=8, out=A16B, lse=A16, phys=None, ws=None, wsb=0, opts=None):
+    return getattr(lib, name)(q, kv, bt, req, idx, scale, T, H, K, R, MB, NB, out, lse, phys,
+                              ws, wsb, opts, None)
+
+
+@pytest.mark.parametrize("name", ["smla_decode_fp8", "smla_prefill_bf16"])
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), 1), (dict(kv=None), 1), (dict(bt=None), 1), (dict(req=None), 1),
+    (dict(idx=None), 1), (dict(out=None), 1),
+    (dict(H=8), 2), (dict(H=96), 2), (dict(K=0), 2), (dict(K=(1 << 20) + 1), 2), (dict(T=-1), 2),
+    (dict(R=0), 2), (dict(MB=0), 2), (dict(NB=0), 2), (dict(NB=(1 << 31) // 64 + 1), 2),
+    (dict(q=MIS), 3), (dict(kv=MIS), 3), (dict(out=MIS), 3), (dict(bt=A16 + 2), 3),
+    (dict(lse=A16 + 1), 3), (dict(phys=A16 + 2), 3), (dict(ws=A16 + 16, wsb=1024), 3),
+    (dict(scale=0.0), 6), (dict(scale=-1.0), 6), (dict(scale=float("inf")), 6),
+    (dict(scale=float("nan")), 6),
+])
+def test_attention_rejects_before_any_hip_call(lib, name, kw, code):
+    assert _attn(lib, name, **kw) == code
+
+
+@pytest.mark.parametrize("name", ["smla_decode_fp8", "smla_prefill_bf16"])
+def test_attention_rejects_bad_options(lib, name):
+    o = smla.SmlaOptions()
+    o.reserved[0] = 5
+    assert _attn(lib, name, opts=ctypes.byref(o)) == 6
+    o = smla.SmlaOptions()
+    o.num_splits = -1
+    assert _attn(lib, name, opts=ctypes.byref(o)) == 6
+
+
+@pytest.mark.parametrize("name", ["smla_decode_fp8", "smla_prefill_bf16"])
+def test_zero_tokens_is_a_noop(lib, name):
+    # no pointer is needed and nothing is launched
+    assert _attn(lib, name, q=None, kv=None, bt=None, req=None, idx=None, out=None, T=0) == 0
+
+
+def test_workspace_size_validation(lib):
+    b = ctypes.c_size_t(123)
+    assert lib.smla_workspace_size(4, 16, 64, None, None) == 1
+    assert lib.smla_workspace_size(4, 20, 64, None, ctypes.byref(b)) == 2
+    assert lib.smla_workspace_size(0, 16, 64, None, ctypes.byref(b)) == 0 and b.value == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(req=None), 1), (dict(out=None), 1), (dict(K=0), 2), (dict(T=-3), 2), (dict(R=0), 2),
+    (dict(NB=(1 << 31) // 64 + 1), 2), (dict(out=A16 + 2), 3), (dict(idx=A16 + 1), 3),
+])
+def test_convert_rejects(lib, kw, code):
+    a = dict(req=A16, bt=A16, idx=A16, out=A16B, T=4, K=7, R=3, MB=3, NB=6)
+    a.update(kw)
+    assert lib.smla_convert_indices(a["req"], a["bt"], a["idx"], a["out"], a["T"], a["K"],
+                                    a["R"], a["MB"], a["NB"], None) == code
+
+
+def test_convert_zero_tokens_is_a_noop(lib):
+    assert lib.smla_convert_indices(None, None, None, None, 0, 7, 3, 3, 6, None) == 0

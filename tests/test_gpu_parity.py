@@ -1,0 +1,200 @@
+"""GPU parity: libsmla.so (through its C ABI) against the CPU oracle.
+
+Index conversion is compared bit for bit. Attention outputs are compared element
+by element with the stated tolerances: bf16 cache max-abs <= 1e-2 and rel-L2 <=
+5e-3, fp8_ds_mla cache max-abs <= 2e-2 and rel-L2 <= 1e-2, for o and for lse.
+Small cases are checked in full; the full-size configurations run exactly as the
+benchmark launches them and are checked on sampled tokens the oracle computes one
+by one.
+"""
+
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from sparse_mla_attention_indices_amd import smla
+from sparse_mla_attention_indices_amd import workloads as W
+from tests.gpu_util import DeviceWorkload, assert_parity, log
+
+pytestmark = pytest.mark.gpu
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+@pytest.fixture(scope="session", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    smla.library()          # fail loudly if the HIP library is missing
+    return torch.device("cuda")
+
+
+def small(seed, fmt, h_q, topk, n_req=3, tok_per_req=3, ctx=(60, 700), p_invalid=0.2, mb_extra=2):
+    rng = np.random.default_rng(seed)
+    ctx_lens = rng.integers(ctx[0], ctx[1], size=n_req)
+    req = np.repeat(np.arange(n_req), tok_per_req)
+    vis = ctx_lens[req]
+    mb = int(max(-(-ctx_lens // 64))) + mb_extra
+    return W.build(f"small_{fmt}_h{h_q}_k{topk}_s{seed}", 1000 + seed, seed, ctx_lens, req, vis,
+                   h_q, topk, fmt, p_invalid=p_invalid, max_blocks_per_req=mb)
+
+
+# ------------------------------------------------------------- index convert
+
+def test_convert_golden_bit_exact():
+    g = json.load(open(os.path.join(GOLDEN, "index_convert_cases.json")))
+    req = torch.tensor(g["req_id_per_token"], dtype=torch.int32, device="cuda")
+    bt = torch.tensor(g["block_table"], dtype=torch.int32, device="cuda")
+    idx = torch.tensor(g["topk_indices"], dtype=torch.int32, device="cuda")
+    out = smla.smla_convert_indices(req, bt, idx, g["num_blocks"])
+    torch.cuda.synchronize()
+    assert out.cpu().tolist() == g["expected"]
+
+
+@pytest.mark.parametrize("T,K", [(1, 1), (37, 129), (300, 777)])
+def test_convert_random_bit_exact(T, K):
+    rng = np.random.default_rng(T * 1000 + K)
+    R, MB, NB = 9, 13, 50
+    bt = rng.integers(-3, NB + 3, size=(R, MB)).astype(np.int32)     # includes bad entries
+    req = rng.integers(-1, R + 1, size=T).astype(np.int32)           # includes bad request ids
+    idx = rng.integers(-70, MB * 64 + 70, size=(T, K)).astype(np.int32)
+    want = oracle.convert_indices(req, bt, idx, NB)
+    got = smla.smla_convert_indices(torch.from_numpy(req).cuda(), torch.from_numpy(bt).cuda(),
+                                    torch.from_numpy(idx).cuda(), NB)
+    torch.cuda.synchronize()
+    assert np.array_equal(got.cpu().numpy(), want)
+
+
+# ------------------------------------------------------------ small matrix
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+@pytest.mark.parametrize("h_q", [16, 32, 64, 128])
+@pytest.mark.parametrize("topk", [1, 37, 64, 100, 200])
+def test_small_parity(fmt, h_q, topk):
+    w = small(h_q + topk, fmt, h_q, topk)
+    dw = DeviceWorkload(w)
+    want_phys = oracle.convert_indices(w.req_id_per_token, w.block_table, w.topk_indices, w.num_blocks)
+    for splits in (0, 1, 3):
+        log(f"[case] small {fmt} h_q={h_q} topk={topk} splits={splits}")
+        out, lse, phys = dw.run(num_splits=splits, with_phys=True)
+        assert np.array_equal(phys.cpu().numpy(), want_phys)
+        assert_parity(w, out, lse, label=f"small {fmt} h{h_q} k{topk} s{splits}")
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+def test_long_list_crosses_the_lds_chunk(fmt):
+    """topk 5000 > 2048 positions per LDS round, ragged tail, one split and several."""
+    w = small(7, fmt, 64, 5000, n_req=2, tok_per_req=2, ctx=(6000, 9000), p_invalid=0.1)
+    dw = DeviceWorkload(w)
+    for splits in (1, 2, 0):
+        log(f"[case] long list {fmt} splits={splits}")
+        out, lse, _ = dw.run(num_splits=splits)
+        assert_parity(w, out, lse, label=f"long {fmt} s{splits}")
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+def test_degenerate_rows(fmt):
+    """Whole tokens without a valid slot, bad request ids, bad table entries, duplicates."""
+    w = small(11, fmt, 32, 96, n_req=3, tok_per_req=4, ctx=(100, 300), p_invalid=0.3)
+    w.topk_indices[0, :] = -1                              # nothing valid
+    w.topk_indices[1, :] = w.max_blocks_per_req * 64 + 5   # past the table: nothing valid
+    w.req_id_per_token[2] = w.num_reqs + 4                 # request id outside the table
+    w.block_table[1, 0] = -1                               # bad entries in request 1's table
+    w.block_table[1, 1] = w.num_blocks + 10
+    w.topk_indices[5, :10] = w.topk_indices[5, 10]         # duplicates count per occurrence
+    w.topk_indices[6, :] = -1
+    w.topk_indices[6, 50] = 3                              # exactly one valid slot
+    dw = DeviceWorkload(w)
+    for splits in (0, 2):
+        log(f"[case] degenerate {fmt} splits={splits}")
+        out, lse, phys = dw.run(num_splits=splits, with_phys=True)
+        want = oracle.convert_indices(w.req_id_per_token, w.block_table, w.topk_indices, w.num_blocks)
+        assert np.array_equal(phys.cpu().numpy(), want)
+        assert_parity(w, out, lse, label=f"degenerate {fmt} s{splits}")
+
+
+def test_zero_tokens_writes_nothing():
+    w = small(3, "fp8", 16, 64)
+    dw = DeviceWorkload(w)
+    out = torch.full((0, 16, 512), 1.0, dtype=torch.bfloat16, device="cuda")
+    o, l = smla.smla_decode_fp8(dw.q[:0], dw.cache, dw.bt, dw.req[:0], dw.idx[:0], w.sm_scale, out=out)
+    torch.cuda.synchronize()
+    assert o.numel() == 0
+
+
+def test_repeat_calls_are_bit_identical():
+    w = W.config1_fp8()
+    dw = DeviceWorkload(w)
+    a, la, _ = dw.run(num_splits=2)
+    b, lb, _ = dw.run(num_splits=2)
+    assert torch.equal(a, b) and torch.equal(la, lb)
+
+
+# ------------------------------------------------------------ named configs
+
+@pytest.mark.parametrize("maker", [W.config1, W.config1_fp8])
+def test_config1(maker):
+    w = maker()
+    dw = DeviceWorkload(w)
+    want_phys = oracle.convert_indices(w.req_id_per_token, w.block_table, w.topk_indices, w.num_blocks)
+    for splits in (0, 2, 3):
+        log(f"[case] {w.name} splits={splits}")
+        out, lse, phys = dw.run(num_splits=splits, with_phys=True)
+        assert np.array_equal(phys.cpu().numpy(), want_phys)
+        assert_parity(w, out, lse, label=f"{w.name} s{splits}")
+
+
+@pytest.fixture(scope="module")
+def c2():
+    return W.config2()
+
+
+def test_config2_fp8_decode_full(c2):
+    """The headline decode batch in the benchmark's launch configuration, every token checked."""
+    dw = DeviceWorkload(c2)
+    log("[case] config2 full")
+    out, lse, phys = dw.run(with_phys=True)
+    want = oracle.convert_indices(c2.req_id_per_token, c2.block_table, c2.topk_indices, c2.num_blocks)
+    assert np.array_equal(phys.cpu().numpy(), want)
+    assert_parity(c2, out, lse, label="config2 (64 tok, h64, k2048, fp8)")
+
+
+def _sample_tokens(T, rng, extra=()):
+    pick = set(int(x) for x in extra if 0 <= x < T)
+    pick.update(int(x) for x in rng.choice(T, size=min(T, 24), replace=False))
+    return np.array(sorted(pick), dtype=np.int64)
+
+
+def test_config3_bf16_prefill_sampled():
+    w = W.config3()
+    dw = DeviceWorkload(w)
+    log("[case] config3 full size")
+    out, lse, _ = dw.run()
+    # both ends of the causal ramp, the -1 / full boundary, and the last positions
+    edges = [0, 1, 2, 63, 64, 2046, 2047, 2048, 4095, 4096, 4097, 6143, 16383]
+    tokens = _sample_tokens(w.num_tokens, np.random.default_rng(3), edges)
+    assert_parity(w, out, lse, tokens=tokens, label="config3 (16384 tok, h128, k2048, bf16) sampled")
+
+
+@pytest.mark.parametrize("topk", [512, 1024, 2048])
+def test_config4_spec_decode(topk):
+    w = W.config4(topk=topk)
+    dw = DeviceWorkload(w)
+    log(f"[case] config4 topk={topk}")
+    out, lse, _ = dw.run()
+    tokens = None if topk == 512 else _sample_tokens(w.num_tokens, np.random.default_rng(topk), [0, 1, 255])
+    assert_parity(w, out, lse, tokens=tokens, label=f"config4 (256 tok, h16, k{topk}, fp8)")
+
+
+def test_config5_long_mixed_sampled():
+    w = W.config5()
+    dw = DeviceWorkload(w)
+    log("[case] config5 full size")
+    out, lse, _ = dw.run()
+    edges = list(range(32)) + [32, 33, 2079, 2080, 2081, 4127]
+    tokens = _sample_tokens(w.num_tokens, np.random.default_rng(5), edges)
+    assert_parity(w, out, lse, tokens=tokens, label="config5 (4128 tok, h128, k2048, fp8) sampled")
