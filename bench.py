@@ -1,0 +1,249 @@
+"""Benchmark: sparse MLA fp8 decode on one MI355X.
+
+Workload (the headline decode batch): 64 decode tokens, one per request, contexts
+U{4096..8192}, h_q = 64, top-k = 2048 distinct positions per token, fp8_ds_mla
+paged cache (656-byte rows, block size 64, shuffled block table), bf16 q. One
+step = one smla_decode_fp8 call over the whole batch (index conversion, gather +
+dequant, QK^T, softmax, PV, split merge), inputs already resident in HBM.
+
+Cold-cache timing: before every timed step a 1 GiB buffer is overwritten
+(outside the timed events) so neither L2 nor the 256 MB MALL holds the 95 MB
+working set; each step is bracketed by HIP events on the stream the library
+launches on. Warm-cache throughput (back-to-back calls) is reported beside it.
+
+Prints ONE JSON line. `python bench.py --gpus N --steps K --warmup W`.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "sparse-MLA fp8 decode query-tokens/s & TFLOP/s (h_q=64, topk=2048), % roofline"
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2516.6        # MI355X dense bf16 MFMA, published
+CSRC = os.path.join(ROOT, "sparse_mla_attention_indices_amd", "csrc")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_attn_fp8_decode_c2.json")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_work(w):
+    """Bytes the path must move at minimum and the flops it must do.
+
+    Bytes: unique cache rows read (every valid (request, position) once), q, o,
+    lse, the logical indices, the block-table rows of the requests used, and
+    req_id. Split partials, converted indices and line over-fetch are costs of an
+    implementation, not of the method. Flops: 2 * h_q * (576 + 512) per valid slot.
+    """
+    idx = w.topk_indices
+    valid = idx >= 0
+    n_valid = int(valid.sum())
+    pairs = np.unique((w.req_id_per_token[:, None].astype(np.int64) << 32 | idx.astype(np.int64))[valid])
+    row_bytes = 656 if w.cache_format == "fp8" else 1152
+    T, H, K = w.num_tokens, w.h_q, w.topk
+    reqs = np.unique(w.req_id_per_token)
+    by = {
+        "cache_rows": int(pairs.size) * row_bytes,
+        "q": T * H * 576 * 2,
+        "out": T * H * 512 * 2,
+        "lse": T * H * 4,
+        "indices": T * K * 4,
+        "block_table_rows": int(reqs.size) * w.max_blocks_per_req * 4,
+        "req_id": T * 4,
+    }
+    flops = 2 * H * (576 + 512) * n_valid
+    return sum(by.values()), flops, by, n_valid
+
+
+def cpu_baseline(w, target_s: float = 10.0):
+    """The oracle as it stands, on this host's cores: whole passes over the batch's
+    tokens (in a fixed shuffled order) until about target_s of CPU work is done."""
+    import oracle
+    threads = oracle.num_threads()
+    order = np.random.default_rng(0).permutation(w.num_tokens)
+    n = max(1, min(w.num_tokens, threads))
+    done, t_total, passes = 0, 0.0, 0
+    while t_total < target_s and passes < 100:
+        for s in range(0, w.num_tokens, n):
+            tok = order[s:s + n]
+            t0 = time.perf_counter()
+            oracle.attention(oracle.FP8_CACHE, w.q, w.cache, w.block_table, w.req_id_per_token,
+                             w.topk_indices, w.sm_scale, tokens=tok)
+            t_total += time.perf_counter() - t0
+            done += len(tok)
+            if t_total >= target_s:
+                break
+        passes += 1
+    return {"value": done / t_total, "unit": "query-tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{done} token evaluations ({passes} pass(es) over the batch's {w.num_tokens} "
+                      f"tokens, all {w.h_q} heads, top-k {w.topk}), float64 C + OpenMP, "
+                      f"{t_total:.1f} s"}
+
+
+def traffic_from_profile():
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or None if the
+    kernel sources changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            d = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if d.get("source_hash") != kernel_source_hash():
+        return None
+    return d.get("traffic_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calib", action="store_true",
+                    help="run only a plain device copy of known size (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(this library has no multi-GPU path)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from sparse_mla_attention_indices_amd import smla
+    from sparse_mla_attention_indices_amd import workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+
+    if args.copy_calib:
+        src = torch.ones(256 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calib_bytes": src.numel(), "launches": 5}), flush=True)
+        return
+
+    w = W.config2(args.seed)
+    q = torch.from_numpy(w.q.view(np.int16)).view(torch.bfloat16).to(dev)
+    cache = torch.from_numpy(w.cache).to(dev)
+    bt = torch.from_numpy(w.block_table).to(dev)
+    req = torch.from_numpy(w.req_id_per_token).to(dev)
+    idx = torch.from_numpy(w.topk_indices).to(dev)
+    out = torch.empty((w.num_tokens, w.h_q, 512), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((w.num_tokens, w.h_q), dtype=torch.float32, device=dev)
+    ws_bytes = smla.smla_workspace_size(w.num_tokens, w.h_q, w.topk)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    props = torch.cuda.get_device_properties(dev)
+    splits, _ = smla.smla_plan(w.num_tokens, w.h_q, w.topk, props.multi_processor_count)
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+
+    def step():
+        smla.smla_decode_fp8(q, cache, bt, req, idx, w.sm_scale, out=out, lse=lse, workspace=ws,
+                             stream=stream)
+
+    for i in range(args.warmup):
+        flush.fill_(i & 0xFF)
+        step()
+    torch.cuda.synchronize()
+
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    for i in range(args.steps):
+        flush.fill_((i + 7) & 0xFF)
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    cold_ms = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
+
+    # warm cache: back-to-back calls, working set resident in MALL
+    w0 = torch.cuda.Event(enable_timing=True)
+    w1 = torch.cuda.Event(enable_timing=True)
+    for _ in range(3):
+        step()
+    w0.record(stream)
+    for _ in range(args.steps):
+        step()
+    w1.record(stream)
+    torch.cuda.synchronize()
+    warm_ms = w0.elapsed_time(w1) / args.steps
+
+    bytes_alg, flops, by, n_valid = algorithmic_work(w)
+    ms = float(cold_ms.mean())
+    tok_s = w.num_tokens / (ms * 1e-3)
+    tflops = flops / (ms * 1e-3) / 1e12
+    ai = flops / bytes_alg
+    roof_tflops = min(BF16_PEAK_TFLOPS, HBM_PEAK_GBS * 1e9 * ai / 1e12)
+    roof_tok_s = w.num_tokens * roof_tflops * 1e12 / flops
+    achieved_gbs = bytes_alg / (ms * 1e-3) / 1e9
+    traffic = traffic_from_profile()
+
+    rec = {
+        "metric": METRIC,
+        "value": tok_s,
+        "unit": "query-tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "fp8_ds_mla sparse MLA decode: 64 tokens (1 per request), ctx U{4096..8192}, "
+                        "h_q 64, top-k 2048 distinct, block 64, shuffled block table, cold cache",
+            "num_tokens": w.num_tokens, "h_q": w.h_q, "topk": w.topk, "cache": "fp8_ds_mla",
+            "num_splits": splits, "seed": args.seed,
+        },
+        "tflops": tflops,
+        "pct_of_binding_roofline": 100.0 * tok_s / roof_tok_s,
+        "binding_roofline": {"bound": "hbm" if roof_tflops < BF16_PEAK_TFLOPS else "mfma",
+                             "arith_intensity_flop_per_byte": ai, "tflops": roof_tflops,
+                             "query_tokens_per_s": roof_tok_s},
+        "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved_gbs / HBM_PEAK_GBS, "traffic": traffic},
+        "algorithmic_bytes_per_step": bytes_alg,
+        "algorithmic_bytes_breakdown": by,
+        "flops_per_step": flops,
+        "valid_slots": n_valid,
+        "ms_per_step_median": float(np.median(cold_ms)),
+        "ms_per_step_p10": float(np.percentile(cold_ms, 10)),
+        "ms_per_step_p90": float(np.percentile(cold_ms, 90)),
+        "warm_cache": {"ms_per_step": warm_ms, "query_tokens_per_s": w.num_tokens / (warm_ms * 1e-3)},
+        "timed_region_wall_s_incl_flushes": t_wall,
+        "timing": "HIP events around each smla_decode_fp8 call (all its kernels), on its stream",
+        "kernel_source_hash": kernel_source_hash(),
+        "device": props.name,
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -55,6 +55,8 @@ def _load():
     lib = ctypes.CDLL(path)
     i64, i32, dbl = ctypes.c_int64, ctypes.c_int32, ctypes.c_double
     vp = ctypes.c_void_p
+    lib.smla_oracle_num_threads.restype = ctypes.c_int
+    lib.smla_oracle_num_threads.argtypes = []
     lib.smla_oracle_e4m3fn.restype = dbl
     lib.smla_oracle_e4m3fn.argtypes = [ctypes.c_uint8]
     lib.smla_oracle_bf16.restype = dbl
@@ -80,6 +82,11 @@ def _c(a: np.ndarray, dtype) -> np.ndarray:
 
 def _ptr(a):
     return None if a is None else a.ctypes.data
+
+
+def num_threads() -> int:
+    """OpenMP threads the oracle's parallel loop uses."""
+    return int(_load().smla_oracle_num_threads())
 
 
 def e4m3fn(code: int) -> float:

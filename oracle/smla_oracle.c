@@ -42,6 +42,7 @@
  * (tests/test_oracle_pins.py); none of them re-types these formulas.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -50,6 +51,12 @@
 #define ORACLE_DQK 576    /* 512 latent (NoPE) + 64 RoPE                     */
 #define ORACLE_DV 512     /* value width = latent part                       */
 #define ORACLE_FP8_ROW 656
+
+/* Threads an OpenMP parallel region of this library will use. */
+int smla_oracle_num_threads(void)
+{
+    return omp_get_max_threads();
+}
 
 /* ---------------------------------------------------------------- values */
 

@@ -15,10 +15,13 @@
 //  * The workgroup first converts its part of the token's top-k list to cache
 //    slots and compacts the valid ones into LDS, so whole tiles of -1 cost
 //    nothing and only the last tile is ragged.
-//  * Gather: each thread loads 16-byte pieces of four rows, dequantises fp8
-//    with the row's per-128 scale (or takes bf16 as is), and writes the tile
-//    twice into LDS: row-major (the K operand of QK^T) and transposed (the V
-//    operand of PV, whose contraction runs over rows).
+//  * Gather: each thread loads 16-byte pieces of four rows, converts e4m3 to
+//    bf16 exactly (or takes bf16 as is), and writes the tile twice into LDS:
+//    row-major (the K operand of QK^T) and transposed (the V operand of PV,
+//    whose contraction runs over rows). The fp8 rows' per-128 scales are kept
+//    apart in fp32 and applied to the 128-column partial sums of QK^T and to
+//    the softmax weights of each 128-wide output group, so the dequantisation
+//    itself adds no rounding.
 //  * QK^T is computed transposed, S^T = K q^T, with v_mfma_f32_16x16x32_bf16,
 //    q held in registers for the whole workgroup. The accumulator layout of
 //    S^T gives every lane one head and 4 rows per 16-row block, which is
@@ -54,9 +57,11 @@ constexpr int kVtStride = kTile * 2 + 16;     // bytes per row of the transposed
 constexpr int kLdsK = kTile * kKStride;       // 74752
 constexpr int kLdsVt = kDv * kVtStride;       // 73728
 constexpr int kLdsSlots = kMaxChunk * 4;      // 8192
+constexpr int kLdsScale = 4 * kTile * 4;     // fp8 scales of the tile, [group][row] fp32
 constexpr int kLdsMisc = 64;
-constexpr int kLdsBytes = kLdsK + kLdsVt + kLdsSlots + kLdsMisc;
+constexpr int kLdsBytes = kLdsK + kLdsVt + kLdsSlots + kLdsScale + kLdsMisc;
 constexpr int kOStride = kDv + 4;             // floats per staged output row (padded)
+constexpr int kExactPRows = 128;              // lists this short take P as hi + lo bf16 terms
 static_assert(kLdsBytes <= 160 * 1024, "LDS budget of one gfx950 workgroup");
 static_assert(kWaves * 16 * (kOStride + 2) * 4 <= kLdsK + kLdsVt, "output staging fits the tile region");
 
@@ -100,6 +105,17 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b)
     return __builtin_bit_cast(uint32_t, v);
 }
 
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// bf16 rounding of what is left of four fp32 values after their bf16 rounding
+// `w` (two packed pairs): the low term of a two-term bf16 split.
+__device__ __forceinline__ uint2 bf16_residual2(const f32x4 &v, uint2 w)
+{
+    return make_uint2(pack_bf16(v[0] - bf16_lo(w.x), v[1] - bf16_hi(w.x)),
+                      pack_bf16(v[2] - bf16_lo(w.y), v[3] - bf16_hi(w.y)));
+}
+
 // Position of tile row 4*rq .. 4*rq+3 in a row of the transposed V tile.
 // Within every 32-row chunk, rows 4a+i (a < 4) go to 8a+i and rows 16+4a+i to
 // 8a+4+i, so the 8 values one lane feeds to a 16x16x32 MFMA (two S^T blocks'
@@ -117,59 +133,58 @@ __device__ __forceinline__ uint32_t word_of(const uint4 &v, int w)
 
 // ---------------------------------------------------------------- gather
 
-// fp8_ds_mla rows: latent bytes are dequantised with their row's scale and
-// rounded once to bf16; RoPE (bf16) is copied as is.
+// fp8_ds_mla rows. Every e4m3 value is exactly a bf16 value, so the latent
+// bytes are converted exactly (v_cvt_scalef32_pk_bf16_fp8 with scale 1) and
+// the row's four fp32 scales go to lds_scale[group][row]; they are applied in
+// fp32 to the QK^T partial sums and to the softmax weights, never rounded into
+// the tile. RoPE (bf16) is copied as is.
+template <bool kHighHalf>
+__device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t word)
+{
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(word, 1.0f, kHighHalf));
+}
+
 __device__ __forceinline__ void load_tile_fp8(const uint8_t *__restrict__ cache,
                                               const int32_t *slots, int n_tile,
-                                              uint8_t *lds_k, uint8_t *lds_vt, int tid)
+                                              uint8_t *lds_k, uint8_t *lds_vt, float *lds_scale,
+                                              int tid)
 {
 #pragma unroll
     for (int ui = 0; ui < 2; ++ui) {
         const int u = tid + kThreads * ui;       // 16 row-quads x 32 pieces of 16 bytes
         const int rq = u >> 5, c = u & 31;
         uint4 raw[4];
-        float sc[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int r = 4 * rq + j;
             const int slot = r < n_tile ? slots[r] : -1;
-            if (slot >= 0) {
-                const uint8_t *row = cache + (size_t)slot * kFp8RowBytes;
-                raw[j] = *(const uint4 *)(row + 16 * c);
-                sc[j] = *(const float *)(row + 512 + 4 * (c >> 3));
-            } else {
-                raw[j] = make_uint4(0, 0, 0, 0);
-                sc[j] = 0.f;
-            }
+            raw[j] = slot >= 0 ? *(const uint4 *)(cache + (size_t)slot * kFp8RowBytes + 16 * c)
+                               : make_uint4(0, 0, 0, 0);
         }
-        float f[4][16];
+        uint32_t b[4][8];                        // row j: bf16 pairs (dims 2e, 2e+1)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
 #pragma unroll
             for (int w = 0; w < 4; ++w) {
-                const uint32_t word = word_of(raw[j], w);
-                const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(word, false);
-                const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(word, true);
-                f[j][4 * w + 0] = lo[0] * sc[j];
-                f[j][4 * w + 1] = lo[1] * sc[j];
-                f[j][4 * w + 2] = hi[0] * sc[j];
-                f[j][4 * w + 3] = hi[1] * sc[j];
+                b[j][2 * w] = e4m3x2_to_bf16x2<false>(word_of(raw[j], w));
+                b[j][2 * w + 1] = e4m3x2_to_bf16x2<true>(word_of(raw[j], w));
             }
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
             uint4 *dst = (uint4 *)(lds_k + (4 * rq + j) * kKStride + 32 * c);
-            dst[0] = make_uint4(pack_bf16(f[j][0], f[j][1]), pack_bf16(f[j][2], f[j][3]),
-                                pack_bf16(f[j][4], f[j][5]), pack_bf16(f[j][6], f[j][7]));
-            dst[1] = make_uint4(pack_bf16(f[j][8], f[j][9]), pack_bf16(f[j][10], f[j][11]),
-                                pack_bf16(f[j][12], f[j][13]), pack_bf16(f[j][14], f[j][15]));
+            dst[0] = make_uint4(b[j][0], b[j][1], b[j][2], b[j][3]);
+            dst[1] = make_uint4(b[j][4], b[j][5], b[j][6], b[j][7]);
         }
         const int vpos = vt_pos(rq);
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
+            const int w = e >> 1;
             uint2 v;
-            v.x = pack_bf16(f[0][e], f[1][e]);
-            v.y = pack_bf16(f[2][e], f[3][e]);
+            if (e & 1) {
+                v.x = (b[0][w] >> 16) | (b[1][w] & 0xFFFF0000u);
+                v.y = (b[2][w] >> 16) | (b[3][w] & 0xFFFF0000u);
+            } else {
+                v.x = (b[0][w] & 0xFFFFu) | (b[1][w] << 16);
+                v.y = (b[2][w] & 0xFFFFu) | (b[3][w] << 16);
+            }
             *(uint2 *)(lds_vt + (16 * c + e) * kVtStride + 2 * vpos) = v;
         }
     }
@@ -182,6 +197,15 @@ __device__ __forceinline__ void load_tile_fp8(const uint8_t *__restrict__ cache,
         if (slot >= 0)
             v = *(const uint4 *)(cache + (size_t)slot * kFp8RowBytes + 528 + 16 * rc);
         *(uint4 *)(lds_k + r * kKStride + 1024 + 16 * rc) = v;
+        if (rc == 0) {
+            float4 sc = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (slot >= 0)
+                sc = *(const float4 *)(cache + (size_t)slot * kFp8RowBytes + 512);
+            lds_scale[0 * kTile + r] = sc.x;
+            lds_scale[1 * kTile + r] = sc.y;
+            lds_scale[2 * kTile + r] = sc.z;
+            lds_scale[3 * kTile + r] = sc.w;
+        }
     }
 }
 
@@ -245,7 +269,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(const KParams p)
     uint8_t *lds_k = smem;
     uint8_t *lds_vt = smem + kLdsK;
     int32_t *lds_slots = (int32_t *)(smem + kLdsK + kLdsVt);
-    int32_t *lds_misc = (int32_t *)(smem + kLdsK + kLdsVt + kLdsSlots);
+    float *lds_scale = (float *)(smem + kLdsK + kLdsVt + kLdsSlots);
+    int32_t *lds_misc = (int32_t *)(smem + kLdsK + kLdsVt + kLdsSlots + kLdsScale);
 
     constexpr int HG = kWaves / KW;      // groups of 16 heads in this workgroup
     constexpr int RW = kTile / KW;       // tile rows per wave
@@ -319,11 +344,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(const KParams p)
             __syncthreads();
         }
 
+        // A short list puts large weights on few rows: use the two-term P.
+        const bool exact_p = n_valid <= kExactPRows;
+
         // ---- tiles of 64 gathered rows
         for (int tile0 = 0; tile0 < n_valid; tile0 += kTile) {
             const int n_tile = min(kTile, n_valid - tile0);
             if (FMT == kCacheFp8)
-                load_tile_fp8(p.cache, lds_slots + tile0, n_tile, lds_k, lds_vt, tid);
+                load_tile_fp8(p.cache, lds_slots + tile0, n_tile, lds_k, lds_vt, lds_scale, tid);
             else
                 load_tile_bf16(p.cache, lds_slots + tile0, n_tile, lds_k, lds_vt, tid);
             __syncthreads();
@@ -333,13 +361,49 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(const KParams p)
 #pragma unroll
             for (int b = 0; b < NBLK; ++b)
                 acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if constexpr (FMT == kCacheFp8) {
+                // latent columns in four 128-wide groups, each partial sum times its
+                // rows' scale (lane rows row_base + 16b + 4g + i), then RoPE unscaled
 #pragma unroll
-            for (int k = 0; k < kKSteps; ++k) {
+                for (int grp = 0; grp < 4; ++grp) {
+                    f32x4 part[NBLK];
 #pragma unroll
-                for (int b = 0; b < NBLK; ++b) {
-                    const bf16x8 a = *(const bf16x8 *)(lds_k + (row_base + 16 * b + n16) * kKStride +
-                                                       (32 * k + 8 * g) * 2);
-                    acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qb[k], acc[b], 0, 0, 0);
+                    for (int b = 0; b < NBLK; ++b)
+                        part[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int kk = 0; kk < 4; ++kk) {
+                        const int k = 4 * grp + kk;
+#pragma unroll
+                        for (int b = 0; b < NBLK; ++b) {
+                            const bf16x8 a = *(const bf16x8 *)(lds_k + (row_base + 16 * b + n16) * kKStride +
+                                                               (32 * k + 8 * g) * 2);
+                            part[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qb[k], part[b], 0, 0, 0);
+                        }
+                    }
+#pragma unroll
+                    for (int b = 0; b < NBLK; ++b) {
+                        const f32x4 sc = *(const f32x4 *)(lds_scale + grp * kTile + row_base + 16 * b + 4 * g);
+                        acc[b] += sc * part[b];
+                    }
+                }
+#pragma unroll
+                for (int k = 16; k < kKSteps; ++k) {
+#pragma unroll
+                    for (int b = 0; b < NBLK; ++b) {
+                        const bf16x8 a = *(const bf16x8 *)(lds_k + (row_base + 16 * b + n16) * kKStride +
+                                                           (32 * k + 8 * g) * 2);
+                        acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qb[k], acc[b], 0, 0, 0);
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int k = 0; k < kKSteps; ++k) {
+#pragma unroll
+                    for (int b = 0; b < NBLK; ++b) {
+                        const bf16x8 a = *(const bf16x8 *)(lds_k + (row_base + 16 * b + n16) * kKStride +
+                                                           (32 * k + 8 * g) * 2);
+                        acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qb[k], acc[b], 0, 0, 0);
+                    }
                 }
             }
 
@@ -379,35 +443,59 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(const KParams p)
             for (int i = 0; i < 32; ++i)
                 o[i] *= alpha;
 
-            // O^T += V^T P^T
-            if constexpr (KW == 4) {
-                const uint2 pw = make_uint2(pack_bf16(acc[0][0], acc[0][1]), pack_bf16(acc[0][2], acc[0][3]));
-                const i16x4 pb = __builtin_bit_cast(i16x4, pw);
-                const int col = 32 * (kw >> 1) + 8 * g + 4 * (kw & 1);
+            // O^T += V^T P^T. Output dims 128*grp .. 128*grp+127 take the weights
+            // times their rows' scale of group grp (fp8; 1 for bf16 rows). For a
+            // short list (exact_p) every weight is large and its bf16 rounding would
+            // show in the output, so P goes in as two bf16 terms, hi + lo, against the
+            // same V^T operand.
 #pragma unroll
-                for (int db = 0; db < 32; ++db) {
-                    const i16x4 a = *(const i16x4 *)(lds_vt + (16 * db + n16) * kVtStride + 2 * col);
-                    o[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, pb, o[db], 0, 0, 0);
-                }
-            } else {
-                constexpr int NCH = NBLK / 2;
-                bf16x8 pb[NCH];
+            for (int grp = 0; grp < 4; ++grp) {
+                if constexpr (KW == 4) {
+                    f32x4 pv = acc[0];
+                    if constexpr (FMT == kCacheFp8)
+                        pv *= *(const f32x4 *)(lds_scale + grp * kTile + row_base + 4 * g);
+                    const uint2 pw = make_uint2(pack_bf16(pv[0], pv[1]), pack_bf16(pv[2], pv[3]));
+                    const i16x4 pb = __builtin_bit_cast(i16x4, pw);
+                    const i16x4 pl = __builtin_bit_cast(i16x4, bf16_residual2(pv, pw));
+                    const int col = 32 * (kw >> 1) + 8 * g + 4 * (kw & 1);
 #pragma unroll
-                for (int ch = 0; ch < NCH; ++ch) {
-                    const uint4 pw = make_uint4(pack_bf16(acc[2 * ch][0], acc[2 * ch][1]),
-                                                pack_bf16(acc[2 * ch][2], acc[2 * ch][3]),
-                                                pack_bf16(acc[2 * ch + 1][0], acc[2 * ch + 1][1]),
-                                                pack_bf16(acc[2 * ch + 1][2], acc[2 * ch + 1][3]));
-                    pb[ch] = __builtin_bit_cast(bf16x8, pw);
-                }
-#pragma unroll
-                for (int db = 0; db < 32; ++db) {
+                    for (int d8 = 0; d8 < 8; ++d8) {
+                        const int db = 8 * grp + d8;
+                        const i16x4 a = *(const i16x4 *)(lds_vt + (16 * db + n16) * kVtStride + 2 * col);
+                        o[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, pb, o[db], 0, 0, 0);
+                        if (exact_p)
+                            o[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, pl, o[db], 0, 0, 0);
+                    }
+                } else {
+                    constexpr int NCH = NBLK / 2;
+                    bf16x8 pb[NCH], pl[NCH];
 #pragma unroll
                     for (int ch = 0; ch < NCH; ++ch) {
-                        const int chunk = KW == 1 ? ch : kw;
-                        const bf16x8 a = *(const bf16x8 *)(lds_vt + (16 * db + n16) * kVtStride +
-                                                           2 * (32 * chunk + 8 * g));
-                        o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[ch], o[db], 0, 0, 0);
+                        f32x4 p0 = acc[2 * ch], p1 = acc[2 * ch + 1];
+                        if constexpr (FMT == kCacheFp8) {
+                            const float *sg = lds_scale + grp * kTile + row_base + 32 * ch + 4 * g;
+                            p0 *= *(const f32x4 *)sg;
+                            p1 *= *(const f32x4 *)(sg + 16);
+                        }
+                        const uint4 pw = make_uint4(pack_bf16(p0[0], p0[1]), pack_bf16(p0[2], p0[3]),
+                                                    pack_bf16(p1[0], p1[1]), pack_bf16(p1[2], p1[3]));
+                        pb[ch] = __builtin_bit_cast(bf16x8, pw);
+                        const uint2 r0 = bf16_residual2(p0, make_uint2(pw.x, pw.y));
+                        const uint2 r1 = bf16_residual2(p1, make_uint2(pw.z, pw.w));
+                        pl[ch] = __builtin_bit_cast(bf16x8, make_uint4(r0.x, r0.y, r1.x, r1.y));
+                    }
+#pragma unroll
+                    for (int d8 = 0; d8 < 8; ++d8) {
+                        const int db = 8 * grp + d8;
+#pragma unroll
+                        for (int ch = 0; ch < NCH; ++ch) {
+                            const int chunk = KW == 1 ? ch : kw;
+                            const bf16x8 a = *(const bf16x8 *)(lds_vt + (16 * db + n16) * kVtStride +
+                                                               2 * (32 * chunk + 8 * g));
+                            o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[ch], o[db], 0, 0, 0);
+                            if (exact_p)
+                                o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pl[ch], o[db], 0, 0, 0);
+                        }
                     }
                 }
             }

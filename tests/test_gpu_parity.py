@@ -117,6 +117,35 @@ def test_degenerate_rows(fmt):
         assert_parity(w, out, lse, label=f"degenerate {fmt} s{splits}")
 
 
+@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+def test_short_lists_are_exact_up_to_output_rounding(fmt):
+    """Tokens with 1..8 valid rows put large weights on few rows, so |o| can reach the
+    bf16 range where half an ulp (0.0156 above 4) exceeds the stated max-abs bound by
+    itself. There the kernel must be exact up to the output's own rounding: error <=
+    half a bf16 ulp of the true value + 2e-3 (fp8: one more half ulp, for the one
+    bf16 rounding of the dequantised rows), and the stated rel-L2 bound."""
+    w = small(21, fmt, 128, 64, n_req=4, tok_per_req=8, ctx=(200, 400), p_invalid=0.0)
+    rng = np.random.default_rng(21)
+    for t in range(w.num_tokens):
+        keep = 1 + t % 8
+        w.topk_indices[t, keep:] = -1
+        w.topk_indices[t] = rng.permutation(w.topk_indices[t])
+    dw = DeviceWorkload(w)
+    for splits in (0, 3):
+        log(f"[case] short lists {fmt} splits={splits}")
+        out, lse, _ = dw.run(num_splits=splits)
+        o_ref, lse_ref = oracle.attention(0 if fmt == "bf16" else 1, w.q, w.cache, w.block_table,
+                                          w.req_id_per_token, w.topk_indices, w.sm_scale)
+        o = out.float().cpu().numpy().astype(np.float64)
+        half_ulp = np.ldexp(1.0, np.frexp(np.abs(o_ref))[1] - 9)    # bf16: 8 significant bits
+        excess = np.abs(o - o_ref) - half_ulp * (2 if fmt == "fp8" else 1)
+        rel = np.linalg.norm(o - o_ref) / np.linalg.norm(o_ref)
+        log(f"[parity] short lists {fmt} s{splits}: max |o| {np.abs(o_ref).max():.2f}, "
+            f"max error beyond half-ulp {excess.max():.3e}, rel_l2 {rel:.3e}")
+        assert excess.max() <= 2e-3 and rel <= (5e-3 if fmt == "bf16" else 1e-2)
+        np.testing.assert_allclose(lse.cpu().numpy(), lse_ref, rtol=0, atol=2e-3)
+
+
 def test_zero_tokens_writes_nothing():
     w = small(3, "fp8", 16, 64)
     dw = DeviceWorkload(w)
