@@ -24,11 +24,13 @@ Plan make_plan(int num_tokens, int h_q, int topk, int num_cus, int forced_splits
         splits = std::min(forced_splits, topk);
     } else {
         // One workgroup per (token, head block) when that fills the chip;
-        // otherwise cut each token's list so the grid covers every CU once.
+        // otherwise cut each token's list so the grid covers every workgroup
+        // slot once (four-wave workgroups: one per CU; two-wave: two per CU).
         const int64_t units = (int64_t)num_tokens * p.head_blocks;
+        const int64_t slots = (int64_t)num_cus * (h_q >= kHeadsPerGroup ? 1 : 2);
         const int64_t tiles = (topk + kBlock - 1) / kBlock;
-        if (units > 0 && units < num_cus)
-            splits = (int)std::min<int64_t>(tiles, (num_cus + units - 1) / units);
+        if (units > 0 && units < slots)
+            splits = (int)std::min<int64_t>(tiles, (slots + units - 1) / units);
         splits = std::max(splits, 1);
     }
     p.split_len = (topk + splits - 1) / splits;
@@ -37,7 +39,8 @@ Plan make_plan(int num_tokens, int h_q, int topk, int num_cus, int forced_splits
         const size_t rows = (size_t)num_tokens * p.num_splits * h_q;
         p.part_o_off = 0;
         p.part_lse_off = align_up(rows * kDv * sizeof(float), 256);
-        p.workspace = align_up(p.part_lse_off + rows * sizeof(float), 256);
+        p.counters_off = align_up(p.part_lse_off + rows * sizeof(float), 256);
+        p.workspace = align_up(p.counters_off + (size_t)num_tokens * p.head_blocks * sizeof(int32_t), 256);
     }
     return p;
 }

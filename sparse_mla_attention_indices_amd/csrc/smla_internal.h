@@ -18,9 +18,9 @@ constexpr int kBf16RowBytes = kDqk * 2;
 
 enum CacheFormat { kCacheBf16 = 0, kCacheFp8 = 1 };
 
-// Heads one workgroup covers: 64 (as four waves of 16); h_q = 128 takes two
-// workgroups per token, h_q = 16 / 32 one workgroup whose spare waves split the
-// rows of each tile instead.
+// Heads one workgroup covers: 64 (four waves) for h_q >= 64, so h_q = 128 takes
+// two workgroups per token; h_q = 16 / 32 use one two-wave workgroup, and two
+// of those share a compute unit.
 constexpr int kHeadsPerGroup = 64;
 
 struct Plan {
@@ -30,6 +30,7 @@ struct Plan {
     size_t workspace;    // bytes of partial results needed (0 when num_splits == 1)
     size_t part_o_off;   // byte offsets inside the workspace
     size_t part_lse_off;
+    size_t counters_off; // one int32 per (token, head block): arrivals of its splits
 };
 
 // Host arithmetic only.

@@ -51,11 +51,15 @@ def test_plan_fills_the_chip_for_small_decode_batches(lib):
     # 64 tokens x 64 heads: one workgroup per token -> 4 top-k splits on 256 CUs
     s, ws = smla.smla_plan(64, 64, 2048, 256)
     assert s == 4
+    up = lambda v: -(-v // 256) * 256
     rows = 64 * 4 * 64
-    lse_off = -(-rows * 512 * 4 // 256) * 256
-    assert ws == -(-(lse_off + rows * 4) // 256) * 256
+    lse_off = up(rows * 512 * 4)
+    counters_off = up(lse_off + rows * 4)
+    assert ws == up(counters_off + 64 * 1 * 4)
+    # two-wave workgroups (h_q <= 32) fit two per CU: 256 tokens x 16 heads -> 2 splits
+    assert smla.smla_plan(256, 16, 2048, 256)[0] == 2
     # enough (token, head-block) units already: no split, no workspace
-    assert smla.smla_plan(256, 16, 2048, 256) == (1, 0)
+    assert smla.smla_plan(512, 16, 2048, 256) == (1, 0)
     assert smla.smla_plan(16384, 128, 2048, 256) == (1, 0)
     # a split never exceeds the number of 64-row tiles of the list
     assert smla.smla_plan(1, 64, 100, 256)[0] == 2
