@@ -10,39 +10,48 @@
 // both cache formats. How it is computed here is this library's own design for
 // 64-wide wavefronts, MFMA and the 160 KB LDS of a gfx950 compute unit:
 //
-//  * Workgroup = one query token x up to 64 heads x one part ("split") of the
-//    token's top-k list. Waves: two halves of the 576 columns ("dh") x one or
-//    two groups of up to 32 heads ("hh"). Every wave sees every row.
+//  * Workgroup = one query token x 16, 32 or 64 heads x one part ("split") of
+//    the token's top-k list. Every wave owns 16 heads and one half of the 576
+//    columns ("dh"), so a 64-head workgroup has eight waves, two per SIMD, and
+//    each wave stays within 256 registers.
 //  * Prologue: the workgroup converts its part of the top-k list to cache
-//    slots and compacts the valid ones into LDS (whole runs of -1 cost
-//    nothing; only the last tile is ragged).
+//    slots (one round trip for the indices, one for the block table) and
+//    compacts the valid ones into LDS: runs of -1 cost nothing, only the last
+//    tile is ragged.
 //  * Gather: global_load_lds_dwordx4 copies the cache rows of a 32-row tile,
 //    as stored (fp8_ds_mla 656 B or bf16 1152 B), straight into one of a ring
-//    of LDS buffers; the next tiles are in flight while this one is used.
+//    of LDS buffers; the next tiles are in flight while one is used.
 //  * QK^T runs transposed, S^T = K q^T, on v_mfma_f32_16x16x32_bf16 with q in
-//    registers. Each wave reads its half of the columns for 16-row blocks
-//    (ds_read_b64 of fp8 bytes or ds_read_b128 of bf16), converts fp8 to bf16
-//    exactly in registers (every e4m3 value is a bf16 value) and feeds one
-//    fragment to the MFMAs of both its 16-head blocks. fp8 partial sums of each
-//    128-column group are multiplied by that group's row scales in fp32. The
-//    two column halves exchange their partial S^T through LDS.
+//    registers. K fragments are read from the raw tile (ds_read_b64 of fp8
+//    bytes, converted to bf16 exactly in registers: every e4m3 value is a bf16
+//    value; or ds_read_b128 of bf16). fp8 partial sums of each 128-column group
+//    are multiplied by that group's row scales in fp32. The two column halves
+//    add their partial S^T through LDS.
 //  * Softmax: the S^T accumulator layout gives a lane one head and four rows
-//    per block, so row max / row sum take two cross-lane steps, and the weights
-//    are already in the B-operand layout of O^T += V^T P^T. The running max is
-//    only moved (and O rescaled) when the tile max exceeds it by 2^8.
+//    per block, and the weights are already in the B-operand layout of
+//    O^T += V^T P^T. The running max moves (and O is rescaled) only when a tile
+//    exceeds it by 2^8; the test uses each lane's own rows, so the common case
+//    needs no cross-lane step. Row sums stay per lane until the end.
 //  * PV reads V straight from the row-major raw tile with the gfx950 LDS
 //    transpose loads (ds_read_b64_tr_b8 for fp8, ds_read_b64_tr_b16 for bf16).
 //    For fp8 the weights of each 128-wide output group carry that group's row
-//    scales, so dequantisation adds no rounding anywhere.
-//  * A short list (few valid rows) puts large weights on few rows; then P goes
-//    into PV as two bf16 terms, hi + lo.
-//  * Splits of one token run on one XCD (workgroup id mod 8). Each writes fp32
-//    partials; the last to finish (atomic counter) merges them by log-sum-exp
-//    weights and writes the bf16 output, so no separate merge pass runs.
+//    scales, so dequantisation adds no rounding anywhere. A short list (few
+//    valid rows, so large weights) feeds P as two bf16 terms, hi + lo.
+//  * Splits of one token are given workgroup ids with the same value mod 8 and
+//    so normally run on one XCD, which has one L2. Each split publishes an fp32
+//    partial with plain stores, then one 64-bit atomic add counts its arrival
+//    both in total and for its XCD. The last arrival checks that every split
+//    ran on its own XCD, then reads the other partials through that shared L2
+//    (its own is still in registers) and merges them by log-sum-exp weights; no
+//    cache write-back is needed. If the check fails it recomputes the whole
+//    token itself, so results never depend on where the hardware placed a
+//    workgroup. It leaves the arrival word at zero again.
 
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "smla_internal.h"
 
@@ -73,30 +82,52 @@ template <> struct RowFmt<kCacheBf16> {
     static constexpr int kRope = 1024;
 };
 
-// Compile-time shape of one kernel instantiation.
-template <int FMT, int HPW, int NHH>
+// Compile-time shape of one instantiation: NHH groups of 16 heads, two waves
+// (column halves) per group.
+//
+// A tile's rows sit in LDS as stored in HBM, but with a row stride and a gap
+// after every 16 rows chosen so that the LDS reads of one instruction spread
+// over distinct banks: fp8 rows keep their 656-byte stride (16 consecutive rows
+// fall on distinct banks) and rows 16..31 start 16 bytes later than a plain
+// stride would put them (the transposed V reads touch rows r and r + 16
+// together); bf16 rows get a 1168-byte stride (1152 + 16).
+template <int FMT, int NHH>
 struct Cfg {
-    static constexpr int kWaves = 2 * NHH;                 // (dh, hh)
+    static constexpr int kWaves = 2 * NHH;
     static constexpr int kThreads = 64 * kWaves;
-    static constexpr int kHBW = HPW / 16;                  // 16-head blocks per wave
-    static constexpr int kHeads = HPW * NHH;               // heads per workgroup
-    static constexpr int kRowBytes = RowFmt<FMT>::kBytes;
-    static constexpr int kChunksPerRow = kRowBytes / 16;
-    static constexpr int kTileChunks = kTile * kChunksPerRow;
-    static constexpr int kDmaInstr = (kTileChunks + 63) / 64;        // wave instructions per tile
+    static constexpr int kHeads = 16 * NHH;                          // heads per workgroup
+    static constexpr int kRowBytes = RowFmt<FMT>::kBytes;            // bytes of a row in HBM
+    static constexpr int kChunksPerRow = kRowBytes / 16;             // 16-byte pieces per row
+    static constexpr int kRowStride = FMT == kCacheFp8 ? kRowBytes : kRowBytes + 16;   // in LDS
+    static constexpr int kBlockGap = FMT == kCacheFp8 ? 16 : 0;
+    static constexpr int kRowBlockBytes = 16 * kRowStride + kBlockGap;                 // 16 rows
+    static constexpr int kSlotsPerRow = kRowStride / 16;
+    static constexpr int kSlotsPerBlock = kRowBlockBytes / 16;
+    static constexpr int kTileSlots = kRB * kSlotsPerBlock;
+    static constexpr int kDmaInstr = (kTileSlots + 63) / 64;         // wave instructions per tile
     static constexpr int kBufBytes = kDmaInstr * 1024;               // ring buffer stride
-    // Four waves hold one workgroup per CU: deep ring. Two waves: two
-    // workgroups per CU share the LDS.
-    static constexpr int kNBuf = FMT == kCacheFp8 ? (NHH == 2 ? 4 : 3) : (NHH == 2 ? 3 : 2);
-    static constexpr int kXchgBytes = kWaves * kRB * kHBW * 1024;    // partial S^T exchange
+    // 64 heads: one workgroup per CU and a deep ring. Fewer heads: two
+    // workgroups per CU share the LDS (fp8).
+    static constexpr int kNBuf = NHH == 4 ? (FMT == kCacheFp8 ? 5 : 3) : 2;
+    static constexpr int kXchgBytes = kWaves * kRB * 1024;           // partial S^T exchange
     static constexpr int kSlotsBytes = kMaxChunk * 4;
     static constexpr int kOffXchg = kNBuf * kBufBytes;
     static constexpr int kOffSlots = kOffXchg + kXchgBytes;
     static constexpr int kOffMisc = kOffSlots + kSlotsBytes;
-    static constexpr int kLdsBytes = kOffMisc + 512;   // flags + per-wave counts of compaction
+    static constexpr int kLdsBytes = kOffMisc + 512;                 // verdict + compaction counts
+    static_assert(kRowBlockBytes % 16 == 0, "row blocks are whole 16-byte slots");
+    static_assert(kRB * kRowBlockBytes <= kBufBytes, "a tile fits its ring buffer");
     static_assert(kLdsBytes <= 160 * 1024, "LDS of one gfx950 workgroup");
     static_assert(kHeads * kDv * 2 <= kOffSlots, "bf16 output staging fits the ring + exchange");
+    static_assert(16 + (kMaxChunk / kThreads) * kWaves <= 128, "compaction counts fit");
 };
+
+// Byte offset of tile row r in a ring buffer.
+template <class C>
+__device__ __forceinline__ int lds_row(int r)
+{
+    return (r >> 4) * C::kRowBlockBytes + (r & 15) * C::kRowStride;
+}
 
 struct KParams {
     const uint16_t *q;
@@ -109,12 +140,12 @@ struct KParams {
     int32_t *phys_out;
     float *part_o;        // [T][S][H][512] fp32, O / l of each split
     float *part_lse;      // [T][S][H]
-    int32_t *counters;    // [T][HB] arrivals of a token's splits
-    float sm_scale;
+    uint64_t *arrivals;   // [T][HB]: arrivals (bits 48..63) + arrivals per XCD (6 bits each)
     float log2e_scale;    // sm_scale * log2(e): logits are kept in log2 units
     int T, H, K, R, MB;
     int64_t NB;
     int S, split_len, HB;
+    int force_recompute;  // treat every split check as failed (exercises that path)
 };
 
 __device__ __forceinline__ int convert_slot(int req, int idx, const int32_t *__restrict__ bt,
@@ -154,17 +185,21 @@ __device__ __forceinline__ bf16x8 e4m3x8_to_bf16x8(uint2 v)
 }
 
 // P^T block (two 16-row blocks x 4 rows of one head) as the bf16 B operand of a
-// 16x16x32 MFMA, plus the bf16 rounding of its residual.
-__device__ __forceinline__ void pack_p(const f32x4 &p0, const f32x4 &p1, bf16x8 &hi, bf16x8 &lo)
+// 16x16x32 MFMA.
+__device__ __forceinline__ bf16x8 pack_p(const f32x4 &p0, const f32x4 &p1)
 {
-    const uint4 w = make_uint4(pack_bf16(p0[0], p0[1]), pack_bf16(p0[2], p0[3]),
-                               pack_bf16(p1[0], p1[1]), pack_bf16(p1[2], p1[3]));
-    hi = __builtin_bit_cast(bf16x8, w);
-    const uint4 r = make_uint4(pack_bf16(p0[0] - bf16_lo(w.x), p0[1] - bf16_hi(w.x)),
-                               pack_bf16(p0[2] - bf16_lo(w.y), p0[3] - bf16_hi(w.y)),
-                               pack_bf16(p1[0] - bf16_lo(w.z), p1[1] - bf16_hi(w.z)),
-                               pack_bf16(p1[2] - bf16_lo(w.w), p1[3] - bf16_hi(w.w)));
-    lo = __builtin_bit_cast(bf16x8, r);
+    return __builtin_bit_cast(bf16x8, make_uint4(pack_bf16(p0[0], p0[1]), pack_bf16(p0[2], p0[3]),
+                                                 pack_bf16(p1[0], p1[1]), pack_bf16(p1[2], p1[3])));
+}
+
+// bf16 rounding of what p0 | p1 lose in their rounding `hi`.
+__device__ __forceinline__ bf16x8 pack_p_residual(const f32x4 &p0, const f32x4 &p1, const bf16x8 &hi)
+{
+    const uint4 w = __builtin_bit_cast(uint4, hi);
+    return __builtin_bit_cast(bf16x8, make_uint4(pack_bf16(p0[0] - bf16_lo(w.x), p0[1] - bf16_hi(w.x)),
+                                                 pack_bf16(p0[2] - bf16_lo(w.y), p0[3] - bf16_hi(w.y)),
+                                                 pack_bf16(p1[0] - bf16_lo(w.z), p1[1] - bf16_hi(w.z)),
+                                                 pack_bf16(p1[2] - bf16_lo(w.w), p1[3] - bf16_hi(w.w))));
 }
 
 // Wait until at most n of this wave's vector-memory instructions are pending
@@ -186,19 +221,31 @@ __device__ __forceinline__ void wait_vmcnt(int n)
 #undef SMLA_VMCNT_CASE
 }
 
-// Copy the rows of one tile, as stored, into an LDS ring buffer (row-major,
-// row stride = row bytes). Wave w issues instructions w, w + W, ...; each moves
-// 64 consecutive 16-byte pieces. Rows past the tile's valid count repeat the
-// tile's first row (finite data whose weights are masked to zero).
+// Id of the XCD (accelerator complex die) this wave runs on, 0..7 on MI355X.
+__device__ __forceinline__ uint32_t xcc_id()
+{
+    uint32_t x;
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(x));
+    return x & 0xF;
+}
+
+// Copy the rows of one tile, as stored, into an LDS ring buffer in the layout
+// lds_row() describes. Wave w issues instructions w, w + W, ...; each fills 64
+// consecutive 16-byte LDS slots (lanes whose slot is padding stay idle). Rows
+// past the tile's valid count repeat the tile's first row (finite data whose
+// weights are masked to zero).
 template <class C>
 __device__ __forceinline__ void issue_tile(const uint8_t *__restrict__ cache, const int32_t *slots,
                                            int n_tile, uint8_t *buf, int wave, int lane)
 {
     for (int j = wave; j < C::kDmaInstr; j += C::kWaves) {
-        const int piece = j * 64 + lane;
-        if (piece < C::kTileChunks) {
-            const int r = piece / C::kChunksPerRow;
-            const int c = piece - r * C::kChunksPerRow;
+        const int slot_i = j * 64 + lane;
+        const int blk = slot_i / C::kSlotsPerBlock;
+        const int in_blk = slot_i - blk * C::kSlotsPerBlock;
+        const int r16 = in_blk / C::kSlotsPerRow;
+        const int c = in_blk - r16 * C::kSlotsPerRow;
+        if (blk < kRB && r16 < 16 && c < C::kChunksPerRow) {
+            const int r = 16 * blk + r16;
             const int slot = slots[r < n_tile ? r : 0];
             const uint8_t *src = cache + (size_t)slot * C::kRowBytes + 16 * c;
             __builtin_amdgcn_global_load_lds(src, LDS_PTR(void, buf + j * 1024), 16, 0, 0);
@@ -208,35 +255,14 @@ __device__ __forceinline__ void issue_tile(const uint8_t *__restrict__ cache, co
 
 // ------------------------------------------------------------- attention
 
-// Device-scope (sc1) stores and loads, visible to every compute unit once they
-// have completed. Used for the split partials, so publishing them needs no
-// L2-wide write-back. The stores are relaxed agent-scope atomics (the compiler
-// tracks their hazards); the loads carry their own wait.
-__device__ __forceinline__ void store_dev_x4(float *addr, const f32x4 &v)
+template <int FMT, int NHH>
+__global__ __launch_bounds__(128 * NHH) __attribute__((amdgpu_waves_per_eu(NHH == 4 ? 2 : 1)))
+void attn_kernel(const KParams p)
 {
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-        __hip_atomic_store(addr + e, v[e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-// Two device-scope 16-byte loads; the wait is inside the same statement, so no
-// use of the results can be scheduled before the data has arrived.
-__device__ __forceinline__ void load_dev_2x4(const float *a0, const float *a1, f32x4 &v0, f32x4 &v1)
-{
-    asm volatile("global_load_dwordx4 %0, %2, off sc1\n\t"
-                 "global_load_dwordx4 %1, %3, off sc1\n\t"
-                 "s_waitcnt vmcnt(0)"
-                 : "=&v"(v0), "=&v"(v1)
-                 : "v"(a0), "v"(a1)
-                 : "memory");
-}
-
-template <int FMT, int HPW, int NHH>
-__global__ __launch_bounds__(128 * NHH, 1) void attn_kernel(const KParams p)
-{
-    using C = Cfg<FMT, HPW, NHH>;
-    constexpr int HBW = C::kHBW;
+    using C = Cfg<FMT, NHH>;
     constexpr int RB = kRB;
-    constexpr int ROWB = C::kRowBytes;
+    constexpr int RS = C::kRowStride;
+    constexpr int RBB = C::kRowBlockBytes;
     constexpr int kPer = kMaxChunk / C::kThreads;    // top-k positions per thread per round
 
     __shared__ __attribute__((aligned(1024))) uint8_t smem[C::kLdsBytes];
@@ -250,7 +276,7 @@ __global__ __launch_bounds__(128 * NHH, 1) void attn_kernel(const KParams p)
     const int dh = wave & 1, hh = wave >> 1;
 
     // Workgroup id -> (token, split, head block); all workgroups of one token
-    // get the same id mod 8, i.e. the same XCD and L2.
+    // get the same id mod 8, the XCD the hardware dispatches them to.
     int bid = blockIdx.x;
     const int xcd = bid & 7;
     bid >>= 3;
@@ -261,404 +287,407 @@ __global__ __launch_bounds__(128 * NHH, 1) void attn_kernel(const KParams p)
     if (t >= p.T)
         return;
 
-    const int head0 = hb_wg * C::kHeads + hh * HPW;     // first head of this wave
+    const int wg_head0 = hb_wg * C::kHeads;
+    const int head = wg_head0 + 16 * hh + n16;      // this lane's head
     const float c2 = p.log2e_scale;
-    const int pos_begin = s * p.split_len;
-    const int pos_end = min(p.K, pos_begin + p.split_len);
     const int32_t *topk_row = p.topk + (size_t)t * p.K;
-    // one workgroup of the token's head blocks writes the converted slots
-    const bool write_phys = p.phys_out != nullptr && hb_wg == 0;
-
-    // Issue the first round's index loads, the request id and q together.
-    int idxv[kPer];
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-        const int i = pos_begin + tid + C::kThreads * j;
-        idxv[j] = i < min(pos_end, pos_begin + kMaxChunk) ? topk_row[i] : -1;
-    }
     const int req = p.req_id[t];
 
-    // q^T B operands: lane (head n16 of block hb, group g) holds 8 columns per
-    // k-step: latent 256*dh + 32k + 8g (k < 8), RoPE 512 + 32*dh + 8g (k = 8).
-    bf16x8 qb[HBW][9];
-#pragma unroll
-    for (int hb = 0; hb < HBW; ++hb) {
-        const uint16_t *qrow = p.q + ((size_t)t * p.H + head0 + 16 * hb + n16) * kDqk;
+    // q^T B operand: lane (head, group g) holds 8 columns per k-step: latent
+    // 256*dh + 32k + 8g (k < 8), RoPE 512 + 32*dh + 8g (k = 8).
+    bf16x8 qb[9];
+    {
+        const uint16_t *qrow = p.q + ((size_t)t * p.H + head) * kDqk;
 #pragma unroll
         for (int k = 0; k < 9; ++k) {
             const int col = k < 8 ? 256 * dh + 32 * k + 8 * g : 512 + 32 * dh + 8 * g;
-            qb[hb][k] = __builtin_bit_cast(bf16x8, *(const uint4 *)(qrow + col));
+            qb[k] = __builtin_bit_cast(bf16x8, *(const uint4 *)(qrow + col));
         }
     }
 
-    f32x4 o[16][HBW];                   // O^T: dims 256*dh + 16*db + 4g + i, head n16 of hb
-#pragma unroll
-    for (int db = 0; db < 16; ++db)
-#pragma unroll
-        for (int hb = 0; hb < HBW; ++hb)
-            o[db][hb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // log2-domain running max (shared by the 4 lanes of a head) and this lane's
-    // share of the running sum (its rows), per head
-    float m_run[HBW], l_part[HBW];
-#pragma unroll
-    for (int hb = 0; hb < HBW; ++hb) {
-        m_run[hb] = -INFINITY;
-        l_part[hb] = 0.f;
-    }
+    // `solo`: this workgroup computes its whole range and writes the output
+    // directly (no split, or the recompute after a failed XCD check).
+    bool solo = p.S == 1;
+    int pos_begin = s * p.split_len;
+    int pos_end = min(p.K, pos_begin + p.split_len);
 
-    for (int chunk0 = pos_begin; chunk0 < pos_end; chunk0 += kMaxChunk) {
-        const int chunk_n = min(kMaxChunk, pos_end - chunk0);
+    f32x4 o[16];            // O^T: dims 256*dh + 16*db + 4g + i of this lane's head
+    float m_run, l_part;    // log2-domain running max (same in a head's 4 lanes); lane's row sum
+    float out_scale, out_lse;
 
-        // ---- convert (all lookups in flight together), then compact the valid
-        //      slots in list order with one exchange of per-wave counts
-        int slotv[kPer];
+    // One tile: S^T = K q^T, online softmax, O^T += V^T P^T. exact: P enters PV
+    // as hi + lo bf16 terms (wave-uniform).
+    auto tile = [&](const uint8_t *buf, int n_tile, bool exact) __attribute__((always_inline)) {
+        // per-lane LDS offsets inside the tile buffer
+        const int off_k = n16 * RS;                      // K rows 16*rb + n16 (+ rb * RBB)
+        const int off_sc = (4 * g) * RS;                 // accumulator rows 16*rb + 4g + i
+        // fp8 V^T (ds_read_b64_tr_b8): source lane n16 = 2k + h reads row k of
+        // {4g..4g+3, 16+4g..16+4g+3}, bytes 8h..8h+7 of a 16-byte column block
+        const int vk = n16 >> 1;
+        const int off_v8 = (vk >> 2) * RBB + (4 * g + (vk & 3)) * RS + 8 * (n16 & 1);
+        // bf16 V^T (ds_read_b64_tr_b16): source lane n16 = 4k + a reads row 4g + k
+        // (and 16 + 4g + k), dims 4a..4a+3 of a 16-dim block
+        const int off_v16 = (4 * g + (n16 >> 2)) * RS + 8 * (n16 & 3);
+        // ---- S^T over this wave's column half (K rows 16*rb + n16; accumulator
+        //      rows 16*rb + 4g + i)
+        f32x4 acc[RB];
+        f32x4 sc[2][RB];        // fp8: scales of rows 16*rb + 4g + i, groups 2*dh + gi
+        uint2 vf8[16];          // fp8: V^T fragments, read before the exchange
+        if constexpr (FMT == kCacheFp8) {
+            bf16x8 rf[RB];
 #pragma unroll
-        for (int j = 0; j < kPer; ++j)
-            slotv[j] = convert_slot(req, idxv[j], p.bt, p.R, p.MB, p.NB);
-        if (write_phys) {
-#pragma unroll
-            for (int j = 0; j < kPer; ++j) {
-                const int i = tid + C::kThreads * j;
-                if (i < chunk_n)
-                    p.phys_out[(size_t)t * p.K + chunk0 + i] = slotv[j];
-            }
-        }
-        uint64_t masks[kPer];
-#pragma unroll
-        for (int j = 0; j < kPer; ++j) {
-            masks[j] = __ballot(slotv[j] >= 0);
-            if (lane == 0)
-                lds_misc[16 + j * C::kWaves + wave] = __popcll(masks[j]);
-        }
-        __syncthreads();
-        int n_valid = 0;
-#pragma unroll
-        for (int j = 0; j < kPer; ++j) {
-#pragma unroll
-            for (int w = 0; w < C::kWaves; ++w) {
-                const int cw = lds_misc[16 + j * C::kWaves + w];
-                if (w == wave && slotv[j] >= 0)
-                    lds_slots[n_valid + __popcll(masks[j] & ((1ull << lane) - 1ull))] = slotv[j];
-                n_valid += cw;
-            }
-        }
-        __syncthreads();
-        const bool exact_p = n_valid <= kExactPRows;
-        const int n_tiles = (n_valid + kTile - 1) / kTile;
-        // from here on the only vector-memory instructions in flight are tile copies
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        // this wave's copy instructions per tile
-        const int dma_w = (C::kDmaInstr - wave + C::kWaves - 1) / C::kWaves;
-
-        for (int i = 0; i < min(C::kNBuf - 1, n_tiles); ++i)
-            issue_tile<C>(p.cache, lds_slots + i * kTile, min(kTile, n_valid - i * kTile),
-                          ring + i * C::kBufBytes, wave, lane);
-
-        for (int it = 0; it < n_tiles; ++it) {
-            const int n_tile = min(kTile, n_valid - it * kTile);
-            const uint8_t *buf = ring + (it % C::kNBuf) * C::kBufBytes;
-            wait_vmcnt(dma_w * min(C::kNBuf - 2, n_tiles - 1 - it));
-            __syncthreads();     // every wave's pieces of tile `it` landed; tile it-1 is done
-            if (it + C::kNBuf - 1 < n_tiles) {
-                const int nt = it + C::kNBuf - 1;
-                issue_tile<C>(p.cache, lds_slots + nt * kTile, min(kTile, n_valid - nt * kTile),
-                              ring + (nt % C::kNBuf) * C::kBufBytes, wave, lane);
-            }
-
-            // ---- read this wave's K fragments (rows 16*rb + n16), all at once
-            f32x4 acc[RB][HBW];
+            for (int rb = 0; rb < RB; ++rb)
+                rf[rb] = *(const bf16x8 *)(buf + rb * RBB + off_k + RowFmt<FMT>::kRope + 64 * dh + 16 * g);
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-                for (int hb = 0; hb < HBW; ++hb)
-                    acc[rb][hb] = f32x4{0.f, 0.f, 0.f, 0.f};
-            f32x4 sc[2][RB];            // fp8: scales of rows 16*rb + 4g + i, groups 2*dh + gi
-            if constexpr (FMT == kCacheFp8) {
-                uint2 kf[2][4][RB];
-                bf16x8 rf[RB];
-#pragma unroll
-                for (int gi = 0; gi < 2; ++gi)
-#pragma unroll
-                    for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-                        for (int rb = 0; rb < RB; ++rb)
-                            kf[gi][kk][rb] = *(const uint2 *)(buf + (16 * rb + n16) * ROWB +
-                                                              128 * (2 * dh + gi) + 32 * kk + 8 * g);
-#pragma unroll
-                for (int rb = 0; rb < RB; ++rb)
-                    rf[rb] = *(const bf16x8 *)(buf + (16 * rb + n16) * ROWB + RowFmt<FMT>::kRope + 64 * dh + 16 * g);
-#pragma unroll
-                for (int gi = 0; gi < 2; ++gi)
-#pragma unroll
-                    for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-                        for (int i = 0; i < 4; ++i)
-                            sc[gi][rb][i] = *(const float *)(buf + (16 * rb + 4 * g + i) * ROWB + 512 + 4 * (2 * dh + gi));
-                // S^T = K q^T: each 128-column group's partial sum times its row scales
-#pragma unroll
-                for (int gi = 0; gi < 2; ++gi) {
-                    f32x4 part[RB][HBW];
-#pragma unroll
-                    for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-                        for (int hb = 0; hb < HBW; ++hb)
-                            part[rb][hb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-                        for (int rb = 0; rb < RB; ++rb) {
-                            const bf16x8 a = e4m3x8_to_bf16x8(kf[gi][kk][rb]);
-#pragma unroll
-                            for (int hb = 0; hb < HBW; ++hb)
-                                part[rb][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                                    a, qb[hb][4 * gi + kk], part[rb][hb], 0, 0, 0);
-                        }
-#pragma unroll
-                    for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-                        for (int hb = 0; hb < HBW; ++hb)
-                            acc[rb][hb] += sc[gi][rb] * part[rb][hb];
+                for (int i = 0; i < 4; ++i) {
+                    const float2 v = *(const float2 *)(buf + rb * RBB + off_sc + i * RS + 512 + 8 * dh);
+                    sc[0][rb][i] = v.x;
+                    sc[1][rb][i] = v.y;
                 }
-#pragma unroll
-                for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-                    for (int hb = 0; hb < HBW; ++hb)
-                        acc[rb][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(rf[rb], qb[hb][8], acc[rb][hb], 0, 0, 0);
-            } else {
-#pragma unroll
-                for (int k = 0; k < 9; ++k) {
-                    const int col = k < 8 ? 2 * (256 * dh + 32 * k + 8 * g) : RowFmt<FMT>::kRope + 64 * dh + 16 * g;
-#pragma unroll
-                    for (int rb = 0; rb < RB; ++rb) {
-                        const bf16x8 a = *(const bf16x8 *)(buf + (16 * rb + n16) * ROWB + col);
-#pragma unroll
-                        for (int hb = 0; hb < HBW; ++hb)
-                            acc[rb][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qb[hb][k], acc[rb][hb], 0, 0, 0);
-                    }
-                }
-            }
-
-            // ---- V^T fragments for PV (independent of the softmax): read them now,
-            //      so their latency hides behind the exchange barrier
-            uint2 vf8[16];
-            if constexpr (FMT == kCacheFp8) {
-#pragma unroll
-                for (int db = 0; db < 16; ++db) {
-                    // source lane n16 = 2k + h: row k of {4g..4g+3, 16+4g..16+4g+3}, bytes 8h..8h+7
-                    const int k = n16 >> 1;
-                    const int row = (k < 4 ? 4 * g + k : 16 + 4 * g + (k - 4));
-                    const i32x2 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-                        LDS_PTR(i32x2, buf + row * ROWB + 256 * dh + 16 * db + 8 * (n16 & 1)));
-                    vf8[db] = make_uint2((uint32_t)v[0], (uint32_t)v[1]);
-                }
-            }
-
-            // ---- add the other column half's partial S^T (same lane slots)
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb)
+                acc[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int hb = 0; hb < HBW; ++hb)
-                    xchg[((wave * RB + rb) * HBW + hb) * 64 + lane] = acc[rb][hb];
-            __syncthreads();
+            for (int gi = 0; gi < 2; ++gi) {
+                // K fragments of column group 2*dh + gi
+                uint2 kf[4][RB];
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+                    for (int rb = 0; rb < RB; ++rb)
+                        kf[kk][rb] = *(const uint2 *)(buf + rb * RBB + off_k + 128 * (2 * dh + gi) + 32 * kk + 8 * g);
+                f32x4 part[RB];
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb)
+                    part[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+                    for (int rb = 0; rb < RB; ++rb)
+                        part[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            e4m3x8_to_bf16x8(kf[kk][rb]), qb[4 * gi + kk], part[rb], 0, 0, 0);
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb)
+                    acc[rb] += sc[gi][rb] * part[rb];
+            }
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-                for (int hb = 0; hb < HBW; ++hb)
-                    acc[rb][hb] += xchg[(((wave ^ 1) * RB + rb) * HBW + hb) * 64 + lane];
-
-            // ---- online softmax in log2 units (rows 16*rb + 4g + i >= n_tile masked).
-            //      The running max moves only when some row exceeds it by 2^8; the
-            //      test uses each lane's own rows, the move uses the whole head's max.
-            bool need = false;
-            float lmax[HBW];
-#pragma unroll
-            for (int hb = 0; hb < HBW; ++hb) {
-                lmax[hb] = -INFINITY;
-#pragma unroll
-                for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const float v = 16 * rb + 4 * g + i < n_tile ? acc[rb][hb][i] * c2 : -INFINITY;
-                        acc[rb][hb][i] = v;
-                        lmax[hb] = fmaxf(lmax[hb], v);
-                    }
-                need |= lmax[hb] > m_run[hb] + kLazyRescale;
-            }
-            if (__ballot(need) != 0) {
-#pragma unroll
-                for (int hb = 0; hb < HBW; ++hb) {
-                    float mx = lmax[hb];
-                    mx = fmaxf(mx, __shfl_xor(mx, 16));
-                    mx = fmaxf(mx, __shfl_xor(mx, 32));
-                    if (mx > m_run[hb] + kLazyRescale) {
-                        const float alpha = m_run[hb] == -INFINITY ? 0.f : exp2f(m_run[hb] - mx);
-                        l_part[hb] *= alpha;
-#pragma unroll
-                        for (int db = 0; db < 16; ++db)
-                            o[db][hb] *= alpha;
-                        m_run[hb] = mx;
-                    }
-                }
-            }
-#pragma unroll
-            for (int hb = 0; hb < HBW; ++hb)
-#pragma unroll
-                for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        acc[rb][hb][i] = exp2f(acc[rb][hb][i] - m_run[hb]);
-                        l_part[hb] += acc[rb][hb][i];
-                    }
-
-            // ---- O^T += V^T P^T over this wave's 256 output dims. fp8: the weights
-            //      of output group 2*dh + gi carry that group's row scales.
-            bf16x8 pb[2][HBW], pl[2][HBW];
-#pragma unroll
-            for (int gi = 0; gi < 2; ++gi)
-#pragma unroll
-                for (int hb = 0; hb < HBW; ++hb) {
-                    f32x4 p0 = acc[0][hb], p1 = acc[1][hb];
-                    if constexpr (FMT == kCacheFp8) {
-                        p0 *= sc[gi][0];
-                        p1 *= sc[gi][1];
-                    }
-                    if (exact_p)
-                        pack_p(p0, p1, pb[gi][hb], pl[gi][hb]);
-                    else
-                        pb[gi][hb] = __builtin_bit_cast(bf16x8, make_uint4(pack_bf16(p0[0], p0[1]), pack_bf16(p0[2], p0[3]),
-                                                                           pack_bf16(p1[0], p1[1]), pack_bf16(p1[2], p1[3])));
-                }
+                acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(rf[rb], qb[8], acc[rb], 0, 0, 0);
 #pragma unroll
             for (int db = 0; db < 16; ++db) {
-                const int gi = db >> 3;
+                const i32x2 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                    LDS_PTR(i32x2, buf + off_v8 + 256 * dh + 16 * db));
+                vf8[db] = make_uint2((uint32_t)v[0], (uint32_t)v[1]);
+            }
+        } else {
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb)
+                acc[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int k = 0; k < 9; ++k) {
+                const int col = k < 8 ? 2 * (256 * dh + 32 * k + 8 * g) : RowFmt<FMT>::kRope + 64 * dh + 16 * g;
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb) {
+                    const bf16x8 a = *(const bf16x8 *)(buf + rb * RBB + off_k + col);
+                    acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qb[k], acc[rb], 0, 0, 0);
+                }
+            }
+        }
+
+        // ---- add the other column half's partial S^T (same lane slots)
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+            xchg[(wave * RB + rb) * 64 + lane] = acc[rb];
+        __syncthreads();
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+            acc[rb] += xchg[((wave ^ 1) * RB + rb) * 64 + lane];
+
+        // ---- online softmax in log2 units. The running max moves only when
+        //      some row exceeds it by 2^8 (tested on each lane's own rows,
+        //      moved to the whole head's max).
+        float lmax = -INFINITY;
+        if (n_tile == kTile) {
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    acc[rb][i] *= c2;
+                    lmax = fmaxf(lmax, acc[rb][i]);
+                }
+        } else {
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    acc[rb][i] = 16 * rb + 4 * g + i < n_tile ? acc[rb][i] * c2 : -INFINITY;
+                    lmax = fmaxf(lmax, acc[rb][i]);
+                }
+        }
+        if (__ballot(lmax > m_run + kLazyRescale) != 0) {
+            float mx = fmaxf(lmax, __shfl_xor(lmax, 16));
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            if (mx > m_run + kLazyRescale) {
+                const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - mx);
+                l_part *= alpha;
+#pragma unroll
+                for (int db = 0; db < 16; ++db)
+                    o[db] *= alpha;
+                m_run = mx;
+            }
+        }
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                acc[rb][i] = __builtin_amdgcn_exp2f(acc[rb][i] - m_run);
+                l_part += acc[rb][i];
+            }
+
+        // ---- O^T += V^T P^T over this wave's 256 output dims. fp8: the weights
+        //      of output group 2*dh + gi carry that group's row scales.
+#pragma unroll
+        for (int gi = 0; gi < 2; ++gi) {
+            f32x4 p0 = acc[0], p1 = acc[1];
+            if constexpr (FMT == kCacheFp8) {
+                p0 *= sc[gi][0];
+                p1 *= sc[gi][1];
+            }
+            const bf16x8 pb = pack_p(p0, p1);
+#pragma unroll
+            for (int d8 = 0; d8 < 8; ++d8) {
+                const int db = 8 * gi + d8;
                 bf16x8 a;
                 if constexpr (FMT == kCacheFp8) {
                     a = e4m3x8_to_bf16x8(vf8[db]);
                 } else {
-                    // source lane n16 = 4k + a: row 4g + k (then 16 + 4g + k), dims 4a..4a+3
-                    const int k = n16 >> 2;
-                    const int colb = 2 * (256 * dh + 16 * db + 4 * (n16 & 3));
+                    const int colb = 2 * (256 * dh + 16 * db);
                     const uint2 w0 = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        LDS_PTR(i16x4, buf + (4 * g + k) * ROWB + colb)));
+                        LDS_PTR(i16x4, buf + off_v16 + colb)));
                     const uint2 w1 = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        LDS_PTR(i16x4, buf + (16 + 4 * g + k) * ROWB + colb)));
+                        LDS_PTR(i16x4, buf + RBB + off_v16 + colb)));
                     a = __builtin_bit_cast(bf16x8, make_uint4(w0.x, w0.y, w1.x, w1.y));
                 }
+                o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb, o[db], 0, 0, 0);
+            }
+            if (exact) {
+                // short lists: add the bf16 rounding residual of P as a second term
+                const bf16x8 pl = pack_p_residual(p0, p1, pb);
 #pragma unroll
-                for (int hb = 0; hb < HBW; ++hb)
-                    o[db][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[gi][hb], o[db][hb], 0, 0, 0);
-                if (exact_p) {
-#pragma unroll
-                    for (int hb = 0; hb < HBW; ++hb)
-                        o[db][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pl[gi][hb], o[db][hb], 0, 0, 0);
+                for (int d8 = 0; d8 < 8; ++d8) {
+                    const int db = 8 * gi + d8;
+                    bf16x8 a;
+                    if constexpr (FMT == kCacheFp8) {
+                        const i32x2 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                            LDS_PTR(i32x2, buf + off_v8 + 256 * dh + 16 * db));
+                        a = e4m3x8_to_bf16x8(make_uint2((uint32_t)v[0], (uint32_t)v[1]));
+                    } else {
+                        const int colb = 2 * (256 * dh + 16 * db);
+                        const uint2 w0 = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                            LDS_PTR(i16x4, buf + off_v16 + colb)));
+                        const uint2 w1 = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                            LDS_PTR(i16x4, buf + RBB + off_v16 + colb)));
+                        a = __builtin_bit_cast(bf16x8, make_uint4(w0.x, w0.y, w1.x, w1.y));
+                    }
+                    o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pl, o[db], 0, 0, 0);
                 }
             }
         }
-        __syncthreads();     // ring, exchange and slot list are free for the next round
-        // the next round's indices
+    };
+
+    for (;;) {
+#pragma unroll
+        for (int db = 0; db < 16; ++db)
+            o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+        m_run = -INFINITY;
+        l_part = 0.f;
+        // the splits of head block 0 write the converted slots (a recompute does not repeat it)
+        const bool write_phys = p.phys_out != nullptr && hb_wg == 0 && (p.S == 1 || !solo);
+
+        int idxv[kPer];
 #pragma unroll
         for (int j = 0; j < kPer; ++j) {
-            const int i = chunk0 + kMaxChunk + tid + C::kThreads * j;
-            idxv[j] = i < pos_end ? topk_row[i] : -1;
+            const int i = pos_begin + tid + C::kThreads * j;
+            idxv[j] = i < min(pos_end, pos_begin + kMaxChunk) ? topk_row[i] : -1;
         }
-    }
 
-    // ---- epilogue. m_run and the row sums are identical in both column halves.
-    float inv_l[HBW], lse_v[HBW];
-#pragma unroll
-    for (int hb = 0; hb < HBW; ++hb) {
-        float l = l_part[hb];
-        l += __shfl_xor(l, 16);
-        l += __shfl_xor(l, 32);
-        inv_l[hb] = l > 0.f ? 1.f / l : 0.f;
-        lse_v[hb] = l > 0.f ? (m_run[hb] + log2f(l)) * 0.69314718055994531f : -INFINITY;
-    }
-    const int wg_head0 = hb_wg * C::kHeads;
+        for (int chunk0 = pos_begin; chunk0 < pos_end; chunk0 += kMaxChunk) {
+            const int chunk_n = min(kMaxChunk, pos_end - chunk0);
 
-    if (p.S == 1) {
-        // stage bf16 rows [head][512] in LDS, then write them out coalesced
-        uint16_t *stage = (uint16_t *)smem;
+            // ---- convert (all lookups in flight together), then compact the valid
+            //      slots in list order with one exchange of per-wave counts
+            int slotv[kPer];
 #pragma unroll
-        for (int db = 0; db < 16; ++db)
+            for (int j = 0; j < kPer; ++j)
+                slotv[j] = convert_slot(req, idxv[j], p.bt, p.R, p.MB, p.NB);
+            if (write_phys) {
 #pragma unroll
-            for (int hb = 0; hb < HBW; ++hb) {
-                const f32x4 v = o[db][hb] * inv_l[hb];
-                *(uint2 *)(stage + (hh * HPW + 16 * hb + n16) * kDv + 256 * dh + 16 * db + 4 * g) =
-                    make_uint2(pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3]));
-            }
-        if (dh == 0 && g == 0 && p.lse != nullptr)
-#pragma unroll
-            for (int hb = 0; hb < HBW; ++hb)
-                p.lse[(size_t)t * p.H + head0 + 16 * hb + n16] = lse_v[hb];
-        __syncthreads();
-        uint16_t *dst = p.out + ((size_t)t * p.H + wg_head0) * kDv;
-        for (int u = tid; u < C::kHeads * kDv / 8; u += C::kThreads)
-            *(uint4 *)(dst + 8 * u) = *(const uint4 *)(stage + 8 * u);
-        return;
-    }
-
-    // ---- top-k split: publish the fp32 partial (O / l) and lse with device-scope
-    //      stores, count this arrival; the last of the token's splits merges.
-    {
-        float *po = p.part_o + (((size_t)t * p.S + s) * p.H + head0) * kDv;
-#pragma unroll
-        for (int db = 0; db < 16; ++db)
-#pragma unroll
-            for (int hb = 0; hb < HBW; ++hb)
-                store_dev_x4(po + (16 * hb + n16) * kDv + 256 * dh + 16 * db + 4 * g, o[db][hb] * inv_l[hb]);
-        if (dh == 0 && g == 0)
-#pragma unroll
-            for (int hb = 0; hb < HBW; ++hb)
-                __hip_atomic_store(p.part_lse + ((size_t)t * p.S + s) * p.H + head0 + 16 * hb + n16, lse_v[hb],
-                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");    // this thread's partial stores completed
-    __syncthreads();
-    if (tid == 0) {
-        const int prev = atomicAdd(p.counters + (size_t)t * p.HB + hb_wg, 1);
-        lds_misc[0] = prev == p.S - 1;
-    }
-    __syncthreads();
-    if (!lds_misc[0])
-        return;
-    for (int u = tid; u < C::kHeads * (kDv / 8); u += C::kThreads) {
-        const int hl = u / (kDv / 8);
-        const int d0 = (u % (kDv / 8)) * 8;
-        const int head = wg_head0 + hl;
-        const size_t base = (size_t)t * p.S * p.H + head;
-        float M = -INFINITY;
-        for (int s2 = 0; s2 < p.S; ++s2)
-            M = fmaxf(M, __hip_atomic_load(p.part_lse + base + (size_t)s2 * p.H, __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_AGENT));
-        float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        float W = 0.f;
-        if (M != -INFINITY) {
-            for (int s2 = 0; s2 < p.S; ++s2) {
-                const float w = expf(__hip_atomic_load(p.part_lse + base + (size_t)s2 * p.H, __ATOMIC_RELAXED,
-                                                       __HIP_MEMORY_SCOPE_AGENT) - M);
-                const float *src = p.part_o + (base + (size_t)s2 * p.H) * kDv + d0;
-                f32x4 a, b;
-                load_dev_2x4(src, src + 4, a, b);
-                W += w;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    v[e] += w * a[e];
-                    v[4 + e] += w * b[e];
+                for (int j = 0; j < kPer; ++j) {
+                    const int i = tid + C::kThreads * j;
+                    if (i < chunk_n)
+                        p.phys_out[(size_t)t * p.K + chunk0 + i] = slotv[j];
                 }
             }
+            uint64_t masks[kPer];
+#pragma unroll
+            for (int j = 0; j < kPer; ++j) {
+                masks[j] = __ballot(slotv[j] >= 0);
+                if (lane == 0)
+                    lds_misc[16 + j * C::kWaves + wave] = __popcll(masks[j]);
+            }
+            __syncthreads();
+            int n_valid = 0;
+#pragma unroll
+            for (int j = 0; j < kPer; ++j) {
+#pragma unroll
+                for (int w = 0; w < C::kWaves; ++w) {
+                    const int cw = lds_misc[16 + j * C::kWaves + w];
+                    if (w == wave && slotv[j] >= 0)
+                        lds_slots[n_valid + __popcll(masks[j] & ((1ull << lane) - 1ull))] = slotv[j];
+                    n_valid += cw;
+                }
+            }
+            __syncthreads();
+            const bool exact_p = n_valid <= kExactPRows;
+            const int n_tiles = (n_valid + kTile - 1) / kTile;
+            // from here on the only vector-memory instructions in flight are tile copies
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            // this wave's copy instructions per tile
+            const int dma_w = (C::kDmaInstr - wave + C::kWaves - 1) / C::kWaves;
+
+            for (int i = 0; i < min(C::kNBuf - 1, n_tiles); ++i)
+                issue_tile<C>(p.cache, lds_slots + i * kTile, min(kTile, n_valid - i * kTile),
+                              ring + i * C::kBufBytes, wave, lane);
+
+            for (int it = 0; it < n_tiles; ++it) {
+                wait_vmcnt(dma_w * min(C::kNBuf - 2, n_tiles - 1 - it));
+                __syncthreads();     // every wave's pieces of tile `it` landed; tile it-1 is done
+                if (it + C::kNBuf - 1 < n_tiles) {
+                    const int nt = it + C::kNBuf - 1;
+                    issue_tile<C>(p.cache, lds_slots + nt * kTile, min(kTile, n_valid - nt * kTile),
+                                  ring + (nt % C::kNBuf) * C::kBufBytes, wave, lane);
+                }
+                tile(ring + (it % C::kNBuf) * C::kBufBytes, min(kTile, n_valid - it * kTile), exact_p);
+            }
+            __syncthreads();     // ring, exchange and slot list are free for the next round
+            // the next round's indices
+#pragma unroll
+            for (int j = 0; j < kPer; ++j) {
+                const int i = chunk0 + kMaxChunk + tid + C::kThreads * j;
+                idxv[j] = i < pos_end ? topk_row[i] : -1;
+            }
         }
-        const float inv = W > 0.f ? 1.f / W : 0.f;
-        *(uint4 *)(p.out + ((size_t)t * p.H + head) * kDv + d0) =
-            make_uint4(pack_bf16(v[0] * inv, v[1] * inv), pack_bf16(v[2] * inv, v[3] * inv),
-                       pack_bf16(v[4] * inv, v[5] * inv), pack_bf16(v[6] * inv, v[7] * inv));
-        if (d0 == 0 && p.lse != nullptr)
-            p.lse[(size_t)t * p.H + head] = W > 0.f ? M + logf(W) : -INFINITY;
+
+        // ---- per-head results. m_run and the row sums are the same in both halves.
+        float l = l_part;
+        l += __shfl_xor(l, 16);
+        l += __shfl_xor(l, 32);
+        const float inv_l = l > 0.f ? 1.f / l : 0.f;
+        // natural-log LSE; v_log_f32 is log2 (l >= 1 here: the row that set m_run adds >= 1)
+        const float lse_v = l > 0.f ? (m_run + __builtin_amdgcn_logf(l)) * 0.69314718055994531f : -INFINITY;
+
+        if (solo) {
+            out_scale = inv_l;
+            out_lse = lse_v;
+            break;
+        }
+
+        // ---- top-k split: publish this split's fp32 partial (O / l) and lse with
+        //      plain stores; they land in this XCD's L2.
+        {
+            float *po = p.part_o + (((size_t)t * p.S + s) * p.H + head) * kDv + 256 * dh + 4 * g;
+#pragma unroll
+            for (int db = 0; db < 16; ++db)
+                *(f32x4 *)(po + 16 * db) = o[db] * inv_l;
+            if (dh == 0 && g == 0)
+                p.part_lse[((size_t)t * p.S + s) * p.H + head] = lse_v;
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");    // this thread's stores reached L2
+        __syncthreads();
+        if (tid == 0) {
+            // one atomic adds this arrival to the total (bits 48..63) and to this
+            // XCD's count (6 bits at 6 * xcd); splits never exceed 32
+            const uint32_t x = xcc_id();
+            const uint64_t inc = (1ull << 48) | (x < 8 ? 1ull << (6 * x) : 0ull);
+            uint64_t *word = p.arrivals + (size_t)t * p.HB + hb_wg;
+            const uint64_t now = __hip_atomic_fetch_add(word, inc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + inc;
+            int verdict = 0;                                     // 0: not the last arrival
+            if ((now >> 48) == (uint64_t)p.S) {
+                const bool local = x < 8 && ((now >> (6 * x)) & 63u) == (uint64_t)p.S;
+                verdict = (local && !p.force_recompute) ? 1 : 2; // 1: merge, 2: recompute
+                __hip_atomic_store(word, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+            lds_misc[0] = verdict;
+        }
+        __syncthreads();
+        const int verdict = lds_misc[0];
+        if (verdict == 0)
+            return;
+        if (verdict == 1) {
+            // ---- last arrival, on the XCD of every split: merge through the shared
+            //      L2 (this CU's L1 is invalidated first so every load reaches L2).
+            //      This split's own partial is still in registers.
+            asm volatile("buffer_inv sc0" ::: "memory");
+            const float *plse = p.part_lse + (size_t)t * p.S * p.H + head;
+            float M = lse_v;
+            for (int s2 = 0; s2 < p.S; ++s2)
+                M = fmaxf(M, plse[(size_t)s2 * p.H]);
+            const float w_me = M == -INFINITY ? 0.f : __expf(lse_v - M);
+            float W = w_me;
+#pragma unroll
+            for (int db = 0; db < 16; ++db)
+                o[db] *= inv_l * w_me;
+            for (int s2 = 0; s2 < p.S; ++s2) {
+                if (s2 == s)
+                    continue;
+                const float ws = M == -INFINITY ? 0.f : __expf(plse[(size_t)s2 * p.H] - M);
+                W += ws;
+                const float *src = p.part_o + (((size_t)t * p.S + s2) * p.H + head) * kDv + 256 * dh + 4 * g;
+#pragma unroll
+                for (int h8 = 0; h8 < 2; ++h8) {     // eight loads in flight at a time
+                    f32x4 v[8];
+#pragma unroll
+                    for (int d = 0; d < 8; ++d)
+                        v[d] = *(const f32x4 *)(src + 16 * (8 * h8 + d));
+#pragma unroll
+                    for (int d = 0; d < 8; ++d)
+                        o[8 * h8 + d] += ws * v[d];
+                }
+            }
+            out_scale = W > 0.f ? 1.f / W : 0.f;
+            out_lse = W > 0.f ? M + logf(W) : -INFINITY;
+            break;
+        }
+        // some split ran on another XCD, whose partial may sit in another L2:
+        // compute the whole list here instead
+        solo = true;
+        pos_begin = 0;
+        pos_end = p.K;
+        __syncthreads();     // every wave has read the verdict before LDS is reused
     }
+
+    // ---- output rows of this workgroup's heads: staged as bf16 [head][512] in
+    //      LDS (free now), then written out coalesced
+    uint16_t *stage = (uint16_t *)smem;
+#pragma unroll
+    for (int db = 0; db < 16; ++db) {
+        const f32x4 v = o[db] * out_scale;
+        *(uint2 *)(stage + (16 * hh + n16) * kDv + 256 * dh + 16 * db + 4 * g) =
+            make_uint2(pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3]));
+    }
+    if (dh == 0 && g == 0 && p.lse != nullptr)
+        p.lse[(size_t)t * p.H + head] = out_lse;
+    __syncthreads();
+    uint16_t *dst = p.out + ((size_t)t * p.H + wg_head0) * kDv;
+    for (int u = tid; u < C::kHeads * kDv / 8; u += C::kThreads)
+        *(uint4 *)(dst + 8 * u) = *(const uint4 *)(stage + 8 * u);
 }
 
-__global__ __launch_bounds__(256) void zero_kernel(int32_t *__restrict__ p, int n)
+__global__ __launch_bounds__(256) void zero_kernel(uint32_t *__restrict__ p, int64_t n)
 {
-    for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256)
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
         p[i] = 0;
 }
 
@@ -676,13 +705,13 @@ __global__ __launch_bounds__(256) void convert_kernel(const int32_t *__restrict_
     }
 }
 
-template <int FMT, int HPW, int NHH>
+template <int FMT, int NHH>
 hipError_t launch_one(const KParams &p, hipStream_t stream)
 {
-    using C = Cfg<FMT, HPW, NHH>;
+    using C = Cfg<FMT, NHH>;
     const int64_t tq = (p.T + 7) / 8;
     const dim3 grid((unsigned)(tq * 8 * p.S * p.HB));
-    hipLaunchKernelGGL((attn_kernel<FMT, HPW, NHH>), grid, dim3(C::kThreads), 0, stream, p);
+    hipLaunchKernelGGL((attn_kernel<FMT, NHH>), grid, dim3(C::kThreads), 0, stream, p);
     return hipGetLastError();
 }
 
@@ -690,13 +719,24 @@ template <int FMT>
 hipError_t launch_fmt(const KParams &p, hipStream_t stream)
 {
     if (p.H >= 64)
-        return launch_one<FMT, 32, 2>(p, stream);
+        return launch_one<FMT, 4>(p, stream);
     if (p.H == 32)
-        return launch_one<FMT, 32, 1>(p, stream);
-    return launch_one<FMT, 16, 1>(p, stream);
+        return launch_one<FMT, 2>(p, stream);
+    return launch_one<FMT, 1>(p, stream);
 }
 
 }  // namespace
+
+hipError_t launch_zero(void *ptr, size_t bytes, hipStream_t stream)
+{
+    const int64_t n = (int64_t)(bytes / 4);
+    if (n == 0)
+        return hipSuccess;
+    const int64_t blocks = (n + 255) / 256;
+    hipLaunchKernelGGL(zero_kernel, dim3((unsigned)(blocks < 4096 ? blocks : 4096)), dim3(256), 0, stream,
+                       (uint32_t *)ptr, n);
+    return hipGetLastError();
+}
 
 hipError_t launch_convert(const int32_t *req_id, const int32_t *block_table, const int32_t *topk,
                           int32_t *out, int num_tokens, int topk_len, int num_reqs, int max_blocks,
@@ -710,7 +750,8 @@ hipError_t launch_convert(const int32_t *req_id, const int32_t *block_table, con
     return hipGetLastError();
 }
 
-hipError_t launch_attention(CacheFormat fmt, const AttnArgs &a, const Plan &pl, hipStream_t stream)
+hipError_t launch_attention(CacheFormat fmt, const AttnArgs &a, const Plan &pl, bool counters_clean,
+                            bool force_recompute, hipStream_t stream)
 {
     KParams p;
     p.q = (const uint16_t *)a.q;
@@ -722,10 +763,9 @@ hipError_t launch_attention(CacheFormat fmt, const AttnArgs &a, const Plan &pl, 
     p.lse = a.lse;
     p.phys_out = a.phys_out;
     const bool split = pl.num_splits > 1;
+    p.arrivals = split ? (uint64_t *)((char *)a.workspace + pl.counters_off) : nullptr;
     p.part_o = split ? (float *)((char *)a.workspace + pl.part_o_off) : nullptr;
     p.part_lse = split ? (float *)((char *)a.workspace + pl.part_lse_off) : nullptr;
-    p.counters = split ? (int32_t *)((char *)a.workspace + pl.counters_off) : nullptr;
-    p.sm_scale = a.sm_scale;
     p.log2e_scale = a.sm_scale * 1.4426950408889634f;
     p.T = a.num_tokens;
     p.H = a.h_q;
@@ -736,12 +776,9 @@ hipError_t launch_attention(CacheFormat fmt, const AttnArgs &a, const Plan &pl, 
     p.S = pl.num_splits;
     p.split_len = pl.split_len;
     p.HB = pl.head_blocks;
-    if (split) {
-        const int n = a.num_tokens * pl.head_blocks;
-        const int blocks = (n + 255) / 256;
-        hipLaunchKernelGGL(zero_kernel, dim3(blocks < 1024 ? blocks : 1024), dim3(256), 0, stream,
-                           p.counters, n);
-        const hipError_t err = hipGetLastError();
+    p.force_recompute = force_recompute ? 1 : 0;
+    if (split && !(counters_clean && pl.counters_in_block)) {
+        const hipError_t err = launch_zero(p.arrivals, pl.counters_bytes, stream);
         if (err != hipSuccess)
             return err;
     }

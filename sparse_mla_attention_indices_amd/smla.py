@@ -24,7 +24,9 @@ SMLA_OK = 0
 STATUS_NAMES = {0: "SMLA_OK", 1: "SMLA_ERR_NULL", 2: "SMLA_ERR_SHAPE", 3: "SMLA_ERR_ALIGN",
                 4: "SMLA_ERR_WORKSPACE", 5: "SMLA_ERR_HIP", 6: "SMLA_ERR_ARG"}
 EXPORTS = ("smla_status_string", "smla_abi_version", "smla_plan", "smla_workspace_size",
-           "smla_convert_indices", "smla_prefill_bf16", "smla_decode_fp8")
+           "smla_workspace_init", "smla_convert_indices", "smla_prefill_bf16", "smla_decode_fp8")
+FLAG_WORKSPACE_READY = 0x1
+FLAG_TEST_SPLIT_RECOMPUTE = 0x2
 
 
 class SmlaError(RuntimeError):
@@ -34,7 +36,8 @@ class SmlaError(RuntimeError):
 
 
 class SmlaOptions(ctypes.Structure):
-    _fields_ = [("num_splits", ctypes.c_int32), ("reserved", ctypes.c_int32 * 7)]
+    _fields_ = [("num_splits", ctypes.c_int32), ("flags", ctypes.c_uint32),
+                ("reserved", ctypes.c_int32 * 6)]
 
 
 _lib = None
@@ -59,6 +62,8 @@ def library() -> ctypes.CDLL:
     lib.smla_plan.argtypes = [i32, i32, i32, i32, vp, ctypes.POINTER(i32), ctypes.POINTER(sz)]
     lib.smla_workspace_size.restype = ctypes.c_int
     lib.smla_workspace_size.argtypes = [i32, i32, i32, vp, ctypes.POINTER(sz)]
+    lib.smla_workspace_init.restype = ctypes.c_int
+    lib.smla_workspace_init.argtypes = [vp, sz, vp]
     lib.smla_convert_indices.restype = ctypes.c_int
     lib.smla_convert_indices.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i64, vp]
     attn = [vp, vp, vp, vp, vp, fl, i32, i32, i32, i32, i32, i64, vp, vp, vp, vp, sz, vp, vp]
@@ -74,11 +79,12 @@ def _check(status: int, where: str) -> None:
         raise SmlaError(status, where)
 
 
-def _options(num_splits: int):
-    if not num_splits:
+def _options(num_splits: int, flags: int = 0):
+    if not num_splits and not flags:
         return None
     o = SmlaOptions()
     o.num_splits = int(num_splits)
+    o.flags = int(flags)
     return ctypes.byref(o)
 
 
@@ -121,6 +127,29 @@ def smla_workspace_size(num_tokens: int, h_q: int, topk: int, num_splits: int = 
     return b.value
 
 
+def smla_workspace_init(workspace: torch.Tensor, stream=None) -> torch.Tensor:
+    """Zero the counter block of a workspace so calls may pass workspace_ready=True."""
+    _check(library().smla_workspace_init(_dev(workspace, "workspace"),
+                                         workspace.numel() * workspace.element_size(),
+                                         _stream(stream)), "smla_workspace_init")
+    return workspace
+
+
+# Workspaces the binding allocates itself, one per (device, stream), grown on
+# demand and initialised once, so repeated calls skip the clearing launch.
+_own_workspaces: dict = {}
+
+
+def _own_workspace(device: torch.device, stream, need: int) -> torch.Tensor:
+    key = (device.index, _stream(stream))
+    ws = _own_workspaces.get(key)
+    if ws is None or ws.numel() < need:
+        ws = torch.empty(need, dtype=torch.uint8, device=device)
+        smla_workspace_init(ws, stream)
+        _own_workspaces[key] = ws
+    return ws
+
+
 def smla_convert_indices(req_id_per_token, block_table, topk_indices, num_blocks: int,
                          out=None, stream=None):
     """Logical top-k indices -> physical cache slots (int32, -1 = invalid)."""
@@ -137,7 +166,8 @@ def smla_convert_indices(req_id_per_token, block_table, topk_indices, num_blocks
 
 
 def _attention(name: str, q, kv_cache, block_table, req_id_per_token, topk_indices, sm_scale,
-               out, lse, phys_indices_out, workspace, num_splits, stream, want_lse):
+               out, lse, phys_indices_out, workspace, num_splits, stream, want_lse, workspace_ready,
+               flags):
     T, H, D = q.shape
     if D != 576:
         raise ValueError("q must be [num_tokens, h_q, 576]")
@@ -148,7 +178,13 @@ def _attention(name: str, q, kv_cache, block_table, req_id_per_token, topk_indic
         lse = torch.empty((T, H), dtype=torch.float32, device=q.device)
     if workspace is None:
         need = smla_workspace_size(T, H, K, num_splits)
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+        if need > 0:
+            workspace = _own_workspace(q.device, stream, need)
+            workspace_ready = True
+    if workspace_ready:
+        flags |= FLAG_WORKSPACE_READY
+    ws_ptr = _dev(workspace, "workspace") if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     fn = getattr(library(), name)
     _check(fn(_dev(q, "q", torch.bfloat16, 3), _dev(kv_cache, "kv_cache"),
               _dev(block_table, "block_table", torch.int32, 2),
@@ -157,26 +193,34 @@ def _attention(name: str, q, kv_cache, block_table, req_id_per_token, topk_indic
               block_table.shape[0], block_table.shape[1], kv_cache.shape[0],
               _dev(out, "out", torch.bfloat16, 3), _dev(lse, "lse", torch.float32, 2),
               _dev(phys_indices_out, "phys_indices_out", torch.int32, 2),
-              _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
-              _options(num_splits), _stream(stream)), name)
+              ws_ptr, ws_bytes, _options(num_splits, flags), _stream(stream)), name)
     return out, lse
 
 
 def smla_prefill_bf16(q, kv_cache, block_table, req_id_per_token, topk_indices, sm_scale,
                       out=None, lse=None, phys_indices_out=None, workspace=None, num_splits=0,
-                      stream=None, want_lse=True):
-    """Sparse MLA forward over a bf16 cache [num_blocks, 64, 576]. Returns (out, lse)."""
+                      stream=None, want_lse=True, workspace_ready=False, flags=0):
+    """Sparse MLA forward over a bf16 cache [num_blocks, 64, 576]. Returns (out, lse).
+
+    workspace: uint8 device tensor of at least smla_workspace_size bytes, or None for
+    one the binding keeps per (device, stream). workspace_ready: the given workspace
+    went through smla_workspace_init and only completed calls since. flags: extra
+    SMLA_FLAG_* bits (FLAG_TEST_SPLIT_RECOMPUTE)."""
     if kv_cache.dtype != torch.bfloat16 or kv_cache.shape[1:] != (64, 576):
         raise ValueError("kv_cache must be bf16 [num_blocks, 64, 576]")
     return _attention("smla_prefill_bf16", q, kv_cache, block_table, req_id_per_token, topk_indices,
-                      sm_scale, out, lse, phys_indices_out, workspace, num_splits, stream, want_lse)
+                      sm_scale, out, lse, phys_indices_out, workspace, num_splits, stream, want_lse,
+                      workspace_ready, flags)
 
 
 def smla_decode_fp8(q, kv_cache, block_table, req_id_per_token, topk_indices, sm_scale,
                     out=None, lse=None, phys_indices_out=None, workspace=None, num_splits=0,
-                    stream=None, want_lse=True):
-    """Sparse MLA forward over an fp8_ds_mla cache uint8 [num_blocks, 64, 656]. Returns (out, lse)."""
+                    stream=None, want_lse=True, workspace_ready=False, flags=0):
+    """Sparse MLA forward over an fp8_ds_mla cache uint8 [num_blocks, 64, 656]. Returns (out, lse).
+
+    Other arguments as for smla_prefill_bf16."""
     if kv_cache.dtype != torch.uint8 or kv_cache.shape[1:] != (64, 656):
         raise ValueError("kv_cache must be uint8 [num_blocks, 64, 656]")
     return _attention("smla_decode_fp8", q, kv_cache, block_table, req_id_per_token, topk_indices,
-                      sm_scale, out, lse, phys_indices_out, workspace, num_splits, stream, want_lse)
+                      sm_scale, out, lse, phys_indices_out, workspace, num_splits, stream, want_lse,
+                      workspace_ready, flags)

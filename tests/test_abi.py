@@ -39,7 +39,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_abi_version(lib):
-    assert smla.smla_abi_version() == 1
+    assert smla.smla_abi_version() == 2
 
 
 def test_status_strings(lib):
@@ -53,9 +53,9 @@ def test_plan_fills_the_chip_for_small_decode_batches(lib):
     assert s == 4
     up = lambda v: -(-v // 256) * 256
     rows = 64 * 4 * 64
-    lse_off = up(rows * 512 * 4)
-    counters_off = up(lse_off + rows * 4)
-    assert ws == up(counters_off + 64 * 1 * 4)
+    counter_block = 4096 * 8                 # fixed block of arrival counters first
+    o_off = up(counter_block + rows * 4)     # then the partial lse, then the partial o
+    assert ws == up(o_off + rows * 512 * 4)
     # two-wave workgroups (h_q <= 32) fit two per CU: 256 tokens x 16 heads -> 2 splits
     assert smla.smla_plan(256, 16, 2048, 256)[0] == 2
     # enough (token, head-block) units already: no split, no workspace
@@ -68,6 +68,19 @@ def test_plan_fills_the_chip_for_small_decode_batches(lib):
     assert smla.smla_plan(8, 16, 64, 256, num_splits=3)[0] == 3
     assert smla.smla_plan(8, 16, 5, 256, num_splits=9)[0] == 5
     assert smla.smla_plan(0, 16, 64, 256) == (1, 0)
+    # never more than 32 parts, forced or planned
+    assert smla.smla_plan(8, 16, 4096, 256, num_splits=100)[0] == 32
+    assert smla.smla_plan(1, 16, 16384, 256)[0] == 32
+
+
+def test_plan_counters_beyond_the_fixed_block(lib):
+    # 5000 (token, head block) units > 4096: the counters grow past the block and
+    # the partial results move behind them
+    up = lambda v: -(-v // 256) * 256
+    s, ws = smla.smla_plan(5000, 16, 64, 256, num_splits=2)
+    rows = 5000 * 2 * 16
+    o_off = up(up(5000 * 8) + rows * 4)
+    assert s == 2 and ws == up(o_off + rows * 512 * 4)
 
 
 @pytest.mark.parametrize("args,code", [
@@ -90,6 +103,11 @@ def test_plan_rejects_bad_options(lib):
     o = smla.SmlaOptions()
     o.num_splits = -2
     assert lib.smla_plan(8, 16, 64, 256, ctypes.byref(o), ctypes.byref(s), ctypes.byref(b)) == 6
+    o = smla.SmlaOptions()
+    o.flags = 0x4                            # unknown flag bit
+    assert lib.smla_plan(8, 16, 64, 256, ctypes.byref(o), ctypes.byref(s), ctypes.byref(b)) == 6
+    o.flags = smla.FLAG_WORKSPACE_READY | smla.FLAG_TEST_SPLIT_RECOMPUTE
+    assert lib.smla_plan(8, 16, 64, 256, ctypes.byref(o), ctypes.byref(s), ctypes.byref(b)) == 0
     assert lib.smla_plan(8, 16, 64, 256, None, None, ctypes.byref(b)) == 1
 
 
@@ -122,12 +140,27 @@ def test_attention_rejects_bad_options(lib, name):
     o = smla.SmlaOptions()
     o.num_splits = -1
     assert _attn(lib, name, opts=ctypes.byref(o)) == 6
+    o = smla.SmlaOptions()
+    o.flags = 0x80000000
+    assert _attn(lib, name, opts=ctypes.byref(o)) == 6
 
 
 @pytest.mark.parametrize("name", ["smla_decode_fp8", "smla_prefill_bf16"])
 def test_zero_tokens_is_a_noop(lib, name):
     # no pointer is needed and nothing is launched
     assert _attn(lib, name, q=None, kv=None, bt=None, req=None, idx=None, out=None, T=0) == 0
+
+
+def test_options_struct_layout():
+    # num_splits, flags, reserved[6]: 32 bytes, as in include/smla.h
+    assert ctypes.sizeof(smla.SmlaOptions) == 32
+    assert smla.SmlaOptions.flags.offset == 4 and smla.SmlaOptions.reserved.offset == 8
+
+
+def test_workspace_init_validation(lib):
+    assert lib.smla_workspace_init(None, 0, None) == 0          # nothing to do, no HIP call
+    assert lib.smla_workspace_init(None, 1024, None) == 1
+    assert lib.smla_workspace_init(A16 + 16, 1024, None) == 3
 
 
 def test_workspace_size_validation(lib):
