@@ -63,6 +63,9 @@ typedef __bf16 bf16x2 __attribute__((__vector_size__(4)));
 typedef short i16x4 __attribute__((__vector_size__(8)));
 typedef int i32x2 __attribute__((__vector_size__(8)));
 typedef float f32x4 __attribute__((__vector_size__(16)));
+typedef float f32x2 __attribute__((__vector_size__(8)));
+typedef int i32x8 __attribute__((__vector_size__(32)));
+typedef short s16x2 __attribute__((__vector_size__(4)));
 
 #define LDS_PTR(T, p) ((__attribute__((address_space(3))) T *)(p))
 
@@ -106,19 +109,28 @@ struct Cfg {
     static constexpr int kTileSlots = kRB * kSlotsPerBlock;
     static constexpr int kDmaInstr = (kTileSlots + 63) / 64;         // wave instructions per tile
     static constexpr int kBufBytes = kDmaInstr * 1024;               // ring buffer stride
-    // 64 heads: one workgroup per CU and a deep ring. Fewer heads: two
-    // workgroups per CU share the LDS (fp8).
-    static constexpr int kNBuf = NHH == 4 ? (FMT == kCacheFp8 ? 5 : 3) : 2;
+    // 64 heads: one workgroup per CU; fewer heads: two workgroups per CU
+    // share the LDS (fp8).
+    static constexpr int kNBuf = NHH == 4 ? (FMT == kCacheFp8 ? 4 : 2) : 2;
+    // PV is split by output dims: wave w owns dims [w * kDimsPerWave, ...) of
+    // every head of the workgroup, kDimBlocks blocks of 16 dims.
+    static constexpr int kDimsPerWave = kDv / kWaves;
+    static constexpr int kDimBlocks = kDimsPerWave / 16;
+    static_assert(NHH * kDimBlocks == 16, "sixteen 16x16 output blocks per wave");
     static constexpr int kXchgBytes = kWaves * kRB * 1024;           // partial S^T exchange
+    // P^T operands per (scale group, head block): hi and lo terms, 1 KB each
+    static constexpr int kPBytes = NHH > 1 ? 2 * 4 * NHH * 1024 : 0;
     static constexpr int kSlotsBytes = kMaxChunk * 4;
     static constexpr int kOffXchg = kNBuf * kBufBytes;
-    static constexpr int kOffSlots = kOffXchg + kXchgBytes;
-    static constexpr int kOffMisc = kOffSlots + kSlotsBytes;
-    static constexpr int kLdsBytes = kOffMisc + 512;                 // verdict + compaction counts
+    static constexpr int kOffP = kOffXchg + kXchgBytes;
+    static constexpr int kOffSlots = kOffP + kPBytes;
+    static constexpr int kOffMisc = kOffSlots + kSlotsBytes;         // verdict + compaction counts
+    static constexpr int kOffHead = kOffMisc + 512;                  // per-head factors, rescale flags
+    static constexpr int kLdsBytes = kOffHead + 1024;
     static_assert(kRowBlockBytes % 16 == 0, "row blocks are whole 16-byte slots");
     static_assert(kRB * kRowBlockBytes <= kBufBytes, "a tile fits its ring buffer");
     static_assert(kLdsBytes <= 160 * 1024, "LDS of one gfx950 workgroup");
-    static_assert(kHeads * kDv * 2 <= kOffSlots, "bf16 output staging fits the ring + exchange");
+    static_assert(kHeads * kDv * 2 <= kOffSlots, "bf16 output staging fits below the slot list");
     static_assert(16 + (kMaxChunk / kThreads) * kWaves <= 128, "compaction counts fit");
 };
 
@@ -138,8 +150,8 @@ struct KParams {
     uint16_t *out;
     float *lse;
     int32_t *phys_out;
-    float *part_o;        // [T][S][H][512] fp32, O / l of each split
-    float *part_lse;      // [T][S][H]
+    float *part_o;        // [T][S][HB] blobs of kHeads x 512 fp32 (O / l), in register order
+    float *part_lse;      // [T][S][H] natural-log lse of each split
     uint64_t *arrivals;   // [T][HB]: arrivals (bits 48..63) + arrivals per XCD (6 bits each)
     float log2e_scale;    // sm_scale * log2(e): logits are kept in log2 units
     int T, H, K, R, MB;
@@ -293,17 +305,16 @@ void attn_kernel(const KParams p)
     const int32_t *topk_row = p.topk + (size_t)t * p.K;
     const int req = p.req_id[t];
 
-    // q^T B operand: lane (head, group g) holds 8 columns per k-step: latent
-    // 256*dh + 32k + 8g (k < 8), RoPE 512 + 32*dh + 8g (k = 8).
+    // q^T B operands. bf16 cache: lane (head, group g) holds 8 columns per
+    // k-step of v_mfma_f32_16x16x32_bf16: latent 256*dh + 32k + 8g (k < 8), RoPE
+    // 512 + 32*dh + 8g (k = 8). fp8 cache: the RoPE step is the same (qb[8]); the
+    // latent goes through v_mfma_scale_f32_16x16x128_f8f6f4 on the raw e4m3 K
+    // bytes, so q is written exactly as hi + lo e4m3 terms with a power-of-two
+    // scale per head and 128-column group: lane (head, g) holds columns
+    // 128*(2*dh + gi) + 32g .. +31.
     bf16x8 qb[9];
-    {
-        const uint16_t *qrow = p.q + ((size_t)t * p.H + head) * kDqk;
-#pragma unroll
-        for (int k = 0; k < 9; ++k) {
-            const int col = k < 8 ? 256 * dh + 32 * k + 8 * g : 512 + 32 * dh + 8 * g;
-            qb[k] = __builtin_bit_cast(bf16x8, *(const uint4 *)(qrow + col));
-        }
-    }
+    i32x8 qh[2], ql[2];         // fp8: hi and lo e4m3 terms of the 32 columns
+    int qsh[2], qsl[2];         // fp8: their e8m0 block scales (2^(e - 127))
 
     // `solo`: this workgroup computes its whole range and writes the output
     // directly (no split, or the recompute after a failed XCD check).
@@ -311,9 +322,15 @@ void attn_kernel(const KParams p)
     int pos_begin = s * p.split_len;
     int pos_end = min(p.K, pos_begin + p.split_len);
 
-    f32x4 o[16];            // O^T: dims 256*dh + 16*db + 4g + i of this lane's head
-    float m_run, l_part;    // log2-domain running max (same in a head's 4 lanes); lane's row sum
-    float out_scale, out_lse;
+    constexpr int DB = C::kDimBlocks;
+    // O^T, 16 blocks: o[hb * DB + db] holds dims dim0 + 16*db + 4g + i of head
+    // 16*hb + n16 of the workgroup, dim0 = wave * kDimsPerWave
+    f32x4 o[16];
+    const int dim0 = wave * C::kDimsPerWave;
+    float m_run, l_part;    // head block hh: log2-domain running max (same in a head's 4 lanes), lane's row sum
+    float *head_f = (float *)(smem + C::kOffHead);           // [4][16] per-head factors
+    int *resc_flag = (int *)(smem + C::kOffHead + 256);      // [4] head block moved its max this tile
+    float *alpha_lds = (float *)(smem + C::kOffHead + 512);  // [4][16] rescale factors
 
     // One tile: S^T = K q^T, online softmax, O^T += V^T P^T. exact: P enters PV
     // as hi + lo bf16 terms (wave-uniform).
@@ -328,11 +345,12 @@ void attn_kernel(const KParams p)
         // bf16 V^T (ds_read_b64_tr_b16): source lane n16 = 4k + a reads row 4g + k
         // (and 16 + 4g + k), dims 4a..4a+3 of a 16-dim block
         const int off_v16 = (4 * g + (n16 >> 2)) * RS + 8 * (n16 & 3);
-        // ---- S^T over this wave's column half (K rows 16*rb + n16; accumulator
-        //      rows 16*rb + 4g + i)
+
+        // ---- S^T over this wave's column half for head block hh (K rows
+        //      16*rb + n16; accumulator rows 16*rb + 4g + i)
         f32x4 acc[RB];
         f32x4 sc[2][RB];        // fp8: scales of rows 16*rb + 4g + i, groups 2*dh + gi
-        uint2 vf8[16];          // fp8: V^T fragments, read before the exchange
+        uint2 vf8[DB];          // fp8: V^T fragments of this wave's dims, read before the exchange
         if constexpr (FMT == kCacheFp8) {
             bf16x8 rf[RB];
 #pragma unroll
@@ -351,23 +369,24 @@ void attn_kernel(const KParams p)
                 acc[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int gi = 0; gi < 2; ++gi) {
-                // K fragments of column group 2*dh + gi
-                uint2 kf[4][RB];
+                // raw e4m3 K bytes of column group 2*dh + gi: row 16*rb + n16,
+                // columns 32g .. 32g + 31 of the group
+                i32x8 kf[RB];
 #pragma unroll
-                for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-                    for (int rb = 0; rb < RB; ++rb)
-                        kf[kk][rb] = *(const uint2 *)(buf + rb * RBB + off_k + 128 * (2 * dh + gi) + 32 * kk + 8 * g);
+                for (int rb = 0; rb < RB; ++rb) {
+                    const uint4 *src = (const uint4 *)(buf + rb * RBB + off_k + 128 * (2 * dh + gi) + 32 * g);
+                    const uint4 a0 = src[0], a1 = src[1];
+                    kf[rb] = i32x8{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+                }
                 f32x4 part[RB];
 #pragma unroll
                 for (int rb = 0; rb < RB; ++rb)
-                    part[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    part[rb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                        kf[rb], qh[gi], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, qsh[gi]);
 #pragma unroll
-                for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-                    for (int rb = 0; rb < RB; ++rb)
-                        part[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                            e4m3x8_to_bf16x8(kf[kk][rb]), qb[4 * gi + kk], part[rb], 0, 0, 0);
+                for (int rb = 0; rb < RB; ++rb)
+                    part[rb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                        kf[rb], ql[gi], part[rb], 0, 0, 0, 127, 0, qsl[gi]);
 #pragma unroll
                 for (int rb = 0; rb < RB; ++rb)
                     acc[rb] += sc[gi][rb] * part[rb];
@@ -376,9 +395,9 @@ void attn_kernel(const KParams p)
             for (int rb = 0; rb < RB; ++rb)
                 acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(rf[rb], qb[8], acc[rb], 0, 0, 0);
 #pragma unroll
-            for (int db = 0; db < 16; ++db) {
+            for (int db = 0; db < DB; ++db) {
                 const i32x2 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-                    LDS_PTR(i32x2, buf + off_v8 + 256 * dh + 16 * db));
+                    LDS_PTR(i32x2, buf + off_v8 + dim0 + 16 * db));
                 vf8[db] = make_uint2((uint32_t)v[0], (uint32_t)v[1]);
             }
         } else {
@@ -405,9 +424,9 @@ void attn_kernel(const KParams p)
         for (int rb = 0; rb < RB; ++rb)
             acc[rb] += xchg[((wave ^ 1) * RB + rb) * 64 + lane];
 
-        // ---- online softmax in log2 units. The running max moves only when
-        //      some row exceeds it by 2^8 (tested on each lane's own rows,
-        //      moved to the whole head's max).
+        // ---- online softmax of head block hh in log2 units. The running max
+        //      moves only when some row exceeds it by 2^8 (tested on each lane's
+        //      own rows, moved to the whole head's max).
         float lmax = -INFINITY;
         if (n_tile == kTile) {
 #pragma unroll
@@ -426,17 +445,17 @@ void attn_kernel(const KParams p)
                     lmax = fmaxf(lmax, acc[rb][i]);
                 }
         }
+        bool moved = false;
+        float alpha = 1.f;
         if (__ballot(lmax > m_run + kLazyRescale) != 0) {
             float mx = fmaxf(lmax, __shfl_xor(lmax, 16));
             mx = fmaxf(mx, __shfl_xor(mx, 32));
             if (mx > m_run + kLazyRescale) {
-                const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - mx);
+                alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - mx);
                 l_part *= alpha;
-#pragma unroll
-                for (int db = 0; db < 16; ++db)
-                    o[db] *= alpha;
                 m_run = mx;
             }
+            moved = true;
         }
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb)
@@ -446,8 +465,9 @@ void attn_kernel(const KParams p)
                 l_part += acc[rb][i];
             }
 
-        // ---- O^T += V^T P^T over this wave's 256 output dims. fp8: the weights
-        //      of output group 2*dh + gi carry that group's row scales.
+        // ---- P^T operands. fp8: the weights for output group G carry that
+        //      group's row scales; this wave has the scales of groups 2*dh, 2*dh+1.
+        bf16x8 pbh[2], pbl[2];
 #pragma unroll
         for (int gi = 0; gi < 2; ++gi) {
             f32x4 p0 = acc[0], p1 = acc[1];
@@ -455,63 +475,176 @@ void attn_kernel(const KParams p)
                 p0 *= sc[gi][0];
                 p1 *= sc[gi][1];
             }
-            const bf16x8 pb = pack_p(p0, p1);
+            pbh[gi] = pack_p(p0, p1);
+            if (exact)
+                pbl[gi] = pack_p_residual(p0, p1, pbh[gi]);
+        }
+
+        if constexpr (NHH == 1) {
+            // one head block: this wave's dims are groups 2*dh, 2*dh + 1 and it
+            // holds their operands itself
+            if (moved) {
 #pragma unroll
-            for (int d8 = 0; d8 < 8; ++d8) {
-                const int db = 8 * gi + d8;
+                for (int k = 0; k < 16; ++k)
+                    o[k] *= alpha;
+            }
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                const int gi = db >> 3;
                 bf16x8 a;
                 if constexpr (FMT == kCacheFp8) {
                     a = e4m3x8_to_bf16x8(vf8[db]);
                 } else {
-                    const int colb = 2 * (256 * dh + 16 * db);
+                    const int colb = 2 * (dim0 + 16 * db);
                     const uint2 w0 = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                         LDS_PTR(i16x4, buf + off_v16 + colb)));
                     const uint2 w1 = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                         LDS_PTR(i16x4, buf + RBB + off_v16 + colb)));
                     a = __builtin_bit_cast(bf16x8, make_uint4(w0.x, w0.y, w1.x, w1.y));
                 }
-                o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb, o[db], 0, 0, 0);
+                o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pbh[gi], o[db], 0, 0, 0);
+                if (exact)
+                    o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pbl[gi], o[db], 0, 0, 0);
             }
-            if (exact) {
-                // short lists: add the bf16 rounding residual of P as a second term
-                const bf16x8 pl = pack_p_residual(p0, p1, pb);
+        } else {
+            // ---- hand P^T of head block hh for groups 2*dh, 2*dh + 1 (and the
+            //      rescale factor when the max moved) to the waves owning those dims
+            bf16x8 *p_lds = (bf16x8 *)(smem + C::kOffP);          // [lo][group][head block][lane]
 #pragma unroll
-                for (int d8 = 0; d8 < 8; ++d8) {
-                    const int db = 8 * gi + d8;
-                    bf16x8 a;
-                    if constexpr (FMT == kCacheFp8) {
-                        const i32x2 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-                            LDS_PTR(i32x2, buf + off_v8 + 256 * dh + 16 * db));
-                        a = e4m3x8_to_bf16x8(make_uint2((uint32_t)v[0], (uint32_t)v[1]));
-                    } else {
-                        const int colb = 2 * (256 * dh + 16 * db);
-                        const uint2 w0 = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                            LDS_PTR(i16x4, buf + off_v16 + colb)));
-                        const uint2 w1 = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                            LDS_PTR(i16x4, buf + RBB + off_v16 + colb)));
-                        a = __builtin_bit_cast(bf16x8, make_uint4(w0.x, w0.y, w1.x, w1.y));
-                    }
-                    o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pl, o[db], 0, 0, 0);
+            for (int gi = 0; gi < 2; ++gi) {
+                p_lds[((2 * dh + gi) * NHH + hh) * 64 + lane] = pbh[gi];
+                if (exact)
+                    p_lds[((4 + 2 * dh + gi) * NHH + hh) * 64 + lane] = pbl[gi];
+            }
+            if (dh == 0) {
+                if (lane == 0)
+                    resc_flag[hh] = moved ? 1 : 0;
+                if (moved && g == 0)
+                    alpha_lds[hh * 16 + n16] = alpha;
+            }
+            __syncthreads();
+            // ---- O^T += V^T P^T over this wave's dims for every head block
+            const int G = dim0 >> 7;                                // scale group of this wave's dims
+#pragma unroll
+            for (int hb = 0; hb < NHH; ++hb) {
+                if (resc_flag[hb]) {
+                    const float al = alpha_lds[hb * 16 + n16];
+#pragma unroll
+                    for (int db = 0; db < DB; ++db)
+                        o[hb * DB + db] *= al;
+                }
+            }
+            bf16x8 pv[NHH];
+#pragma unroll
+            for (int hb = 0; hb < NHH; ++hb)
+                pv[hb] = p_lds[(G * NHH + hb) * 64 + lane];
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                bf16x8 a;
+                if constexpr (FMT == kCacheFp8) {
+                    a = e4m3x8_to_bf16x8(vf8[db]);
+                } else {
+                    const int colb = 2 * (dim0 + 16 * db);
+                    const uint2 w0 = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        LDS_PTR(i16x4, buf + off_v16 + colb)));
+                    const uint2 w1 = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        LDS_PTR(i16x4, buf + RBB + off_v16 + colb)));
+                    a = __builtin_bit_cast(bf16x8, make_uint4(w0.x, w0.y, w1.x, w1.y));
+                }
+#pragma unroll
+                for (int hb = 0; hb < NHH; ++hb)
+                    o[hb * DB + db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pv[hb], o[hb * DB + db], 0, 0, 0);
+                if (exact) {
+#pragma unroll
+                    for (int hb = 0; hb < NHH; ++hb)
+                        o[hb * DB + db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            a, p_lds[((4 + G) * NHH + hb) * 64 + lane], o[hb * DB + db], 0, 0, 0);
                 }
             }
         }
     };
 
+    float inv_l_hb[NHH];        // per head block: 1 / l of head 16*hb + n16
+    float lse_hb[NHH];          // and its natural-log lse
     for (;;) {
-#pragma unroll
-        for (int db = 0; db < 16; ++db)
-            o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-        m_run = -INFINITY;
-        l_part = 0.f;
-        // the splits of head block 0 write the converted slots (a recompute does not repeat it)
-        const bool write_phys = p.phys_out != nullptr && hb_wg == 0 && (p.S == 1 || !solo);
-
+        // the first round's indices first: their round trip overlaps q's
         int idxv[kPer];
 #pragma unroll
         for (int j = 0; j < kPer; ++j) {
             const int i = pos_begin + tid + C::kThreads * j;
             idxv[j] = i < min(pos_end, pos_begin + kMaxChunk) ? topk_row[i] : -1;
         }
+        // (re)load q here: a recompute after a failed XCD check needs it again,
+        // and nothing after the tile loop does
+        {
+            const uint16_t *qrow = p.q + ((size_t)t * p.H + head) * kDqk;
+            if constexpr (FMT == kCacheFp8) {
+                qb[8] = __builtin_bit_cast(bf16x8, *(const uint4 *)(qrow + 512 + 32 * dh + 8 * g));
+#pragma unroll
+                for (int gi = 0; gi < 2; ++gi) {
+                    const uint4 *src = (const uint4 *)(qrow + 128 * (2 * dh + gi) + 32 * g);
+                    float v[32];
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        const uint4 w = src[c];
+                        const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            v[8 * c + 2 * e] = bf16_lo(ww[e]);
+                            v[8 * c + 2 * e + 1] = bf16_hi(ww[e]);
+                        }
+                    }
+                    float amax = 0.f;
+#pragma unroll
+                    for (int i = 0; i < 32; ++i)
+                        amax = fmaxf(amax, fabsf(v[i]));
+                    // the MFMA applies one B scale per column (head) to all 128 k of the
+                    // group, so the exponent is shared by the head's four lanes
+                    amax = fmaxf(amax, __shfl_xor(amax, 16));
+                    amax = fmaxf(amax, __shfl_xor(amax, 32));
+                    // block exponent: the largest |q| maps into [128, 256), within e4m3's range
+                    const int ex = max((int)((__float_as_uint(amax) >> 23) & 0xFF) - 127 - 7, -120);
+                    const float down = __uint_as_float((uint32_t)(127 - ex) << 23);     // 2^-ex, exact
+                    uint32_t hw[8], lw[8];
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        float x[4];
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            x[e] = v[4 * j + e] * down;
+                        s16x2 h = {0, 0};
+                        h = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(h, x[0], x[1], 1.0f, false);
+                        h = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(h, x[2], x[3], 1.0f, true);
+                        hw[j] = __builtin_bit_cast(uint32_t, h);
+                        // what the hi term misses, exactly, times 16 (its scale is 2^(ex - 4))
+                        const f32x2 b0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(hw[j], 1.0f, false);
+                        const f32x2 b1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(hw[j], 1.0f, true);
+                        s16x2 l = {0, 0};
+                        l = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(l, (x[0] - b0[0]) * 16.f, (x[1] - b0[1]) * 16.f, 1.0f, false);
+                        l = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(l, (x[2] - b1[0]) * 16.f, (x[3] - b1[1]) * 16.f, 1.0f, true);
+                        lw[j] = __builtin_bit_cast(uint32_t, l);
+                    }
+                    qh[gi] = i32x8{(int)hw[0], (int)hw[1], (int)hw[2], (int)hw[3], (int)hw[4], (int)hw[5], (int)hw[6], (int)hw[7]};
+                    ql[gi] = i32x8{(int)lw[0], (int)lw[1], (int)lw[2], (int)lw[3], (int)lw[4], (int)lw[5], (int)lw[6], (int)lw[7]};
+                    qsh[gi] = 127 + ex;
+                    qsl[gi] = 127 + ex - 4;
+                }
+            } else {
+#pragma unroll
+                for (int k = 0; k < 9; ++k) {
+                    const int col = k < 8 ? 256 * dh + 32 * k + 8 * g : 512 + 32 * dh + 8 * g;
+                    qb[k] = __builtin_bit_cast(bf16x8, *(const uint4 *)(qrow + col));
+                }
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < 16; ++k)
+            o[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+        m_run = -INFINITY;
+        l_part = 0.f;
+        // the splits of head block 0 write the converted slots (a recompute does not repeat it)
+        const bool write_phys = p.phys_out != nullptr && hb_wg == 0 && (p.S == 1 || !solo);
+
 
         for (int chunk0 = pos_begin; chunk0 < pos_end; chunk0 += kMaxChunk) {
             const int chunk_n = min(kMaxChunk, pos_end - chunk0);
@@ -571,7 +704,7 @@ void attn_kernel(const KParams p)
                 }
                 tile(ring + (it % C::kNBuf) * C::kBufBytes, min(kTile, n_valid - it * kTile), exact_p);
             }
-            __syncthreads();     // ring, exchange and slot list are free for the next round
+            __syncthreads();     // ring, exchanges and slot list are free for the next round
             // the next round's indices
 #pragma unroll
             for (int j = 0; j < kPer; ++j) {
@@ -580,29 +713,44 @@ void attn_kernel(const KParams p)
             }
         }
 
-        // ---- per-head results. m_run and the row sums are the same in both halves.
-        float l = l_part;
-        l += __shfl_xor(l, 16);
-        l += __shfl_xor(l, 32);
-        const float inv_l = l > 0.f ? 1.f / l : 0.f;
-        // natural-log LSE; v_log_f32 is log2 (l >= 1 here: the row that set m_run adds >= 1)
-        const float lse_v = l > 0.f ? (m_run + __builtin_amdgcn_logf(l)) * 0.69314718055994531f : -INFINITY;
-
-        if (solo) {
-            out_scale = inv_l;
-            out_lse = lse_v;
-            break;
+        // ---- per-head results of head block hh (m_run and the row sums are the
+        //      same in both column halves), handed to every wave through LDS
+        {
+            float l = l_part;
+            l += __shfl_xor(l, 16);
+            l += __shfl_xor(l, 32);
+            // natural-log LSE; v_log_f32 is log2 (l >= 1 here: the row that set m_run adds >= 1)
+            const float inv_l = l > 0.f ? 1.f / l : 0.f;
+            const float lse_v = l > 0.f ? (m_run + __builtin_amdgcn_logf(l)) * 0.69314718055994531f : -INFINITY;
+            if (dh == 0 && g == 0) {
+                head_f[hh * 16 + n16] = inv_l;
+                head_f[64 + hh * 16 + n16] = lse_v;
+            }
+            __syncthreads();
+#pragma unroll
+            for (int hb = 0; hb < NHH; ++hb) {
+                inv_l_hb[hb] = head_f[hb * 16 + n16];
+                lse_hb[hb] = head_f[64 + hb * 16 + n16];
+            }
         }
 
-        // ---- top-k split: publish this split's fp32 partial (O / l) and lse with
-        //      plain stores; they land in this XCD's L2.
+        if (solo)
+            break;
+
+        // ---- top-k split: publish this split's fp32 partial (O / l) in register
+        //      order (each store writes 1 KB contiguous) and its lse, with plain
+        //      stores; they land in this XCD's L2.
+        const size_t blob = (((size_t)t * p.S + s) * p.HB + hb_wg) * ((size_t)C::kHeads * kDv);
         {
-            float *po = p.part_o + (((size_t)t * p.S + s) * p.H + head) * kDv + 256 * dh + 4 * g;
+            f32x4 *po = (f32x4 *)(p.part_o + blob) + (size_t)wave * 16 * 64 + lane;
 #pragma unroll
-            for (int db = 0; db < 16; ++db)
-                *(f32x4 *)(po + 16 * db) = o[db] * inv_l;
-            if (dh == 0 && g == 0)
-                p.part_lse[((size_t)t * p.S + s) * p.H + head] = lse_v;
+            for (int k = 0; k < 16; ++k)
+                po[k * 64] = o[k] * inv_l_hb[k / DB];
+            if (wave == 0 && g == 0) {
+#pragma unroll
+                for (int hb = 0; hb < NHH; ++hb)
+                    p.part_lse[((size_t)t * p.S + s) * p.H + wg_head0 + 16 * hb + n16] = lse_hb[hb];
+            }
         }
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");    // this thread's stores reached L2
         __syncthreads();
@@ -628,36 +776,48 @@ void attn_kernel(const KParams p)
         if (verdict == 1) {
             // ---- last arrival, on the XCD of every split: merge through the shared
             //      L2 (this CU's L1 is invalidated first so every load reaches L2).
-            //      This split's own partial is still in registers.
+            //      Every split's stored partial, this one's included, is added in
+            //      index order, so the result does not depend on which split came
+            //      last.
             asm volatile("buffer_inv sc0" ::: "memory");
-            const float *plse = p.part_lse + (size_t)t * p.S * p.H + head;
-            float M = lse_v;
-            for (int s2 = 0; s2 < p.S; ++s2)
-                M = fmaxf(M, plse[(size_t)s2 * p.H]);
-            const float w_me = M == -INFINITY ? 0.f : __expf(lse_v - M);
-            float W = w_me;
+            const float *plse = p.part_lse + (size_t)t * p.S * p.H + wg_head0 + n16;
+            float M[NHH], W[NHH];
 #pragma unroll
-            for (int db = 0; db < 16; ++db)
-                o[db] *= inv_l * w_me;
-            for (int s2 = 0; s2 < p.S; ++s2) {
-                if (s2 == s)
-                    continue;
-                const float ws = M == -INFINITY ? 0.f : __expf(plse[(size_t)s2 * p.H] - M);
-                W += ws;
-                const float *src = p.part_o + (((size_t)t * p.S + s2) * p.H + head) * kDv + 256 * dh + 4 * g;
-#pragma unroll
-                for (int h8 = 0; h8 < 2; ++h8) {     // eight loads in flight at a time
-                    f32x4 v[8];
-#pragma unroll
-                    for (int d = 0; d < 8; ++d)
-                        v[d] = *(const f32x4 *)(src + 16 * (8 * h8 + d));
-#pragma unroll
-                    for (int d = 0; d < 8; ++d)
-                        o[8 * h8 + d] += ws * v[d];
-                }
+            for (int hb = 0; hb < NHH; ++hb) {
+                M[hb] = -INFINITY;
+                W[hb] = 0.f;
             }
-            out_scale = W > 0.f ? 1.f / W : 0.f;
-            out_lse = W > 0.f ? M + logf(W) : -INFINITY;
+            for (int s2 = 0; s2 < p.S; ++s2)
+#pragma unroll
+                for (int hb = 0; hb < NHH; ++hb)
+                    M[hb] = fmaxf(M[hb], plse[(size_t)s2 * p.H + 16 * hb]);
+            const size_t split_stride = (size_t)p.HB * C::kHeads * kDv / 4;       // in f32x4
+            const f32x4 *src0 = (const f32x4 *)(p.part_o + blob) - (size_t)s * split_stride +
+                                (size_t)wave * 16 * 64 + lane;                 // split 0
+#pragma unroll
+            for (int k = 0; k < 16; ++k)
+                o[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int s0 = 0; s0 < p.S; ++s0) {
+                float wa[NHH];
+#pragma unroll
+                for (int hb = 0; hb < NHH; ++hb) {
+                    wa[hb] = M[hb] == -INFINITY ? 0.f : __expf(plse[(size_t)s0 * p.H + 16 * hb] - M[hb]);
+                    W[hb] += wa[hb];
+                }
+                const f32x4 *sa = src0 + (size_t)s0 * split_stride;
+                f32x4 va[16];
+#pragma unroll
+                for (int k = 0; k < 16; ++k)
+                    va[k] = sa[k * 64];
+#pragma unroll
+                for (int k = 0; k < 16; ++k)
+                    o[k] += wa[k / DB] * va[k];
+            }
+#pragma unroll
+            for (int hb = 0; hb < NHH; ++hb) {
+                inv_l_hb[hb] = W[hb] > 0.f ? 1.f / W[hb] : 0.f;
+                lse_hb[hb] = W[hb] > 0.f ? M[hb] + logf(W[hb]) : -INFINITY;
+            }
             break;
         }
         // some split ran on another XCD, whose partial may sit in another L2:
@@ -669,16 +829,21 @@ void attn_kernel(const KParams p)
     }
 
     // ---- output rows of this workgroup's heads: staged as bf16 [head][512] in
-    //      LDS (free now), then written out coalesced
+    //      LDS, then written out coalesced
+    __syncthreads();        // every wave is done with the exchange areas
     uint16_t *stage = (uint16_t *)smem;
 #pragma unroll
-    for (int db = 0; db < 16; ++db) {
-        const f32x4 v = o[db] * out_scale;
-        *(uint2 *)(stage + (16 * hh + n16) * kDv + 256 * dh + 16 * db + 4 * g) =
+    for (int k = 0; k < 16; ++k) {
+        const int hb = k / DB, db = k % DB;
+        const f32x4 v = o[k] * inv_l_hb[hb];
+        *(uint2 *)(stage + (16 * hb + n16) * kDv + dim0 + 16 * db + 4 * g) =
             make_uint2(pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3]));
     }
-    if (dh == 0 && g == 0 && p.lse != nullptr)
-        p.lse[(size_t)t * p.H + head] = out_lse;
+    if (wave == 0 && g == 0 && p.lse != nullptr) {
+#pragma unroll
+        for (int hb = 0; hb < NHH; ++hb)
+            p.lse[(size_t)t * p.H + wg_head0 + 16 * hb + n16] = lse_hb[hb];
+    }
     __syncthreads();
     uint16_t *dst = p.out + ((size_t)t * p.H + wg_head0) * kDv;
     for (int u = tid; u < C::kHeads * kDv / 8; u += C::kThreads)
