@@ -233,6 +233,15 @@ __device__ __forceinline__ void wait_vmcnt(int n)
 #undef SMLA_VMCNT_CASE
 }
 
+// The value of v, opaque to the optimiser from here on: addresses derived from
+// it are computed where they are used instead of being hoisted to the kernel's
+// start and kept (or spilled) across the tile loop.
+__device__ __forceinline__ int late(int v)
+{
+    asm volatile("" : "+v"(v));
+    return v;
+}
+
 // Id of the XCD (accelerator complex die) this wave runs on, 0..7 on MI355X.
 __device__ __forceinline__ uint32_t xcc_id()
 {
@@ -268,7 +277,7 @@ __device__ __forceinline__ void issue_tile(const uint8_t *__restrict__ cache, co
 // ------------------------------------------------------------- attention
 
 template <int FMT, int NHH>
-__global__ __launch_bounds__(128 * NHH) __attribute__((amdgpu_waves_per_eu(NHH == 4 ? 2 : 1)))
+__global__ __launch_bounds__(128 * NHH) __attribute__((amdgpu_waves_per_eu(NHH == 1 ? 1 : 2)))
 void attn_kernel(const KParams p)
 {
     using C = Cfg<FMT, NHH>;
@@ -742,7 +751,7 @@ void attn_kernel(const KParams p)
         //      stores; they land in this XCD's L2.
         const size_t blob = (((size_t)t * p.S + s) * p.HB + hb_wg) * ((size_t)C::kHeads * kDv);
         {
-            f32x4 *po = (f32x4 *)(p.part_o + blob) + (size_t)wave * 16 * 64 + lane;
+            f32x4 *po = (f32x4 *)(p.part_o + blob) + (size_t)wave * 16 * 64 + late(lane);
 #pragma unroll
             for (int k = 0; k < 16; ++k)
                 po[k * 64] = o[k] * inv_l_hb[k / DB];
@@ -780,7 +789,7 @@ void attn_kernel(const KParams p)
             //      index order, so the result does not depend on which split came
             //      last.
             asm volatile("buffer_inv sc0" ::: "memory");
-            const float *plse = p.part_lse + (size_t)t * p.S * p.H + wg_head0 + n16;
+            const float *plse = p.part_lse + (size_t)t * p.S * p.H + wg_head0 + late(n16);
             float M[NHH], W[NHH];
 #pragma unroll
             for (int hb = 0; hb < NHH; ++hb) {
@@ -793,7 +802,7 @@ void attn_kernel(const KParams p)
                     M[hb] = fmaxf(M[hb], plse[(size_t)s2 * p.H + 16 * hb]);
             const size_t split_stride = (size_t)p.HB * C::kHeads * kDv / 4;       // in f32x4
             const f32x4 *src0 = (const f32x4 *)(p.part_o + blob) - (size_t)s * split_stride +
-                                (size_t)wave * 16 * 64 + lane;                 // split 0
+                                (size_t)wave * 16 * 64 + late(lane);           // split 0
 #pragma unroll
             for (int k = 0; k < 16; ++k)
                 o[k] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -832,11 +841,12 @@ void attn_kernel(const KParams p)
     //      LDS, then written out coalesced
     __syncthreads();        // every wave is done with the exchange areas
     uint16_t *stage = (uint16_t *)smem;
+    const int n16_late = late(n16);
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
         const int hb = k / DB, db = k % DB;
         const f32x4 v = o[k] * inv_l_hb[hb];
-        *(uint2 *)(stage + (16 * hb + n16) * kDv + dim0 + 16 * db + 4 * g) =
+        *(uint2 *)(stage + (16 * hb + n16_late) * kDv + dim0 + 16 * db + 4 * g) =
             make_uint2(pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3]));
     }
     if (wave == 0 && g == 0 && p.lse != nullptr) {
@@ -883,9 +893,10 @@ hipError_t launch_one(const KParams &p, hipStream_t stream)
 template <int FMT>
 hipError_t launch_fmt(const KParams &p, hipStream_t stream)
 {
-    if (p.H >= 64)
+    const int heads = p.H / p.HB;     // heads per workgroup: 64, 32 or 16
+    if (heads == 64)
         return launch_one<FMT, 4>(p, stream);
-    if (p.H == 32)
+    if (heads == 32)
         return launch_one<FMT, 2>(p, stream);
     return launch_one<FMT, 1>(p, stream);
 }
