@@ -104,11 +104,12 @@ struct Cfg {
     static constexpr int kRowStride = FMT == kCacheFp8 ? kRowBytes : kRowBytes + 16;   // in LDS
     static constexpr int kBlockGap = FMT == kCacheFp8 ? 16 : 0;
     static constexpr int kRowBlockBytes = 16 * kRowStride + kBlockGap;                 // 16 rows
-    static constexpr int kSlotsPerRow = kRowStride / 16;
-    static constexpr int kSlotsPerBlock = kRowBlockBytes / 16;
-    static constexpr int kTileSlots = kRB * kSlotsPerBlock;
-    static constexpr int kDmaInstr = (kTileSlots + 63) / 64;         // wave instructions per tile
-    static constexpr int kBufBytes = kDmaInstr * 1024;               // ring buffer stride
+    // Tile copies: one wave instruction moves 64 16-byte pieces of one row, so
+    // a row takes kInstrPerRow of them; each wave copies kRowsPerWave rows.
+    static constexpr int kInstrPerRow = (kChunksPerRow + 63) / 64;
+    static constexpr int kRowsPerWave = kTile / kWaves;
+    static constexpr int kDmaPerWave = kRowsPerWave * kInstrPerRow;  // wave instructions per tile
+    static constexpr int kBufBytes = (kRB * kRowBlockBytes + 1023) / 1024 * 1024;   // ring buffer stride
     // 64 heads: one workgroup per CU; fewer heads: two workgroups per CU
     // share the LDS (fp8).
     static constexpr int kNBuf = NHH == 4 ? (FMT == kCacheFp8 ? 4 : 2) : 2;
@@ -129,6 +130,7 @@ struct Cfg {
     static constexpr int kLdsBytes = kOffHead + 1024;
     static_assert(kRowBlockBytes % 16 == 0, "row blocks are whole 16-byte slots");
     static_assert(kRB * kRowBlockBytes <= kBufBytes, "a tile fits its ring buffer");
+    static_assert(kTile % kWaves == 0 && kRowsPerWave <= 64, "whole rows per wave");
     static_assert(kLdsBytes <= 160 * 1024, "LDS of one gfx950 workgroup");
     static_assert(kHeads * kDv * 2 <= kOffSlots, "bf16 output staging fits below the slot list");
     static_assert(16 + (kMaxChunk / kThreads) * kWaves <= 128, "compaction counts fit");
@@ -250,26 +252,55 @@ __device__ __forceinline__ uint32_t xcc_id()
     return x & 0xF;
 }
 
+// global_load_lds_dwordx4: 16 bytes per active lane from `src` into LDS at
+// lds_base + 16 * lane. Written as inline assembly on purpose: the compiler
+// cannot see that the LDS reads which follow touch a different ring buffer,
+// and for the builtin it waits for the whole copy before the next LDS read,
+// which would serialise every gather with the compute on the previous tile.
+// Completion is ordered by the explicit vmcnt waits and barriers around the
+// ring instead.
+__device__ __forceinline__ void dma16(const uint8_t *src, uint32_t lds_base)
+{
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(src), "s"(lds_base)
+                 : "memory", "m0");
+}
+
 // Copy the rows of one tile, as stored, into an LDS ring buffer in the layout
-// lds_row() describes. Wave w issues instructions w, w + W, ...; each fills 64
-// consecutive 16-byte LDS slots (lanes whose slot is padding stay idle). Rows
-// past the tile's valid count repeat the tile's first row (finite data whose
-// weights are masked to zero).
+// lds_row() describes. Wave w copies rows w * kRowsPerWave ...: one lane reads
+// the slots of those rows from the compacted list, each row's slot is then a
+// scalar, and each copy instruction needs a single per-lane address add (lane
+// c moves bytes 16c .. 16c + 15 of the row). Rows past the tile's valid count
+// repeat the tile's first row (finite data whose weights are masked to zero).
+// Every instruction has at least one active lane, so a wave always issues
+// kDmaPerWave of them per tile.
 template <class C>
 __device__ __forceinline__ void issue_tile(const uint8_t *__restrict__ cache, const int32_t *slots,
                                            int n_tile, uint8_t *buf, int wave, int lane)
 {
-    for (int j = wave; j < C::kDmaInstr; j += C::kWaves) {
-        const int slot_i = j * 64 + lane;
-        const int blk = slot_i / C::kSlotsPerBlock;
-        const int in_blk = slot_i - blk * C::kSlotsPerBlock;
-        const int r16 = in_blk / C::kSlotsPerRow;
-        const int c = in_blk - r16 * C::kSlotsPerRow;
-        if (blk < kRB && r16 < 16 && c < C::kChunksPerRow) {
-            const int r = 16 * blk + r16;
-            const int slot = slots[r < n_tile ? r : 0];
-            const uint8_t *src = cache + (size_t)slot * C::kRowBytes + 16 * c;
-            __builtin_amdgcn_global_load_lds(src, LDS_PTR(void, buf + j * 1024), 16, 0, 0);
+    // recomputed per tile: kept across the tile loop they would be spilled, and a
+    // reload from scratch waits for every copy in flight
+    lane = late(lane);
+    const int r0 = wave * C::kRowsPerWave;
+    const int ri = r0 + lane % C::kRowsPerWave;
+    const int my_slot = slots[ri < n_tile ? ri : 0];
+    const uint32_t base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)LDS_PTR(uint8_t, buf) +
+                                                         (uint32_t)lds_row<C>(r0));
+#pragma unroll
+    for (int i = 0; i < C::kRowsPerWave; ++i) {
+        const int r = r0 + i;
+        const int slot = __builtin_amdgcn_readlane(my_slot, i);
+        const uint8_t *row = cache + (size_t)(uint32_t)slot * C::kRowBytes;
+        // lds_row(r) - lds_row(r0): r0 is a multiple of kRowsPerWave, so whether
+        // row r crosses into the next 16-row block is known from i alone when
+        // kRowsPerWave divides 16; otherwise it is computed
+        const uint32_t lds = base + (uint32_t)(lds_row<C>(r) - lds_row<C>(r0));
+#pragma unroll
+        for (int k = 0; k < C::kInstrPerRow; ++k) {
+            const int chunk = 64 * k + lane;
+            if (chunk < C::kChunksPerRow)
+                dma16(row + 16 * chunk, __builtin_amdgcn_readfirstlane(lds + 1024u * k));
         }
     }
 }
@@ -588,7 +619,14 @@ void attn_kernel(const KParams p)
         {
             const uint16_t *qrow = p.q + ((size_t)t * p.H + head) * kDqk;
             if constexpr (FMT == kCacheFp8) {
-                qb[8] = __builtin_bit_cast(bf16x8, *(const uint4 *)(qrow + 512 + 32 * dh + 8 * g));
+                {
+                    uint4 w = *(const uint4 *)(qrow + 512 + 32 * dh + 8 * g);
+                    // used here, so the compiler waits for this load before the tile
+                    // loop rather than at its first use inside it (it cannot see the
+                    // explicit waits that order the tile copies)
+                    asm volatile("" : "+v"(w.x), "+v"(w.y), "+v"(w.z), "+v"(w.w));
+                    qb[8] = __builtin_bit_cast(bf16x8, w);
+                }
 #pragma unroll
                 for (int gi = 0; gi < 2; ++gi) {
                     const uint4 *src = (const uint4 *)(qrow + 128 * (2 * dh + gi) + 32 * g);
@@ -642,7 +680,10 @@ void attn_kernel(const KParams p)
 #pragma unroll
                 for (int k = 0; k < 9; ++k) {
                     const int col = k < 8 ? 256 * dh + 32 * k + 8 * g : 512 + 32 * dh + 8 * g;
-                    qb[k] = __builtin_bit_cast(bf16x8, *(const uint4 *)(qrow + col));
+                    uint4 w = *(const uint4 *)(qrow + col);
+                    // waited for here, not inside the tile loop (as for the fp8 RoPE part)
+                    asm volatile("" : "+v"(w.x), "+v"(w.y), "+v"(w.z), "+v"(w.w));
+                    qb[k] = __builtin_bit_cast(bf16x8, w);
                 }
             }
         }
@@ -697,7 +738,7 @@ void attn_kernel(const KParams p)
             // from here on the only vector-memory instructions in flight are tile copies
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             // this wave's copy instructions per tile
-            const int dma_w = (C::kDmaInstr - wave + C::kWaves - 1) / C::kWaves;
+            constexpr int dma_w = C::kDmaPerWave;
 
             for (int i = 0; i < min(C::kNBuf - 1, n_tiles); ++i)
                 issue_tile<C>(p.cache, lds_slots + i * kTile, min(kTile, n_valid - i * kTile),
@@ -790,6 +831,14 @@ void attn_kernel(const KParams p)
             //      last.
             asm volatile("buffer_inv sc0" ::: "memory");
             const float *plse = p.part_lse + (size_t)t * p.S * p.H + wg_head0 + late(n16);
+            const size_t split_stride = (size_t)p.HB * C::kHeads * kDv / 4;       // in f32x4
+            const f32x4 *src0 = (const f32x4 *)(p.part_o + blob) - (size_t)s * split_stride +
+                                (size_t)wave * 16 * 64 + late(lane);           // split 0
+            // split 0's partial is in flight while the weights are worked out
+            f32x4 va[16];
+#pragma unroll
+            for (int k = 0; k < 16; ++k)
+                va[k] = src0[k * 64];
             float M[NHH], W[NHH];
 #pragma unroll
             for (int hb = 0; hb < NHH; ++hb) {
@@ -800,9 +849,6 @@ void attn_kernel(const KParams p)
 #pragma unroll
                 for (int hb = 0; hb < NHH; ++hb)
                     M[hb] = fmaxf(M[hb], plse[(size_t)s2 * p.H + 16 * hb]);
-            const size_t split_stride = (size_t)p.HB * C::kHeads * kDv / 4;       // in f32x4
-            const f32x4 *src0 = (const f32x4 *)(p.part_o + blob) - (size_t)s * split_stride +
-                                (size_t)wave * 16 * 64 + late(lane);           // split 0
 #pragma unroll
             for (int k = 0; k < 16; ++k)
                 o[k] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -813,11 +859,12 @@ void attn_kernel(const KParams p)
                     wa[hb] = M[hb] == -INFINITY ? 0.f : __expf(plse[(size_t)s0 * p.H + 16 * hb] - M[hb]);
                     W[hb] += wa[hb];
                 }
-                const f32x4 *sa = src0 + (size_t)s0 * split_stride;
-                f32x4 va[16];
+                if (s0 > 0) {
+                    const f32x4 *sa = src0 + (size_t)s0 * split_stride;
 #pragma unroll
-                for (int k = 0; k < 16; ++k)
-                    va[k] = sa[k * 64];
+                    for (int k = 0; k < 16; ++k)
+                        va[k] = sa[k * 64];
+                }
 #pragma unroll
                 for (int k = 0; k < 16; ++k)
                     o[k] += wa[k / DB] * va[k];
