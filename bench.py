@@ -154,7 +154,6 @@ def main():
     lse = torch.empty((w.num_tokens, w.h_q), dtype=torch.float32, device=dev)
     ws_bytes = smla.smla_workspace_size(w.num_tokens, w.h_q, w.topk)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
-    smla.smla_workspace_init(ws, stream=stream)      # once; every call keeps its counters zero
     props = torch.cuda.get_device_properties(dev)
     splits, _ = smla.smla_plan(w.num_tokens, w.h_q, w.topk, props.multi_processor_count)
     flush = torch.ones(1 << 28, dtype=torch.int32, device=dev)     # 1 GiB, read to evict caches
@@ -162,7 +161,7 @@ def main():
 
     def step():
         smla.smla_decode_fp8(q, cache, bt, req, idx, w.sm_scale, out=out, lse=lse, workspace=ws,
-                             workspace_ready=True, stream=stream)
+                             stream=stream)
 
     for i in range(args.warmup):
         torch.amax(flush, 0, out=sink)

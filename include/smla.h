@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define SMLA_ABI_VERSION 2
+#define SMLA_ABI_VERSION 3
 #define SMLA_BLOCK_SIZE 64
 #define SMLA_HEAD_DIM_QK 576
 #define SMLA_HEAD_DIM_V 512
@@ -65,26 +65,14 @@ typedef enum smla_status {
     SMLA_ERR_ARG = 6        /* invalid scalar argument or option                 */
 } smla_status;
 
-/* Bits of smla_options.flags. */
-#define SMLA_FLAG_WORKSPACE_READY 0x1u
-    /* The workspace was zeroed by smla_workspace_init and has since been used
-       only by attention calls of this library that ran to completion (on one
-       stream at a time). The call then skips the small clearing kernel it
-       otherwise launches before the attention kernel when it splits. */
-#define SMLA_FLAG_TEST_SPLIT_RECOMPUTE 0x2u
-    /* Testing aid: the last split of every token behaves as if the token's
-       splits had run on different XCDs, i.e. it recomputes the whole token
-       instead of merging the partial results. The results are the same; the
-       call is slower. */
-#define SMLA_FLAG_ALL (SMLA_FLAG_WORKSPACE_READY | SMLA_FLAG_TEST_SPLIT_RECOMPUTE)
-
 /* Tuning options (host struct, may be NULL for defaults). */
 typedef struct smla_options {
     int32_t num_splits;     /* 0 = automatic; > 0 = split every token's top-k
                                list into this many parts (capped at topk and at
                                32), each part computed by its own workgroups and
-                               merged by log-sum-exp weights. */
-    uint32_t flags;         /* SMLA_FLAG_* bits; any other bit is SMLA_ERR_ARG */
+                               merged by log-sum-exp weights in a second kernel
+                               on the same stream. */
+    uint32_t flags;         /* reserved, must be 0 (SMLA_ERR_ARG otherwise) */
     int32_t reserved[6];    /* must be zero */
 } smla_options;
 
@@ -109,14 +97,6 @@ smla_status smla_plan(int32_t num_tokens, int32_t h_q, int32_t topk, int32_t num
  * the device cannot be queried. */
 smla_status smla_workspace_size(int32_t num_tokens, int32_t h_q, int32_t topk,
                                 const smla_options *options, size_t *workspace_bytes);
-
-/* Prepare a workspace for calls that pass SMLA_FLAG_WORKSPACE_READY: zeroes its
- * counter block (the first min(workspace_bytes, 32 KiB) bytes) with a kernel on
- * `stream`. Call it once after allocating the workspace; attention calls keep
- * the block zero. workspace is a 256-B aligned device pointer (may be NULL when
- * workspace_bytes is 0, a no-op). Errors: SMLA_ERR_NULL, SMLA_ERR_ALIGN,
- * SMLA_ERR_HIP. */
-smla_status smla_workspace_init(void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Logical-to-physical index conversion alone [flashmla_sparse.py page,
  * triton_convert_req_index_to_global_index and docstring]:
@@ -147,11 +127,12 @@ smla_status smla_convert_indices(const int32_t *req_id_per_token, const int32_t 
  *   lse               fp32 [num_tokens, h_q] natural-log LSE of the scaled logits; may be NULL
  *   phys_indices_out  int32 [num_tokens, topk] converted slots (-1 = invalid), bit-identical
  *                     to smla_convert_indices; may be NULL
- *   workspace         device scratch for the partial results and arrival counters of a
- *                     top-k split, 256-B aligned; may be NULL when smla_workspace_size
- *                     reports 0 bytes for these sizes. Its contents need not be
- *                     initialised unless options set SMLA_FLAG_WORKSPACE_READY. Calls that
- *                     overlap in time (other streams) must not share a workspace.
+ *   workspace         device scratch for the per-part results of a top-k split (fp32
+ *                     partial outputs and their lse), 256-B aligned; may be NULL when
+ *                     smla_workspace_size reports 0 bytes for these sizes. Its contents
+ *                     need not be initialised; they are written before they are read
+ *                     within the call. Calls that overlap in time (other streams) must
+ *                     not share a workspace.
  *   workspace_bytes   capacity of `workspace` in bytes (SMLA_ERR_WORKSPACE if too small)
  *   options           host pointer or NULL; the same options must be given to
  *                     smla_workspace_size

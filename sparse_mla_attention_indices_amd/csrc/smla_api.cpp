@@ -44,12 +44,8 @@ Plan make_plan(int num_tokens, int h_q, int topk, int num_cus, int forced_splits
     p.split_len = (topk + splits - 1) / splits;
     p.num_splits = (topk + p.split_len - 1) / p.split_len;
     if (p.num_splits > 1) {
-        const size_t units = (size_t)num_tokens * p.head_blocks;
         const size_t rows = (size_t)num_tokens * p.num_splits * h_q;
-        p.counters_off = 0;
-        p.counters_bytes = units * 8;
-        p.counters_in_block = units <= (size_t)kCounterBlockUnits;
-        p.part_lse_off = p.counters_in_block ? kCounterBlockBytes : align_up(p.counters_bytes, 256);
+        p.part_lse_off = 0;
         p.part_o_off = align_up(p.part_lse_off + rows * sizeof(float), 256);
         p.workspace = align_up(p.part_o_off + rows * kDv * sizeof(float), 256);
     }
@@ -64,7 +60,7 @@ smla_status check_options(const smla_options *o)
 {
     if (o == nullptr)
         return SMLA_OK;
-    if (o->num_splits < 0 || (o->flags & ~(uint32_t)SMLA_FLAG_ALL) != 0)
+    if (o->num_splits < 0 || o->flags != 0)
         return SMLA_ERR_ARG;
     for (int i = 0; i < 6; ++i)
         if (o->reserved[i] != 0)
@@ -164,9 +160,7 @@ smla_status attention_entry(CacheFormat fmt, const void *q, const void *kv_cache
     a.num_reqs = num_reqs;
     a.max_blocks = max_blocks_per_req;
     a.num_blocks = num_blocks;
-    const uint32_t flags = options ? options->flags : 0u;
-    return launch_attention(fmt, a, plan, (flags & SMLA_FLAG_WORKSPACE_READY) != 0,
-                            (flags & SMLA_FLAG_TEST_SPLIT_RECOMPUTE) != 0, stream) == hipSuccess
+    return launch_attention(fmt, a, plan, stream) == hipSuccess
                ? SMLA_OK
                : SMLA_ERR_HIP;
 }
@@ -235,18 +229,6 @@ smla_status smla_workspace_size(int32_t num_tokens, int32_t h_q, int32_t topk,
     *workspace_bytes =
         smla::make_plan(num_tokens, h_q, topk, cus, options ? options->num_splits : 0).workspace;
     return SMLA_OK;
-}
-
-smla_status smla_workspace_init(void *workspace, size_t workspace_bytes, hipStream_t stream)
-{
-    if (workspace_bytes == 0)
-        return SMLA_OK;
-    if (workspace == nullptr)
-        return SMLA_ERR_NULL;
-    if (!smla::aligned(workspace, 256))
-        return SMLA_ERR_ALIGN;
-    const size_t n = std::min(workspace_bytes, smla::kCounterBlockBytes) & ~(size_t)3;
-    return smla::launch_zero(workspace, n, stream) == hipSuccess ? SMLA_OK : SMLA_ERR_HIP;
 }
 
 smla_status smla_convert_indices(const int32_t *req_id_per_token, const int32_t *block_table,

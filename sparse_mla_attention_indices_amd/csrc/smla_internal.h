@@ -24,27 +24,16 @@ enum CacheFormat { kCacheBf16 = 0, kCacheFp8 = 1 };
 // workgroups per token instead (two per CU).
 constexpr int kHeadsPerGroup = 64;
 
-// Most top-k parts one token's list is cut into (the merge keeps one weight
-// per head and part in LDS).
+// Most top-k parts one token's list is cut into.
 constexpr int kMaxSplits = 32;
-
-// The workspace starts with a fixed block of arrival counters: 8 bytes per
-// (token, head block) for up to this many units. Every call that splits leaves
-// its counters at zero, and partial results never overlap the block, so a
-// workspace zeroed once stays ready for any later call whose units fit.
-constexpr int kCounterBlockUnits = 4096;
-constexpr size_t kCounterBlockBytes = (size_t)kCounterBlockUnits * 8;
 
 struct Plan {
     int num_splits;          // top-k parts per token
     int split_len;           // top-k positions per part (the last part may be shorter)
     int head_blocks;         // workgroups per (token, part) along heads
     size_t workspace;        // bytes needed (0 when num_splits == 1)
-    size_t counters_off;     // byte offsets inside the workspace
-    size_t counters_bytes;   // bytes of counters this call uses
-    bool counters_in_block;  // its counters lie inside the fixed counter block
-    size_t part_lse_off;
-    size_t part_o_off;
+    size_t part_lse_off;     // byte offsets inside the workspace: [T][S][H] fp32 lse
+    size_t part_o_off;       // and [T][S][H][512] fp32 partial outputs
 };
 
 // Host arithmetic only.
@@ -70,13 +59,8 @@ hipError_t launch_convert(const int32_t *req_id, const int32_t *block_table, con
                           int32_t *out, int num_tokens, int topk_len, int num_reqs,
                           int max_blocks, int64_t num_blocks, hipStream_t stream);
 
-// counters_clean: the caller guarantees the fixed counter block is zero, so no
-// clearing launch precedes the attention kernel when the counters fit in it.
-// force_recompute: every split check fails (exercises the recompute path).
-hipError_t launch_attention(CacheFormat fmt, const AttnArgs &a, const Plan &p, bool counters_clean,
-                            bool force_recompute, hipStream_t stream);
-
-// Zero `bytes` (a multiple of 4) of device memory with a kernel (no memset node).
-hipError_t launch_zero(void *ptr, size_t bytes, hipStream_t stream);
+// The attention kernel and, when the plan splits the top-k lists, the merge
+// kernel after it on the same stream.
+hipError_t launch_attention(CacheFormat fmt, const AttnArgs &a, const Plan &p, hipStream_t stream);
 
 }  // namespace smla

@@ -125,14 +125,15 @@ struct Cfg {
     static constexpr int kOffXchg = kNBuf * kBufBytes;
     static constexpr int kOffP = kOffXchg + kXchgBytes;
     static constexpr int kOffSlots = kOffP + kPBytes;
-    static constexpr int kOffMisc = kOffSlots + kSlotsBytes;         // verdict + compaction counts
+    static constexpr int kOffMisc = kOffSlots + kSlotsBytes;         // compaction counts
     static constexpr int kOffHead = kOffMisc + 512;                  // per-head factors, rescale flags
     static constexpr int kLdsBytes = kOffHead + 1024;
     static_assert(kRowBlockBytes % 16 == 0, "row blocks are whole 16-byte slots");
     static_assert(kRB * kRowBlockBytes <= kBufBytes, "a tile fits its ring buffer");
     static_assert(kTile % kWaves == 0 && kRowsPerWave <= 64, "whole rows per wave");
     static_assert(kLdsBytes <= 160 * 1024, "LDS of one gfx950 workgroup");
-    static_assert(kHeads * kDv * 2 <= kOffSlots, "bf16 output staging fits below the slot list");
+    static_assert(kHeads * kDv * 2 <= kLdsBytes, "bf16 output staging fits");
+    static_assert(kHeads * (kDv + 4) * 4 <= kLdsBytes, "fp32 partial staging fits");
     static_assert(16 + (kMaxChunk / kThreads) * kWaves <= 128, "compaction counts fit");
 };
 
@@ -152,14 +153,12 @@ struct KParams {
     uint16_t *out;
     float *lse;
     int32_t *phys_out;
-    float *part_o;        // [T][S][HB] blobs of kHeads x 512 fp32 (O / l), in register order
+    float *part_o;        // [T][S][H][512] fp32 partial output (O / l) of each split
     float *part_lse;      // [T][S][H] natural-log lse of each split
-    uint64_t *arrivals;   // [T][HB]: arrivals (bits 48..63) + arrivals per XCD (6 bits each)
     float log2e_scale;    // sm_scale * log2(e): logits are kept in log2 units
     int T, H, K, R, MB;
     int64_t NB;
     int S, split_len, HB;
-    int force_recompute;  // treat every split check as failed (exercises that path)
 };
 
 __device__ __forceinline__ int convert_slot(int req, int idx, const int32_t *__restrict__ bt,
@@ -174,6 +173,30 @@ __device__ __forceinline__ int convert_slot(int req, int idx, const int32_t *__r
     if (base < 0 || (int64_t)base >= num_blocks)
         return -1;
     return base * kBlock + (idx & (kBlock - 1));
+}
+
+// convert_slot in two steps and without branches: lookup_block always issues
+// the block-table load (entry 0 stands in for an invalid position; it exists
+// since num_reqs and max_blocks_per_req are >= 1), so the compiler can count
+// the loads in flight and wait for earlier ones while these are outstanding;
+// finish_slot turns the entry into the slot. Same results as convert_slot.
+__device__ __forceinline__ bool slot_position_ok(int req, int idx, int num_reqs, int max_blocks)
+{
+    return (unsigned)req < (unsigned)num_reqs && idx >= 0 && (idx >> 6) < max_blocks;
+}
+
+__device__ __forceinline__ int lookup_block(int req, int idx, const int32_t *__restrict__ bt,
+                                            int num_reqs, int max_blocks)
+{
+    return bt[slot_position_ok(req, idx, num_reqs, max_blocks) ? (size_t)req * max_blocks + (idx >> 6) : 0];
+}
+
+__device__ __forceinline__ int finish_slot(int base, int req, int idx, int num_reqs, int max_blocks,
+                                           int64_t num_blocks)
+{
+    return slot_position_ok(req, idx, num_reqs, max_blocks) && base >= 0 && (int64_t)base < num_blocks
+               ? base * kBlock + (idx & (kBlock - 1))
+               : -1;
 }
 
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b)
@@ -242,14 +265,6 @@ __device__ __forceinline__ int late(int v)
 {
     asm volatile("" : "+v"(v));
     return v;
-}
-
-// Id of the XCD (accelerator complex die) this wave runs on, 0..7 on MI355X.
-__device__ __forceinline__ uint32_t xcc_id()
-{
-    uint32_t x;
-    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(x));
-    return x & 0xF;
 }
 
 // global_load_lds_dwordx4: 16 bytes per active lane from `src` into LDS at
@@ -356,11 +371,8 @@ void attn_kernel(const KParams p)
     i32x8 qh[2], ql[2];         // fp8: hi and lo e4m3 terms of the 32 columns
     int qsh[2], qsl[2];         // fp8: their e8m0 block scales (2^(e - 127))
 
-    // `solo`: this workgroup computes its whole range and writes the output
-    // directly (no split, or the recompute after a failed XCD check).
-    bool solo = p.S == 1;
-    int pos_begin = s * p.split_len;
-    int pos_end = min(p.K, pos_begin + p.split_len);
+    const int pos_begin = s * p.split_len;
+    const int pos_end = min(p.K, pos_begin + p.split_len);
 
     constexpr int DB = C::kDimBlocks;
     // O^T, 16 blocks: o[hb * DB + db] holds dims dim0 + 16*db + 4g + i of head
@@ -606,7 +618,7 @@ void attn_kernel(const KParams p)
 
     float inv_l_hb[NHH];        // per head block: 1 / l of head 16*hb + n16
     float lse_hb[NHH];          // and its natural-log lse
-    for (;;) {
+    {
         // the first round's indices first: their round trip overlaps q's
         int idxv[kPer];
 #pragma unroll
@@ -614,26 +626,43 @@ void attn_kernel(const KParams p)
             const int i = pos_begin + tid + C::kThreads * j;
             idxv[j] = i < min(pos_end, pos_begin + kMaxChunk) ? topk_row[i] : -1;
         }
-        // (re)load q here: a recompute after a failed XCD check needs it again,
-        // and nothing after the tile loop does
+        // q's raw bytes are loaded now and worked on once the first round's
+        // block-table lookups are in flight.
+        const uint16_t *qrow = p.q + ((size_t)t * p.H + head) * kDqk;
+        uint4 qraw[9];      // fp8: [4 * gi + c] latent, [8] RoPE; bf16: k-steps 0..8
+        if constexpr (FMT == kCacheFp8) {
+#pragma unroll
+            for (int gi = 0; gi < 2; ++gi)
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    qraw[4 * gi + c] = ((const uint4 *)(qrow + 128 * (2 * dh + gi) + 32 * g))[c];
+            qraw[8] = *(const uint4 *)(qrow + 512 + 32 * dh + 8 * g);
+        } else {
+#pragma unroll
+            for (int k = 0; k < 9; ++k) {
+                const int col = k < 8 ? 256 * dh + 32 * k + 8 * g : 512 + 32 * dh + 8 * g;
+                qraw[k] = *(const uint4 *)(qrow + col);
+            }
+        }
+        int slotv[kPer];    // block-table entries until q is done, then slots
+#pragma unroll
+        for (int j = 0; j < kPer; ++j)
+            slotv[j] = lookup_block(req, idxv[j], p.bt, p.R, p.MB);
         {
-            const uint16_t *qrow = p.q + ((size_t)t * p.H + head) * kDqk;
+            // each q value is used here, so the compiler waits for these loads
+            // before the tile loop rather than inside it (it cannot see the
+            // explicit waits that order the tile copies)
+#pragma unroll
+            for (int k = 0; k < 9; ++k)
+                asm volatile("" : "+v"(qraw[k].x), "+v"(qraw[k].y), "+v"(qraw[k].z), "+v"(qraw[k].w));
             if constexpr (FMT == kCacheFp8) {
-                {
-                    uint4 w = *(const uint4 *)(qrow + 512 + 32 * dh + 8 * g);
-                    // used here, so the compiler waits for this load before the tile
-                    // loop rather than at its first use inside it (it cannot see the
-                    // explicit waits that order the tile copies)
-                    asm volatile("" : "+v"(w.x), "+v"(w.y), "+v"(w.z), "+v"(w.w));
-                    qb[8] = __builtin_bit_cast(bf16x8, w);
-                }
+                qb[8] = __builtin_bit_cast(bf16x8, qraw[8]);
 #pragma unroll
                 for (int gi = 0; gi < 2; ++gi) {
-                    const uint4 *src = (const uint4 *)(qrow + 128 * (2 * dh + gi) + 32 * g);
                     float v[32];
 #pragma unroll
                     for (int c = 0; c < 4; ++c) {
-                        const uint4 w = src[c];
+                        const uint4 w = qraw[4 * gi + c];
                         const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
@@ -678,22 +707,25 @@ void attn_kernel(const KParams p)
                 }
             } else {
 #pragma unroll
-                for (int k = 0; k < 9; ++k) {
-                    const int col = k < 8 ? 256 * dh + 32 * k + 8 * g : 512 + 32 * dh + 8 * g;
-                    uint4 w = *(const uint4 *)(qrow + col);
-                    // waited for here, not inside the tile loop (as for the fp8 RoPE part)
-                    asm volatile("" : "+v"(w.x), "+v"(w.y), "+v"(w.z), "+v"(w.w));
-                    qb[k] = __builtin_bit_cast(bf16x8, w);
-                }
+                for (int k = 0; k < 9; ++k)
+                    qb[k] = __builtin_bit_cast(bf16x8, qraw[k]);
             }
+        }
+        // finish the lookups only now: tied to the last q operand, the wait for
+        // the block-table loads is not scheduled into the q arithmetic above
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) {
+            if constexpr (FMT == kCacheFp8)
+                asm volatile("" : "+v"(slotv[j]) : "v"(ql[0]), "v"(ql[1]));
+            slotv[j] = finish_slot(slotv[j], req, idxv[j], p.R, p.MB, p.NB);
         }
 #pragma unroll
         for (int k = 0; k < 16; ++k)
             o[k] = f32x4{0.f, 0.f, 0.f, 0.f};
         m_run = -INFINITY;
         l_part = 0.f;
-        // the splits of head block 0 write the converted slots (a recompute does not repeat it)
-        const bool write_phys = p.phys_out != nullptr && hb_wg == 0 && (p.S == 1 || !solo);
+        // the workgroups of head block 0 write the converted slots
+        const bool write_phys = p.phys_out != nullptr && hb_wg == 0;
 
 
         for (int chunk0 = pos_begin; chunk0 < pos_end; chunk0 += kMaxChunk) {
@@ -701,10 +733,19 @@ void attn_kernel(const KParams p)
 
             // ---- convert (all lookups in flight together), then compact the valid
             //      slots in list order with one exchange of per-wave counts
-            int slotv[kPer];
+            if (chunk0 != pos_begin) {
+                // a later round of a long list: its indices, then their slots (loaded
+                // here, so no load is left in flight across the tile loop)
 #pragma unroll
-            for (int j = 0; j < kPer; ++j)
-                slotv[j] = convert_slot(req, idxv[j], p.bt, p.R, p.MB, p.NB);
+                for (int j = 0; j < kPer; ++j) {
+                    const int i = chunk0 + tid + C::kThreads * j;
+                    idxv[j] = i < pos_end ? topk_row[i] : -1;
+                }
+#pragma unroll
+                for (int j = 0; j < kPer; ++j)
+                    slotv[j] = finish_slot(lookup_block(req, idxv[j], p.bt, p.R, p.MB), req, idxv[j],
+                                           p.R, p.MB, p.NB);
+            }
             if (write_phys) {
 #pragma unroll
                 for (int j = 0; j < kPer; ++j) {
@@ -721,12 +762,15 @@ void attn_kernel(const KParams p)
                     lds_misc[16 + j * C::kWaves + wave] = __popcll(masks[j]);
             }
             __syncthreads();
+            // all counts in one read (lane i holds count i), then taken as scalars:
+            // no chain of dependent LDS round trips
+            const int my_count = lds_misc[16 + (lane & 31)];
             int n_valid = 0;
 #pragma unroll
             for (int j = 0; j < kPer; ++j) {
 #pragma unroll
                 for (int w = 0; w < C::kWaves; ++w) {
-                    const int cw = lds_misc[16 + j * C::kWaves + w];
+                    const int cw = __builtin_amdgcn_readlane(my_count, j * C::kWaves + w);
                     if (w == wave && slotv[j] >= 0)
                         lds_slots[n_valid + __popcll(masks[j] & ((1ull << lane) - 1ull))] = slotv[j];
                     n_valid += cw;
@@ -755,12 +799,6 @@ void attn_kernel(const KParams p)
                 tile(ring + (it % C::kNBuf) * C::kBufBytes, min(kTile, n_valid - it * kTile), exact_p);
             }
             __syncthreads();     // ring, exchanges and slot list are free for the next round
-            // the next round's indices
-#pragma unroll
-            for (int j = 0; j < kPer; ++j) {
-                const int i = chunk0 + kMaxChunk + tid + C::kThreads * j;
-                idxv[j] = i < pos_end ? topk_row[i] : -1;
-            }
         }
 
         // ---- per-head results of head block hh (m_run and the row sums are the
@@ -784,133 +822,87 @@ void attn_kernel(const KParams p)
             }
         }
 
-        if (solo)
-            break;
-
-        // ---- top-k split: publish this split's fp32 partial (O / l) in register
-        //      order (each store writes 1 KB contiguous) and its lse, with plain
-        //      stores; they land in this XCD's L2.
-        const size_t blob = (((size_t)t * p.S + s) * p.HB + hb_wg) * ((size_t)C::kHeads * kDv);
-        {
-            f32x4 *po = (f32x4 *)(p.part_o + blob) + (size_t)wave * 16 * 64 + late(lane);
-#pragma unroll
-            for (int k = 0; k < 16; ++k)
-                po[k * 64] = o[k] * inv_l_hb[k / DB];
-            if (wave == 0 && g == 0) {
-#pragma unroll
-                for (int hb = 0; hb < NHH; ++hb)
-                    p.part_lse[((size_t)t * p.S + s) * p.H + wg_head0 + 16 * hb + n16] = lse_hb[hb];
-            }
-        }
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");    // this thread's stores reached L2
-        __syncthreads();
-        if (tid == 0) {
-            // one atomic adds this arrival to the total (bits 48..63) and to this
-            // XCD's count (6 bits at 6 * xcd); splits never exceed 32
-            const uint32_t x = xcc_id();
-            const uint64_t inc = (1ull << 48) | (x < 8 ? 1ull << (6 * x) : 0ull);
-            uint64_t *word = p.arrivals + (size_t)t * p.HB + hb_wg;
-            const uint64_t now = __hip_atomic_fetch_add(word, inc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + inc;
-            int verdict = 0;                                     // 0: not the last arrival
-            if ((now >> 48) == (uint64_t)p.S) {
-                const bool local = x < 8 && ((now >> (6 * x)) & 63u) == (uint64_t)p.S;
-                verdict = (local && !p.force_recompute) ? 1 : 2; // 1: merge, 2: recompute
-                __hip_atomic_store(word, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            }
-            lds_misc[0] = verdict;
-        }
-        __syncthreads();
-        const int verdict = lds_misc[0];
-        if (verdict == 0)
-            return;
-        if (verdict == 1) {
-            // ---- last arrival, on the XCD of every split: merge through the shared
-            //      L2 (this CU's L1 is invalidated first so every load reaches L2).
-            //      Every split's stored partial, this one's included, is added in
-            //      index order, so the result does not depend on which split came
-            //      last.
-            asm volatile("buffer_inv sc0" ::: "memory");
-            const float *plse = p.part_lse + (size_t)t * p.S * p.H + wg_head0 + late(n16);
-            const size_t split_stride = (size_t)p.HB * C::kHeads * kDv / 4;       // in f32x4
-            const f32x4 *src0 = (const f32x4 *)(p.part_o + blob) - (size_t)s * split_stride +
-                                (size_t)wave * 16 * 64 + late(lane);           // split 0
-            // split 0's partial is in flight while the weights are worked out
-            f32x4 va[16];
-#pragma unroll
-            for (int k = 0; k < 16; ++k)
-                va[k] = src0[k * 64];
-            float M[NHH], W[NHH];
-#pragma unroll
-            for (int hb = 0; hb < NHH; ++hb) {
-                M[hb] = -INFINITY;
-                W[hb] = 0.f;
-            }
-            for (int s2 = 0; s2 < p.S; ++s2)
-#pragma unroll
-                for (int hb = 0; hb < NHH; ++hb)
-                    M[hb] = fmaxf(M[hb], plse[(size_t)s2 * p.H + 16 * hb]);
-#pragma unroll
-            for (int k = 0; k < 16; ++k)
-                o[k] = f32x4{0.f, 0.f, 0.f, 0.f};
-            for (int s0 = 0; s0 < p.S; ++s0) {
-                float wa[NHH];
-#pragma unroll
-                for (int hb = 0; hb < NHH; ++hb) {
-                    wa[hb] = M[hb] == -INFINITY ? 0.f : __expf(plse[(size_t)s0 * p.H + 16 * hb] - M[hb]);
-                    W[hb] += wa[hb];
-                }
-                if (s0 > 0) {
-                    const f32x4 *sa = src0 + (size_t)s0 * split_stride;
-#pragma unroll
-                    for (int k = 0; k < 16; ++k)
-                        va[k] = sa[k * 64];
-                }
-#pragma unroll
-                for (int k = 0; k < 16; ++k)
-                    o[k] += wa[k / DB] * va[k];
-            }
-#pragma unroll
-            for (int hb = 0; hb < NHH; ++hb) {
-                inv_l_hb[hb] = W[hb] > 0.f ? 1.f / W[hb] : 0.f;
-                lse_hb[hb] = W[hb] > 0.f ? M[hb] + logf(W[hb]) : -INFINITY;
-            }
-            break;
-        }
-        // some split ran on another XCD, whose partial may sit in another L2:
-        // compute the whole list here instead
-        solo = true;
-        pos_begin = 0;
-        pos_end = p.K;
-        __syncthreads();     // every wave has read the verdict before LDS is reused
     }
 
-    // ---- output rows of this workgroup's heads: staged as bf16 [head][512] in
-    //      LDS, then written out coalesced
+    // ---- output rows of this workgroup's heads, staged in LDS and written out
+    //      coalesced. One split: the bf16 rows of the result. A top-k split: the
+    //      fp32 partial O / l and its lse, head-major, for merge_kernel.
     __syncthreads();        // every wave is done with the exchange areas
-    uint16_t *stage = (uint16_t *)smem;
     const int n16_late = late(n16);
+    if (p.S == 1) {
+        uint16_t *stage = (uint16_t *)smem;
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
-        const int hb = k / DB, db = k % DB;
-        const f32x4 v = o[k] * inv_l_hb[hb];
-        *(uint2 *)(stage + (16 * hb + n16_late) * kDv + dim0 + 16 * db + 4 * g) =
-            make_uint2(pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3]));
-    }
-    if (wave == 0 && g == 0 && p.lse != nullptr) {
+        for (int k = 0; k < 16; ++k) {
+            const int hb = k / DB, db = k % DB;
+            const f32x4 v = o[k] * inv_l_hb[hb];
+            *(uint2 *)(stage + (16 * hb + n16_late) * kDv + dim0 + 16 * db + 4 * g) =
+                make_uint2(pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3]));
+        }
+        if (wave == 0 && g == 0 && p.lse != nullptr) {
 #pragma unroll
-        for (int hb = 0; hb < NHH; ++hb)
-            p.lse[(size_t)t * p.H + wg_head0 + 16 * hb + n16] = lse_hb[hb];
+            for (int hb = 0; hb < NHH; ++hb)
+                p.lse[(size_t)t * p.H + wg_head0 + 16 * hb + n16] = lse_hb[hb];
+        }
+        __syncthreads();
+        uint16_t *dst = p.out + ((size_t)t * p.H + wg_head0) * kDv;
+        for (int u = tid; u < C::kHeads * kDv / 8; u += C::kThreads)
+            *(uint4 *)(dst + 8 * u) = *(const uint4 *)(stage + 8 * u);
+    } else {
+        // rows padded by 16 bytes: the 16 heads of one store fall on distinct banks
+        constexpr int kRow = kDv + 4;
+        float *stage = (float *)smem;
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            const int hb = k / DB, db = k % DB;
+            *(f32x4 *)(stage + (16 * hb + n16_late) * kRow + dim0 + 16 * db + 4 * g) = o[k] * inv_l_hb[hb];
+        }
+        if (wave == 0 && g == 0) {
+#pragma unroll
+            for (int hb = 0; hb < NHH; ++hb)
+                p.part_lse[((size_t)t * p.S + s) * p.H + wg_head0 + 16 * hb + n16] = lse_hb[hb];
+        }
+        __syncthreads();
+        float *dst = p.part_o + (((size_t)t * p.S + s) * p.H + wg_head0) * kDv;
+        for (int u = tid; u < C::kHeads * kDv / 4; u += C::kThreads) {
+            const int row = u / (kDv / 4), c4 = u % (kDv / 4);
+            *(f32x4 *)(dst + 4 * u) = *(const f32x4 *)(stage + row * kRow + 4 * c4);
+        }
     }
-    __syncthreads();
-    uint16_t *dst = p.out + ((size_t)t * p.H + wg_head0) * kDv;
-    for (int u = tid; u < C::kHeads * kDv / 8; u += C::kThreads)
-        *(uint4 *)(dst + 8 * u) = *(const uint4 *)(stage + 8 * u);
 }
 
-__global__ __launch_bounds__(256) void zero_kernel(uint32_t *__restrict__ p, int64_t n)
+// Log-sum-exp merge of a token's top-k splits: thread (t, h, c) combines
+// dims 4c .. 4c + 3 of head h over the splits in index order (weights
+// exp(lse_s - max lse), normalised by their sum) and writes the bf16 output
+// and, once per head, the merged natural-log lse. A split with lse = -inf
+// (no valid position) has weight 0; a head with none at all gets 0 and -inf.
+__global__ __launch_bounds__(256) void merge_kernel(const float *__restrict__ part_o,
+                                                    const float *__restrict__ part_lse,
+                                                    uint16_t *__restrict__ out, float *__restrict__ lse,
+                                                    int T, int H, int S)
 {
-    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
-        p[i] = 0;
+    const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (gid >= (int64_t)T * H * (kDv / 4))
+        return;
+    const int c = (int)(gid % (kDv / 4));
+    const int64_t th = gid / (kDv / 4);           // t * H + h
+    const int t = (int)(th / H), h = (int)(th - (int64_t)t * H);
+    const float *pl = part_lse + (size_t)t * S * H + h;
+    const f32x4 *po = (const f32x4 *)part_o + ((size_t)t * S * H + h) * (kDv / 4) + c;
+    float M = -INFINITY;
+    for (int s2 = 0; s2 < S; ++s2)
+        M = fmaxf(M, pl[(size_t)s2 * H]);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    float W = 0.f;
+#pragma unroll 4
+    for (int s2 = 0; s2 < S; ++s2) {
+        const float w = M == -INFINITY ? 0.f : __expf(pl[(size_t)s2 * H] - M);
+        acc += w * po[(size_t)s2 * H * (kDv / 4)];
+        W += w;
+    }
+    const f32x4 v = acc * (W > 0.f ? 1.f / W : 0.f);
+    *(uint2 *)(out + th * kDv + 4 * c) = make_uint2(pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3]));
+    if (c == 0 && lse != nullptr)
+        lse[th] = W > 0.f ? M + logf(W) : -INFINITY;
 }
 
 __global__ __launch_bounds__(256) void convert_kernel(const int32_t *__restrict__ req_id,
@@ -950,17 +942,6 @@ hipError_t launch_fmt(const KParams &p, hipStream_t stream)
 
 }  // namespace
 
-hipError_t launch_zero(void *ptr, size_t bytes, hipStream_t stream)
-{
-    const int64_t n = (int64_t)(bytes / 4);
-    if (n == 0)
-        return hipSuccess;
-    const int64_t blocks = (n + 255) / 256;
-    hipLaunchKernelGGL(zero_kernel, dim3((unsigned)(blocks < 4096 ? blocks : 4096)), dim3(256), 0, stream,
-                       (uint32_t *)ptr, n);
-    return hipGetLastError();
-}
-
 hipError_t launch_convert(const int32_t *req_id, const int32_t *block_table, const int32_t *topk,
                           int32_t *out, int num_tokens, int topk_len, int num_reqs, int max_blocks,
                           int64_t num_blocks, hipStream_t stream)
@@ -973,8 +954,7 @@ hipError_t launch_convert(const int32_t *req_id, const int32_t *block_table, con
     return hipGetLastError();
 }
 
-hipError_t launch_attention(CacheFormat fmt, const AttnArgs &a, const Plan &pl, bool counters_clean,
-                            bool force_recompute, hipStream_t stream)
+hipError_t launch_attention(CacheFormat fmt, const AttnArgs &a, const Plan &pl, hipStream_t stream)
 {
     KParams p;
     p.q = (const uint16_t *)a.q;
@@ -986,7 +966,6 @@ hipError_t launch_attention(CacheFormat fmt, const AttnArgs &a, const Plan &pl, 
     p.lse = a.lse;
     p.phys_out = a.phys_out;
     const bool split = pl.num_splits > 1;
-    p.arrivals = split ? (uint64_t *)((char *)a.workspace + pl.counters_off) : nullptr;
     p.part_o = split ? (float *)((char *)a.workspace + pl.part_o_off) : nullptr;
     p.part_lse = split ? (float *)((char *)a.workspace + pl.part_lse_off) : nullptr;
     p.log2e_scale = a.sm_scale * 1.4426950408889634f;
@@ -999,13 +978,13 @@ hipError_t launch_attention(CacheFormat fmt, const AttnArgs &a, const Plan &pl, 
     p.S = pl.num_splits;
     p.split_len = pl.split_len;
     p.HB = pl.head_blocks;
-    p.force_recompute = force_recompute ? 1 : 0;
-    if (split && !(counters_clean && pl.counters_in_block)) {
-        const hipError_t err = launch_zero(p.arrivals, pl.counters_bytes, stream);
-        if (err != hipSuccess)
-            return err;
-    }
-    return fmt == kCacheFp8 ? launch_fmt<kCacheFp8>(p, stream) : launch_fmt<kCacheBf16>(p, stream);
+    const hipError_t err = fmt == kCacheFp8 ? launch_fmt<kCacheFp8>(p, stream) : launch_fmt<kCacheBf16>(p, stream);
+    if (err != hipSuccess || !split)
+        return err;
+    const int64_t threads = (int64_t)p.T * p.H * (kDv / 4);
+    hipLaunchKernelGGL(merge_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream,
+                       (const float *)p.part_o, (const float *)p.part_lse, p.out, p.lse, p.T, p.H, p.S);
+    return hipGetLastError();
 }
 
 }  // namespace smla

@@ -24,9 +24,7 @@ SMLA_OK = 0
 STATUS_NAMES = {0: "SMLA_OK", 1: "SMLA_ERR_NULL", 2: "SMLA_ERR_SHAPE", 3: "SMLA_ERR_ALIGN",
                 4: "SMLA_ERR_WORKSPACE", 5: "SMLA_ERR_HIP", 6: "SMLA_ERR_ARG"}
 EXPORTS = ("smla_status_string", "smla_abi_version", "smla_plan", "smla_workspace_size",
-           "smla_workspace_init", "smla_convert_indices", "smla_prefill_bf16", "smla_decode_fp8")
-FLAG_WORKSPACE_READY = 0x1
-FLAG_TEST_SPLIT_RECOMPUTE = 0x2
+           "smla_convert_indices", "smla_prefill_bf16", "smla_decode_fp8")
 
 
 class SmlaError(RuntimeError):
@@ -62,8 +60,6 @@ def library() -> ctypes.CDLL:
     lib.smla_plan.argtypes = [i32, i32, i32, i32, vp, ctypes.POINTER(i32), ctypes.POINTER(sz)]
     lib.smla_workspace_size.restype = ctypes.c_int
     lib.smla_workspace_size.argtypes = [i32, i32, i32, vp, ctypes.POINTER(sz)]
-    lib.smla_workspace_init.restype = ctypes.c_int
-    lib.smla_workspace_init.argtypes = [vp, sz, vp]
     lib.smla_convert_indices.restype = ctypes.c_int
     lib.smla_convert_indices.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i64, vp]
     attn = [vp, vp, vp, vp, vp, fl, i32, i32, i32, i32, i32, i64, vp, vp, vp, vp, sz, vp, vp]
@@ -127,16 +123,8 @@ def smla_workspace_size(num_tokens: int, h_q: int, topk: int, num_splits: int = 
     return b.value
 
 
-def smla_workspace_init(workspace: torch.Tensor, stream=None) -> torch.Tensor:
-    """Zero the counter block of a workspace so calls may pass workspace_ready=True."""
-    _check(library().smla_workspace_init(_dev(workspace, "workspace"),
-                                         workspace.numel() * workspace.element_size(),
-                                         _stream(stream)), "smla_workspace_init")
-    return workspace
-
-
 # Workspaces the binding allocates itself, one per (device, stream), grown on
-# demand and initialised once, so repeated calls skip the clearing launch.
+# demand.
 _own_workspaces: dict = {}
 
 
@@ -145,7 +133,6 @@ def _own_workspace(device: torch.device, stream, need: int) -> torch.Tensor:
     ws = _own_workspaces.get(key)
     if ws is None or ws.numel() < need:
         ws = torch.empty(need, dtype=torch.uint8, device=device)
-        smla_workspace_init(ws, stream)
         _own_workspaces[key] = ws
     return ws
 
@@ -166,8 +153,7 @@ def smla_convert_indices(req_id_per_token, block_table, topk_indices, num_blocks
 
 
 def _attention(name: str, q, kv_cache, block_table, req_id_per_token, topk_indices, sm_scale,
-               out, lse, phys_indices_out, workspace, num_splits, stream, want_lse, workspace_ready,
-               flags):
+               out, lse, phys_indices_out, workspace, num_splits, stream, want_lse):
     T, H, D = q.shape
     if D != 576:
         raise ValueError("q must be [num_tokens, h_q, 576]")
@@ -180,9 +166,6 @@ def _attention(name: str, q, kv_cache, block_table, req_id_per_token, topk_indic
         need = smla_workspace_size(T, H, K, num_splits)
         if need > 0:
             workspace = _own_workspace(q.device, stream, need)
-            workspace_ready = True
-    if workspace_ready:
-        flags |= FLAG_WORKSPACE_READY
     ws_ptr = _dev(workspace, "workspace") if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     fn = getattr(library(), name)
@@ -193,34 +176,30 @@ def _attention(name: str, q, kv_cache, block_table, req_id_per_token, topk_indic
               block_table.shape[0], block_table.shape[1], kv_cache.shape[0],
               _dev(out, "out", torch.bfloat16, 3), _dev(lse, "lse", torch.float32, 2),
               _dev(phys_indices_out, "phys_indices_out", torch.int32, 2),
-              ws_ptr, ws_bytes, _options(num_splits, flags), _stream(stream)), name)
+              ws_ptr, ws_bytes, _options(num_splits), _stream(stream)), name)
     return out, lse
 
 
 def smla_prefill_bf16(q, kv_cache, block_table, req_id_per_token, topk_indices, sm_scale,
                       out=None, lse=None, phys_indices_out=None, workspace=None, num_splits=0,
-                      stream=None, want_lse=True, workspace_ready=False, flags=0):
+                      stream=None, want_lse=True):
     """Sparse MLA forward over a bf16 cache [num_blocks, 64, 576]. Returns (out, lse).
 
-    workspace: uint8 device tensor of at least smla_workspace_size bytes, or None for
-    one the binding keeps per (device, stream). workspace_ready: the given workspace
-    went through smla_workspace_init and only completed calls since. flags: extra
-    SMLA_FLAG_* bits (FLAG_TEST_SPLIT_RECOMPUTE)."""
+    workspace: uint8 device tensor of at least smla_workspace_size bytes (contents
+    need not be initialised), or None for one the binding keeps per (device, stream)."""
     if kv_cache.dtype != torch.bfloat16 or kv_cache.shape[1:] != (64, 576):
         raise ValueError("kv_cache must be bf16 [num_blocks, 64, 576]")
     return _attention("smla_prefill_bf16", q, kv_cache, block_table, req_id_per_token, topk_indices,
-                      sm_scale, out, lse, phys_indices_out, workspace, num_splits, stream, want_lse,
-                      workspace_ready, flags)
+                      sm_scale, out, lse, phys_indices_out, workspace, num_splits, stream, want_lse)
 
 
 def smla_decode_fp8(q, kv_cache, block_table, req_id_per_token, topk_indices, sm_scale,
                     out=None, lse=None, phys_indices_out=None, workspace=None, num_splits=0,
-                    stream=None, want_lse=True, workspace_ready=False, flags=0):
+                    stream=None, want_lse=True):
     """Sparse MLA forward over an fp8_ds_mla cache uint8 [num_blocks, 64, 656]. Returns (out, lse).
 
     Other arguments as for smla_prefill_bf16."""
     if kv_cache.dtype != torch.uint8 or kv_cache.shape[1:] != (64, 656):
         raise ValueError("kv_cache must be uint8 [num_blocks, 64, 656]")
     return _attention("smla_decode_fp8", q, kv_cache, block_table, req_id_per_token, topk_indices,
-                      sm_scale, out, lse, phys_indices_out, workspace, num_splits, stream, want_lse,
-                      workspace_ready, flags)
+                      sm_scale, out, lse, phys_indices_out, workspace, num_splits, stream, want_lse)

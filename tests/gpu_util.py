@@ -36,16 +36,14 @@ class DeviceWorkload:
         self.req = torch.from_numpy(w.req_id_per_token).to(device)
         self.idx = torch.from_numpy(w.topk_indices).to(device)
 
-    def run(self, num_splits=0, with_phys=False, num_tokens=None, workspace=None,
-            workspace_ready=False, flags=0):
+    def run(self, num_splits=0, with_phys=False, num_tokens=None, workspace=None):
         """One call over the first num_tokens tokens (default all)."""
         fn = smla.smla_prefill_bf16 if self.w.cache_format == "bf16" else smla.smla_decode_fp8
         T = self.w.num_tokens if num_tokens is None else num_tokens
         idx = self.idx[:T]
         phys = torch.full_like(idx, -7) if with_phys else None
         out, lse = fn(self.q[:T], self.cache, self.bt, self.req[:T], idx, self.w.sm_scale,
-                      phys_indices_out=phys, num_splits=num_splits, workspace=workspace,
-                      workspace_ready=workspace_ready, flags=flags)
+                      phys_indices_out=phys, num_splits=num_splits, workspace=workspace)
         torch.cuda.synchronize()
         return out, lse, phys
 

@@ -39,7 +39,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_abi_version(lib):
-    assert smla.smla_abi_version() == 2
+    assert smla.smla_abi_version() == 3
 
 
 def test_status_strings(lib):
@@ -53,8 +53,7 @@ def test_plan_fills_the_chip_for_small_decode_batches(lib):
     assert s == 4
     up = lambda v: -(-v // 256) * 256
     rows = 64 * 4 * 64
-    counter_block = 4096 * 8                 # fixed block of arrival counters first
-    o_off = up(counter_block + rows * 4)     # then the partial lse, then the partial o
+    o_off = up(rows * 4)                     # the partial lse first, then the partial o
     assert ws == up(o_off + rows * 512 * 4)
     # two-wave workgroups (h_q <= 32) fit two per CU: 256 tokens x 16 heads -> 2 splits
     assert smla.smla_plan(256, 16, 2048, 256)[0] == 2
@@ -73,14 +72,12 @@ def test_plan_fills_the_chip_for_small_decode_batches(lib):
     assert smla.smla_plan(1, 16, 16384, 256)[0] == 32
 
 
-def test_plan_counters_beyond_the_fixed_block(lib):
-    # 5000 (token, head block) units > 4096: the counters grow past the block and
-    # the partial results move behind them
+def test_plan_workspace_layout_for_large_batches(lib):
+    # [T][S][H] fp32 lse, then [T][S][H][512] fp32 partial outputs, 256-B aligned
     up = lambda v: -(-v // 256) * 256
     s, ws = smla.smla_plan(5000, 16, 64, 256, num_splits=2)
     rows = 5000 * 2 * 16
-    o_off = up(up(5000 * 8) + rows * 4)
-    assert s == 2 and ws == up(o_off + rows * 512 * 4)
+    assert s == 2 and ws == up(up(rows * 4) + rows * 512 * 4)
 
 
 @pytest.mark.parametrize("args,code", [
@@ -104,9 +101,10 @@ def test_plan_rejects_bad_options(lib):
     o.num_splits = -2
     assert lib.smla_plan(8, 16, 64, 256, ctypes.byref(o), ctypes.byref(s), ctypes.byref(b)) == 6
     o = smla.SmlaOptions()
-    o.flags = 0x4                            # unknown flag bit
-    assert lib.smla_plan(8, 16, 64, 256, ctypes.byref(o), ctypes.byref(s), ctypes.byref(b)) == 6
-    o.flags = smla.FLAG_WORKSPACE_READY | smla.FLAG_TEST_SPLIT_RECOMPUTE
+    for bit in (0x1, 0x2, 0x4):              # flags are reserved: any bit is rejected
+        o.flags = bit
+        assert lib.smla_plan(8, 16, 64, 256, ctypes.byref(o), ctypes.byref(s), ctypes.byref(b)) == 6
+    o.flags = 0
     assert lib.smla_plan(8, 16, 64, 256, ctypes.byref(o), ctypes.byref(s), ctypes.byref(b)) == 0
     assert lib.smla_plan(8, 16, 64, 256, None, None, ctypes.byref(b)) == 1
 
@@ -155,12 +153,6 @@ def test_options_struct_layout():
     # num_splits, flags, reserved[6]: 32 bytes, as in include/smla.h
     assert ctypes.sizeof(smla.SmlaOptions) == 32
     assert smla.SmlaOptions.flags.offset == 4 and smla.SmlaOptions.reserved.offset == 8
-
-
-def test_workspace_init_validation(lib):
-    assert lib.smla_workspace_init(None, 0, None) == 0          # nothing to do, no HIP call
-    assert lib.smla_workspace_init(None, 1024, None) == 1
-    assert lib.smla_workspace_init(A16 + 16, 1024, None) == 3
 
 
 def test_workspace_size_validation(lib):

@@ -150,45 +150,38 @@ def test_short_lists_are_exact_up_to_output_rounding(fmt):
 
 @pytest.mark.parametrize("fmt", ["bf16", "fp8"])
 @pytest.mark.parametrize("h_q", [16, 64, 128])
-def test_split_recompute_path(fmt, h_q):
-    """The path a token takes when its splits did not all run on one XCD: the last
-    split recomputes the whole token. Forced here for every token; results must
-    match the oracle, and the converted indices are still written once, in full."""
+def test_split_merge_with_converted_indices(fmt, h_q):
+    """Top-k splits merged by the second kernel, with invalid positions spread over
+    the parts (some parts of a short list hold none): results match the oracle and
+    the converted indices are written once, in full."""
     w = small(31 + h_q, fmt, h_q, 300, n_req=3, tok_per_req=3, ctx=(400, 900), p_invalid=0.15)
     dw = DeviceWorkload(w)
     want_phys = oracle.convert_indices(w.req_id_per_token, w.block_table, w.topk_indices, w.num_blocks)
     for splits in (2, 5):
-        log(f"[case] recompute path {fmt} h_q={h_q} splits={splits}")
-        out, lse, phys = dw.run(num_splits=splits, with_phys=True, flags=smla.FLAG_TEST_SPLIT_RECOMPUTE)
+        log(f"[case] split merge {fmt} h_q={h_q} splits={splits}")
+        out, lse, phys = dw.run(num_splits=splits, with_phys=True)
         assert np.array_equal(phys.cpu().numpy(), want_phys)
-        assert_parity(w, out, lse, label=f"recompute {fmt} h{h_q} s{splits}")
+        assert_parity(w, out, lse, label=f"split merge {fmt} h{h_q} s{splits}")
 
 
 @pytest.mark.parametrize("fmt", ["bf16", "fp8"])
-def test_ready_workspace_reused_across_batch_sizes(fmt):
-    """One workspace, zeroed once by smla_workspace_init, then calls of changing
-    token counts with SMLA_FLAG_WORKSPACE_READY: each call must find its arrival
-    counters at zero although earlier calls wrote partial results elsewhere in the
-    buffer. The 4100-token calls need more counters than the fixed block holds
-    (4100 units > 4096), so they clear their own; the calls after them rely on
-    the block again."""
+def test_workspace_reused_across_batch_sizes(fmt):
+    """One workspace, filled with garbage once, then calls of changing token counts
+    that share it: every call writes what it reads, so results depend neither on
+    the initial contents nor on the calls before."""
     w = small(41, fmt, 16, 48, n_req=41, tok_per_req=100, ctx=(60, 300), p_invalid=0.2)
     dw = DeviceWorkload(w)
     need = max(smla.smla_workspace_size(T, 16, 48, num_splits=3) for T in (9, 4100))
     ws = torch.full((need,), 0xA5, dtype=torch.uint8, device="cuda")
-    smla.smla_workspace_init(ws)
     for T in (9, 3, 4100, 9, 200, 4100, 5):
-        log(f"[case] ready workspace {fmt} T={T}")
-        out, lse, _ = dw.run(num_splits=3, num_tokens=T, workspace=ws, workspace_ready=True)
-        assert_parity(w, out, lse, tokens=np.arange(T), label=f"ready ws {fmt} T{T}")
-    # the counter block is zero again after every call
-    assert int(ws[:32768].count_nonzero()) == 0
+        log(f"[case] reused workspace {fmt} T={T}")
+        out, lse, _ = dw.run(num_splits=3, num_tokens=T, workspace=ws)
+        assert_parity(w, out, lse, tokens=np.arange(T), label=f"reused ws {fmt} T{T}")
 
 
 @pytest.mark.parametrize("fmt", ["bf16", "fp8"])
-def test_uninitialised_workspace_without_ready_flag(fmt):
-    """Without the flag the call clears its own counters: a workspace full of
-    garbage gives the same results."""
+def test_uninitialised_workspace(fmt):
+    """A workspace full of 0xFF bytes (NaN patterns) gives the same results."""
     w = small(43, fmt, 64, 200, n_req=2, tok_per_req=4)
     dw = DeviceWorkload(w)
     ws = torch.full((smla.smla_workspace_size(w.num_tokens, 64, 200, num_splits=4),), 0xFF,
