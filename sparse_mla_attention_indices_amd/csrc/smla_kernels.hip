@@ -384,8 +384,58 @@ void attn_kernel(const KParams p)
     int *resc_flag = (int *)(smem + C::kOffHead + 256);      // [4] head block moved its max this tile
     float *alpha_lds = (float *)(smem + C::kOffHead + 512);  // [4][16] rescale factors
 
+    // fp8 with several head blocks runs software-pipelined: one phase of the
+    // tile loop does PV of tile i - 1 (its V^T fragments were read into
+    // registers before the previous exchange, its P^T waits in LDS) together
+    // with QK^T of tile i, so two independent MFMA chains interleave and a
+    // tile needs two barriers instead of three.
+    constexpr bool kPipe = FMT == kCacheFp8 && NHH > 1;
+    bf16x8 *p_lds = (bf16x8 *)(smem + C::kOffP);          // [lo][group][head block][lane]
+    uint2 vf8_pend[DB];         // pipelined fp8: V^T fragments of the tile whose PV is pending
+
+    // PV, part 1 (after the barrier that publishes P^T): rescale O for head
+    // blocks whose max moved, and in exact mode add the lo terms of P.
+    auto pv_pre = [&](const uint2 *vf, bool exact) __attribute__((always_inline)) {
+        const int G = dim0 >> 7;                                // scale group of this wave's dims
+#pragma unroll
+        for (int hb = 0; hb < NHH; ++hb) {
+            if (resc_flag[hb]) {
+                const float al = alpha_lds[hb * 16 + n16];
+#pragma unroll
+                for (int db = 0; db < DB; ++db)
+                    o[hb * DB + db] *= al;
+            }
+        }
+        if (exact) {
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                const bf16x8 a = e4m3x8_to_bf16x8(vf[db]);
+#pragma unroll
+                for (int hb = 0; hb < NHH; ++hb)
+                    o[hb * DB + db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        a, p_lds[((4 + G) * NHH + hb) * 64 + lane], o[hb * DB + db], 0, 0, 0);
+            }
+        }
+    };
+    // PV, part 2: O^T += V^T P^T (hi terms) over this wave's dims, branch-free.
+    auto pv_main = [&](const uint2 *vf) __attribute__((always_inline)) {
+        const int G = dim0 >> 7;
+        bf16x8 pv[NHH];
+#pragma unroll
+        for (int hb = 0; hb < NHH; ++hb)
+            pv[hb] = p_lds[(G * NHH + hb) * 64 + lane];
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+            const bf16x8 a = e4m3x8_to_bf16x8(vf[db]);
+#pragma unroll
+            for (int hb = 0; hb < NHH; ++hb)
+                o[hb * DB + db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pv[hb], o[hb * DB + db], 0, 0, 0);
+        }
+    };
+
     // One tile: S^T = K q^T, online softmax, O^T += V^T P^T. exact: P enters PV
-    // as hi + lo bf16 terms (wave-uniform).
+    // as hi + lo bf16 terms (wave-uniform). Pipelined: the tile stops after
+    // publishing P^T; its PV runs in the next phase.
     auto tile = [&](const uint8_t *buf, int n_tile, bool exact) __attribute__((always_inline)) {
         // per-lane LDS offsets inside the tile buffer
         const int off_k = n16 * RS;                      // K rows 16*rb + n16 (+ rb * RBB)
@@ -561,7 +611,6 @@ void attn_kernel(const KParams p)
         } else {
             // ---- hand P^T of head block hh for groups 2*dh, 2*dh + 1 (and the
             //      rescale factor when the max moved) to the waves owning those dims
-            bf16x8 *p_lds = (bf16x8 *)(smem + C::kOffP);          // [lo][group][head block][lane]
 #pragma unroll
             for (int gi = 0; gi < 2; ++gi) {
                 p_lds[((2 * dh + gi) * NHH + hh) * 64 + lane] = pbh[gi];
@@ -573,6 +622,12 @@ void attn_kernel(const KParams p)
                     resc_flag[hh] = moved ? 1 : 0;
                 if (moved && g == 0)
                     alpha_lds[hh * 16 + n16] = alpha;
+            }
+            if constexpr (kPipe) {
+#pragma unroll
+                for (int db = 0; db < DB; ++db)
+                    vf8_pend[db] = vf8[db];
+                return;
             }
             __syncthreads();
             // ---- O^T += V^T P^T over this wave's dims for every head block
@@ -788,15 +843,39 @@ void attn_kernel(const KParams p)
                 issue_tile<C>(p.cache, lds_slots + i * kTile, min(kTile, n_valid - i * kTile),
                               ring + i * C::kBufBytes, wave, lane);
 
+            if constexpr (kPipe) {
+                // the PV pending before the first tile adds nothing: zero weights,
+                // zero fragments, no rescale (ordered before any read by the first
+                // barrier below)
+#pragma unroll
+                for (int k = wave; k < 2 * 4 * NHH; k += C::kWaves)
+                    p_lds[k * 64 + lane] = bf16x8{};
+                if (tid < NHH)
+                    resc_flag[tid] = 0;
+#pragma unroll
+                for (int db = 0; db < DB; ++db)
+                    vf8_pend[db] = make_uint2(0u, 0u);
+            }
             for (int it = 0; it < n_tiles; ++it) {
                 wait_vmcnt(dma_w * min(C::kNBuf - 2, n_tiles - 1 - it));
-                __syncthreads();     // every wave's pieces of tile `it` landed; tile it-1 is done
+                // every wave's pieces of tile `it` landed; tile it-1 is done (its PV
+                // only needs registers and the published P^T)
+                __syncthreads();
                 if (it + C::kNBuf - 1 < n_tiles) {
                     const int nt = it + C::kNBuf - 1;
                     issue_tile<C>(p.cache, lds_slots + nt * kTile, min(kTile, n_valid - nt * kTile),
                                   ring + (nt % C::kNBuf) * C::kBufBytes, wave, lane);
                 }
+                if constexpr (kPipe) {
+                    pv_pre(vf8_pend, exact_p);
+                    pv_main(vf8_pend);
+                }
                 tile(ring + (it % C::kNBuf) * C::kBufBytes, min(kTile, n_valid - it * kTile), exact_p);
+            }
+            if constexpr (kPipe) {
+                __syncthreads();     // P^T of the last tile is visible
+                pv_pre(vf8_pend, exact_p);
+                pv_main(vf8_pend);
             }
             __syncthreads();     // ring, exchanges and slot list are free for the next round
         }
@@ -875,6 +954,9 @@ void attn_kernel(const KParams p)
 // exp(lse_s - max lse), normalised by their sum) and writes the bf16 output
 // and, once per head, the merged natural-log lse. A split with lse = -inf
 // (no valid position) has weight 0; a head with none at all gets 0 and -inf.
+// KS > 0: exactly KS splits, every load issued before the first is used;
+// KS = 0: any count, in batches of 8.
+template <int KS>
 __global__ __launch_bounds__(256) void merge_kernel(const float *__restrict__ part_o,
                                                     const float *__restrict__ part_lse,
                                                     uint16_t *__restrict__ out, float *__restrict__ lse,
@@ -886,21 +968,50 @@ __global__ __launch_bounds__(256) void merge_kernel(const float *__restrict__ pa
     const int c = (int)(gid % (kDv / 4));
     const int64_t th = gid / (kDv / 4);           // t * H + h
     const int t = (int)(th / H), h = (int)(th - (int64_t)t * H);
+    if constexpr (KS > 0)
+        S = KS;
     const float *pl = part_lse + (size_t)t * S * H + h;
     const f32x4 *po = (const f32x4 *)part_o + ((size_t)t * S * H + h) * (kDv / 4) + c;
-    float M = -INFINITY;
-    for (int s2 = 0; s2 < S; ++s2)
-        M = fmaxf(M, pl[(size_t)s2 * H]);
+    const size_t ostride = (size_t)H * (kDv / 4);
+    float M = -INFINITY, W = 0.f;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    float W = 0.f;
-#pragma unroll 4
-    for (int s2 = 0; s2 < S; ++s2) {
-        const float w = M == -INFINITY ? 0.f : __expf(pl[(size_t)s2 * H] - M);
-        acc += w * po[(size_t)s2 * H * (kDv / 4)];
-        W += w;
+    if constexpr (KS > 0) {
+        float l[KS];
+        f32x4 v[KS];
+#pragma unroll
+        for (int s2 = 0; s2 < KS; ++s2) {
+            l[s2] = pl[(size_t)s2 * H];
+            v[s2] = po[s2 * ostride];
+        }
+#pragma unroll
+        for (int s2 = 0; s2 < KS; ++s2)
+            M = fmaxf(M, l[s2]);
+#pragma unroll
+        for (int s2 = 0; s2 < KS; ++s2) {
+            const float w = M == -INFINITY ? 0.f : __expf(l[s2] - M);
+            acc += w * v[s2];
+            W += w;
+        }
+    } else {
+        for (int s2 = 0; s2 < S; ++s2)
+            M = fmaxf(M, pl[(size_t)s2 * H]);
+        for (int s0 = 0; s0 < S; s0 += 8) {
+            f32x4 v[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k)
+                if (s0 + k < S)
+                    v[k] = po[(size_t)(s0 + k) * ostride];
+#pragma unroll
+            for (int k = 0; k < 8; ++k)
+                if (s0 + k < S) {
+                    const float w = M == -INFINITY ? 0.f : __expf(pl[(size_t)(s0 + k) * H] - M);
+                    acc += w * v[k];
+                    W += w;
+                }
+        }
     }
-    const f32x4 v = acc * (W > 0.f ? 1.f / W : 0.f);
-    *(uint2 *)(out + th * kDv + 4 * c) = make_uint2(pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3]));
+    const f32x4 o = acc * (W > 0.f ? 1.f / W : 0.f);
+    *(uint2 *)(out + th * kDv + 4 * c) = make_uint2(pack_bf16(o[0], o[1]), pack_bf16(o[2], o[3]));
     if (c == 0 && lse != nullptr)
         lse[th] = W > 0.f ? M + logf(W) : -INFINITY;
 }
@@ -982,8 +1093,17 @@ hipError_t launch_attention(CacheFormat fmt, const AttnArgs &a, const Plan &pl, 
     if (err != hipSuccess || !split)
         return err;
     const int64_t threads = (int64_t)p.T * p.H * (kDv / 4);
-    hipLaunchKernelGGL(merge_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream,
-                       (const float *)p.part_o, (const float *)p.part_lse, p.out, p.lse, p.T, p.H, p.S);
+    const dim3 grid((unsigned)((threads + 255) / 256));
+    const float *po = p.part_o, *plse = p.part_lse;
+    switch (p.S) {
+    case 2: hipLaunchKernelGGL(merge_kernel<2>, grid, dim3(256), 0, stream, po, plse, p.out, p.lse, p.T, p.H, p.S); break;
+    case 3: hipLaunchKernelGGL(merge_kernel<3>, grid, dim3(256), 0, stream, po, plse, p.out, p.lse, p.T, p.H, p.S); break;
+    case 4: hipLaunchKernelGGL(merge_kernel<4>, grid, dim3(256), 0, stream, po, plse, p.out, p.lse, p.T, p.H, p.S); break;
+    case 5: hipLaunchKernelGGL(merge_kernel<5>, grid, dim3(256), 0, stream, po, plse, p.out, p.lse, p.T, p.H, p.S); break;
+    case 6: hipLaunchKernelGGL(merge_kernel<6>, grid, dim3(256), 0, stream, po, plse, p.out, p.lse, p.T, p.H, p.S); break;
+    case 8: hipLaunchKernelGGL(merge_kernel<8>, grid, dim3(256), 0, stream, po, plse, p.out, p.lse, p.T, p.H, p.S); break;
+    default: hipLaunchKernelGGL(merge_kernel<0>, grid, dim3(256), 0, stream, po, plse, p.out, p.lse, p.T, p.H, p.S); break;
+    }
     return hipGetLastError();
 }
 
