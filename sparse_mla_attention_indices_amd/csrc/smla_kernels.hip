@@ -395,12 +395,14 @@ void attn_kernel(const KParams p)
 
     // PV, part 1 (after the barrier that publishes P^T): rescale O for head
     // blocks whose max moved, and in exact mode add the lo terms of P.
-    auto pv_pre = [&](const uint2 *vf, bool exact) __attribute__((always_inline)) {
+    // flags / al: resc_flag and alpha_lds of the pending tile, read right after
+    // the barrier so their latency overlaps the copy issue.
+    auto pv_pre = [&](const uint2 *vf, bool exact, const int *flags, const float *al_in) __attribute__((always_inline)) {
         const int G = dim0 >> 7;                                // scale group of this wave's dims
 #pragma unroll
         for (int hb = 0; hb < NHH; ++hb) {
-            if (resc_flag[hb]) {
-                const float al = alpha_lds[hb * 16 + n16];
+            if (flags[hb]) {
+                const float al = al_in[hb];
 #pragma unroll
                 for (int db = 0; db < DB; ++db)
                     o[hb * DB + db] *= al;
@@ -529,24 +531,25 @@ void attn_kernel(const KParams p)
         // ---- online softmax of head block hh in log2 units. The running max
         //      moves only when some row exceeds it by 2^8 (tested on each lane's
         //      own rows, moved to the whole head's max).
+        // (the scale c2 > 0 is applied to the maximum here and inside the exp2
+        // argument below: max(c2 * a) = c2 * max(a) exactly)
         float lmax = -INFINITY;
         if (n_tile == kTile) {
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    acc[rb][i] *= c2;
+                for (int i = 0; i < 4; ++i)
                     lmax = fmaxf(lmax, acc[rb][i]);
-                }
         } else {
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    acc[rb][i] = 16 * rb + 4 * g + i < n_tile ? acc[rb][i] * c2 : -INFINITY;
+                    acc[rb][i] = 16 * rb + 4 * g + i < n_tile ? acc[rb][i] : -INFINITY;
                     lmax = fmaxf(lmax, acc[rb][i]);
                 }
         }
+        lmax *= c2;
         bool moved = false;
         float alpha = 1.f;
         if (__ballot(lmax > m_run + kLazyRescale) != 0) {
@@ -563,7 +566,7 @@ void attn_kernel(const KParams p)
         for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                acc[rb][i] = __builtin_amdgcn_exp2f(acc[rb][i] - m_run);
+                acc[rb][i] = __builtin_amdgcn_exp2f(fmaf(acc[rb][i], c2, -m_run));
                 l_part += acc[rb][i];
             }
 
@@ -861,20 +864,36 @@ void attn_kernel(const KParams p)
                 // every wave's pieces of tile `it` landed; tile it-1 is done (its PV
                 // only needs registers and the published P^T)
                 __syncthreads();
+                int rflag[NHH];
+                float ralpha[NHH];
+                if constexpr (kPipe) {
+#pragma unroll
+                    for (int hb = 0; hb < NHH; ++hb) {
+                        rflag[hb] = resc_flag[hb];
+                        ralpha[hb] = alpha_lds[hb * 16 + n16];
+                    }
+                }
                 if (it + C::kNBuf - 1 < n_tiles) {
                     const int nt = it + C::kNBuf - 1;
                     issue_tile<C>(p.cache, lds_slots + nt * kTile, min(kTile, n_valid - nt * kTile),
                                   ring + (nt % C::kNBuf) * C::kBufBytes, wave, lane);
                 }
                 if constexpr (kPipe) {
-                    pv_pre(vf8_pend, exact_p);
+                    pv_pre(vf8_pend, exact_p, rflag, ralpha);
                     pv_main(vf8_pend);
                 }
                 tile(ring + (it % C::kNBuf) * C::kBufBytes, min(kTile, n_valid - it * kTile), exact_p);
             }
             if constexpr (kPipe) {
                 __syncthreads();     // P^T of the last tile is visible
-                pv_pre(vf8_pend, exact_p);
+                int rflag[NHH];
+                float ralpha[NHH];
+#pragma unroll
+                for (int hb = 0; hb < NHH; ++hb) {
+                    rflag[hb] = resc_flag[hb];
+                    ralpha[hb] = alpha_lds[hb * 16 + n16];
+                }
+                pv_pre(vf8_pend, exact_p, rflag, ralpha);
                 pv_main(vf8_pend);
             }
             __syncthreads();     // ring, exchanges and slot list are free for the next round
