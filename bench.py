@@ -3,8 +3,12 @@
 Workload (the headline decode batch): 64 decode tokens, one per request, contexts
 U{4096..8192}, h_q = 64, top-k = 2048 distinct positions per token, fp8_ds_mla
 paged cache (656-byte rows, block size 64, shuffled block table), bf16 q. One
-step = one smla_decode_fp8 call over the whole batch (index conversion, gather +
-dequant, QK^T, softmax, PV, split merge), inputs already resident in HBM.
+step = the whole hot path over the batch (index conversion, gather + dequant,
+QK^T, softmax, PV, split merge), inputs already resident in HBM: one
+smla_decode_fp8 call (the attention kernel, then the merge kernel). A second
+pass issues the same two kernels as smla_decode_fp8 with partials_only followed
+by smla_merge_partials, with a HIP event between them, to time each kernel; the
+roofline object is the attention kernel's.
 
 Cold-cache timing: before every timed step a 1 GiB buffer is read (outside the
 timed events) so neither L2 nor the 256 MB MALL holds the 95 MB working set; a
@@ -154,8 +158,10 @@ def main():
     lse = torch.empty((w.num_tokens, w.h_q), dtype=torch.float32, device=dev)
     ws_bytes = smla.smla_workspace_size(w.num_tokens, w.h_q, w.topk)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    ws_parts = torch.empty(max(smla.smla_workspace_size(w.num_tokens, w.h_q, w.topk, partials_only=True), 1),
+                           dtype=torch.uint8, device=dev)
     props = torch.cuda.get_device_properties(dev)
-    splits, _ = smla.smla_plan(w.num_tokens, w.h_q, w.topk, props.multi_processor_count)
+    splits, _ = smla.smla_plan(w.num_tokens, w.h_q, w.topk, props.multi_processor_count, partials_only=True)
     flush = torch.ones(1 << 28, dtype=torch.int32, device=dev)     # 1 GiB, read to evict caches
     sink = torch.empty((), dtype=torch.int32, device=dev)
 
@@ -163,13 +169,22 @@ def main():
         smla.smla_decode_fp8(q, cache, bt, req, idx, w.sm_scale, out=out, lse=lse, workspace=ws,
                              stream=stream)
 
+    def attention():
+        smla.smla_decode_fp8(q, cache, bt, req, idx, w.sm_scale, workspace=ws_parts, stream=stream,
+                             partials_only=True)
+
+    def merge():
+        smla.smla_merge_partials(ws_parts, w.num_tokens, w.h_q, splits, out=out, lse=lse, stream=stream)
+
     for i in range(args.warmup):
         torch.amax(flush, 0, out=sink)
         step()
     torch.cuda.synchronize()
 
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    def events(n):
+        return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+
+    starts, ends = events(args.steps), events(args.steps)
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
     for i in range(args.steps):
@@ -180,6 +195,19 @@ def main():
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
     cold_ms = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
+
+    # per-kernel times: the same kernels issued as two calls with an event between
+    a0, a1, m1 = events(args.steps), events(args.steps), events(args.steps)
+    for i in range(args.steps):
+        torch.amax(flush, 0, out=sink)
+        a0[i].record(stream)
+        attention()
+        a1[i].record(stream)
+        merge()
+        m1[i].record(stream)
+    torch.cuda.synchronize()
+    attn_ms = np.array([s.elapsed_time(e) for s, e in zip(a0, a1)])
+    merge_ms = np.array([s.elapsed_time(e) for s, e in zip(a1, m1)])
 
     # warm cache: back-to-back calls, working set resident in MALL
     w0 = torch.cuda.Event(enable_timing=True)
@@ -200,7 +228,11 @@ def main():
     ai = flops / bytes_alg
     roof_tflops = min(BF16_PEAK_TFLOPS, HBM_PEAK_GBS * 1e9 * ai / 1e12)
     roof_tok_s = w.num_tokens * roof_tflops * 1e12 / flops
-    achieved_gbs = bytes_alg / (ms * 1e-3) / 1e9
+    # the dominant kernel: attention reads every input byte of the method; the
+    # merge kernel writes the output (and re-reads the split partials)
+    attn_bytes = bytes_alg - by["out"] - by["lse"]
+    attn_avg_ms = float(attn_ms.mean())
+    achieved_gbs = attn_bytes / (attn_avg_ms * 1e-3) / 1e9
     traffic = traffic_from_profile()
 
     rec = {
@@ -228,7 +260,11 @@ def main():
                              "arith_intensity_flop_per_byte": ai, "tflops": roof_tflops,
                              "query_tokens_per_s": roof_tok_s},
         "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved_gbs / HBM_PEAK_GBS, "traffic": traffic},
+                     "frac": achieved_gbs / HBM_PEAK_GBS, "traffic": traffic,
+                     "kernel": "attn_kernel", "algorithmic_bytes_per_launch": attn_bytes,
+                     "avg_launch_ms": attn_avg_ms},
+        "kernels_ms_cold": {"attn_kernel": attn_avg_ms, "merge_kernel": float(merge_ms.mean())},
+        "whole_step_hbm_frac": bytes_alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "algorithmic_bytes_per_step": bytes_alg,
         "algorithmic_bytes_breakdown": by,
         "flops_per_step": flops,
@@ -238,7 +274,8 @@ def main():
         "ms_per_step_p90": float(np.percentile(cold_ms, 90)),
         "warm_cache": {"ms_per_step": warm_ms, "query_tokens_per_s": w.num_tokens / (warm_ms * 1e-3)},
         "timed_region_wall_s_incl_flushes": t_wall,
-        "timing": "HIP events around each smla_decode_fp8 call (all its kernels), on its stream",
+        "timing": ("HIP events on the library's stream around each step (attention kernel, then merge "
+                   "kernel) and between the two kernels"),
         "kernel_source_hash": kernel_source_hash(),
         "device": props.name,
     }

@@ -65,6 +65,15 @@ typedef enum smla_status {
     SMLA_ERR_ARG = 6        /* invalid scalar argument or option                 */
 } smla_status;
 
+/* Bits of smla_options.flags. */
+#define SMLA_FLAG_PARTIALS_ONLY 0x1u
+    /* The call stops before the merge: it writes every top-k part's result into
+       the workspace (layout at smla_merge_partials) and neither out nor lse.
+       The workspace is required even when the list is not split (one part).
+       smla_merge_partials then finishes the result; it also merges parts that
+       were computed by separate calls, e.g. on different devices. */
+#define SMLA_FLAG_ALL SMLA_FLAG_PARTIALS_ONLY
+
 /* Tuning options (host struct, may be NULL for defaults). */
 typedef struct smla_options {
     int32_t num_splits;     /* 0 = automatic; > 0 = split every token's top-k
@@ -72,7 +81,7 @@ typedef struct smla_options {
                                32), each part computed by its own workgroups and
                                merged by log-sum-exp weights in a second kernel
                                on the same stream. */
-    uint32_t flags;         /* reserved, must be 0 (SMLA_ERR_ARG otherwise) */
+    uint32_t flags;         /* SMLA_FLAG_* bits; any other bit is SMLA_ERR_ARG */
     int32_t reserved[6];    /* must be zero */
 } smla_options;
 
@@ -97,6 +106,28 @@ smla_status smla_plan(int32_t num_tokens, int32_t h_q, int32_t topk, int32_t num
  * the device cannot be queried. */
 smla_status smla_workspace_size(int32_t num_tokens, int32_t h_q, int32_t topk,
                                 const smla_options *options, size_t *workspace_bytes);
+
+/* Log-sum-exp merge of per-part results into the final output
+ * [flashmla_sparse.py page, FlashMLASparseImpl.forward: the sparse kernels return
+ * the output and its log-sum-exp; parts of one list combine by the usual
+ * log-sum-exp weights].
+ *
+ *   partials   device buffer, 256-B aligned, in this layout (F = num_parts):
+ *                byte 0:               fp32 lse[num_tokens][F][h_q], natural log
+ *                byte align256(T*F*h_q*4): fp32 o[num_tokens][F][h_q][512], each
+ *                                      part's output normalised by its own sum
+ *              (what an attention call with SMLA_FLAG_PARTIALS_ONLY writes into its
+ *              workspace, F = its number of splits from smla_plan). A part with
+ *              lse = -inf contributes nothing.
+ *   partials_bytes  capacity of `partials` (SMLA_ERR_WORKSPACE if too small)
+ *   out        bf16 [num_tokens, h_q, 512], 16-B aligned, every element written
+ *   lse        fp32 [num_tokens, h_q] merged natural-log lse; may be NULL
+ * h_q as for the attention calls; 1 <= num_parts <= 4096; num_tokens == 0 is a
+ * no-op. Parts are added in index order, so results do not depend on timing.
+ */
+smla_status smla_merge_partials(const void *partials, size_t partials_bytes, int32_t num_tokens,
+                                int32_t h_q, int32_t num_parts, void *out, float *lse,
+                                hipStream_t stream);
 
 /* Logical-to-physical index conversion alone [flashmla_sparse.py page,
  * triton_convert_req_index_to_global_index and docstring]:
@@ -124,6 +155,7 @@ smla_status smla_convert_indices(const int32_t *req_id_per_token, const int32_t 
  *   sm_scale          softmax scale, finite and > 0 (e.g. 1/sqrt(576))
  *   h_q               16, 32, 64 or 128
  *   out               bf16 [num_tokens, h_q, 512], 16-B aligned, every element written
+ *                     (may be NULL with SMLA_FLAG_PARTIALS_ONLY, which does not write it)
  *   lse               fp32 [num_tokens, h_q] natural-log LSE of the scaled logits; may be NULL
  *   phys_indices_out  int32 [num_tokens, topk] converted slots (-1 = invalid), bit-identical
  *                     to smla_convert_indices; may be NULL

@@ -15,7 +15,9 @@ namespace smla {
 
 static size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
-Plan make_plan(int num_tokens, int h_q, int topk, int num_cus, int forced_splits)
+size_t partials_o_offset(size_t rows) { return align_up(rows * sizeof(float), 256); }
+
+Plan make_plan(int num_tokens, int h_q, int topk, int num_cus, int forced_splits, bool partials)
 {
     Plan p{};
     p.head_blocks = h_q >= kHeadsPerGroup ? h_q / kHeadsPerGroup : 1;
@@ -43,10 +45,10 @@ Plan make_plan(int num_tokens, int h_q, int topk, int num_cus, int forced_splits
     }
     p.split_len = (topk + splits - 1) / splits;
     p.num_splits = (topk + p.split_len - 1) / p.split_len;
-    if (p.num_splits > 1) {
+    if (p.num_splits > 1 || partials) {
         const size_t rows = (size_t)num_tokens * p.num_splits * h_q;
         p.part_lse_off = 0;
-        p.part_o_off = align_up(p.part_lse_off + rows * sizeof(float), 256);
+        p.part_o_off = partials_o_offset(rows);
         p.workspace = align_up(p.part_o_off + rows * kDv * sizeof(float), 256);
     }
     return p;
@@ -60,7 +62,7 @@ smla_status check_options(const smla_options *o)
 {
     if (o == nullptr)
         return SMLA_OK;
-    if (o->num_splits < 0 || o->flags != 0)
+    if (o->num_splits < 0 || (o->flags & ~(uint32_t)SMLA_FLAG_ALL) != 0)
         return SMLA_ERR_ARG;
     for (int i = 0; i < 6; ++i)
         if (o->reserved[i] != 0)
@@ -127,7 +129,8 @@ smla_status attention_entry(CacheFormat fmt, const void *q, const void *kv_cache
         return st;
     if (num_tokens == 0)
         return SMLA_OK;
-    if (!q || !kv_cache || !block_table || !req_id_per_token || !topk_indices || !out)
+    const bool partials_only = options && (options->flags & SMLA_FLAG_PARTIALS_ONLY);
+    if (!q || !kv_cache || !block_table || !req_id_per_token || !topk_indices || (!out && !partials_only))
         return SMLA_ERR_NULL;
     if (!aligned(q, 16) || !aligned(kv_cache, 16) || !aligned(out, 16))
         return SMLA_ERR_ALIGN;
@@ -139,7 +142,7 @@ smla_status attention_entry(CacheFormat fmt, const void *q, const void *kv_cache
     int cus = 0;
     if ((st = device_cus(&cus)) != SMLA_OK)
         return st;
-    const Plan plan = make_plan(num_tokens, h_q, topk, cus, forced);
+    const Plan plan = make_plan(num_tokens, h_q, topk, cus, forced, partials_only);
     if (plan.workspace > 0 && (workspace == nullptr || workspace_bytes < plan.workspace))
         return SMLA_ERR_WORKSPACE;
 
@@ -160,7 +163,7 @@ smla_status attention_entry(CacheFormat fmt, const void *q, const void *kv_cache
     a.num_reqs = num_reqs;
     a.max_blocks = max_blocks_per_req;
     a.num_blocks = num_blocks;
-    return launch_attention(fmt, a, plan, stream) == hipSuccess
+    return launch_attention(fmt, a, plan, partials_only, stream) == hipSuccess
                ? SMLA_OK
                : SMLA_ERR_HIP;
 }
@@ -203,7 +206,8 @@ smla_status smla_plan(int32_t num_tokens, int32_t h_q, int32_t topk, int32_t num
         *workspace_bytes = 0;
         return SMLA_OK;
     }
-    const smla::Plan p = smla::make_plan(num_tokens, h_q, topk, num_cus, options ? options->num_splits : 0);
+    const smla::Plan p = smla::make_plan(num_tokens, h_q, topk, num_cus, options ? options->num_splits : 0,
+                                         options && (options->flags & SMLA_FLAG_PARTIALS_ONLY));
     *num_splits = p.num_splits;
     *workspace_bytes = p.workspace;
     return SMLA_OK;
@@ -227,8 +231,35 @@ smla_status smla_workspace_size(int32_t num_tokens, int32_t h_q, int32_t topk,
     if ((st = smla::device_cus(&cus)) != SMLA_OK)
         return st;
     *workspace_bytes =
-        smla::make_plan(num_tokens, h_q, topk, cus, options ? options->num_splits : 0).workspace;
+        smla::make_plan(num_tokens, h_q, topk, cus, options ? options->num_splits : 0,
+                        options && (options->flags & SMLA_FLAG_PARTIALS_ONLY))
+            .workspace;
     return SMLA_OK;
+}
+
+smla_status smla_merge_partials(const void *partials, size_t partials_bytes, int32_t num_tokens,
+                                int32_t h_q, int32_t num_parts, void *out, float *lse,
+                                hipStream_t stream)
+{
+    if (h_q != 16 && h_q != 32 && h_q != 64 && h_q != 128)
+        return SMLA_ERR_SHAPE;
+    if (num_tokens < 0 || num_parts < 1 || num_parts > 4096)
+        return SMLA_ERR_SHAPE;
+    if (num_tokens == 0)
+        return SMLA_OK;
+    if (!partials || !out)
+        return SMLA_ERR_NULL;
+    if (!smla::aligned(partials, 256) || !smla::aligned(out, 16) || !smla::aligned(lse, 4))
+        return SMLA_ERR_ALIGN;
+    const size_t rows = (size_t)num_tokens * num_parts * h_q;
+    const size_t o_off = smla::partials_o_offset(rows);
+    if (partials_bytes < o_off + rows * smla::kDv * sizeof(float))
+        return SMLA_ERR_WORKSPACE;
+    const float *base = (const float *)partials;
+    return smla::launch_merge(base, (const float *)((const char *)partials + o_off), out, lse, num_tokens,
+                              h_q, num_parts, stream) == hipSuccess
+               ? SMLA_OK
+               : SMLA_ERR_HIP;
 }
 
 smla_status smla_convert_indices(const int32_t *req_id_per_token, const int32_t *block_table,

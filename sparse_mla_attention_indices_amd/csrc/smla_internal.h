@@ -36,8 +36,12 @@ struct Plan {
     size_t part_o_off;       // and [T][S][H][512] fp32 partial outputs
 };
 
-// Host arithmetic only.
-Plan make_plan(int num_tokens, int h_q, int topk, int num_cus, int forced_splits);
+// Host arithmetic only. partials: the call writes per-part results (workspace
+// needed even for one part).
+Plan make_plan(int num_tokens, int h_q, int topk, int num_cus, int forced_splits, bool partials);
+
+// Byte offset of the partial outputs in a partials buffer of T x F x H entries.
+size_t partials_o_offset(size_t rows);
 
 struct AttnArgs {
     const void *q;
@@ -59,8 +63,13 @@ hipError_t launch_convert(const int32_t *req_id, const int32_t *block_table, con
                           int32_t *out, int num_tokens, int topk_len, int num_reqs,
                           int max_blocks, int64_t num_blocks, hipStream_t stream);
 
-// The attention kernel and, when the plan splits the top-k lists, the merge
-// kernel after it on the same stream.
-hipError_t launch_attention(CacheFormat fmt, const AttnArgs &a, const Plan &p, hipStream_t stream);
+// The attention kernel and, when the plan splits the top-k lists (and
+// partials_only is false), the merge kernel after it on the same stream.
+hipError_t launch_attention(CacheFormat fmt, const AttnArgs &a, const Plan &p, bool partials_only,
+                            hipStream_t stream);
+
+// merge_kernel alone over a partials buffer of T x S x H entries.
+hipError_t launch_merge(const float *part_lse, const float *part_o, void *out, float *lse, int T,
+                        int H, int S, hipStream_t stream);
 
 }  // namespace smla

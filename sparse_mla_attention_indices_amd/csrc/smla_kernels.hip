@@ -1,6 +1,6 @@
 // smla_kernels.hip -- CDNA4 (gfx950) kernels for sparse MLA forward over top-k
-// indices: index conversion, and the fused gather -> QK^T -> online softmax ->
-// PV attention kernel with an in-kernel log-sum-exp merge of top-k splits.
+// indices: index conversion, the fused gather -> QK^T -> online softmax -> PV
+// attention kernel, and the log-sum-exp merge of top-k splits.
 //
 // What is computed follows the vLLM page "vllm/v1/attention/backends/mla/
 // flashmla_sparse.py" (FLASHMLA_SPARSE backend): the index conversion of
@@ -14,19 +14,19 @@
 //    the token's top-k list. Every wave owns 16 heads and one half of the 576
 //    columns ("dh"), so a 64-head workgroup has eight waves, two per SIMD, and
 //    each wave stays within 256 registers.
-//  * Prologue: the workgroup converts its part of the top-k list to cache
-//    slots (one round trip for the indices, one for the block table) and
-//    compacts the valid ones into LDS: runs of -1 cost nothing, only the last
-//    tile is ragged.
+//  * Prologue: the indices and q are requested together, the block-table
+//    lookups as soon as the indices arrive, and q is prepared while those are in
+//    flight. The valid slots are compacted into LDS: runs of -1 cost nothing,
+//    only the last tile is ragged.
 //  * Gather: global_load_lds_dwordx4 copies the cache rows of a 32-row tile,
-//    as stored (fp8_ds_mla 656 B or bf16 1152 B), straight into one of a ring
-//    of LDS buffers; the next tiles are in flight while one is used.
-//  * QK^T runs transposed, S^T = K q^T, on v_mfma_f32_16x16x32_bf16 with q in
-//    registers. K fragments are read from the raw tile (ds_read_b64 of fp8
-//    bytes, converted to bf16 exactly in registers: every e4m3 value is a bf16
-//    value; or ds_read_b128 of bf16). fp8 partial sums of each 128-column group
-//    are multiplied by that group's row scales in fp32. The two column halves
-//    add their partial S^T through LDS.
+//    as stored (fp8_ds_mla 656 B or bf16 1152 B), one row per wave instruction,
+//    straight into one of a ring of LDS buffers; the next tiles are in flight
+//    while one is used.
+//  * QK^T runs transposed, S^T = K q^T, with q in registers. fp8: the raw e4m3
+//    K bytes feed v_mfma_scale_f32_16x16x128_f8f6f4 against q written exactly as
+//    hi + lo e4m3 terms; each 128-column group's partial sum is multiplied by
+//    that group's row scales in fp32. bf16: v_mfma_f32_16x16x32_bf16. The two
+//    column halves add their partial S^T through LDS.
 //  * Softmax: the S^T accumulator layout gives a lane one head and four rows
 //    per block, and the weights are already in the B-operand layout of
 //    O^T += V^T P^T. The running max moves (and O is rescaled) only when a tile
@@ -36,16 +36,12 @@
 //    transpose loads (ds_read_b64_tr_b8 for fp8, ds_read_b64_tr_b16 for bf16).
 //    For fp8 the weights of each 128-wide output group carry that group's row
 //    scales, so dequantisation adds no rounding anywhere. A short list (few
-//    valid rows, so large weights) feeds P as two bf16 terms, hi + lo.
-//  * Splits of one token are given workgroup ids with the same value mod 8 and
-//    so normally run on one XCD, which has one L2. Each split publishes an fp32
-//    partial with plain stores, then one 64-bit atomic add counts its arrival
-//    both in total and for its XCD. The last arrival checks that every split
-//    ran on its own XCD, then reads the other partials through that shared L2
-//    (its own is still in registers) and merges them by log-sum-exp weights; no
-//    cache write-back is needed. If the check fails it recomputes the whole
-//    token itself, so results never depend on where the hardware placed a
-//    workgroup. It leaves the arrival word at zero again.
+//    valid rows, so large weights) feeds P as two bf16 terms, hi + lo. With
+//    fp8 and several head blocks, PV of one tile runs in the same phase as QK^T
+//    of the next.
+//  * Output: one split writes the bf16 rows and lse; a top-k split writes its
+//    fp32 partial (O / l) and lse, and merge_kernel, launched after it on the
+//    same stream, combines the parts in index order.
 
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -159,6 +155,7 @@ struct KParams {
     int T, H, K, R, MB;
     int64_t NB;
     int S, split_len, HB;
+    int partials;         // write fp32 partials (O / l) and lse instead of the bf16 output
 };
 
 __device__ __forceinline__ int convert_slot(int req, int idx, const int32_t *__restrict__ bt,
@@ -927,7 +924,7 @@ void attn_kernel(const KParams p)
     //      fp32 partial O / l and its lse, head-major, for merge_kernel.
     __syncthreads();        // every wave is done with the exchange areas
     const int n16_late = late(n16);
-    if (p.S == 1) {
+    if (!p.partials) {
         uint16_t *stage = (uint16_t *)smem;
 #pragma unroll
         for (int k = 0; k < 16; ++k) {
@@ -1084,7 +1081,26 @@ hipError_t launch_convert(const int32_t *req_id, const int32_t *block_table, con
     return hipGetLastError();
 }
 
-hipError_t launch_attention(CacheFormat fmt, const AttnArgs &a, const Plan &pl, hipStream_t stream)
+hipError_t launch_merge(const float *part_lse, const float *part_o, void *out, float *lse, int T,
+                        int H, int S, hipStream_t stream)
+{
+    const int64_t threads = (int64_t)T * H * (kDv / 4);
+    const dim3 grid((unsigned)((threads + 255) / 256));
+    uint16_t *o = (uint16_t *)out;
+    switch (S) {
+    case 2: hipLaunchKernelGGL(merge_kernel<2>, grid, dim3(256), 0, stream, part_o, part_lse, o, lse, T, H, S); break;
+    case 3: hipLaunchKernelGGL(merge_kernel<3>, grid, dim3(256), 0, stream, part_o, part_lse, o, lse, T, H, S); break;
+    case 4: hipLaunchKernelGGL(merge_kernel<4>, grid, dim3(256), 0, stream, part_o, part_lse, o, lse, T, H, S); break;
+    case 5: hipLaunchKernelGGL(merge_kernel<5>, grid, dim3(256), 0, stream, part_o, part_lse, o, lse, T, H, S); break;
+    case 6: hipLaunchKernelGGL(merge_kernel<6>, grid, dim3(256), 0, stream, part_o, part_lse, o, lse, T, H, S); break;
+    case 8: hipLaunchKernelGGL(merge_kernel<8>, grid, dim3(256), 0, stream, part_o, part_lse, o, lse, T, H, S); break;
+    default: hipLaunchKernelGGL(merge_kernel<0>, grid, dim3(256), 0, stream, part_o, part_lse, o, lse, T, H, S); break;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_attention(CacheFormat fmt, const AttnArgs &a, const Plan &pl, bool partials_only,
+                            hipStream_t stream)
 {
     KParams p;
     p.q = (const uint16_t *)a.q;
@@ -1095,7 +1111,7 @@ hipError_t launch_attention(CacheFormat fmt, const AttnArgs &a, const Plan &pl, 
     p.out = (uint16_t *)a.out;
     p.lse = a.lse;
     p.phys_out = a.phys_out;
-    const bool split = pl.num_splits > 1;
+    const bool split = pl.num_splits > 1 || partials_only;
     p.part_o = split ? (float *)((char *)a.workspace + pl.part_o_off) : nullptr;
     p.part_lse = split ? (float *)((char *)a.workspace + pl.part_lse_off) : nullptr;
     p.log2e_scale = a.sm_scale * 1.4426950408889634f;
@@ -1108,22 +1124,11 @@ hipError_t launch_attention(CacheFormat fmt, const AttnArgs &a, const Plan &pl, 
     p.S = pl.num_splits;
     p.split_len = pl.split_len;
     p.HB = pl.head_blocks;
+    p.partials = split ? 1 : 0;
     const hipError_t err = fmt == kCacheFp8 ? launch_fmt<kCacheFp8>(p, stream) : launch_fmt<kCacheBf16>(p, stream);
-    if (err != hipSuccess || !split)
+    if (err != hipSuccess || !split || partials_only)
         return err;
-    const int64_t threads = (int64_t)p.T * p.H * (kDv / 4);
-    const dim3 grid((unsigned)((threads + 255) / 256));
-    const float *po = p.part_o, *plse = p.part_lse;
-    switch (p.S) {
-    case 2: hipLaunchKernelGGL(merge_kernel<2>, grid, dim3(256), 0, stream, po, plse, p.out, p.lse, p.T, p.H, p.S); break;
-    case 3: hipLaunchKernelGGL(merge_kernel<3>, grid, dim3(256), 0, stream, po, plse, p.out, p.lse, p.T, p.H, p.S); break;
-    case 4: hipLaunchKernelGGL(merge_kernel<4>, grid, dim3(256), 0, stream, po, plse, p.out, p.lse, p.T, p.H, p.S); break;
-    case 5: hipLaunchKernelGGL(merge_kernel<5>, grid, dim3(256), 0, stream, po, plse, p.out, p.lse, p.T, p.H, p.S); break;
-    case 6: hipLaunchKernelGGL(merge_kernel<6>, grid, dim3(256), 0, stream, po, plse, p.out, p.lse, p.T, p.H, p.S); break;
-    case 8: hipLaunchKernelGGL(merge_kernel<8>, grid, dim3(256), 0, stream, po, plse, p.out, p.lse, p.T, p.H, p.S); break;
-    default: hipLaunchKernelGGL(merge_kernel<0>, grid, dim3(256), 0, stream, po, plse, p.out, p.lse, p.T, p.H, p.S); break;
-    }
-    return hipGetLastError();
+    return launch_merge(p.part_lse, p.part_o, p.out, p.lse, p.T, p.H, p.S, stream);
 }
 
 }  // namespace smla

@@ -24,7 +24,8 @@ SMLA_OK = 0
 STATUS_NAMES = {0: "SMLA_OK", 1: "SMLA_ERR_NULL", 2: "SMLA_ERR_SHAPE", 3: "SMLA_ERR_ALIGN",
                 4: "SMLA_ERR_WORKSPACE", 5: "SMLA_ERR_HIP", 6: "SMLA_ERR_ARG"}
 EXPORTS = ("smla_status_string", "smla_abi_version", "smla_plan", "smla_workspace_size",
-           "smla_convert_indices", "smla_prefill_bf16", "smla_decode_fp8")
+           "smla_merge_partials", "smla_convert_indices", "smla_prefill_bf16", "smla_decode_fp8")
+FLAG_PARTIALS_ONLY = 0x1
 
 
 class SmlaError(RuntimeError):
@@ -60,6 +61,8 @@ def library() -> ctypes.CDLL:
     lib.smla_plan.argtypes = [i32, i32, i32, i32, vp, ctypes.POINTER(i32), ctypes.POINTER(sz)]
     lib.smla_workspace_size.restype = ctypes.c_int
     lib.smla_workspace_size.argtypes = [i32, i32, i32, vp, ctypes.POINTER(sz)]
+    lib.smla_merge_partials.restype = ctypes.c_int
+    lib.smla_merge_partials.argtypes = [vp, sz, i32, i32, i32, vp, vp, vp]
     lib.smla_convert_indices.restype = ctypes.c_int
     lib.smla_convert_indices.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i64, vp]
     attn = [vp, vp, vp, vp, vp, fl, i32, i32, i32, i32, i32, i64, vp, vp, vp, vp, sz, vp, vp]
@@ -107,20 +110,48 @@ def smla_abi_version() -> int:
     return int(library().smla_abi_version())
 
 
-def smla_plan(num_tokens: int, h_q: int, topk: int, num_cus: int, num_splits: int = 0):
+def smla_plan(num_tokens: int, h_q: int, topk: int, num_cus: int, num_splits: int = 0,
+              partials_only: bool = False):
     """Host-only split plan: returns (num_splits, workspace_bytes)."""
     s = ctypes.c_int32()
     b = ctypes.c_size_t()
-    _check(library().smla_plan(num_tokens, h_q, topk, num_cus, _options(num_splits),
+    flags = FLAG_PARTIALS_ONLY if partials_only else 0
+    _check(library().smla_plan(num_tokens, h_q, topk, num_cus, _options(num_splits, flags),
                                ctypes.byref(s), ctypes.byref(b)), "smla_plan")
     return s.value, b.value
 
 
-def smla_workspace_size(num_tokens: int, h_q: int, topk: int, num_splits: int = 0) -> int:
+def smla_workspace_size(num_tokens: int, h_q: int, topk: int, num_splits: int = 0,
+                        partials_only: bool = False) -> int:
     b = ctypes.c_size_t()
-    _check(library().smla_workspace_size(num_tokens, h_q, topk, _options(num_splits), ctypes.byref(b)),
-           "smla_workspace_size")
+    flags = FLAG_PARTIALS_ONLY if partials_only else 0
+    _check(library().smla_workspace_size(num_tokens, h_q, topk, _options(num_splits, flags),
+                                         ctypes.byref(b)), "smla_workspace_size")
     return b.value
+
+
+def partials_layout(num_tokens: int, h_q: int, num_parts: int):
+    """Byte offsets and sizes of a partials buffer: (o_offset, total_bytes). lse is
+    fp32 [T][F][H] at offset 0, o is fp32 [T][F][H][512] at o_offset."""
+    rows = num_tokens * num_parts * h_q
+    o_off = -(-rows * 4 // 256) * 256
+    return o_off, o_off + rows * 512 * 4
+
+
+def smla_merge_partials(partials: torch.Tensor, num_tokens: int, h_q: int, num_parts: int,
+                        out=None, lse=None, stream=None, want_lse=True):
+    """Log-sum-exp merge of a partials buffer (the workspace of a call made with
+    partials_only=True, or parts assembled by the caller). Returns (out, lse)."""
+    if out is None:
+        out = torch.empty((num_tokens, h_q, 512), dtype=torch.bfloat16, device=partials.device)
+    if lse is None and want_lse:
+        lse = torch.empty((num_tokens, h_q), dtype=torch.float32, device=partials.device)
+    _check(library().smla_merge_partials(_dev(partials, "partials"),
+                                         partials.numel() * partials.element_size(), num_tokens, h_q,
+                                         num_parts, _dev(out, "out", torch.bfloat16, 3),
+                                         _dev(lse, "lse", torch.float32, 2), _stream(stream)),
+           "smla_merge_partials")
+    return out, lse
 
 
 # Workspaces the binding allocates itself, one per (device, stream), grown on
@@ -153,15 +184,21 @@ def smla_convert_indices(req_id_per_token, block_table, topk_indices, num_blocks
 
 
 def _attention(name: str, q, kv_cache, block_table, req_id_per_token, topk_indices, sm_scale,
-               out, lse, phys_indices_out, workspace, num_splits, stream, want_lse):
+               out, lse, phys_indices_out, workspace, num_splits, stream, want_lse, partials_only=False):
     T, H, D = q.shape
     if D != 576:
         raise ValueError("q must be [num_tokens, h_q, 576]")
     K = topk_indices.shape[1]
-    if out is None:
-        out = torch.empty((T, H, 512), dtype=torch.bfloat16, device=q.device)
-    if lse is None and want_lse:
-        lse = torch.empty((T, H), dtype=torch.float32, device=q.device)
+    flags = FLAG_PARTIALS_ONLY if partials_only else 0
+    if partials_only:
+        if workspace is None:
+            raise ValueError("partials_only needs a workspace (the partial results go there)")
+        out = lse = None
+    else:
+        if out is None:
+            out = torch.empty((T, H, 512), dtype=torch.bfloat16, device=q.device)
+        if lse is None and want_lse:
+            lse = torch.empty((T, H), dtype=torch.float32, device=q.device)
     if workspace is None:
         need = smla_workspace_size(T, H, K, num_splits)
         if need > 0:
@@ -176,30 +213,34 @@ def _attention(name: str, q, kv_cache, block_table, req_id_per_token, topk_indic
               block_table.shape[0], block_table.shape[1], kv_cache.shape[0],
               _dev(out, "out", torch.bfloat16, 3), _dev(lse, "lse", torch.float32, 2),
               _dev(phys_indices_out, "phys_indices_out", torch.int32, 2),
-              ws_ptr, ws_bytes, _options(num_splits), _stream(stream)), name)
+              ws_ptr, ws_bytes, _options(num_splits, flags), _stream(stream)), name)
     return out, lse
 
 
 def smla_prefill_bf16(q, kv_cache, block_table, req_id_per_token, topk_indices, sm_scale,
                       out=None, lse=None, phys_indices_out=None, workspace=None, num_splits=0,
-                      stream=None, want_lse=True):
+                      stream=None, want_lse=True, partials_only=False):
     """Sparse MLA forward over a bf16 cache [num_blocks, 64, 576]. Returns (out, lse).
 
     workspace: uint8 device tensor of at least smla_workspace_size bytes (contents
-    need not be initialised), or None for one the binding keeps per (device, stream)."""
+    need not be initialised), or None for one the binding keeps per (device, stream).
+    partials_only: write the per-part results into `workspace` (required) for
+    smla_merge_partials and return (None, None)."""
     if kv_cache.dtype != torch.bfloat16 or kv_cache.shape[1:] != (64, 576):
         raise ValueError("kv_cache must be bf16 [num_blocks, 64, 576]")
     return _attention("smla_prefill_bf16", q, kv_cache, block_table, req_id_per_token, topk_indices,
-                      sm_scale, out, lse, phys_indices_out, workspace, num_splits, stream, want_lse)
+                      sm_scale, out, lse, phys_indices_out, workspace, num_splits, stream, want_lse,
+                      partials_only)
 
 
 def smla_decode_fp8(q, kv_cache, block_table, req_id_per_token, topk_indices, sm_scale,
                     out=None, lse=None, phys_indices_out=None, workspace=None, num_splits=0,
-                    stream=None, want_lse=True):
+                    stream=None, want_lse=True, partials_only=False):
     """Sparse MLA forward over an fp8_ds_mla cache uint8 [num_blocks, 64, 656]. Returns (out, lse).
 
     Other arguments as for smla_prefill_bf16."""
     if kv_cache.dtype != torch.uint8 or kv_cache.shape[1:] != (64, 656):
         raise ValueError("kv_cache must be uint8 [num_blocks, 64, 656]")
     return _attention("smla_decode_fp8", q, kv_cache, block_table, req_id_per_token, topk_indices,
-                      sm_scale, out, lse, phys_indices_out, workspace, num_splits, stream, want_lse)
+                      sm_scale, out, lse, phys_indices_out, workspace, num_splits, stream, want_lse,
+                      partials_only)

@@ -17,6 +17,7 @@ HEADER = os.path.join(ROOT, "include", "smla.h")
 A16 = 0x10000          # fake, 256-byte aligned addresses: never dereferenced
 A16B = 0x20000
 MIS = 0x10002          # misaligned
+A256 = 0x30000
 
 
 def declared_functions():
@@ -101,10 +102,10 @@ def test_plan_rejects_bad_options(lib):
     o.num_splits = -2
     assert lib.smla_plan(8, 16, 64, 256, ctypes.byref(o), ctypes.byref(s), ctypes.byref(b)) == 6
     o = smla.SmlaOptions()
-    for bit in (0x1, 0x2, 0x4):              # flags are reserved: any bit is rejected
+    for bit in (0x2, 0x4, 0x80000000):       # unknown flag bits
         o.flags = bit
         assert lib.smla_plan(8, 16, 64, 256, ctypes.byref(o), ctypes.byref(s), ctypes.byref(b)) == 6
-    o.flags = 0
+    o.flags = smla.FLAG_PARTIALS_ONLY
     assert lib.smla_plan(8, 16, 64, 256, ctypes.byref(o), ctypes.byref(s), ctypes.byref(b)) == 0
     assert lib.smla_plan(8, 16, 64, 256, None, None, ctypes.byref(b)) == 1
 
@@ -175,3 +176,36 @@ def test_convert_rejects(lib, kw, code):
 
 def test_convert_zero_tokens_is_a_noop(lib):
     assert lib.smla_convert_indices(None, None, None, None, 0, 7, 3, 3, 6, None) == 0
+
+
+def test_plan_partials_only_needs_a_workspace_even_unsplit(lib):
+    # 512 tokens x 16 heads fill the chip: one part, no workspace ...
+    assert smla.smla_plan(512, 16, 2048, 256) == (1, 0)
+    # ... but a partials-only call writes its one part there
+    s, ws = smla.smla_plan(512, 16, 2048, 256, partials_only=True)
+    o_off, total = smla.partials_layout(512, 16, 1)
+    assert s == 1 and ws == total and o_off == 512 * 16 * 4
+
+
+def test_partials_layout_matches_the_plan(lib):
+    for T, H, K, S in ((64, 64, 2048, 4), (5, 16, 300, 3), (1000, 128, 64, 2)):
+        s, ws = smla.smla_plan(T, H, K, 256, num_splits=S)
+        assert s == S and ws == smla.partials_layout(T, H, S)[1]
+
+
+def _merge(lib, part=A256, pb=1 << 30, T=4, H=16, F=2, out=A16B, lse=A16):
+    return lib.smla_merge_partials(part, pb, T, H, F, out, lse, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(part=None), 1), (dict(out=None), 1),
+    (dict(H=48), 2), (dict(F=0), 2), (dict(F=4097), 2), (dict(T=-1), 2),
+    (dict(part=A256 + 16), 3), (dict(out=MIS), 3), (dict(lse=A16 + 2), 3),
+    (dict(pb=1024), 4),
+])
+def test_merge_rejects_before_any_hip_call(lib, kw, code):
+    assert _merge(lib, **kw) == code
+
+
+def test_merge_zero_tokens_is_a_noop(lib):
+    assert _merge(lib, part=None, out=None, T=0) == 0

@@ -192,6 +192,56 @@ def test_uninitialised_workspace(fmt):
         assert_parity(w, out, lse, label=f"garbage ws {fmt}")
 
 
+@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+def test_partials_only_then_merge_equals_the_call(fmt):
+    """A call with partials_only followed by smla_merge_partials runs the same
+    kernels as one ordinary call: the results are bit-identical, also for an
+    unsplit list (one part)."""
+    w = small(51, fmt, 64, 300, n_req=3, tok_per_req=5, ctx=(200, 900), p_invalid=0.1)
+    dw = DeviceWorkload(w)
+    fn = smla.smla_prefill_bf16 if fmt == "bf16" else smla.smla_decode_fp8
+    T, H, K = w.num_tokens, 64, 300
+    for splits in (1, 3, 0):
+        log(f"[case] partials then merge {fmt} splits={splits}")
+        ref_out, ref_lse, _ = dw.run(num_splits=splits)
+        S, need = smla.smla_plan(T, H, K, torch.cuda.get_device_properties(0).multi_processor_count,
+                                 num_splits=splits, partials_only=True)
+        ws = torch.full((need,), 0xEE, dtype=torch.uint8, device="cuda")
+        assert fn(dw.q, dw.cache, dw.bt, dw.req, dw.idx, w.sm_scale, workspace=ws, num_splits=splits,
+                  partials_only=True) == (None, None)
+        out, lse = smla.smla_merge_partials(ws, T, H, S)
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_out) and torch.equal(lse, ref_lse)
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+def test_parts_of_a_list_merged_like_context_parallel(fmt):
+    """Each token's top-k list cut in two halves, each half computed by its own
+    call (as two devices would), the two parts stacked into one partials buffer
+    and merged: the result is the attention over the whole list."""
+    w = small(53, fmt, 32, 400, n_req=4, tok_per_req=4, ctx=(300, 1500), p_invalid=0.1)
+    dw = DeviceWorkload(w)
+    fn = smla.smla_prefill_bf16 if fmt == "bf16" else smla.smla_decode_fp8
+    T, H, K = w.num_tokens, 32, 400
+    halves = ((0, 160), (160, K))          # uneven cut
+    o_off, total = smla.partials_layout(T, H, len(halves))
+    merged = torch.empty(total, dtype=torch.uint8, device="cuda")
+    lse_all = merged[:T * len(halves) * H * 4].view(torch.float32).view(T, len(halves), H)
+    o_all = merged[o_off:].view(torch.float32).view(T, len(halves), H, 512)
+    for f, (a, b) in enumerate(halves):
+        idx = dw.idx[:, a:b].contiguous()
+        s1, need = smla.smla_plan(T, H, b - a, 256, num_splits=1, partials_only=True)
+        ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+        fn(dw.q, dw.cache, dw.bt, dw.req, idx, w.sm_scale, workspace=ws, num_splits=1, partials_only=True)
+        po, _ = smla.partials_layout(T, H, 1)
+        lse_all[:, f] = ws[:T * H * 4].view(torch.float32).view(T, H)
+        o_all[:, f] = ws[po:po + T * H * 512 * 4].view(torch.float32).view(T, H, 512)
+    out, lse = smla.smla_merge_partials(merged, T, H, len(halves))
+    torch.cuda.synchronize()
+    log(f"[case] two-part merge {fmt}")
+    assert_parity(w, out, lse, label=f"two-part merge {fmt}")
+
+
 def test_zero_tokens_writes_nothing():
     w = small(3, "fp8", 16, 64)
     dw = DeviceWorkload(w)
