@@ -66,6 +66,10 @@ def _load():
     lib.smla_oracle_decode_bf16_row.restype = None
     lib.smla_oracle_decode_bf16_row.argtypes = [vp, vp]
     lib.smla_oracle_convert_one.restype = i32
+    lib.smla_oracle_e4m3fn_encode.restype = ctypes.c_uint8
+    lib.smla_oracle_e4m3fn_encode.argtypes = [ctypes.c_float]
+    lib.smla_oracle_cache_write.restype = None
+    lib.smla_oracle_cache_write.argtypes = [ctypes.c_int, vp, vp, vp, i64, vp, i64]
     lib.smla_oracle_convert_one.argtypes = [i32, i32, vp, i64, i64, i64]
     lib.smla_oracle_convert_indices.restype = None
     lib.smla_oracle_convert_indices.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64]
@@ -117,6 +121,29 @@ def decode_bf16_rows(rows: np.ndarray) -> np.ndarray:
     for i in range(rows.shape[0]):
         lib.smla_oracle_decode_bf16_row(rows[i].ctypes.data, out[i].ctypes.data)
     return out
+
+
+def e4m3fn_encode(x: float) -> int:
+    """float32 value -> E4M3FN byte, nearest with ties to even, saturating at 448."""
+    return int(_load().smla_oracle_e4m3fn_encode(float(x)))
+
+
+def cache_write(cache_format: int, k_c_bits: np.ndarray, k_pe_bits: np.ndarray,
+                slot_mapping: np.ndarray, cache: np.ndarray) -> np.ndarray:
+    """Write token rows into `cache` in place (the page's concat_and_cache_mla).
+    k_c_bits uint16 [T, 512] and k_pe_bits uint16 [T, 64] are bf16 bit patterns;
+    slot_mapping int64 [T]; cache uint16 [NB, 64, 576] (format 0, bf16) or uint8
+    [NB, 64, 656] (format 1, fp8_ds_mla). Returns cache."""
+    T = int(slot_mapping.shape[0])
+    k_c = _c(k_c_bits.reshape(T, 512), np.uint16)
+    k_pe = _c(k_pe_bits.reshape(T, 64), np.uint16)
+    sm = _c(slot_mapping, np.int64)
+    assert cache.flags["C_CONTIGUOUS"]
+    want = np.uint16 if cache_format == BF16_CACHE else np.uint8
+    assert cache.dtype == want
+    _load().smla_oracle_cache_write(int(cache_format), _ptr(k_c), _ptr(k_pe), _ptr(sm), T, _ptr(cache),
+                                    int(cache.shape[0]) * 64)
+    return cache
 
 
 def convert_indices(req_id_per_token, block_table, topk_indices, num_blocks: int) -> np.ndarray:

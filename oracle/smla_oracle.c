@@ -26,7 +26,10 @@
  *            value is the first 512 columns), _fp8_flash_mla_kernel (head_dim_v=512),
  *            and the softmax_scale the backend passes to the kernels.
  *   The OCP 8-bit floating point specification (the E4M3FN encoding) for the
- *   value of an e4m3 byte.
+ *   value of an e4m3 byte, and its round-to-nearest-even encoding.
+ *   [P2] FlashMLASparseImpl.forward: the concat_and_cache_mla call that writes
+ *   a token's latent (k_c_normed) and RoPE (k_pe) into the cache slot given by
+ *   slot_mapping, in the cache's dtype ("auto" = bf16 or "fp8_ds_mla").
  *
  * Readings where the pages are silent:
  *   - the second kernel return value is the natural-log log-sum-exp of the
@@ -36,7 +39,12 @@
  *   - a request id outside [0, num_reqs) or a block-table entry outside
  *     [0, num_blocks) yields slot -1 (the page's kernel would read out of
  *     bounds there);
- *   - the per-128 scales multiply the decoded e4m3 values.
+ *   - the per-128 scales multiply the decoded e4m3 values;
+ *   - cache writer (the pages give the row layout, not the quantisation): each
+ *     128-value group's scale is amax / 448 in float32 (1.0 for an all-zero
+ *     group), and each byte is the e4m3 value nearest to x / scale (float32
+ *     division), ties to the even code, saturating at +-448; a negative slot,
+ *     or one past the cache, writes nothing.
  *
  * Parity pins for every function here live in the CPU test suite
  * (tests/test_oracle_pins.py); none of them re-types these formulas.
@@ -109,6 +117,68 @@ void smla_oracle_decode_bf16_row(const uint16_t *row, double *out)
 {
     for (int i = 0; i < ORACLE_DQK; ++i)
         out[i] = smla_oracle_bf16(row[i]);
+}
+
+/* ------------------------------------------------------------ cache write */
+
+/* float -> OCP E4M3FN byte: the finite code whose value is nearest to x, ties
+ * to the code with an even mantissa (RNE); magnitudes beyond the largest finite
+ * value (448) take 448; NaN gives 0x7F. Found by scanning the 127 non-negative
+ * finite codes with the decoder above: slow on purpose, no bit manipulation. */
+uint8_t smla_oracle_e4m3fn_encode(float x)
+{
+    if (isnan(x))
+        return 0x7F;
+    const double a = fabs((double)x);
+    int best = 0;
+    double best_d = INFINITY;
+    for (int c = 0; c <= 0x7E; ++c) {
+        const double d = fabs(smla_oracle_e4m3fn((uint8_t)c) - a);
+        if (d < best_d || (d == best_d && (c & 1) == 0)) {
+            best = c;
+            best_d = d;
+        }
+    }
+    return (uint8_t)(signbit(x) ? (0x80 | best) : best);
+}
+
+/* Write num_tokens token rows into a paged cache [P2, FlashMLASparseImpl.forward:
+ * concat_and_cache_mla; cache format note]. k_c: bfloat16 [T][512] latent,
+ * k_pe: bfloat16 [T][64] RoPE, slot_mapping: int64 [T] (flat slot = block * 64
+ * + offset). cache_format 0: bf16 rows [slots][576] (latent then RoPE, copied);
+ * 1: fp8_ds_mla rows [slots][656] (see the readings above). num_slots bounds the
+ * cache; slots outside [0, num_slots) are skipped. */
+void smla_oracle_cache_write(int cache_format, const uint16_t *k_c, const uint16_t *k_pe,
+                             const int64_t *slot_mapping, int64_t num_tokens, void *cache,
+                             int64_t num_slots)
+{
+    for (int64_t t = 0; t < num_tokens; ++t) {
+        const int64_t slot = slot_mapping[t];
+        if (slot < 0 || slot >= num_slots)
+            continue;
+        const uint16_t *lat = k_c + t * ORACLE_DV;
+        const uint16_t *rope = k_pe + t * (ORACLE_DQK - ORACLE_DV);
+        if (cache_format == 0) {
+            uint16_t *row = (uint16_t *)cache + slot * ORACLE_DQK;
+            memcpy(row, lat, ORACLE_DV * sizeof(uint16_t));
+            memcpy(row + ORACLE_DV, rope, (ORACLE_DQK - ORACLE_DV) * sizeof(uint16_t));
+            continue;
+        }
+        uint8_t *row = (uint8_t *)cache + slot * ORACLE_FP8_ROW;
+        for (int g = 0; g < 4; ++g) {
+            float amax = 0.0f;
+            for (int i = 128 * g; i < 128 * g + 128; ++i) {
+                const float v = fabsf((float)smla_oracle_bf16(lat[i]));
+                if (v > amax)
+                    amax = v;
+            }
+            const float scale = amax > 0.0f ? amax / 448.0f : 1.0f;
+            for (int i = 128 * g; i < 128 * g + 128; ++i)
+                row[i] = smla_oracle_e4m3fn_encode((float)smla_oracle_bf16(lat[i]) / scale);
+            memcpy(row + 512 + 4 * g, &scale, sizeof scale);
+        }
+        memcpy(row + 528, rope, 64 * sizeof(uint16_t));
+    }
 }
 
 /* --------------------------------------------------------- index convert */

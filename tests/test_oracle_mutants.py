@@ -29,6 +29,13 @@ MUTANTS = {
     "table_width_off_by_one": ("if (blk >= max_blocks_per_req)", "if (blk > max_blocks_per_req)"),
     "in_block_offset": ("return (int32_t)(base * ORACLE_BLOCK + off);", "return (int32_t)(base * ORACLE_BLOCK + off + 1);"),
     "weights_unnormalised": ("double p = exp(s[j] - lse_th);", "double p = exp(s[j] - m);"),
+    "encode_ties_to_odd": ("(d == best_d && (c & 1) == 0)", "(d == best_d && (c & 1) == 1)"),
+    "encode_drops_sign": ("return (uint8_t)(signbit(x) ? (0x80 | best) : best);", "return (uint8_t)best;"),
+    "writer_scale_447": ("amax > 0.0f ? amax / 448.0f : 1.0f", "amax > 0.0f ? amax / 447.0f : 1.0f"),
+    "writer_scales_reversed": ("memcpy(row + 512 + 4 * g, &scale, sizeof scale);",
+                               "memcpy(row + 512 + 4 * (3 - g), &scale, sizeof scale);"),
+    "writer_rope_offset": ("memcpy(row + 528, rope, 64 * sizeof(uint16_t));",
+                           "memcpy(row + 526, rope, 64 * sizeof(uint16_t));"),
 }
 
 

@@ -3,6 +3,9 @@
 - value decoding: hand-worked OCP E4M3 values, every code against torch's
   float8_e4m3fn cast, bf16 widening against torch, a hand-worked fp8_ds_mla row,
   and random rows against a torch library decode;
+- e4m3 encoding and the cache writer: hand-worked OCP encodings, every value
+  of a sweep against torch's float8_e4m3fn cast, a hand-worked fp8_ds_mla row,
+  round-trip bounds through the decoder, and slot handling;
 - index conversion: hand-worked cases, and a paged-cache writer simulation that
   places tokens by appending (never by dividing by the block size);
 - attention: the dense special case against torch's scaled_dot_product_attention
@@ -110,6 +113,117 @@ def test_bf16_rows_match_torch_decode():
 
 
 # ---------------------------------------------------------- index conversion
+
+# ------------------------------------------------------- e4m3 encode, writer
+
+def test_e4m3_encode_hand_worked_values():
+    g = _golden("e4m3_encode_cases.json")
+    for text, want in g["cases"]:
+        assert oracle.e4m3fn_encode(float(text)) == want, (text, want)
+
+
+def test_e4m3_encode_matches_torch_cast_in_range():
+    # torch's cast rounds to nearest even; beyond 448 it does not saturate, so
+    # the sweep stays within the finite range
+    rng = np.random.default_rng(5)
+    x = np.concatenate([rng.uniform(-448, 448, 3000), rng.normal(0, 1e-2, 1000),
+                        rng.normal(0, 3, 1000)]).astype(np.float32)
+    # every exact tie of consecutive codes as well
+    vals = np.array([oracle.e4m3fn(c) for c in range(0x7F)])
+    ties = ((vals[:-1] + vals[1:]) / 2).astype(np.float32)
+    x = np.concatenate([x, ties, -ties])
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = np.array([oracle.e4m3fn_encode(v) for v in x], dtype=np.uint8)
+    assert np.array_equal(got, ref)
+
+
+def test_e4m3_encode_decode_round_trip():
+    for c in range(256):
+        v = oracle.e4m3fn(c)
+        if not math.isnan(v):
+            assert oracle.e4m3fn_encode(v) == c, c
+
+
+def _bf16_bits(x):
+    return torch.from_numpy(np.asarray(x, dtype=np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def test_cache_write_fp8_hand_worked_row():
+    # group 0 peaks at 448 (scale 1.0), group 1 is all zero (scale 1.0),
+    # group 2 peaks at 2.0 (x / scale = 448, 224, 112 up to float32 rounding),
+    # group 3 peaks at -0.25
+    lat = np.zeros(512, dtype=np.float32)
+    lat[0:4] = [448.0, 224.0, -1.0, 0.015625]
+    lat[256:260] = [2.0, 1.0, 0.5, -2.0]
+    lat[384] = -0.25
+    rope = np.linspace(-1, 1, 64).astype(np.float32)
+    cache = np.full((2, 64, 656), 0x5A, dtype=np.uint8)
+    oracle.cache_write(oracle.FP8_CACHE, _bf16_bits(lat)[None], _bf16_bits(rope)[None],
+                       np.array([64 + 3], dtype=np.int64), cache)
+    row = cache[1, 3]
+    assert list(row[0:5]) == [0x7E, 0x76, 0xB8, 0x08, 0x00]
+    assert not row[4:128].any() and not row[128:256].any()
+    assert list(row[256:260]) == [0x7E, 0x76, 0x6E, 0xFE]
+    assert row[384] == 0xFE and not row[385:512].any()
+    scales = row[512:528].view(np.float32)
+    assert scales[0] == 1.0 and scales[1] == 1.0
+    assert abs(scales[2] * 448 - 2.0) < 1e-6 and abs(scales[3] * 448 - 0.25) < 1e-7
+    assert np.array_equal(row[528:656].view(np.uint16), _bf16_bits(rope))
+    # every other row untouched
+    untouched = np.ones((2, 64), dtype=bool)
+    untouched[1, 3] = False
+    assert (cache[untouched] == 0x5A).all()
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_cache_write_fp8_round_trip(seed):
+    rng = np.random.default_rng(seed)
+    T = 40
+    lat = (rng.normal(0, 1, (T, 512)) * rng.choice([1e-3, 1.0, 50.0], size=(T, 1))).astype(np.float32)
+    lat[3, 128:256] = 0.0                       # an all-zero group
+    lat_b = _bf16_bits(lat)
+    rope_b = _bf16_bits(rng.normal(0, 1, (T, 64)))
+    slots = rng.permutation(4 * 64)[:T].astype(np.int64)
+    cache = np.zeros((4, 64, 656), dtype=np.uint8)
+    oracle.cache_write(oracle.FP8_CACHE, lat_b, rope_b, slots, cache)
+    x = torch.from_numpy(lat_b.view(np.int16)).view(torch.bfloat16).double().numpy()
+    rows = cache.reshape(-1, 656)[slots]
+    dec = oracle.decode_fp8_rows(rows)
+    for g in range(4):
+        xs = x[:, 128 * g:128 * g + 128]
+        scale = rows[:, 512 + 4 * g:516 + 4 * g].copy().view(np.float32)[:, 0].astype(np.float64)
+        amax = np.abs(xs).max(axis=1)
+        assert np.allclose(scale[amax > 0] * 448, amax[amax > 0], rtol=2e-7)
+        assert (scale[amax == 0] == 1.0).all()
+        err = np.abs(dec[:, 128 * g:128 * g + 128] - xs)
+        # half an e4m3 step: 2^-4 relative for normals, 2^-10 absolute (in units of
+        # the scale) for subnormals, plus the float32 rounding of x / scale
+        bound = np.maximum(np.abs(xs) * 2.0 ** -4, 2.0 ** -10 * scale[:, None]) * (1 + 1e-6)
+        assert (err <= bound).all()
+        # each group's largest magnitude maps to the largest code
+        top = np.abs(xs).argmax(axis=1)
+        codes = rows[np.arange(T), 128 * g + top]
+        assert ((codes[amax > 0] & 0x7F) == 0x7E).all()
+    assert np.array_equal(rows[:, 528:].copy().view(np.uint16), rope_b)
+
+
+def test_cache_write_bf16_copies_and_skips_bad_slots():
+    rng = np.random.default_rng(7)
+    T = 6
+    lat_b = rng.integers(0, 1 << 16, (T, 512), dtype=np.uint16)
+    rope_b = rng.integers(0, 1 << 16, (T, 64), dtype=np.uint16)
+    slots = np.array([5, -1, 127, 128, 1000, 0], dtype=np.int64)     # cache holds 128 slots
+    cache = np.full((2, 64, 576), 0x1234, dtype=np.uint16)
+    oracle.cache_write(oracle.BF16_CACHE, lat_b, rope_b, slots, cache)
+    flat = cache.reshape(-1, 576)
+    for t, sl in enumerate(slots):
+        if 0 <= sl < 128:
+            assert np.array_equal(flat[sl, :512], lat_b[t]) and np.array_equal(flat[sl, 512:], rope_b[t])
+    written = {int(s) for s in slots if 0 <= s < 128}
+    for sl in range(128):
+        if sl not in written:
+            assert (flat[sl] == 0x1234).all()
+
 
 def test_convert_hand_worked_cases():
     g = _golden("index_convert_cases.json")
