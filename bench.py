@@ -78,6 +78,38 @@ def algorithmic_work(w):
     return sum(by.values()), flops, by, n_valid
 
 
+def cache_writer_bench(torch, smla, dev, stream, flush, sink, steps: int):
+    """The cache writer (smla_concat_and_cache_mla, fp8_ds_mla) on a prefill-sized
+    batch (16384 tokens into random slots of a 1.3 GB pool) and on the decode
+    batch size (64 tokens), cold cache. Algorithmic bytes per token: 1024 latent +
+    128 RoPE + 8 slot read, 656 written."""
+    res = {}
+    g = torch.Generator(device="cpu").manual_seed(21)
+    NB = 32768
+    cache = torch.zeros((NB, 64, 656), dtype=torch.uint8, device=dev)
+    for T in (16384, 64):
+        lat = (torch.randn(T, 512, generator=g) * 2).to(torch.bfloat16).to(dev)
+        rope = torch.randn(T, 64, generator=g).to(torch.bfloat16).to(dev)
+        slots = torch.randperm(NB * 64, generator=g)[:T].to(torch.int64).to(dev)
+        for _ in range(3):
+            smla.smla_concat_and_cache_mla(lat, rope, cache, slots, stream=stream)
+        e0 = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+        e1 = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+        for i in range(steps):
+            torch.amax(flush, 0, out=sink)
+            e0[i].record(stream)
+            smla.smla_concat_and_cache_mla(lat, rope, cache, slots, stream=stream)
+            e1[i].record(stream)
+        torch.cuda.synchronize()
+        ms = float(np.mean([a.elapsed_time(b) for a, b in zip(e0, e1)]))
+        nbytes = T * (1024 + 128 + 8 + 656)
+        res[f"tokens_{T}"] = {"ms": ms, "tokens_per_s": T / (ms * 1e-3), "algorithmic_bytes": nbytes,
+                              "achieved_GBps": nbytes / (ms * 1e-3) / 1e9,
+                              "frac_of_hbm_peak": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    del cache
+    return res
+
+
 def cpu_baseline(w, target_s: float = 10.0):
     """The oracle as it stands, on this host's cores: whole passes over the batch's
     tokens (in a fixed shuffled order) until about target_s of CPU work is done."""
@@ -279,6 +311,7 @@ def main():
         "kernel_source_hash": kernel_source_hash(),
         "device": props.name,
     }
+    rec["cache_writer"] = cache_writer_bench(torch, smla, dev, stream, flush, sink, min(args.steps, 20))
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(rec), flush=True)

@@ -129,6 +129,34 @@ smla_status smla_merge_partials(const void *partials, size_t partials_bytes, int
                                 int32_t h_q, int32_t num_parts, void *out, float *lse,
                                 hipStream_t stream);
 
+/* Cache formats of smla_concat_and_cache_mla. */
+#define SMLA_CACHE_BF16 0         /* bf16 rows [num_blocks, 64, 576] ("auto" on the page) */
+#define SMLA_CACHE_FP8_DS_MLA 1   /* 656-byte fp8_ds_mla rows [num_blocks, 64, 656]     */
+
+/* Write tokens' latent and RoPE values into their slots of a paged cache
+ * [flashmla_sparse.py page, FlashMLASparseImpl.forward: the concat_and_cache_mla
+ * call before attention; module note on the fp8_ds_mla format].
+ *
+ *   k_c_normed    bf16 [num_tokens, 512] latent values, 16-B aligned
+ *   k_pe          bf16 [num_tokens, 64] RoPE values, 16-B aligned
+ *   slot_mapping  int64 [num_tokens]: flat slot (block * 64 + offset) of each
+ *                 token; a slot < 0 or >= num_blocks * 64 writes nothing. Each
+ *                 slot at most once per call (two tokens with one slot race).
+ *   kv_cache      the cache, 16-B aligned, cache_format:
+ *                 SMLA_CACHE_BF16: row = latent ++ RoPE, copied.
+ *                 SMLA_CACHE_FP8_DS_MLA: row = 512 e4m3 bytes, 4 fp32 scales, 64
+ *                 bf16 RoPE. Scale g = max |latent[128g .. 128g+127]| / 448 in
+ *                 fp32 (1.0 for an all-zero group); byte i = latent[i] / scale g
+ *                 (fp32 division) rounded to the nearest e4m3 value, ties to
+ *                 even. (The page passes a k_scale here as well; the per-group
+ *                 scales of this format do not use it.)
+ * Only the rows of the given slots are written. num_tokens == 0 is a no-op.
+ * Errors: SMLA_ERR_ARG (format), SMLA_ERR_SHAPE, SMLA_ERR_NULL, SMLA_ERR_ALIGN,
+ * SMLA_ERR_HIP. */
+smla_status smla_concat_and_cache_mla(const void *k_c_normed, const void *k_pe,
+                                      const int64_t *slot_mapping, int32_t num_tokens, void *kv_cache,
+                                      int64_t num_blocks, int32_t cache_format, hipStream_t stream);
+
 /* Logical-to-physical index conversion alone [flashmla_sparse.py page,
  * triton_convert_req_index_to_global_index and docstring]:
  *   out[t,j] = block_table[req_id_per_token[t], topk_indices[t,j] / 64] * 64

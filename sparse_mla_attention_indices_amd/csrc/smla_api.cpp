@@ -262,6 +262,28 @@ smla_status smla_merge_partials(const void *partials, size_t partials_bytes, int
                : SMLA_ERR_HIP;
 }
 
+smla_status smla_concat_and_cache_mla(const void *k_c_normed, const void *k_pe,
+                                      const int64_t *slot_mapping, int32_t num_tokens, void *kv_cache,
+                                      int64_t num_blocks, int32_t cache_format, hipStream_t stream)
+{
+    if (cache_format != SMLA_CACHE_BF16 && cache_format != SMLA_CACHE_FP8_DS_MLA)
+        return SMLA_ERR_ARG;
+    if (num_tokens < 0 || num_blocks < 1 || num_blocks > INT64_MAX / (smla::kBlock * smla::kBf16RowBytes))
+        return SMLA_ERR_SHAPE;
+    if (num_tokens == 0)
+        return SMLA_OK;
+    if (!k_c_normed || !k_pe || !slot_mapping || !kv_cache)
+        return SMLA_ERR_NULL;
+    if (!smla::aligned(k_c_normed, 16) || !smla::aligned(k_pe, 16) || !smla::aligned(slot_mapping, 8) ||
+        !smla::aligned(kv_cache, 16))
+        return SMLA_ERR_ALIGN;
+    return smla::launch_cache_write(cache_format == SMLA_CACHE_FP8_DS_MLA ? smla::kCacheFp8 : smla::kCacheBf16,
+                                    k_c_normed, k_pe, slot_mapping, kv_cache, num_tokens,
+                                    num_blocks * smla::kBlock, stream) == hipSuccess
+               ? SMLA_OK
+               : SMLA_ERR_HIP;
+}
+
 smla_status smla_convert_indices(const int32_t *req_id_per_token, const int32_t *block_table,
                                  const int32_t *topk_indices, int32_t *out, int32_t num_tokens,
                                  int32_t topk, int32_t num_reqs, int32_t max_blocks_per_req,

@@ -68,6 +68,10 @@ hipError_t launch_convert(const int32_t *req_id, const int32_t *block_table, con
 hipError_t launch_attention(CacheFormat fmt, const AttnArgs &a, const Plan &p, bool partials_only,
                             hipStream_t stream);
 
+// cache_write_kernel: rows of num_tokens tokens into their slots (< num_slots).
+hipError_t launch_cache_write(CacheFormat fmt, const void *k_c, const void *k_pe, const int64_t *slot_mapping,
+                             void *cache, int64_t num_tokens, int64_t num_slots, hipStream_t stream);
+
 // merge_kernel alone over a partials buffer of T x S x H entries.
 hipError_t launch_merge(const float *part_lse, const float *part_o, void *out, float *lse, int T,
                         int H, int S, hipStream_t stream);

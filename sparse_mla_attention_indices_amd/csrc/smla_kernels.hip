@@ -1032,6 +1032,70 @@ __global__ __launch_bounds__(256) void merge_kernel(const float *__restrict__ pa
         lse[th] = W > 0.f ? M + logf(W) : -INFINITY;
 }
 
+// Cache writer [flashmla_sparse.py page, FlashMLASparseImpl.forward: the
+// concat_and_cache_mla call; cache format note]: one wave per token writes its
+// 512 latent and 64 RoPE values into the row at slot_mapping[t]. fp8_ds_mla:
+// lane l holds latent values 8l .. 8l + 7, so each 128-value group is one row of
+// 16 lanes; the group's scale is amax / 448 in float32 (1.0 for an all-zero
+// group) and each byte is x / scale (float32 division) rounded to the nearest
+// e4m3 value, ties to even. bf16: the row is copied. Slots outside
+// [0, num_slots) write nothing. Four tokens per 256-thread block.
+template <int FMT>
+__global__ __launch_bounds__(256) void cache_write_kernel(const uint16_t *__restrict__ k_c,
+                                                          const uint16_t *__restrict__ k_pe,
+                                                          const int64_t *__restrict__ slot_mapping,
+                                                          uint8_t *__restrict__ cache, int64_t num_tokens,
+                                                          int64_t num_slots)
+{
+    const int lane = threadIdx.x & 63;
+    const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= num_tokens)
+        return;
+    const int64_t slot = slot_mapping[t];
+    if (slot < 0 || slot >= num_slots)
+        return;
+    const uint4 lat = ((const uint4 *)(k_c + t * kDv))[lane];
+    uint4 rope = make_uint4(0u, 0u, 0u, 0u);
+    if (lane < 8)
+        rope = ((const uint4 *)(k_pe + t * (kDqk - kDv)))[lane];
+    if constexpr (FMT == kCacheBf16) {
+        uint8_t *row = cache + slot * kBf16RowBytes;
+        ((uint4 *)row)[lane] = lat;
+        if (lane < 8)
+            ((uint4 *)(row + 2 * kDv))[lane] = rope;
+    } else {
+        uint8_t *row = cache + slot * kFp8RowBytes;
+        const uint32_t w[4] = {lat.x, lat.y, lat.z, lat.w};
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            v[2 * e] = bf16_lo(w[e]);
+            v[2 * e + 1] = bf16_hi(w[e]);
+        }
+        float amax = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            amax = fmaxf(amax, fabsf(v[i]));
+#pragma unroll
+        for (int d = 1; d < 16; d <<= 1)
+            amax = fmaxf(amax, __shfl_xor(amax, d));
+        const float scale = amax > 0.f ? amax / 448.f : 1.f;
+        uint32_t code[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            s16x2 c = {0, 0};
+            c = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(c, v[4 * j] / scale, v[4 * j + 1] / scale, 1.0f, false);
+            c = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(c, v[4 * j + 2] / scale, v[4 * j + 3] / scale, 1.0f, true);
+            code[j] = __builtin_bit_cast(uint32_t, c);
+        }
+        ((uint2 *)row)[lane] = make_uint2(code[0], code[1]);
+        if ((lane & 15) == 0)
+            ((float *)(row + kDv))[lane >> 4] = scale;
+        if (lane < 8)
+            ((uint4 *)(row + kDv + 16))[lane] = rope;
+    }
+}
+
 __global__ __launch_bounds__(256) void convert_kernel(const int32_t *__restrict__ req_id,
                                                       const int32_t *__restrict__ bt,
                                                       const int32_t *__restrict__ topk,
@@ -1078,6 +1142,19 @@ hipError_t launch_convert(const int32_t *req_id, const int32_t *block_table, con
     const int grid = (int)(blocks < 16384 ? blocks : 16384);
     hipLaunchKernelGGL(convert_kernel, dim3(grid), dim3(256), 0, stream, req_id, block_table, topk,
                        out, total, topk_len, num_reqs, max_blocks, num_blocks);
+    return hipGetLastError();
+}
+
+hipError_t launch_cache_write(CacheFormat fmt, const void *k_c, const void *k_pe, const int64_t *slot_mapping,
+                             void *cache, int64_t num_tokens, int64_t num_slots, hipStream_t stream)
+{
+    const dim3 grid((unsigned)((num_tokens + 3) / 4));
+    if (fmt == kCacheFp8)
+        hipLaunchKernelGGL(cache_write_kernel<kCacheFp8>, grid, dim3(256), 0, stream, (const uint16_t *)k_c,
+                           (const uint16_t *)k_pe, slot_mapping, (uint8_t *)cache, num_tokens, num_slots);
+    else
+        hipLaunchKernelGGL(cache_write_kernel<kCacheBf16>, grid, dim3(256), 0, stream, (const uint16_t *)k_c,
+                           (const uint16_t *)k_pe, slot_mapping, (uint8_t *)cache, num_tokens, num_slots);
     return hipGetLastError();
 }
 

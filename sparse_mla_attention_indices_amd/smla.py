@@ -24,7 +24,9 @@ SMLA_OK = 0
 STATUS_NAMES = {0: "SMLA_OK", 1: "SMLA_ERR_NULL", 2: "SMLA_ERR_SHAPE", 3: "SMLA_ERR_ALIGN",
                 4: "SMLA_ERR_WORKSPACE", 5: "SMLA_ERR_HIP", 6: "SMLA_ERR_ARG"}
 EXPORTS = ("smla_status_string", "smla_abi_version", "smla_plan", "smla_workspace_size",
-           "smla_merge_partials", "smla_convert_indices", "smla_prefill_bf16", "smla_decode_fp8")
+           "smla_merge_partials", "smla_concat_and_cache_mla", "smla_convert_indices",
+           "smla_prefill_bf16", "smla_decode_fp8")
+CACHE_FORMATS = {"auto": 0, "bf16": 0, "fp8_ds_mla": 1}
 FLAG_PARTIALS_ONLY = 0x1
 
 
@@ -63,6 +65,8 @@ def library() -> ctypes.CDLL:
     lib.smla_workspace_size.argtypes = [i32, i32, i32, vp, ctypes.POINTER(sz)]
     lib.smla_merge_partials.restype = ctypes.c_int
     lib.smla_merge_partials.argtypes = [vp, sz, i32, i32, i32, vp, vp, vp]
+    lib.smla_concat_and_cache_mla.restype = ctypes.c_int
+    lib.smla_concat_and_cache_mla.argtypes = [vp, vp, vp, i32, vp, i64, i32, vp]
     lib.smla_convert_indices.restype = ctypes.c_int
     lib.smla_convert_indices.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i64, vp]
     attn = [vp, vp, vp, vp, vp, fl, i32, i32, i32, i32, i32, i64, vp, vp, vp, vp, sz, vp, vp]
@@ -166,6 +170,24 @@ def _own_workspace(device: torch.device, stream, need: int) -> torch.Tensor:
         ws = torch.empty(need, dtype=torch.uint8, device=device)
         _own_workspaces[key] = ws
     return ws
+
+
+def smla_concat_and_cache_mla(k_c_normed, k_pe, kv_cache, slot_mapping, kv_cache_dtype="fp8_ds_mla",
+                              stream=None):
+    """Write each token's latent ([T, 512] bf16) and RoPE ([T, 64] bf16) into its
+    slot (int64 [T], block * 64 + offset; negative = skip) of kv_cache: uint8
+    [NB, 64, 656] for "fp8_ds_mla", bf16 [NB, 64, 576] for "auto". Returns kv_cache."""
+    fmt = CACHE_FORMATS[kv_cache_dtype]
+    if fmt == 1 and (kv_cache.dtype != torch.uint8 or kv_cache.shape[1:] != (64, 656)):
+        raise ValueError("an fp8_ds_mla cache is uint8 [num_blocks, 64, 656]")
+    if fmt == 0 and (kv_cache.dtype != torch.bfloat16 or kv_cache.shape[1:] != (64, 576)):
+        raise ValueError("a bf16 cache is bfloat16 [num_blocks, 64, 576]")
+    T = slot_mapping.shape[0]
+    _check(library().smla_concat_and_cache_mla(
+        _dev(k_c_normed, "k_c_normed", torch.bfloat16, 2), _dev(k_pe, "k_pe", torch.bfloat16, 2),
+        _dev(slot_mapping, "slot_mapping", torch.int64, 1), T, _dev(kv_cache, "kv_cache"),
+        kv_cache.shape[0], fmt, _stream(stream)), "smla_concat_and_cache_mla")
+    return kv_cache
 
 
 def smla_convert_indices(req_id_per_token, block_table, topk_indices, num_blocks: int,

@@ -209,3 +209,21 @@ def test_merge_rejects_before_any_hip_call(lib, kw, code):
 
 def test_merge_zero_tokens_is_a_noop(lib):
     assert _merge(lib, part=None, out=None, T=0) == 0
+
+
+def _cw(lib, kc=A16, kpe=A16B, sm=A256, T=4, kv=A16, NB=8, fmt=1):
+    return lib.smla_concat_and_cache_mla(kc, kpe, sm, T, kv, NB, fmt, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(kc=None), 1), (dict(kpe=None), 1), (dict(sm=None), 1), (dict(kv=None), 1),
+    (dict(T=-1), 2), (dict(NB=0), 2),
+    (dict(kc=MIS), 3), (dict(kpe=A16 + 8), 3), (dict(sm=A256 + 4), 3), (dict(kv=A16 + 4), 3),
+    (dict(fmt=2), 6), (dict(fmt=-1), 6),
+])
+def test_cache_write_rejects_before_any_hip_call(lib, kw, code):
+    assert _cw(lib, **kw) == code
+
+
+def test_cache_write_zero_tokens_is_a_noop(lib):
+    assert _cw(lib, kc=None, kpe=None, sm=None, kv=None, T=0) == 0
