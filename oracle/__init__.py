@@ -73,6 +73,14 @@ def _load():
     lib.smla_oracle_convert_one.argtypes = [i32, i32, vp, i64, i64, i64]
     lib.smla_oracle_convert_indices.restype = None
     lib.smla_oracle_convert_indices.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64]
+    lib.smla_oracle_convert_indices_ws.restype = None
+    lib.smla_oracle_convert_indices_ws.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64]
+    lib.smla_oracle_bf16_rne.restype = ctypes.c_uint16
+    lib.smla_oracle_bf16_rne.argtypes = [dbl]
+    lib.smla_oracle_gather_upconvert.restype = None
+    lib.smla_oracle_gather_upconvert.argtypes = [vp, i64, vp, i64, vp, vp, i64, vp, i64]
+    lib.smla_oracle_plan_prefill_chunks.restype = i64
+    lib.smla_oracle_plan_prefill_chunks.argtypes = [vp, i64, i64, vp, vp]
     lib.smla_oracle_attention.restype = ctypes.c_int
     lib.smla_oracle_attention.argtypes = [ctypes.c_int, vp, vp, vp, vp, vp, dbl,
                                           i64, i64, i64, i64, i64, i64, vp, i64, vp, vp, vp]
@@ -162,6 +170,69 @@ def convert_indices(req_id_per_token, block_table, topk_indices, num_blocks: int
     return out
 
 
+def convert_indices_workspace(req_id_per_token, block_table, topk_indices, num_blocks: int,
+                              prefill_request_id, workspace_starts) -> np.ndarray:
+    """Index conversion of the separate-prefill mode: tokens with a prefill request
+    id r >= 0 map valid indices to workspace_starts[r] + idx, the others to cache
+    slots. Returns int32 [T, K], -1 = invalid."""
+    req = _c(req_id_per_token, np.int32).reshape(-1)
+    bt = _c(block_table, np.int32)
+    idx = _c(topk_indices, np.int32)
+    pr = _c(prefill_request_id, np.int32).reshape(-1)
+    ws = _c(workspace_starts, np.int32).reshape(-1)
+    if bt.ndim != 2 or idx.ndim != 2 or idx.shape[0] != req.shape[0] or pr.shape[0] != req.shape[0]:
+        raise ValueError("shapes: block_table [R, MB], topk_indices [T, K], req/prefill ids [T]")
+    out = np.empty_like(idx)
+    _load().smla_oracle_convert_indices_ws(req.ctypes.data, bt.ctypes.data, idx.ctypes.data,
+                                           pr.ctypes.data, ws.ctypes.data if ws.size else None,
+                                           out.ctypes.data, idx.shape[0], idx.shape[1], bt.shape[0],
+                                           bt.shape[1], int(num_blocks), ws.shape[0])
+    return out
+
+
+def bf16_rne(x: float) -> int:
+    """Bit pattern of the bfloat16 nearest to x (ties to even)."""
+    return int(_load().smla_oracle_bf16_rne(float(x)))
+
+
+def gather_upconvert(cache, block_table, seq_lens, workspace_starts, workspace_rows: int,
+                     workspace=None) -> np.ndarray:
+    """Upconvert the context rows of prefill requests from an fp8_ds_mla cache
+    (uint8 [NB, 64, 656]) into a bf16 workspace (uint16 bit patterns
+    [workspace_rows, 576]); block_table [B, MB] holds the requests' rows, seq_lens
+    and workspace_starts [B]. Rows no request covers keep their contents (zeros
+    for a new workspace). Returns the workspace."""
+    c = cache if (cache.dtype == np.uint8 and cache.flags.c_contiguous) else _c(cache, np.uint8)
+    if c.shape[-1] != 656:
+        raise ValueError("fp8_ds_mla cache rows must be 656 bytes")
+    bt = _c(block_table, np.int32)
+    sl = _c(seq_lens, np.int32).reshape(-1)
+    st = _c(workspace_starts, np.int32).reshape(-1)
+    if bt.ndim != 2 or bt.shape[0] != sl.shape[0] or st.shape[0] != sl.shape[0]:
+        raise ValueError("block_table [B, MB], seq_lens [B], workspace_starts [B]")
+    if workspace is None:
+        workspace = np.zeros((workspace_rows, 576), dtype=np.uint16)
+    assert workspace.dtype == np.uint16 and workspace.flags.c_contiguous
+    _load().smla_oracle_gather_upconvert(c.ctypes.data, c.size // (64 * 656), bt.ctypes.data, bt.shape[1],
+                                         sl.ctypes.data, st.ctypes.data, sl.shape[0],
+                                         workspace.ctypes.data, int(workspace_rows))
+    return workspace
+
+
+def plan_prefill_chunks(seq_lens, max_rows: int):
+    """Greedy chunks of consecutive prefill requests that fit max_rows workspace
+    rows. Returns (chunk_ends list, chunk-local workspace_starts int32 [B]); raises
+    ValueError when a request alone does not fit."""
+    sl = _c(seq_lens, np.int32).reshape(-1)
+    ends = np.zeros(max(sl.shape[0], 1), dtype=np.int32)
+    starts = np.zeros(sl.shape[0], dtype=np.int32)
+    n = _load().smla_oracle_plan_prefill_chunks(sl.ctypes.data, sl.shape[0], int(max_rows),
+                                                ends.ctypes.data, starts.ctypes.data)
+    if n < 0:
+        raise ValueError("a prefill request does not fit the workspace")
+    return [int(e) for e in ends[:n]], starts
+
+
 def attention(cache_format: int, q_bits, cache, block_table, req_id_per_token, topk_indices,
               sm_scale: float, tokens=None, want_weights: bool = False):
     """Sparse MLA forward on the CPU.
@@ -210,3 +281,49 @@ def attention(cache_format: int, q_bits, cache, block_table, req_id_per_token, t
     if want_weights:
         return o, lse, w
     return o, lse
+
+
+def separate_prefill_attention(q_bits, cache, block_table, req_id_per_token, topk_indices, sm_scale: float,
+                               num_decode_reqs: int, seq_lens, max_rows: int):
+    """The separate-prefill mode of an fp8_ds_mla cache, end to end [P1,
+    _build_fp8_separate_prefill_decode and _forward_fp8_kv_separate_prefill_decode]:
+    requests [0, num_decode_reqs) are decode requests, the rest prefill requests
+    (prefill index r = request id - num_decode_reqs) with context length
+    seq_lens[request]. Decode tokens attend over the fp8 cache; prefill tokens
+    attend, chunk by chunk, over their chunk's context rows upconverted to bf16
+    in a workspace of at most max_rows rows, through indices converted to
+    workspace rows. Returns (o [T, H, 512] float64, lse [T, H] float64)."""
+    q = _c(q_bits, np.uint16)
+    T, H = q.shape[0], q.shape[1]
+    bt = _c(block_table, np.int32)
+    req = _c(req_id_per_token, np.int32).reshape(-1)
+    idx = _c(topk_indices, np.int32)
+    sl = _c(seq_lens, np.int32).reshape(-1)
+    nb = cache.size // (64 * 656)
+    R = bt.shape[0]
+    nd = int(num_decode_reqs)
+    prefill_id = np.where(req >= nd, req - nd, -1).astype(np.int32)
+    ends, starts = plan_prefill_chunks(sl[nd:R], max_rows)
+    phys = convert_indices_workspace(req, bt, idx, nb, prefill_id, starts)
+    o = np.zeros((T, H, 512))
+    lse = np.full((T, H), -np.inf)
+    dec = np.nonzero(prefill_id < 0)[0]
+    if dec.size:
+        od, ld = attention(FP8_CACHE, q, cache, bt, req, idx, sm_scale, tokens=dec)
+        o[dec], lse[dec] = od, ld
+    c0 = 0
+    for c1 in ends:
+        rows = int(sl[nd + c0:nd + c1].sum())
+        nbw = max(1, -(-rows // 64))
+        ws = gather_upconvert(cache, bt[nd + c0:nd + c1], sl[nd + c0:nd + c1], starts[c0:c1], rows,
+                              workspace=np.zeros((nbw * 64, 576), dtype=np.uint16))
+        toks = np.nonzero((prefill_id >= c0) & (prefill_id < c1))[0]
+        if toks.size:
+            # workspace row w = block w // 64, offset w % 64 of a one-request table
+            ident = np.arange(nbw, dtype=np.int32).reshape(1, nbw)
+            op, lp = attention(BF16_CACHE, q[toks], ws.reshape(nbw, 64, 576), ident,
+                               np.zeros(toks.size, dtype=np.int32), phys[toks], sm_scale)
+            o[toks], lse[toks] = op, lp
+        c0 = c1
+    return o, lse
+

@@ -30,6 +30,18 @@
  *   [P2] FlashMLASparseImpl.forward: the concat_and_cache_mla call that writes
  *   a token's latent (k_c_normed) and RoPE (k_pe) into the cache slot given by
  *   slot_mapping, in the cache's dtype ("auto" = bf16 or "fp8_ds_mla").
+ *   [P1] "vllm/v1/attention/backends/mla/flashmla_sparse.py" as changed by the
+ *   vllm-xpu-kernels / vLLM pull requests (the separate-prefill mode of an
+ *   fp8 cache): _convert_req_index_to_global_index_kernel with HAS_PREFILL
+ *   (a prefill token's index maps to its request's workspace start plus the
+ *   index), _build_fp8_separate_prefill_decode (workspace starts are the
+ *   running sum of the prefill sequence lengths, cut into chunks that fit the
+ *   workspace, each chunk's starts made chunk-local; the worked example there:
+ *   lengths [10, 15, 20, 5] in chunks [0, 2) and [2, 4) give starts
+ *   [0, 10, 0, 20]), get_prefill_workspace_size (5 x max_model_len rows), and
+ *   _forward_fp8_kv_separate_prefill_decode (each chunk's context rows are
+ *   gathered from the fp8 cache and upconverted into a bf16 workspace, then
+ *   the bf16 kernel runs over the workspace).
  *
  * Readings where the pages are silent:
  *   - the second kernel return value is the natural-log log-sum-exp of the
@@ -45,6 +57,13 @@
  *     group), and each byte is the e4m3 value nearest to x / scale (float32
  *     division), ties to the even code, saturating at +-448; a negative slot,
  *     or one past the cache, writes nothing.
+ *   - separate-prefill mode: the upconverted value of a latent element is the
+ *     exact product e4m3 x scale rounded once to the nearest bfloat16, ties to
+ *     even (the RoPE part is copied); chunks are formed greedily in request
+ *     order, a new chunk starting when the next request would overflow the
+ *     workspace; a context position whose block lies outside the table (or
+ *     whose table entry lies outside the cache) upconverts to a row of zeros;
+ *     a prefill request id past the prefill count converts to -1.
  *
  * Parity pins for every function here live in the CPU test suite
  * (tests/test_oracle_pins.py); none of them re-types these formulas.
@@ -216,6 +235,120 @@ void smla_oracle_convert_indices(const int32_t *req_id_per_token, const int32_t 
             out[t * topk + j] = smla_oracle_convert_one(
                 req_id_per_token[t], topk_indices[t * topk + j], block_table, num_reqs,
                 max_blocks_per_req, num_blocks);
+}
+
+/* ------------------------------------------------ separate-prefill mode */
+
+/* Index conversion with a prefill workspace [P1,
+ * _convert_req_index_to_global_index_kernel with HAS_PREFILL]: a token whose
+ * prefill request id r is >= 0 maps a valid index to workspace_starts[r] + idx;
+ * other tokens convert as smla_oracle_convert_one. Invalid either way: a
+ * negative index and a block position outside the table width. */
+int32_t smla_oracle_convert_one_ws(int32_t req, int32_t idx, const int32_t *block_table,
+                                   int64_t num_reqs, int64_t max_blocks_per_req, int64_t num_blocks,
+                                   int32_t prefill_req, const int32_t *workspace_starts,
+                                   int64_t num_prefills)
+{
+    if (prefill_req < 0)
+        return smla_oracle_convert_one(req, idx, block_table, num_reqs, max_blocks_per_req,
+                                       num_blocks);
+    if (prefill_req >= num_prefills || idx < 0 || idx / ORACLE_BLOCK >= max_blocks_per_req)
+        return -1;
+    return workspace_starts[prefill_req] + idx;
+}
+
+void smla_oracle_convert_indices_ws(const int32_t *req_id_per_token, const int32_t *block_table,
+                                    const int32_t *topk_indices, const int32_t *prefill_request_id,
+                                    const int32_t *workspace_starts, int32_t *out, int64_t num_tokens,
+                                    int64_t topk, int64_t num_reqs, int64_t max_blocks_per_req,
+                                    int64_t num_blocks, int64_t num_prefills)
+{
+    for (int64_t t = 0; t < num_tokens; ++t)
+        for (int64_t j = 0; j < topk; ++j)
+            out[t * topk + j] = smla_oracle_convert_one_ws(
+                req_id_per_token[t], topk_indices[t * topk + j], block_table, num_reqs,
+                max_blocks_per_req, num_blocks, prefill_request_id[t], workspace_starts,
+                num_prefills);
+}
+
+/* A finite value with at most 53 significant bits -> the bfloat16 bit pattern
+ * of the nearest bfloat16 value, ties to even (8 significant bits for normal
+ * values, a fixed quantum of 2^-133 below 2^-126), infinity past the largest
+ * finite bfloat16. */
+uint16_t smla_oracle_bf16_rne(double x)
+{
+    if (x == 0.0)
+        return signbit(x) ? 0x8000u : 0u;
+    int e;
+    frexp(x, &e);                        /* |x| in [2^(e-1), 2^e) */
+    int q = e - 8;                       /* quantum exponent: 8 significant bits */
+    if (q < -133)
+        q = -133;
+    double r = ldexp(nearbyint(ldexp(x, -q)), q);     /* nearbyint: ties to even */
+    float f = (float)r;                                /* exact: <= 8 significant bits */
+    if (fabs(r) >= 0x1.0p128)
+        f = r > 0 ? INFINITY : -INFINITY;
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    return (uint16_t)(u >> 16);
+}
+
+/* Gather and upconvert the context rows of a batch of prefill requests into a
+ * bf16 workspace [P1, _forward_fp8_kv_separate_prefill_decode: the
+ * cp_gather_and_upconvert_fp8_kv_cache call]: for request b and position
+ * p < seq_lens[b], workspace row workspace_starts[b] + p (when inside
+ * [0, workspace_rows)) receives the row at slot block_table[b, p / 64] * 64 +
+ * p % 64 of the fp8_ds_mla cache, each latent value e4m3 x scale rounded to
+ * bfloat16, the RoPE values copied. */
+void smla_oracle_gather_upconvert(const uint8_t *cache, int64_t num_blocks, const int32_t *block_table,
+                                  int64_t max_blocks_per_req, const int32_t *seq_lens,
+                                  const int32_t *workspace_starts, int64_t batch, uint16_t *workspace,
+                                  int64_t workspace_rows)
+{
+    for (int64_t b = 0; b < batch; ++b) {
+        for (int64_t pos = 0; pos < seq_lens[b]; ++pos) {
+            int64_t w = (int64_t)workspace_starts[b] + pos;
+            if (w < 0 || w >= workspace_rows)
+                continue;
+            uint16_t *dst = workspace + w * ORACLE_DQK;
+            int64_t blk = pos / ORACLE_BLOCK;
+            int64_t base = blk < max_blocks_per_req ? block_table[b * max_blocks_per_req + blk] : -1;
+            if (base < 0 || base >= num_blocks) {
+                memset(dst, 0, ORACLE_DQK * sizeof(uint16_t));
+                continue;
+            }
+            const uint8_t *row = cache + (base * ORACLE_BLOCK + pos % ORACLE_BLOCK) * ORACLE_FP8_ROW;
+            double v[ORACLE_DQK];
+            smla_oracle_decode_fp8_row(row, v);
+            for (int i = 0; i < ORACLE_DV; ++i)
+                dst[i] = smla_oracle_bf16_rne(v[i]);
+            memcpy(dst + ORACLE_DV, row + 528, 64 * sizeof(uint16_t));
+        }
+    }
+}
+
+/* Cut consecutive prefill requests into chunks whose total sequence length fits
+ * max_rows workspace rows [P1, _build_fp8_separate_prefill_decode]: greedy in
+ * request order. Writes chunk_ends[c] (one past the chunk's last request) and,
+ * for every request, its chunk-local workspace start. Returns the chunk count,
+ * or -1 if a single request is longer than max_rows or a length is negative. */
+int64_t smla_oracle_plan_prefill_chunks(const int32_t *seq_lens, int64_t num_prefills, int64_t max_rows,
+                                        int32_t *chunk_ends, int32_t *workspace_starts)
+{
+    int64_t n = 0, used = 0;
+    for (int64_t r = 0; r < num_prefills; ++r) {
+        if (seq_lens[r] < 0 || seq_lens[r] > max_rows)
+            return -1;
+        if (r > 0 && used + seq_lens[r] > max_rows) {
+            chunk_ends[n++] = (int32_t)r;
+            used = 0;
+        }
+        workspace_starts[r] = (int32_t)used;
+        used += seq_lens[r];
+    }
+    if (num_prefills > 0)
+        chunk_ends[n++] = (int32_t)num_prefills;
+    return n;
 }
 
 /* -------------------------------------------------------------- attention */

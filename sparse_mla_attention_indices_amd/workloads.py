@@ -292,4 +292,36 @@ def config5(seed: int = 0) -> Workload:
                  max_blocks_per_req=2048)
 
 
+def mixed_batch(seed: int, h_q: int, topk: int, decode_ctx, prefill_ctx, prefill_queries,
+                p_invalid: float = 0.0, cache_format: str = "fp8") -> Workload:
+    """A batch in the order a serving engine builds it: decode requests first
+    (one query token each, seeing its whole context), then prefill requests whose
+    last prefill_queries[r] positions are query tokens (position p sees 0..p).
+    The Workload's ctx_lens are the requests' sequence lengths (context plus
+    query)."""
+    dec = [int(c) for c in decode_ctx]
+    pre = [int(c) for c in prefill_ctx]
+    ctx = dec + pre
+    req = list(range(len(dec)))
+    vis = list(dec)
+    for r, (c, nq) in enumerate(zip(pre, prefill_queries)):
+        for pos in range(c - int(nq), c):
+            req.append(len(dec) + r)
+            vis.append(pos + 1)
+    return build("mixed", 6, seed, ctx, req, vis, h_q, topk, cache_format, p_invalid=p_invalid)
+
+
+def config5_prefill(seed: int = 0) -> Workload:
+    """Config 5's two prefill requests alone (ctx 131072 and 65536; query tokens are
+    their last 2048 positions), h_q 128, top-k 2048, fp8 cache: the part the
+    separate-prefill mode upconverts."""
+    pre_ctx = np.array([131072, 65536])
+    req, vis = [], []
+    for r, c in enumerate(pre_ctx):
+        for pos in range(int(c) - 2048, int(c)):
+            req.append(r)
+            vis.append(pos + 1)
+    return build("c5_prefill_part", 7, seed, pre_ctx, req, vis, 128, 2048, "fp8", max_blocks_per_req=2048)
+
+
 CONFIGS = {1: config1, 2: config2, 3: config3, 4: config4, 5: config5}

@@ -36,6 +36,18 @@ MUTANTS = {
                                "memcpy(row + 512 + 4 * (3 - g), &scale, sizeof scale);"),
     "writer_rope_offset": ("memcpy(row + 528, rope, 64 * sizeof(uint16_t));",
                            "memcpy(row + 526, rope, 64 * sizeof(uint16_t));"),
+    "ws_start_ignored": ("return workspace_starts[prefill_req] + idx;", "return idx;"),
+    "ws_table_width_unchecked": ("if (prefill_req >= num_prefills || idx < 0 || idx / ORACLE_BLOCK >= max_blocks_per_req)",
+                                 "if (prefill_req >= num_prefills || idx < 0)"),
+    "bf16_truncates": ("nearbyint(ldexp(x, -q))", "trunc(ldexp(x, -q))"),
+    "bf16_ties_away": ("nearbyint(ldexp(x, -q))", "round(ldexp(x, -q))"),
+    "bf16_nine_bits": ("int q = e - 8;", "int q = e - 9;"),
+    "upconvert_rope_offset": ("memcpy(dst + ORACLE_DV, row + 528, 64 * sizeof(uint16_t));",
+                              "memcpy(dst + ORACLE_DV, row + 526, 64 * sizeof(uint16_t));"),
+    "upconvert_block_of_32": ("int64_t blk = pos / ORACLE_BLOCK;", "int64_t blk = pos / 32;"),
+    "chunks_close_early": ("if (r > 0 && used + seq_lens[r] > max_rows) {", "if (r > 0 && used + seq_lens[r] >= max_rows) {"),
+    "chunk_starts_not_reset": ("            chunk_ends[n++] = (int32_t)r;\n            used = 0;",
+                               "            chunk_ends[n++] = (int32_t)r;"),
 }
 
 

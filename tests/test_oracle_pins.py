@@ -432,3 +432,219 @@ def test_token_subset_matches_full_run(sparse_case):
     pick = np.array([4, 0, 7])
     o2, lse2 = oracle.attention(1, q, cache, pc.block_table, req, idx, 0.05, tokens=pick)
     assert np.array_equal(o2, o[pick]) and np.array_equal(lse2, lse[pick])
+
+
+# ------------------------------------------------------- separate-prefill mode
+# (the flashmla_sparse.py page as changed for the separate-prefill mode of an
+# fp8 cache: _build_fp8_separate_prefill_decode, the HAS_PREFILL branch of
+# _convert_req_index_to_global_index_kernel, _forward_fp8_kv_separate_prefill_decode)
+
+def test_prefill_chunks_reproduce_the_page_example():
+    g = _golden("prefill_workspace_example.json")
+    for m in g["chunk_max_rows"]:
+        ends, starts = oracle.plan_prefill_chunks(g["seq_lens"], m)
+        assert ends == g["chunk_ends"] and list(starts) == g["chunked_starts"], m
+    ends, starts = oracle.plan_prefill_chunks(g["seq_lens"], g["one_chunk_max_rows"])
+    assert ends == [4] and list(starts) == g["unchunked_starts"]
+
+
+def test_prefill_chunks_fit_tile_the_workspace_and_are_greedy():
+    rng = np.random.default_rng(5)
+    for _ in range(300):
+        n = int(rng.integers(1, 12))
+        lens = rng.integers(0, 40, n)
+        m = int(rng.integers(max(int(lens.max()), 1), 100))
+        ends, starts = oracle.plan_prefill_chunks(lens, m)
+        assert ends[-1] == n and ends == sorted(set(ends))
+        c0 = 0
+        for c1 in ends:
+            total = int(lens[c0:c1].sum())
+            assert total <= m
+            # the chunk's requests occupy [0, total) in request order, back to back
+            covered = np.zeros(total, dtype=int)
+            prev_end = 0
+            for r in range(c0, c1):
+                assert starts[r] == prev_end
+                covered[starts[r]:starts[r] + lens[r]] += 1
+                prev_end = starts[r] + lens[r]
+            assert (covered == 1).all()
+            if c1 < n:
+                assert total + lens[c1] > m        # the next request would not have fit
+            c0 = c1
+    with pytest.raises(ValueError):
+        oracle.plan_prefill_chunks([5, 30], 20)
+
+
+def _ws_case(seed):
+    rng = np.random.default_rng(seed)
+    R, MB, T, K = 5, 6, 12, 24
+    bt = rng.integers(-2, 40, (R, MB)).astype(np.int32)
+    req = rng.integers(-1, R + 1, T).astype(np.int32)
+    idx = rng.integers(-70, MB * 64 + 70, (T, K)).astype(np.int32)
+    pid = rng.integers(-1, 4, T).astype(np.int32)            # 3 prefill requests; id 3 is out of range
+    starts = np.array([0, 100, 250], dtype=np.int32)
+    return req, bt, idx, pid, starts, MB
+
+
+def test_workspace_conversion_leaves_decode_tokens_to_the_plain_conversion():
+    for seed in range(4):
+        req, bt, idx, pid, starts, MB = _ws_case(seed)
+        got = oracle.convert_indices_workspace(req, bt, idx, 36, pid, starts)
+        plain = oracle.convert_indices(req, bt, idx, 36)
+        dec = pid < 0
+        assert np.array_equal(got[dec], plain[dec])
+
+
+def test_workspace_conversion_offsets_prefill_tokens_by_their_start():
+    for seed in range(4):
+        req, bt, idx, pid, starts, MB = _ws_case(seed)
+        got = oracle.convert_indices_workspace(req, bt, idx, 36, pid, starts)
+        for t in range(idx.shape[0]):
+            if pid[t] < 0:
+                continue
+            valid = (idx[t] >= 0) & (idx[t] < MB * 64) & (pid[t] < len(starts))
+            assert (got[t][~valid] == -1).all()
+            assert (got[t][valid] - idx[t][valid] == (starts[pid[t]] if pid[t] < len(starts) else 0)).all()
+
+
+def test_workspace_conversion_page_example():
+    g = _golden("prefill_workspace_example.json")
+    cases = g["index_cases"]
+    T = len(cases)
+    pid = np.array([c[0] for c in cases], dtype=np.int32)
+    idx = np.array([[c[1]] for c in cases], dtype=np.int32)
+    got = oracle.convert_indices_workspace(np.zeros(T, np.int32), np.zeros((1, 4), np.int32), idx, 8, pid,
+                                           np.array(g["chunked_starts"], dtype=np.int32))
+    assert [int(v) for v in got[:, 0]] == [c[2] for c in cases]
+
+
+def _torch_bf16_bits(v):
+    return int(torch.tensor([v], dtype=torch.float32).to(torch.bfloat16).view(torch.int16)[0]) & 0xFFFF
+
+
+def test_bf16_rounding_matches_torch_on_float32_values():
+    rng = np.random.default_rng(9)
+    vals = list(rng.standard_normal(2000) * np.exp(rng.uniform(-60, 60, 2000)))
+    bits = rng.integers(0, 1 << 32, 3000, dtype=np.uint64).astype(np.uint32)
+    f = bits.view(np.float32)
+    vals += [float(x) for x in f if np.isfinite(x) and abs(x) < 3.3e38]
+    # exact ties: a bf16 value plus half its last place, both parities, and subnormal ties
+    for b in range(0x3F80, 0x3F90):
+        vals.append(float(np.array([(b << 16) | 0x8000], dtype=np.uint32).view(np.float32)[0]))
+    vals += [1.5 * 2.0 ** -133, 2.5 * 2.0 ** -133, -1.5 * 2.0 ** -133, 2.0 ** -140, 0.0, -0.0, 3.3e38]
+    for v in vals:
+        v32 = float(np.float32(v))
+        assert oracle.bf16_rne(v32) == _torch_bf16_bits(v32), v32
+
+
+def test_bf16_rounding_of_values_between_float32_neighbours():
+    # values with more significant bits than float32 holds: rounded once, so a
+    # value just above a bf16 midpoint goes up even when float32 would land on the tie
+    assert oracle.bf16_rne(1.0 + 2.0 ** -8 + 2.0 ** -30) == 0x3F81
+    assert oracle.bf16_rne(1.0 + 2.0 ** -8 - 2.0 ** -30) == 0x3F80
+    assert oracle.bf16_rne(1.0 + 2.0 ** -8) == 0x3F80            # tie: even
+    assert oracle.bf16_rne(1.0 + 3 * 2.0 ** -8) == 0x3F82        # tie: even
+    assert oracle.bf16_rne(-(1.0 + 2.0 ** -8 + 2.0 ** -30)) == 0xBF81
+    assert oracle.bf16_rne(2.0 ** 128) == 0x7F80                 # past the largest finite: infinity
+
+
+def _pow2_scaled_rows(rng, n):
+    rows = np.empty((n, 656), dtype=np.uint8)
+    codes = rng.integers(0, 256, (n, 512)).astype(np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0x38                         # no NaN codes
+    rows[:, :512] = codes
+    scales = (2.0 ** rng.integers(-8, 8, (n, 4))).astype("<f4")
+    rows[:, 512:528] = scales.view(np.uint8).reshape(n, 16)
+    rows[:, 528:] = W.normal_bf16(torch.Generator().manual_seed(int(rng.integers(1 << 30))),
+                                  (n, 64)).astype("<u2").view(np.uint8).reshape(n, 128)
+    return rows
+
+
+def test_upconvert_is_exact_when_every_value_is_a_bf16_value():
+    # e4m3 values have 4 significant bits; times a power of two they are bf16 values
+    rng = np.random.default_rng(11)
+    rows = _pow2_scaled_rows(rng, 128)
+    cache = rows.reshape(2, 64, 656)
+    bt = np.array([[1, 0]], dtype=np.int32)
+    ws = oracle.gather_upconvert(cache, bt, [128], [0], 128)
+    want = oracle.decode_fp8_rows(np.concatenate([rows[64:], rows[:64]]))
+    got = W.bf16_bits_to_f32(ws).astype(np.float64)
+    assert np.array_equal(got, want)
+
+
+def test_upconvert_rounds_each_value_to_the_nearest_bf16():
+    cache = W.random_fp8_cache(3, 99, 2)
+    bt = np.array([[0, 1]], dtype=np.int32)
+    ws = oracle.gather_upconvert(cache, bt, [128], [0], 128)
+    exact = oracle.decode_fp8_rows(cache.reshape(128, 656))[:, :512]
+    got_bits = ws[:, :512].astype(np.int64)
+    got = W.bf16_bits_to_f32(ws[:, :512]).astype(np.float64)
+    # neighbours on the bf16 grid (same sign): one step toward and away from zero
+    up = W.bf16_bits_to_f32((got_bits + 1).astype(np.uint16)).astype(np.float64)
+    dn = W.bf16_bits_to_f32(np.where((got_bits & 0x7FFF) == 0, got_bits ^ 0x8000, got_bits - 1)
+                            .astype(np.uint16)).astype(np.float64)
+    err = np.abs(exact - got)
+    assert (err <= np.abs(exact - up)).all() and (err <= np.abs(exact - dn)).all()
+    tie = (err == np.abs(exact - up)) | (err == np.abs(exact - dn))
+    assert ((got_bits[tie] & 1) == 0).all()                       # ties to even
+    assert np.array_equal(ws[:, 512:], cache.reshape(128, 656)[:, 528:].copy().view("<u2"))
+
+
+def test_upconvert_places_each_request_position_at_its_workspace_row():
+    # rows written by a paged-cache simulation; the RoPE bits carry (request, position)
+    from tests.paged_writer import PagedCache
+    rng = np.random.default_rng(13)
+    lens = [70, 5, 130]
+    pc = PagedCache(rng, lens, extra_blocks=2)
+    cache = np.zeros((pc.num_blocks, 64, 656), dtype=np.uint8)
+    for (r, pos), (blk, off) in pc.where.items():
+        tag = np.array([r, pos], dtype="<u2").view(np.uint8)
+        cache[blk, off, 528:532] = tag
+        cache[blk, off, 512:516] = np.array([1.0], dtype="<f4").view(np.uint8)
+    bt = pc.block_table
+    starts = np.array([3, 80, 90], dtype=np.int32)
+    ws = oracle.gather_upconvert(cache, bt, lens, starts, 230)
+    for r, n in enumerate(lens):
+        for pos in range(n):
+            assert list(ws[starts[r] + pos, 512:514]) == [r, pos]
+    # rows that no request covers stay zero
+    assert (ws[:3] == 0).all() and (ws[73:80] == 0).all() and (ws[220:] == 0).all()
+
+
+def test_upconvert_bad_table_entry_gives_zero_rows_and_skips_rows_past_the_workspace():
+    rng = np.random.default_rng(17)
+    cache = _pow2_scaled_rows(rng, 128).reshape(2, 64, 656)
+    bt = np.array([[0, 7]], dtype=np.int32)                       # block 7 does not exist
+    ws = np.full((100, 576), 0x1234, dtype=np.uint16)
+    oracle.gather_upconvert(cache, bt, [128], [0], 100, workspace=ws)
+    assert (ws[64:100] == 0).all()                                 # positions 64..99: bad block
+    assert not (ws[:64] == 0x1234).any()
+
+
+def _pow2_mixed_batch(seed, p_invalid=0.1):
+    w = W.mixed_batch(seed, 16, 96, decode_ctx=[150, 300], prefill_ctx=[200, 90, 260],
+                      prefill_queries=[5, 3, 4], p_invalid=p_invalid)
+    rng = np.random.default_rng(seed)
+    w.cache = _pow2_scaled_rows(rng, w.cache.shape[0] * 64).reshape(w.cache.shape)
+    return w
+
+
+def test_separate_prefill_equals_the_fused_path_when_rows_are_bf16_values():
+    for seed, max_rows in ((1, 300), (2, 1000)):
+        w = _pow2_mixed_batch(seed)
+        o_f, l_f = oracle.attention(oracle.FP8_CACHE, w.q, w.cache, w.block_table, w.req_id_per_token,
+                                    w.topk_indices, w.sm_scale)
+        o_s, l_s = oracle.separate_prefill_attention(w.q, w.cache, w.block_table, w.req_id_per_token,
+                                                     w.topk_indices, w.sm_scale, 2, w.ctx_lens, max_rows)
+        assert np.array_equal(o_s, o_f) and np.array_equal(l_s, l_f)
+
+
+def test_separate_prefill_differs_from_the_fused_path_by_bf16_rounding_only():
+    w = W.mixed_batch(4, 16, 96, decode_ctx=[150], prefill_ctx=[200, 260], prefill_queries=[4, 6])
+    o_f, l_f = oracle.attention(oracle.FP8_CACHE, w.q, w.cache, w.block_table, w.req_id_per_token,
+                                w.topk_indices, w.sm_scale)
+    o_s, l_s = oracle.separate_prefill_attention(w.q, w.cache, w.block_table, w.req_id_per_token,
+                                                 w.topk_indices, w.sm_scale, 1, w.ctx_lens, 300)
+    assert np.array_equal(o_s[0], o_f[0]) and np.array_equal(l_s[0], l_f[0])     # the decode token
+    rel = np.linalg.norm(o_s - o_f) / np.linalg.norm(o_f)
+    assert 0 < rel < 4e-3 and np.abs(l_s - l_f).max() < 1e-2
