@@ -416,15 +416,17 @@ void attn_kernel(const KParams p)
             }
         }
     };
-    // PV, part 2: O^T += V^T P^T (hi terms) over this wave's dims, branch-free.
-    auto pv_main = [&](const uint2 *vf) __attribute__((always_inline)) {
+    // PV, part 2: O^T += V^T P^T (hi terms) over dim blocks [db0, db1) of this
+    // wave's dims, branch-free; pv: the P^T operands (pv_load).
+    auto pv_load = [&](bf16x8 *pv) __attribute__((always_inline)) {
         const int G = dim0 >> 7;
-        bf16x8 pv[NHH];
 #pragma unroll
         for (int hb = 0; hb < NHH; ++hb)
             pv[hb] = p_lds[(G * NHH + hb) * 64 + lane];
+    };
+    auto pv_part = [&](const uint2 *vf, const bf16x8 *pv, int db0, int db1) __attribute__((always_inline)) {
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
+        for (int db = db0; db < db1; ++db) {
             const bf16x8 a = e4m3x8_to_bf16x8(vf[db]);
 #pragma unroll
             for (int hb = 0; hb < NHH; ++hb)
@@ -434,8 +436,10 @@ void attn_kernel(const KParams p)
 
     // One tile: S^T = K q^T, online softmax, O^T += V^T P^T. exact: P enters PV
     // as hi + lo bf16 terms (wave-uniform). Pipelined: the tile stops after
-    // publishing P^T; its PV runs in the next phase.
-    auto tile = [&](const uint8_t *buf, int n_tile, bool exact) __attribute__((always_inline)) {
+    // publishing P^T; its PV runs in the next phase. mid(gi) runs right after
+    // the QK^T MFMAs of column group gi are issued (fp8), so independent work
+    // (the pending PV) can fill the wait for their results.
+    auto tile = [&](const uint8_t *buf, int n_tile, bool exact, auto &&mid) __attribute__((always_inline)) {
         // per-lane LDS offsets inside the tile buffer
         const int off_k = n16 * RS;                      // K rows 16*rb + n16 (+ rb * RBB)
         const int off_sc = (4 * g) * RS;                 // accumulator rows 16*rb + 4g + i
@@ -488,6 +492,7 @@ void attn_kernel(const KParams p)
                 for (int rb = 0; rb < RB; ++rb)
                     part[rb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
                         kf[rb], ql[gi], part[rb], 0, 0, 0, 127, 0, qsl[gi]);
+                mid(gi);
 #pragma unroll
                 for (int rb = 0; rb < RB; ++rb)
                     acc[rb] += sc[gi][rb] * part[rb];
@@ -517,6 +522,8 @@ void attn_kernel(const KParams p)
         }
 
         // ---- add the other column half's partial S^T (same lane slots)
+        if constexpr (kPipe)
+            __builtin_amdgcn_s_setprio(0);
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb)
             xchg[(wave * RB + rb) * 64 + lane] = acc[rb];
@@ -861,6 +868,12 @@ void attn_kernel(const KParams p)
                 // every wave's pieces of tile `it` landed; tile it-1 is done (its PV
                 // only needs registers and the published P^T)
                 __syncthreads();
+                // The copy issue, the pending PV and QK^T run at raised wave
+                // priority: the SIMD's other wave (another workgroup, usually in
+                // its softmax phase) fills the gaps of this MFMA stream instead of
+                // competing with it.
+                if constexpr (kPipe)
+                    __builtin_amdgcn_s_setprio(1);
                 int rflag[NHH];
                 float ralpha[NHH];
                 if constexpr (kPipe) {
@@ -876,10 +889,19 @@ void attn_kernel(const KParams p)
                                   ring + (nt % C::kNBuf) * C::kBufBytes, wave, lane);
                 }
                 if constexpr (kPipe) {
+                    // PV of the previous tile, half of its dims after each
+                    // column group's QK^T MFMAs
                     pv_pre(vf8_pend, exact_p, rflag, ralpha);
-                    pv_main(vf8_pend);
+                    bf16x8 pvp[NHH];
+                    pv_load(pvp);
+                    tile(ring + (it % C::kNBuf) * C::kBufBytes, min(kTile, n_valid - it * kTile), exact_p,
+                         [&](int gi) __attribute__((always_inline)) {
+                             pv_part(vf8_pend, pvp, gi * (DB / 2), (gi + 1) * (DB / 2));
+                         });
+                } else {
+                    tile(ring + (it % C::kNBuf) * C::kBufBytes, min(kTile, n_valid - it * kTile), exact_p,
+                         [](int) {});
                 }
-                tile(ring + (it % C::kNBuf) * C::kBufBytes, min(kTile, n_valid - it * kTile), exact_p);
             }
             if constexpr (kPipe) {
                 __syncthreads();     // P^T of the last tile is visible
@@ -891,7 +913,9 @@ void attn_kernel(const KParams p)
                     ralpha[hb] = alpha_lds[hb * 16 + n16];
                 }
                 pv_pre(vf8_pend, exact_p, rflag, ralpha);
-                pv_main(vf8_pend);
+                bf16x8 pvp[NHH];
+                pv_load(pvp);
+                pv_part(vf8_pend, pvp, 0, DB);
             }
             __syncthreads();     // ring, exchanges and slot list are free for the next round
         }
