@@ -110,6 +110,42 @@ def cache_writer_bench(torch, smla, dev, stream, flush, sink, steps: int):
     return res
 
 
+def upconvert_bench(torch, smla, W, dev, stream, flush, sink, steps: int):
+    """The separate-prefill mode's gather-and-upconvert (smla_gather_upconvert_fp8)
+    over config 5's two prefill contexts (131072 and 65536 positions, 196608 rows,
+    one launch), cold cache. Algorithmic bytes per row: 656 read + 1152 written;
+    plus one 4-byte block-table entry per 64 rows."""
+    lens = np.array([131072, 65536], dtype=np.int32)
+    bt, nb = W.allocate_block_table(np.random.default_rng(70), lens)
+    g = torch.Generator(device="cpu").manual_seed(70)
+    # contents do not change the work: random bytes, scales forced finite and small
+    cache = torch.randint(0, 256, (nb, 64, 656), dtype=torch.uint8, generator=g)
+    cache[:, :, 512:528] = torch.tensor([0, 0, 128, 60] * 4, dtype=torch.uint8)     # 1/64 as float32
+    cache = cache.to(dev)
+    rows = int(lens.sum())
+    ws = torch.empty((rows, 576), dtype=torch.bfloat16, device=dev)
+    bt_d = torch.from_numpy(bt).to(dev)
+    lens_d = torch.from_numpy(lens).to(dev)
+    starts_d = torch.tensor([0, int(lens[0])], dtype=torch.int32, device=dev)
+    for _ in range(3):
+        smla.smla_gather_upconvert_fp8(cache, bt_d, lens_d, starts_d, int(lens.max()), ws, stream=stream)
+    e0 = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    e1 = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    for i in range(steps):
+        torch.amax(flush, 0, out=sink)
+        e0[i].record(stream)
+        smla.smla_gather_upconvert_fp8(cache, bt_d, lens_d, starts_d, int(lens.max()), ws, stream=stream)
+        e1[i].record(stream)
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) for a, b in zip(e0, e1)]))
+    nbytes = rows * (656 + 1152) + (rows // 64) * 4
+    del cache, ws
+    return {"kernel": "upconvert_kernel", "rows": rows, "ms": ms, "algorithmic_bytes": nbytes,
+            "achieved_GBps": nbytes / (ms * 1e-3) / 1e9,
+            "frac_of_hbm_peak": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "workload": "config 5 prefill contexts: 131072 + 65536 positions, shuffled blocks"}
+
+
 def cpu_baseline(w, target_s: float = 10.0):
     """The oracle as it stands, on this host's cores: whole passes over the batch's
     tokens (in a fixed shuffled order) until about target_s of CPU work is done."""
@@ -312,6 +348,8 @@ def main():
         "device": props.name,
     }
     rec["cache_writer"] = cache_writer_bench(torch, smla, dev, stream, flush, sink, min(args.steps, 20))
+    rec["separate_prefill_upconvert"] = upconvert_bench(torch, smla, W, dev, stream, flush, sink,
+                                                        min(args.steps, 20))
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(rec), flush=True)

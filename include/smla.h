@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define SMLA_ABI_VERSION 3
+#define SMLA_ABI_VERSION 4
 #define SMLA_BLOCK_SIZE 64
 #define SMLA_HEAD_DIM_QK 576
 #define SMLA_HEAD_DIM_V 512
@@ -72,7 +72,14 @@ typedef enum smla_status {
        The workspace is required even when the list is not split (one part).
        smla_merge_partials then finishes the result; it also merges parts that
        were computed by separate calls, e.g. on different devices. */
-#define SMLA_FLAG_ALL SMLA_FLAG_PARTIALS_ONLY
+#define SMLA_FLAG_SLOT_INDICES 0x2u
+    /* topk_indices already hold cache slots (row numbers of kv_cache seen as
+       [num_blocks * 64] rows; -1 or any value outside [0, num_blocks * 64) is an
+       invalid position), e.g. the output of smla_convert_indices or the
+       workspace rows of smla_convert_indices_workspace. block_table and
+       req_id_per_token are not read and may be NULL; num_reqs and
+       max_blocks_per_req are ignored. */
+#define SMLA_FLAG_ALL (SMLA_FLAG_PARTIALS_ONLY | SMLA_FLAG_SLOT_INDICES)
 
 /* Tuning options (host struct, may be NULL for defaults). */
 typedef struct smla_options {
@@ -171,6 +178,77 @@ smla_status smla_convert_indices(const int32_t *req_id_per_token, const int32_t 
                                  int32_t num_tokens, int32_t topk, int32_t num_reqs,
                                  int32_t max_blocks_per_req, int64_t num_blocks,
                                  hipStream_t stream);
+
+/* ---- separate-prefill mode of an fp8_ds_mla cache [flashmla_sparse.py page as
+ * changed for this mode: _build_fp8_separate_prefill_decode,
+ * _forward_fp8_kv_separate_prefill_decode, get_prefill_workspace_size]. Decode
+ * tokens attend over the fp8 cache (smla_decode_fp8); prefill requests are cut
+ * into chunks whose context fits a bf16 workspace, each chunk's context rows are
+ * upconverted into the workspace (smla_gather_upconvert_fp8) and its tokens run
+ * smla_prefill_bf16 over the workspace with SMLA_FLAG_SLOT_INDICES, their indices
+ * converted to workspace rows (smla_convert_indices_workspace). */
+
+/* Workspace rows the page reserves for a model: 5 * max_model_len (bf16 rows
+ * of 576 values, 1152 bytes each). Host arithmetic; 0 for a negative length. */
+int64_t smla_prefill_workspace_rows(int64_t max_model_len);
+
+/* Chunk plan of the prefill requests (host arithmetic, host pointers): requests
+ * are taken in order and a new chunk starts when the next request's length
+ * would take the chunk past max_rows workspace rows (the page's worked example:
+ * lengths [10, 15, 20, 5] give chunks [0, 2) and [2, 4) and starts
+ * [0, 10, 0, 20] for any max_rows from 25 to 34).
+ *   seq_lens          host int32 [num_prefills], context + query length of each
+ *                     prefill request, each in [0, max_rows]
+ *   chunk_ends        host int32 [num_prefills]: chunk c covers requests
+ *                     [chunk_ends[c-1], chunk_ends[c]) (chunk_ends[-1] = 0)
+ *   workspace_starts  host int32 [num_prefills]: each request's first workspace
+ *                     row, counted from its chunk's start
+ *   num_chunks        host out
+ * Errors: SMLA_ERR_NULL, SMLA_ERR_SHAPE (a negative count or length, a request
+ * longer than max_rows). num_prefills == 0 gives 0 chunks. */
+smla_status smla_plan_prefill_chunks(const int32_t *seq_lens, int32_t num_prefills, int64_t max_rows,
+                                     int32_t *chunk_ends, int32_t *workspace_starts, int32_t *num_chunks);
+
+/* Index conversion with a prefill workspace [flashmla_sparse.py page,
+ * _convert_req_index_to_global_index_kernel with HAS_PREFILL]: token t with
+ * prefill_request_id[t] = r >= 0 maps a valid index i to workspace_starts[r] + i
+ * (a workspace row); a token with r < 0 converts exactly as smla_convert_indices.
+ * Either way an index is invalid (-1) when negative or when i / 64 >=
+ * max_blocks_per_req; r >= num_prefills also gives -1.
+ *   prefill_request_id  int32 [num_tokens], -1 for decode tokens
+ *   workspace_starts    int32 [num_prefills] (chunk-local, as planned above);
+ *                       may be NULL when num_prefills == 0
+ * Other arguments as for smla_convert_indices. num_tokens == 0 is a no-op. */
+smla_status smla_convert_indices_workspace(const int32_t *req_id_per_token, const int32_t *block_table,
+                                           const int32_t *topk_indices, const int32_t *prefill_request_id,
+                                           const int32_t *workspace_starts, int32_t *out,
+                                           int32_t num_tokens, int32_t topk, int32_t num_reqs,
+                                           int32_t max_blocks_per_req, int64_t num_blocks,
+                                           int32_t num_prefills, hipStream_t stream);
+
+/* Gather the context rows of a chunk of prefill requests from an fp8_ds_mla
+ * cache and upconvert them into a bf16 workspace [flashmla_sparse.py page,
+ * _forward_fp8_kv_separate_prefill_decode: cp_gather_and_upconvert_fp8_kv_cache]:
+ * for request b < batch and position p < seq_lens[b], workspace row
+ * workspace_starts[b] + p receives the cache row at slot
+ * block_table[b, p / 64] * 64 + p % 64: latent value i is e4m3 byte i times
+ * scale i / 128, rounded once to the nearest bf16 (ties to even); the 64 RoPE
+ * values are copied. A position whose block lies outside the table, or whose
+ * table entry lies outside [0, num_blocks), gives a row of zeros.
+ *   kv_cache          uint8 [num_blocks, 64, 656], 16-B aligned
+ *   block_table       int32 [batch, max_blocks_per_req]: the chunk's requests' rows
+ *   seq_lens          int32 [batch], each <= max_seq_len
+ *   workspace_starts  int32 [batch]
+ *   max_seq_len       host bound on seq_lens (positions past it are not read)
+ *   workspace         bf16 [workspace_rows, 576], 16-B aligned; rows outside
+ *                     [0, workspace_rows) are never written, rows no request
+ *                     covers keep their contents
+ * Errors: SMLA_ERR_NULL, SMLA_ERR_SHAPE, SMLA_ERR_ALIGN, SMLA_ERR_HIP. batch == 0
+ * or max_seq_len == 0 is a no-op. */
+smla_status smla_gather_upconvert_fp8(const void *kv_cache, int64_t num_blocks, const int32_t *block_table,
+                                      int32_t max_blocks_per_req, const int32_t *seq_lens,
+                                      const int32_t *workspace_starts, int32_t batch, int32_t max_seq_len,
+                                      void *workspace, int64_t workspace_rows, hipStream_t stream);
 
 /* Sparse MLA forward over a bf16 paged cache [flashmla_sparse.py page,
  * _bf16_flash_mla_kernel / flash_mla_sparse_prefill].

@@ -125,12 +125,21 @@ smla_status attention_entry(CacheFormat fmt, const void *q, const void *kv_cache
         return SMLA_ERR_ARG;
     if ((st = check_sizes(num_tokens, h_q, topk)) != SMLA_OK)
         return st;
+    const bool slot_in = options && (options->flags & SMLA_FLAG_SLOT_INDICES);
+    if (slot_in) {
+        // indices are cache slots: no request or table is read
+        block_table = nullptr;
+        req_id_per_token = nullptr;
+        num_reqs = 1;
+        max_blocks_per_req = 1;
+    }
     if ((st = check_pool(num_reqs, max_blocks_per_req, num_blocks)) != SMLA_OK)
         return st;
     if (num_tokens == 0)
         return SMLA_OK;
     const bool partials_only = options && (options->flags & SMLA_FLAG_PARTIALS_ONLY);
-    if (!q || !kv_cache || !block_table || !req_id_per_token || !topk_indices || (!out && !partials_only))
+    if (!q || !kv_cache || (!slot_in && (!block_table || !req_id_per_token)) || !topk_indices ||
+        (!out && !partials_only))
         return SMLA_ERR_NULL;
     if (!aligned(q, 16) || !aligned(kv_cache, 16) || !aligned(out, 16))
         return SMLA_ERR_ALIGN;
@@ -163,6 +172,7 @@ smla_status attention_entry(CacheFormat fmt, const void *q, const void *kv_cache
     a.num_reqs = num_reqs;
     a.max_blocks = max_blocks_per_req;
     a.num_blocks = num_blocks;
+    a.slot_indices = slot_in;
     return launch_attention(fmt, a, plan, partials_only, stream) == hipSuccess
                ? SMLA_OK
                : SMLA_ERR_HIP;
@@ -280,6 +290,90 @@ smla_status smla_concat_and_cache_mla(const void *k_c_normed, const void *k_pe,
     return smla::launch_cache_write(cache_format == SMLA_CACHE_FP8_DS_MLA ? smla::kCacheFp8 : smla::kCacheBf16,
                                     k_c_normed, k_pe, slot_mapping, kv_cache, num_tokens,
                                     num_blocks * smla::kBlock, stream) == hipSuccess
+               ? SMLA_OK
+               : SMLA_ERR_HIP;
+}
+
+int64_t smla_prefill_workspace_rows(int64_t max_model_len)
+{
+    return max_model_len > 0 && max_model_len <= INT64_MAX / 5 ? 5 * max_model_len : 0;
+}
+
+smla_status smla_plan_prefill_chunks(const int32_t *seq_lens, int32_t num_prefills, int64_t max_rows,
+                                     int32_t *chunk_ends, int32_t *workspace_starts, int32_t *num_chunks)
+{
+    if (num_chunks == nullptr)
+        return SMLA_ERR_NULL;
+    if (num_prefills < 0 || max_rows < 0 || max_rows > INT32_MAX)
+        return SMLA_ERR_SHAPE;
+    if (num_prefills > 0 && (!seq_lens || !chunk_ends || !workspace_starts))
+        return SMLA_ERR_NULL;
+    for (int32_t r = 0; r < num_prefills; ++r)
+        if (seq_lens[r] < 0 || seq_lens[r] > max_rows)
+            return SMLA_ERR_SHAPE;
+    // a request starts a new chunk when it would not fit the current one
+    int32_t n = 0;
+    int64_t used = 0;
+    for (int32_t r = 0; r < num_prefills; ++r) {
+        if (r > 0 && used + seq_lens[r] > max_rows) {
+            chunk_ends[n++] = r;
+            used = 0;
+        }
+        workspace_starts[r] = (int32_t)used;
+        used += seq_lens[r];
+    }
+    if (num_prefills > 0)
+        chunk_ends[n++] = num_prefills;
+    *num_chunks = n;
+    return SMLA_OK;
+}
+
+smla_status smla_convert_indices_workspace(const int32_t *req_id_per_token, const int32_t *block_table,
+                                           const int32_t *topk_indices, const int32_t *prefill_request_id,
+                                           const int32_t *workspace_starts, int32_t *out,
+                                           int32_t num_tokens, int32_t topk, int32_t num_reqs,
+                                           int32_t max_blocks_per_req, int64_t num_blocks,
+                                           int32_t num_prefills, hipStream_t stream)
+{
+    if (num_tokens < 0 || topk < 1 || topk > SMLA_MAX_TOPK || num_prefills < 0)
+        return SMLA_ERR_SHAPE;
+    smla_status st = smla::check_pool(num_reqs, max_blocks_per_req, num_blocks);
+    if (st != SMLA_OK)
+        return st;
+    if (num_tokens == 0)
+        return SMLA_OK;
+    if (!req_id_per_token || !block_table || !topk_indices || !prefill_request_id || !out ||
+        (num_prefills > 0 && !workspace_starts))
+        return SMLA_ERR_NULL;
+    if (!smla::aligned(req_id_per_token, 4) || !smla::aligned(block_table, 4) ||
+        !smla::aligned(topk_indices, 4) || !smla::aligned(prefill_request_id, 4) ||
+        !smla::aligned(workspace_starts, 4) || !smla::aligned(out, 4))
+        return SMLA_ERR_ALIGN;
+    return smla::launch_convert_ws(req_id_per_token, block_table, topk_indices, prefill_request_id,
+                                   workspace_starts, out, num_tokens, topk, num_reqs, max_blocks_per_req,
+                                   num_blocks, num_prefills, stream) == hipSuccess
+               ? SMLA_OK
+               : SMLA_ERR_HIP;
+}
+
+smla_status smla_gather_upconvert_fp8(const void *kv_cache, int64_t num_blocks, const int32_t *block_table,
+                                      int32_t max_blocks_per_req, const int32_t *seq_lens,
+                                      const int32_t *workspace_starts, int32_t batch, int32_t max_seq_len,
+                                      void *workspace, int64_t workspace_rows, hipStream_t stream)
+{
+    if (batch < 0 || max_seq_len < 0 || workspace_rows < 0 || max_blocks_per_req < 1 || num_blocks < 1 ||
+        num_blocks > (int64_t)INT32_MAX / smla::kBlock)
+        return SMLA_ERR_SHAPE;
+    if (batch == 0 || max_seq_len == 0)
+        return SMLA_OK;
+    if (!kv_cache || !block_table || !seq_lens || !workspace_starts || !workspace)
+        return SMLA_ERR_NULL;
+    if (!smla::aligned(kv_cache, 16) || !smla::aligned(workspace, 16) || !smla::aligned(block_table, 4) ||
+        !smla::aligned(seq_lens, 4) || !smla::aligned(workspace_starts, 4))
+        return SMLA_ERR_ALIGN;
+    return smla::launch_upconvert(kv_cache, num_blocks, block_table, max_blocks_per_req, seq_lens,
+                                  workspace_starts, batch, max_seq_len, workspace, workspace_rows,
+                                  stream) == hipSuccess
                ? SMLA_OK
                : SMLA_ERR_HIP;
 }

@@ -56,12 +56,26 @@ struct AttnArgs {
     float sm_scale;
     int num_tokens, h_q, topk_len, num_reqs, max_blocks;
     int64_t num_blocks;
+    bool slot_indices;       // topk holds cache slots (no request / table lookup)
 };
 
 // Kernel launchers (smla_kernels.hip). Return hipSuccess or the launch error.
 hipError_t launch_convert(const int32_t *req_id, const int32_t *block_table, const int32_t *topk,
                           int32_t *out, int num_tokens, int topk_len, int num_reqs,
                           int max_blocks, int64_t num_blocks, hipStream_t stream);
+
+// convert_kernel with a prefill workspace: tokens with prefill_request_id >= 0
+// map valid indices to workspace_starts[id] + index.
+hipError_t launch_convert_ws(const int32_t *req_id, const int32_t *block_table, const int32_t *topk,
+                             const int32_t *prefill_rid, const int32_t *ws_starts, int32_t *out,
+                             int num_tokens, int topk_len, int num_reqs, int max_blocks, int64_t num_blocks,
+                             int num_prefills, hipStream_t stream);
+
+// upconvert_kernel: context rows of `batch` prefill requests from an fp8_ds_mla
+// cache into a bf16 workspace.
+hipError_t launch_upconvert(const void *cache, int64_t num_blocks, const int32_t *block_table, int max_blocks,
+                            const int32_t *seq_lens, const int32_t *ws_starts, int batch, int max_seq_len,
+                            void *workspace, int64_t workspace_rows, hipStream_t stream);
 
 // The attention kernel and, when the plan splits the top-k lists (and
 // partials_only is false), the merge kernel after it on the same stream.

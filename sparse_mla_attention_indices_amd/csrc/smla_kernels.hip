@@ -156,6 +156,7 @@ struct KParams {
     int64_t NB;
     int S, split_len, HB;
     int partials;         // write fp32 partials (O / l) and lse instead of the bf16 output
+    int slot_in;          // topk holds cache slots: no request id, no block-table lookup
 };
 
 __device__ __forceinline__ int convert_slot(int req, int idx, const int32_t *__restrict__ bt,
@@ -194,6 +195,12 @@ __device__ __forceinline__ int finish_slot(int base, int req, int idx, int num_r
     return slot_position_ok(req, idx, num_reqs, max_blocks) && base >= 0 && (int64_t)base < num_blocks
                ? base * kBlock + (idx & (kBlock - 1))
                : -1;
+}
+
+// A position that already holds a cache slot: valid when inside the cache.
+__device__ __forceinline__ int given_slot(int idx, int64_t num_blocks)
+{
+    return idx >= 0 && (int64_t)idx < num_blocks * kBlock ? idx : -1;
 }
 
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b)
@@ -355,7 +362,7 @@ void attn_kernel(const KParams p)
     const int head = wg_head0 + 16 * hh + n16;      // this lane's head
     const float c2 = p.log2e_scale;
     const int32_t *topk_row = p.topk + (size_t)t * p.K;
-    const int req = p.req_id[t];
+    const int req = p.slot_in ? 0 : p.req_id[t];
 
     // q^T B operands. bf16 cache: lane (head, group g) holds 8 columns per
     // k-step of v_mfma_f32_16x16x32_bf16: latent 256*dh + 32k + 8g (k < 8), RoPE
@@ -709,7 +716,7 @@ void attn_kernel(const KParams p)
         int slotv[kPer];    // block-table entries until q is done, then slots
 #pragma unroll
         for (int j = 0; j < kPer; ++j)
-            slotv[j] = lookup_block(req, idxv[j], p.bt, p.R, p.MB);
+            slotv[j] = p.slot_in ? 0 : lookup_block(req, idxv[j], p.bt, p.R, p.MB);
         {
             // each q value is used here, so the compiler waits for these loads
             // before the tile loop rather than inside it (it cannot see the
@@ -779,7 +786,7 @@ void attn_kernel(const KParams p)
         for (int j = 0; j < kPer; ++j) {
             if constexpr (FMT == kCacheFp8)
                 asm volatile("" : "+v"(slotv[j]) : "v"(ql[0]), "v"(ql[1]));
-            slotv[j] = finish_slot(slotv[j], req, idxv[j], p.R, p.MB, p.NB);
+            slotv[j] = p.slot_in ? given_slot(idxv[j], p.NB) : finish_slot(slotv[j], req, idxv[j], p.R, p.MB, p.NB);
         }
 #pragma unroll
         for (int k = 0; k < 16; ++k)
@@ -805,8 +812,9 @@ void attn_kernel(const KParams p)
                 }
 #pragma unroll
                 for (int j = 0; j < kPer; ++j)
-                    slotv[j] = finish_slot(lookup_block(req, idxv[j], p.bt, p.R, p.MB), req, idxv[j],
-                                           p.R, p.MB, p.NB);
+                    slotv[j] = p.slot_in ? given_slot(idxv[j], p.NB)
+                                         : finish_slot(lookup_block(req, idxv[j], p.bt, p.R, p.MB), req,
+                                                       idxv[j], p.R, p.MB, p.NB);
             }
             if (write_phys) {
 #pragma unroll
@@ -1134,6 +1142,94 @@ __global__ __launch_bounds__(256) void convert_kernel(const int32_t *__restrict_
     }
 }
 
+// Index conversion with a prefill workspace [flashmla_sparse.py page,
+// _convert_req_index_to_global_index_kernel, HAS_PREFILL branch]: a token with
+// a prefill request id r >= 0 maps a valid index to workspace_starts[r] + index
+// (no block-table read); other tokens convert as convert_kernel.
+__global__ __launch_bounds__(256) void convert_ws_kernel(const int32_t *__restrict__ req_id,
+                                                         const int32_t *__restrict__ bt,
+                                                         const int32_t *__restrict__ topk,
+                                                         const int32_t *__restrict__ prefill_rid,
+                                                         const int32_t *__restrict__ ws_starts,
+                                                         int32_t *__restrict__ out, int64_t total, int topk_len,
+                                                         int num_reqs, int max_blocks, int64_t num_blocks,
+                                                         int num_prefills)
+{
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total;
+         i += (int64_t)gridDim.x * 256) {
+        const int t = (int)(i / topk_len);
+        const int r = prefill_rid[t];
+        const int idx = topk[i];
+        if (r < 0)
+            out[i] = convert_slot(req_id[t], idx, bt, num_reqs, max_blocks, num_blocks);
+        else
+            out[i] = r < num_prefills && idx >= 0 && (idx >> 6) < max_blocks ? ws_starts[r] + idx : -1;
+    }
+}
+
+// e4m3 x scale rounded once to the nearest bf16, ties to even. The float32
+// product p and its exact residual e = fma(x, s, -p) (x has 4 significant
+// bits, so x * s is p + e exactly while p is a normal float) decide the one
+// case where rounding p alone could differ: p exactly halfway between two bf16
+// values, where the residual's sign says which side the true product is on.
+__device__ __forceinline__ uint32_t bf16_of_product(float x, float sc)
+{
+    const float pr = x * sc;
+    const float e = fmaf(x, sc, -pr);
+    const uint32_t u = __float_as_uint(pr);
+    uint32_t r = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;        // nearest, ties to even
+    if ((u & 0xFFFFu) == 0x8000u && e != 0.f)                   // p is a tie; the product is not
+        r = ((e > 0.f) == (pr > 0.f)) ? (u >> 16) + 1u : (u >> 16);
+    return r;
+}
+
+// Upconvert [flashmla_sparse.py page, _forward_fp8_kv_separate_prefill_decode:
+// cp_gather_and_upconvert_fp8_kv_cache]: one wave per (request, position);
+// lane l turns latent bytes 8l .. 8l + 7 (scale group l / 16) into 16 bytes of
+// bf16, lanes 0..7 copy the RoPE. A position past the table, or a table entry
+// outside the cache, writes zeros; rows outside the workspace are not written.
+__global__ __launch_bounds__(256) void upconvert_kernel(const uint8_t *__restrict__ cache, int64_t num_blocks,
+                                                        const int32_t *__restrict__ bt, int max_blocks,
+                                                        const int32_t *__restrict__ seq_lens,
+                                                        const int32_t *__restrict__ ws_starts,
+                                                        uint16_t *__restrict__ ws, int64_t ws_rows)
+{
+    const int b = blockIdx.y;
+    const int pos = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (pos >= seq_lens[b])
+        return;
+    const int64_t w = (int64_t)ws_starts[b] + pos;
+    if (w < 0 || w >= ws_rows)
+        return;
+    uint4 *dst = (uint4 *)(ws + w * kDqk);
+    const int blk = pos >> 6;
+    const int base = blk < max_blocks ? bt[(size_t)b * max_blocks + blk] : -1;
+    if (base < 0 || (int64_t)base >= num_blocks) {
+        dst[lane] = make_uint4(0u, 0u, 0u, 0u);
+        if (lane < 8)
+            dst[64 + lane] = make_uint4(0u, 0u, 0u, 0u);
+        return;
+    }
+    const uint8_t *row = cache + ((int64_t)base * kBlock + (pos & (kBlock - 1))) * kFp8RowBytes;
+    const uint2 v = *(const uint2 *)(row + 8 * lane);
+    const float sc = *(const float *)(row + 512 + 4 * (lane >> 4));
+    uint4 rope = make_uint4(0u, 0u, 0u, 0u);
+    if (lane < 8)
+        rope = *(const uint4 *)(row + 528 + 16 * lane);
+    const f32x2 x[4] = {__builtin_amdgcn_cvt_scalef32_pk_f32_fp8(v.x, 1.0f, false),
+                        __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(v.x, 1.0f, true),
+                        __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(v.y, 1.0f, false),
+                        __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(v.y, 1.0f, true)};
+    uint32_t h[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+        h[k] = bf16_of_product(x[k][0], sc) | (bf16_of_product(x[k][1], sc) << 16);
+    dst[lane] = make_uint4(h[0], h[1], h[2], h[3]);
+    if (lane < 8)
+        dst[64 + lane] = rope;
+}
+
 template <int FMT, int NHH>
 hipError_t launch_one(const KParams &p, hipStream_t stream)
 {
@@ -1166,6 +1262,30 @@ hipError_t launch_convert(const int32_t *req_id, const int32_t *block_table, con
     const int grid = (int)(blocks < 16384 ? blocks : 16384);
     hipLaunchKernelGGL(convert_kernel, dim3(grid), dim3(256), 0, stream, req_id, block_table, topk,
                        out, total, topk_len, num_reqs, max_blocks, num_blocks);
+    return hipGetLastError();
+}
+
+hipError_t launch_convert_ws(const int32_t *req_id, const int32_t *block_table, const int32_t *topk,
+                             const int32_t *prefill_rid, const int32_t *ws_starts, int32_t *out,
+                             int num_tokens, int topk_len, int num_reqs, int max_blocks, int64_t num_blocks,
+                             int num_prefills, hipStream_t stream)
+{
+    const int64_t total = (int64_t)num_tokens * topk_len;
+    const int64_t blocks = (total + 255) / 256;
+    const int grid = (int)(blocks < 16384 ? blocks : 16384);
+    hipLaunchKernelGGL(convert_ws_kernel, dim3(grid), dim3(256), 0, stream, req_id, block_table, topk,
+                       prefill_rid, ws_starts, out, total, topk_len, num_reqs, max_blocks, num_blocks,
+                       num_prefills);
+    return hipGetLastError();
+}
+
+hipError_t launch_upconvert(const void *cache, int64_t num_blocks, const int32_t *block_table, int max_blocks,
+                            const int32_t *seq_lens, const int32_t *ws_starts, int batch, int max_seq_len,
+                            void *workspace, int64_t workspace_rows, hipStream_t stream)
+{
+    const dim3 grid((unsigned)((max_seq_len + 3) / 4), (unsigned)batch);
+    hipLaunchKernelGGL(upconvert_kernel, grid, dim3(256), 0, stream, (const uint8_t *)cache, num_blocks,
+                       block_table, max_blocks, seq_lens, ws_starts, (uint16_t *)workspace, workspace_rows);
     return hipGetLastError();
 }
 
@@ -1226,6 +1346,7 @@ hipError_t launch_attention(CacheFormat fmt, const AttnArgs &a, const Plan &pl, 
     p.split_len = pl.split_len;
     p.HB = pl.head_blocks;
     p.partials = split ? 1 : 0;
+    p.slot_in = a.slot_indices ? 1 : 0;
     const hipError_t err = fmt == kCacheFp8 ? launch_fmt<kCacheFp8>(p, stream) : launch_fmt<kCacheBf16>(p, stream);
     if (err != hipSuccess || !split || partials_only)
         return err;

@@ -15,6 +15,7 @@ from __future__ import annotations
 import ctypes
 import os
 
+import numpy as np
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -25,9 +26,11 @@ STATUS_NAMES = {0: "SMLA_OK", 1: "SMLA_ERR_NULL", 2: "SMLA_ERR_SHAPE", 3: "SMLA_
                 4: "SMLA_ERR_WORKSPACE", 5: "SMLA_ERR_HIP", 6: "SMLA_ERR_ARG"}
 EXPORTS = ("smla_status_string", "smla_abi_version", "smla_plan", "smla_workspace_size",
            "smla_merge_partials", "smla_concat_and_cache_mla", "smla_convert_indices",
-           "smla_prefill_bf16", "smla_decode_fp8")
+           "smla_prefill_workspace_rows", "smla_plan_prefill_chunks", "smla_convert_indices_workspace",
+           "smla_gather_upconvert_fp8", "smla_prefill_bf16", "smla_decode_fp8")
 CACHE_FORMATS = {"auto": 0, "bf16": 0, "fp8_ds_mla": 1}
 FLAG_PARTIALS_ONLY = 0x1
+FLAG_SLOT_INDICES = 0x2
 
 
 class SmlaError(RuntimeError):
@@ -69,6 +72,14 @@ def library() -> ctypes.CDLL:
     lib.smla_concat_and_cache_mla.argtypes = [vp, vp, vp, i32, vp, i64, i32, vp]
     lib.smla_convert_indices.restype = ctypes.c_int
     lib.smla_convert_indices.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i64, vp]
+    lib.smla_prefill_workspace_rows.restype = i64
+    lib.smla_prefill_workspace_rows.argtypes = [i64]
+    lib.smla_plan_prefill_chunks.restype = ctypes.c_int
+    lib.smla_plan_prefill_chunks.argtypes = [vp, i32, i64, vp, vp, ctypes.POINTER(i32)]
+    lib.smla_convert_indices_workspace.restype = ctypes.c_int
+    lib.smla_convert_indices_workspace.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i64, i32, vp]
+    lib.smla_gather_upconvert_fp8.restype = ctypes.c_int
+    lib.smla_gather_upconvert_fp8.argtypes = [vp, i64, vp, i32, vp, vp, i32, i32, vp, i64, vp]
     attn = [vp, vp, vp, vp, vp, fl, i32, i32, i32, i32, i32, i64, vp, vp, vp, vp, sz, vp, vp]
     for name in ("smla_prefill_bf16", "smla_decode_fp8"):
         getattr(lib, name).restype = ctypes.c_int
@@ -206,12 +217,16 @@ def smla_convert_indices(req_id_per_token, block_table, topk_indices, num_blocks
 
 
 def _attention(name: str, q, kv_cache, block_table, req_id_per_token, topk_indices, sm_scale,
-               out, lse, phys_indices_out, workspace, num_splits, stream, want_lse, partials_only=False):
+               out, lse, phys_indices_out, workspace, num_splits, stream, want_lse, partials_only=False,
+               slot_indices=False):
     T, H, D = q.shape
     if D != 576:
         raise ValueError("q must be [num_tokens, h_q, 576]")
     K = topk_indices.shape[1]
-    flags = FLAG_PARTIALS_ONLY if partials_only else 0
+    flags = (FLAG_PARTIALS_ONLY if partials_only else 0) | (FLAG_SLOT_INDICES if slot_indices else 0)
+    if slot_indices:
+        block_table = req_id_per_token = None
+    R, MB = (1, 1) if block_table is None else block_table.shape
     if partials_only:
         if workspace is None:
             raise ValueError("partials_only needs a workspace (the partial results go there)")
@@ -232,7 +247,7 @@ def _attention(name: str, q, kv_cache, block_table, req_id_per_token, topk_indic
               _dev(block_table, "block_table", torch.int32, 2),
               _dev(req_id_per_token, "req_id_per_token", torch.int32, 1),
               _dev(topk_indices, "topk_indices", torch.int32, 2), float(sm_scale), T, H, K,
-              block_table.shape[0], block_table.shape[1], kv_cache.shape[0],
+              R, MB, kv_cache.shape[0],
               _dev(out, "out", torch.bfloat16, 3), _dev(lse, "lse", torch.float32, 2),
               _dev(phys_indices_out, "phys_indices_out", torch.int32, 2),
               ws_ptr, ws_bytes, _options(num_splits, flags), _stream(stream)), name)
@@ -241,23 +256,25 @@ def _attention(name: str, q, kv_cache, block_table, req_id_per_token, topk_indic
 
 def smla_prefill_bf16(q, kv_cache, block_table, req_id_per_token, topk_indices, sm_scale,
                       out=None, lse=None, phys_indices_out=None, workspace=None, num_splits=0,
-                      stream=None, want_lse=True, partials_only=False):
+                      stream=None, want_lse=True, partials_only=False, slot_indices=False):
     """Sparse MLA forward over a bf16 cache [num_blocks, 64, 576]. Returns (out, lse).
 
     workspace: uint8 device tensor of at least smla_workspace_size bytes (contents
     need not be initialised), or None for one the binding keeps per (device, stream).
     partials_only: write the per-part results into `workspace` (required) for
-    smla_merge_partials and return (None, None)."""
+    smla_merge_partials and return (None, None).
+    slot_indices: topk_indices already hold cache slots (block_table and
+    req_id_per_token are not used and may be None)."""
     if kv_cache.dtype != torch.bfloat16 or kv_cache.shape[1:] != (64, 576):
         raise ValueError("kv_cache must be bf16 [num_blocks, 64, 576]")
     return _attention("smla_prefill_bf16", q, kv_cache, block_table, req_id_per_token, topk_indices,
                       sm_scale, out, lse, phys_indices_out, workspace, num_splits, stream, want_lse,
-                      partials_only)
+                      partials_only, slot_indices)
 
 
 def smla_decode_fp8(q, kv_cache, block_table, req_id_per_token, topk_indices, sm_scale,
                     out=None, lse=None, phys_indices_out=None, workspace=None, num_splits=0,
-                    stream=None, want_lse=True, partials_only=False):
+                    stream=None, want_lse=True, partials_only=False, slot_indices=False):
     """Sparse MLA forward over an fp8_ds_mla cache uint8 [num_blocks, 64, 656]. Returns (out, lse).
 
     Other arguments as for smla_prefill_bf16."""
@@ -265,4 +282,125 @@ def smla_decode_fp8(q, kv_cache, block_table, req_id_per_token, topk_indices, sm
         raise ValueError("kv_cache must be uint8 [num_blocks, 64, 656]")
     return _attention("smla_decode_fp8", q, kv_cache, block_table, req_id_per_token, topk_indices,
                       sm_scale, out, lse, phys_indices_out, workspace, num_splits, stream, want_lse,
-                      partials_only)
+                      partials_only, slot_indices)
+
+
+# ---- separate-prefill mode of an fp8_ds_mla cache (decode tokens over the fp8
+# cache, prefill requests chunk by chunk over an upconverted bf16 workspace)
+
+def smla_prefill_workspace_rows(max_model_len: int) -> int:
+    """bf16 workspace rows reserved for a model (5 x max_model_len)."""
+    return int(library().smla_prefill_workspace_rows(int(max_model_len)))
+
+
+def smla_plan_prefill_chunks(seq_lens, max_rows: int):
+    """Host chunk plan: (chunk_ends list, chunk-local workspace starts int32 numpy [B])."""
+    sl = np.ascontiguousarray(np.asarray(seq_lens, dtype=np.int32).reshape(-1))
+    n = sl.shape[0]
+    ends = np.zeros(max(n, 1), dtype=np.int32)
+    starts = np.zeros(max(n, 1), dtype=np.int32)
+    nc = ctypes.c_int32()
+    _check(library().smla_plan_prefill_chunks(sl.ctypes.data if n else None, n, int(max_rows),
+                                              ends.ctypes.data, starts.ctypes.data, ctypes.byref(nc)),
+           "smla_plan_prefill_chunks")
+    return [int(e) for e in ends[:nc.value]], starts[:n]
+
+
+def smla_convert_indices_workspace(req_id_per_token, block_table, topk_indices, prefill_request_id,
+                                   workspace_starts, num_blocks: int, out=None, stream=None):
+    """Index conversion of the separate-prefill mode: prefill tokens (id >= 0) get
+    workspace rows workspace_starts[id] + index, decode tokens cache slots."""
+    T, K = topk_indices.shape
+    if out is None:
+        out = torch.empty_like(topk_indices)
+    P = 0 if workspace_starts is None else workspace_starts.shape[0]
+    _check(library().smla_convert_indices_workspace(
+        _dev(req_id_per_token, "req_id_per_token", torch.int32, 1),
+        _dev(block_table, "block_table", torch.int32, 2),
+        _dev(topk_indices, "topk_indices", torch.int32, 2),
+        _dev(prefill_request_id, "prefill_request_id", torch.int32, 1),
+        _dev(workspace_starts, "workspace_starts", torch.int32, 1) if P else None,
+        _dev(out, "out", torch.int32, 2), T, K, block_table.shape[0], block_table.shape[1],
+        int(num_blocks), P, _stream(stream)), "smla_convert_indices_workspace")
+    return out
+
+
+def smla_gather_upconvert_fp8(kv_cache, block_table, seq_lens, workspace_starts, max_seq_len: int,
+                              workspace, stream=None):
+    """Upconvert the context rows of a chunk of prefill requests (block_table rows,
+    seq_lens, workspace_starts: device int32) from an fp8_ds_mla cache into the
+    bf16 workspace [rows, 576]. Returns workspace."""
+    if kv_cache.dtype != torch.uint8 or kv_cache.shape[1:] != (64, 656):
+        raise ValueError("kv_cache must be uint8 [num_blocks, 64, 656]")
+    if workspace.dtype != torch.bfloat16 or workspace.dim() != 2 or workspace.shape[1] != 576:
+        raise ValueError("workspace must be bf16 [rows, 576]")
+    B = seq_lens.shape[0]
+    _check(library().smla_gather_upconvert_fp8(
+        _dev(kv_cache, "kv_cache"), kv_cache.shape[0], _dev(block_table, "block_table", torch.int32, 2),
+        block_table.shape[1], _dev(seq_lens, "seq_lens", torch.int32, 1),
+        _dev(workspace_starts, "workspace_starts", torch.int32, 1), B, int(max_seq_len),
+        _dev(workspace, "workspace"), workspace.shape[0], _stream(stream)), "smla_gather_upconvert_fp8")
+    return workspace
+
+
+def smla_forward_fp8_separate_prefill(q, kv_cache, block_table, req_id_per_token, topk_indices, sm_scale,
+                                      num_decode_reqs: int, seq_lens, max_rows: int, out=None, lse=None,
+                                      bf16_workspace=None, stream=None):
+    """The separate-prefill mode end to end. Requests [0, num_decode_reqs) are
+    decode requests, the rest prefill requests; seq_lens (host sequence, one per
+    request) gives each request's context + query length. Decode tokens run
+    smla_decode_fp8 over the cache; prefill requests are cut into chunks of at
+    most max_rows context rows, and for each chunk the rows are upconverted into
+    bf16_workspace (bf16 [>= max_rows rounded up to 64, 576]; allocated when None)
+    and its tokens run smla_prefill_bf16 over it with workspace-row indices.
+    Tokens must be ordered by request. Returns (out, lse)."""
+    T, H, _ = q.shape
+    dev = q.device
+    R = block_table.shape[0]
+    nd = int(num_decode_reqs)
+    sl = np.asarray(seq_lens, dtype=np.int64).reshape(-1)
+    if sl.shape[0] != R:
+        raise ValueError("seq_lens needs one length per request")
+    if out is None:
+        out = torch.empty((T, H, 512), dtype=torch.bfloat16, device=dev)
+    if lse is None:
+        lse = torch.empty((T, H), dtype=torch.float32, device=dev)
+    ends, starts = smla_plan_prefill_chunks(sl[nd:], max_rows)
+    ws_rows = -(-int(max_rows) // 64) * 64
+    if bf16_workspace is None:
+        bf16_workspace = torch.empty((ws_rows, 576), dtype=torch.bfloat16, device=dev)
+    elif bf16_workspace.shape[0] < ws_rows:
+        raise ValueError(f"bf16_workspace needs {ws_rows} rows")
+    req = req_id_per_token
+    with torch.cuda.stream(stream) if stream is not None else torch.cuda.stream(torch.cuda.current_stream()):
+        prefill_id = torch.where(req >= nd, req - nd, torch.full_like(req, -1))
+        starts_d = torch.from_numpy(np.ascontiguousarray(starts, dtype=np.int32)).to(dev)
+        sl_d = torch.from_numpy(sl[nd:].astype(np.int32)).to(dev)
+    slots = smla_convert_indices_workspace(req, block_table, topk_indices, prefill_id,
+                                           starts_d if len(starts) else None, kv_cache.shape[0],
+                                           stream=stream)
+    req_h = req.cpu().numpy()
+    tok_of = [np.nonzero(req_h == r)[0] for r in range(R)]
+    dec = np.concatenate(tok_of[:nd]) if nd else np.zeros(0, dtype=np.int64)
+    if dec.size:
+        d0, d1 = int(dec.min()), int(dec.max()) + 1
+        if d1 - d0 != dec.size:
+            raise ValueError("decode tokens must be contiguous")
+        smla_decode_fp8(q[d0:d1], kv_cache, None, None, slots[d0:d1], sm_scale, out=out[d0:d1],
+                        lse=lse[d0:d1], stream=stream, slot_indices=True)
+    ws_view = bf16_workspace[:ws_rows].view(ws_rows // 64, 64, 576)
+    c0 = 0
+    for c1 in ends:
+        toks = np.concatenate(tok_of[nd + c0:nd + c1])
+        rows = int(sl[nd + c0:nd + c1].sum())
+        if rows > 0:
+            smla_gather_upconvert_fp8(kv_cache, block_table[nd + c0:nd + c1], sl_d[c0:c1], starts_d[c0:c1],
+                                      int(sl[nd + c0:nd + c1].max()), bf16_workspace, stream=stream)
+        if toks.size:
+            t0, t1 = int(toks.min()), int(toks.max()) + 1
+            if t1 - t0 != toks.size:
+                raise ValueError("a chunk's tokens must be contiguous")
+            smla_prefill_bf16(q[t0:t1], ws_view, None, None, slots[t0:t1], sm_scale, out=out[t0:t1],
+                              lse=lse[t0:t1], stream=stream, slot_indices=True)
+        c0 = c1
+    return out, lse

@@ -40,7 +40,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_abi_version(lib):
-    assert smla.smla_abi_version() == 3
+    assert smla.smla_abi_version() == 4
 
 
 def test_status_strings(lib):
@@ -102,7 +102,7 @@ def test_plan_rejects_bad_options(lib):
     o.num_splits = -2
     assert lib.smla_plan(8, 16, 64, 256, ctypes.byref(o), ctypes.byref(s), ctypes.byref(b)) == 6
     o = smla.SmlaOptions()
-    for bit in (0x2, 0x4, 0x80000000):       # unknown flag bits
+    for bit in (0x4, 0x8, 0x80000000):       # unknown flag bits
         o.flags = bit
         assert lib.smla_plan(8, 16, 64, 256, ctypes.byref(o), ctypes.byref(s), ctypes.byref(b)) == 6
     o.flags = smla.FLAG_PARTIALS_ONLY
@@ -227,3 +227,86 @@ def test_cache_write_rejects_before_any_hip_call(lib, kw, code):
 
 def test_cache_write_zero_tokens_is_a_noop(lib):
     assert _cw(lib, kc=None, kpe=None, sm=None, kv=None, T=0) == 0
+
+
+# ------------------------------------------------------- separate-prefill mode
+
+@pytest.mark.parametrize("name", ["smla_decode_fp8", "smla_prefill_bf16"])
+def test_slot_indices_need_no_table_or_request_ids(lib, name):
+    o = smla.SmlaOptions()
+    o.flags = smla.FLAG_SLOT_INDICES
+    # validation passes the missing table / request ids and stops at the missing q
+    assert _attn(lib, name, q=None, bt=None, req=None, R=0, MB=0, opts=ctypes.byref(o)) == 1
+    assert _attn(lib, name, bt=None, req=None, T=0, opts=ctypes.byref(o)) == 0
+    # without the flag a missing table is an error before anything runs
+    assert _attn(lib, name, bt=None) == 1
+
+
+def test_prefill_workspace_rows(lib):
+    assert smla.smla_prefill_workspace_rows(163840) == 5 * 163840
+    assert smla.smla_prefill_workspace_rows(0) == 0 and smla.smla_prefill_workspace_rows(-4) == 0
+
+
+def test_prefill_chunk_plan_matches_the_oracle():
+    import numpy as np
+    import oracle
+    rng = np.random.default_rng(3)
+    for _ in range(200):
+        n = int(rng.integers(0, 10))
+        lens = rng.integers(0, 50, n)
+        m = int(rng.integers(max(int(lens.max()) if n else 1, 1), 120))
+        got = smla.smla_plan_prefill_chunks(lens, m)
+        if n == 0:
+            assert got[0] == [] and len(got[1]) == 0
+            continue
+        want = oracle.plan_prefill_chunks(lens, m)
+        assert got[0] == want[0] and np.array_equal(got[1], want[1])
+
+
+def test_prefill_chunk_plan_rejects(lib):
+    with pytest.raises(smla.SmlaError):
+        smla.smla_plan_prefill_chunks([5, 30], 20)          # a request longer than the workspace
+    with pytest.raises(smla.SmlaError):
+        smla.smla_plan_prefill_chunks([5, -1], 20)
+    n = ctypes.c_int32()
+    assert lib.smla_plan_prefill_chunks(None, 2, 10, A16, A16, ctypes.byref(n)) == 1
+    assert lib.smla_plan_prefill_chunks(None, 0, 10, None, None, None) == 1
+    assert lib.smla_plan_prefill_chunks(None, 0, 10, None, None, ctypes.byref(n)) == 0 and n.value == 0
+
+
+def _convert_ws(lib, req=A16, bt=A16, idx=A16, pid=A16, st=A16, out=A16B, T=4, K=64, R=2, MB=4, NB=8, P=2):
+    return lib.smla_convert_indices_workspace(req, bt, idx, pid, st, out, T, K, R, MB, NB, P, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(req=None), 1), (dict(bt=None), 1), (dict(idx=None), 1), (dict(pid=None), 1), (dict(out=None), 1),
+    (dict(st=None), 1), (dict(K=0), 2), (dict(T=-1), 2), (dict(P=-1), 2), (dict(R=0), 2), (dict(NB=0), 2),
+    (dict(pid=A16 + 2), 3), (dict(st=A16 + 1), 3), (dict(out=A16B + 2), 3),
+])
+def test_convert_workspace_rejects(lib, kw, code):
+    assert _convert_ws(lib, **kw) == code
+
+
+def test_convert_workspace_zero_tokens_and_no_prefills(lib):
+    assert _convert_ws(lib, req=None, bt=None, idx=None, pid=None, st=None, out=None, T=0) == 0
+    # no prefill requests: workspace_starts may be NULL (validation then stops at idx)
+    assert _convert_ws(lib, st=None, P=0, idx=None) == 1
+
+
+def _upconvert(lib, kv=A16, NB=8, bt=A16, MB=4, sl=A16, st=A16, B=2, L=100, ws=A16B, rows=256):
+    return lib.smla_gather_upconvert_fp8(kv, NB, bt, MB, sl, st, B, L, ws, rows, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(kv=None), 1), (dict(bt=None), 1), (dict(sl=None), 1), (dict(st=None), 1), (dict(ws=None), 1),
+    (dict(B=-1), 2), (dict(L=-1), 2), (dict(rows=-1), 2), (dict(MB=0), 2), (dict(NB=0), 2),
+    (dict(NB=(1 << 31) // 64 + 1), 2),
+    (dict(kv=MIS), 3), (dict(ws=A16B + 8), 3), (dict(bt=A16 + 2), 3), (dict(sl=A16 + 1), 3),
+])
+def test_upconvert_rejects(lib, kw, code):
+    assert _upconvert(lib, **kw) == code
+
+
+def test_upconvert_empty_batch_is_a_noop(lib):
+    assert _upconvert(lib, kv=None, bt=None, sl=None, st=None, ws=None, B=0) == 0
+    assert _upconvert(lib, kv=None, bt=None, sl=None, st=None, ws=None, L=0) == 0
