@@ -27,17 +27,10 @@ Plan make_plan(int num_tokens, int h_q, int topk, int num_cus, int forced_splits
     } else {
         // One workgroup per (token, head block) when that fills the chip;
         // otherwise cut each token's list so the grid covers every workgroup
-        // slot once (64-head workgroups: one per CU; smaller ones: two per CU).
-        // A 64-head batch too small to fill the chip runs as two 32-head
-        // workgroups per token, two per CU: the CU then interleaves two
-        // independent workgroups, and each merge reads half the partials.
-        int64_t units = (int64_t)num_tokens * p.head_blocks;
-        int64_t slots = (int64_t)num_cus * (h_q >= kHeadsPerGroup ? 1 : 2);
-        if (h_q == kHeadsPerGroup && units < slots) {
-            p.head_blocks = 2;
-            units = (int64_t)num_tokens * 2;
-            slots = (int64_t)num_cus * 2;
-        }
+        // slot once: 64-head workgroups take a CU each, 32- and 16-head ones
+        // fit two per CU.
+        const int64_t units = (int64_t)num_tokens * p.head_blocks;
+        const int64_t slots = (int64_t)num_cus * (h_q >= kHeadsPerGroup ? 1 : 2);
         const int64_t tiles = (topk + kBlock - 1) / kBlock;
         if (units > 0 && units < slots)
             splits = (int)std::min<int64_t>(std::min<int64_t>(tiles, kMaxSplits), (slots + units - 1) / units);

@@ -244,7 +244,7 @@ __device__ __forceinline__ bf16x8 pack_p_residual(const f32x4 &p0, const f32x4 &
 }
 
 // Wait until at most n of this wave's vector-memory instructions are pending
-// (n is wave-uniform; values above 31 wait for all).
+// (n is wave-uniform; values above 63, the counter's range, wait for all).
 __device__ __forceinline__ void wait_vmcnt(int n)
 {
 #define SMLA_VMCNT_CASE(k) case k: asm volatile("s_waitcnt vmcnt(" #k ")" ::: "memory"); break;
@@ -257,6 +257,14 @@ __device__ __forceinline__ void wait_vmcnt(int n)
         SMLA_VMCNT_CASE(20) SMLA_VMCNT_CASE(21) SMLA_VMCNT_CASE(22) SMLA_VMCNT_CASE(23)
         SMLA_VMCNT_CASE(24) SMLA_VMCNT_CASE(25) SMLA_VMCNT_CASE(26) SMLA_VMCNT_CASE(27)
         SMLA_VMCNT_CASE(28) SMLA_VMCNT_CASE(29) SMLA_VMCNT_CASE(30) SMLA_VMCNT_CASE(31)
+        SMLA_VMCNT_CASE(32) SMLA_VMCNT_CASE(33) SMLA_VMCNT_CASE(34) SMLA_VMCNT_CASE(35)
+        SMLA_VMCNT_CASE(36) SMLA_VMCNT_CASE(37) SMLA_VMCNT_CASE(38) SMLA_VMCNT_CASE(39)
+        SMLA_VMCNT_CASE(40) SMLA_VMCNT_CASE(41) SMLA_VMCNT_CASE(42) SMLA_VMCNT_CASE(43)
+        SMLA_VMCNT_CASE(44) SMLA_VMCNT_CASE(45) SMLA_VMCNT_CASE(46) SMLA_VMCNT_CASE(47)
+        SMLA_VMCNT_CASE(48) SMLA_VMCNT_CASE(49) SMLA_VMCNT_CASE(50) SMLA_VMCNT_CASE(51)
+        SMLA_VMCNT_CASE(52) SMLA_VMCNT_CASE(53) SMLA_VMCNT_CASE(54) SMLA_VMCNT_CASE(55)
+        SMLA_VMCNT_CASE(56) SMLA_VMCNT_CASE(57) SMLA_VMCNT_CASE(58) SMLA_VMCNT_CASE(59)
+        SMLA_VMCNT_CASE(60) SMLA_VMCNT_CASE(61) SMLA_VMCNT_CASE(62) SMLA_VMCNT_CASE(63)
         default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
     }
 #undef SMLA_VMCNT_CASE
@@ -997,6 +1005,549 @@ void attn_kernel(const KParams p)
     }
 }
 
+// ------------------------------------------------- attention, QK^T waves and PV waves (fp8)
+
+// Shape of an attn_pc_kernel workgroup: 64 heads of one token and one part of
+// its top-k list, eight waves in two roles, one of each per SIMD:
+//  * QK^T wave w (w < 4): head block w (16 heads) over all 576 columns --
+//    S^T = K q^T, the online softmax, and the P^T operands of all four scale
+//    groups, published through LDS;
+//  * PV wave 4 + w: output dims 128 w .. 128 w + 127 (scale group w) of all
+//    four head blocks -- each V^T fragment is read and converted once and
+//    feeds four MFMAs -- and a quarter of every tile's copy instructions.
+// PV runs one tile behind QK^T, so the SIMD interleaves one wave's MFMAs with
+// the other's VALU and LDS work. P^T, the rescale flags and factors are double
+// buffered by tile parity; one barrier per tile orders everything.
+struct CfgPC {
+    static constexpr int kWaves = 8;
+    static constexpr int kThreads = 512;
+    static constexpr int kHeads = 64;
+    static constexpr int kRowBytes = kFp8RowBytes;
+    static constexpr int kChunksPerRow = kRowBytes / 16;
+    static constexpr int kRowStride = kRowBytes;
+    static constexpr int kRowBlockBytes = 16 * kRowStride + 16;
+    static constexpr int kInstrPerRow = 1;
+    static constexpr int kRowsPerWave = kTile / 4;                   // copies: the four PV waves
+    static constexpr int kDmaPerWave = kRowsPerWave;
+    static constexpr int kBufBytes = (kRB * kRowBlockBytes + 1023) / 1024 * 1024;
+    static constexpr int kNBuf = 5;                                  // ring buffers
+    static constexpr int kNBufExact = 3;                             // ring buffers of a short list
+    static constexpr int kPBytes = 2 * 4 * 4 * 1024;                 // [parity][head block][group] P^T hi
+    static constexpr int kSlotsBytes = kMaxChunk * 4;
+    static constexpr int kOffP = kNBuf * kBufBytes;
+    static constexpr int kOffPLo = kNBufExact * kBufBytes;           // short lists: P^T lo terms
+    static constexpr int kOffHead = kOffP + kPBytes;                 // flags, factors, max and sums
+    static constexpr int kOffSlots = kOffHead + 1024;
+    static constexpr int kOffMisc = kOffSlots + kSlotsBytes;         // compaction counts
+    static constexpr int kLdsBytes = kOffMisc + 512;
+    static constexpr int kStageBf16 = kDv + 8;                       // padded staging rows
+    static constexpr int kStageF32 = kDv + 4;
+    static_assert(kChunksPerRow <= 64, "one copy instruction per row");
+    static_assert(kOffPLo + kPBytes <= kOffP, "lo terms fit the ring buffers a short list leaves free");
+    static_assert(kNBufExact >= 3, "the ring holds tiles r - 1, r and the copy of r + 1");
+    static_assert(kLdsBytes <= 160 * 1024, "LDS of one gfx950 workgroup");
+    static_assert(kHeads * kStageF32 * 4 <= kOffHead, "staging fits the ring and P^T");
+    static_assert(16 + (kMaxChunk / kThreads) * kWaves <= 128, "compaction counts fit");
+};
+
+// The fp8_ds_mla path (a1-a6 and the per-split part of a7). Iteration r of the
+// tile loop, after the barrier (tile r has landed; P^T of tile r - 1 is
+// published; tile r - 2 is done): the QK^T waves process tile r into P^T
+// parity r & 1; the PV waves refill tile r - 2's buffer with tile
+// r - 2 + nbuf and add V^T P^T of tile r - 1 to their slices of O.
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_pc_kernel(const KParams p)
+{
+    using C = CfgPC;
+    constexpr int RB = kRB;
+    constexpr int RS = C::kRowStride;
+    constexpr int RBB = C::kRowBlockBytes;
+    constexpr int kPer = kMaxChunk / C::kThreads;    // top-k positions per thread per round
+    constexpr int kRope = RowFmt<kCacheFp8>::kRope;
+
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[C::kLdsBytes];
+    uint8_t *ring = smem;
+    bf16x8 *p_hi = (bf16x8 *)(smem + C::kOffP);              // [parity][hb][group][lane]
+    bf16x8 *p_lo = (bf16x8 *)(smem + C::kOffPLo);
+    int *resc_flag = (int *)(smem + C::kOffHead);            // [parity][hb] the block's max moved
+    float *alpha_lds = (float *)(smem + C::kOffHead + 64);   // [parity][hb][16] its rescale factors
+    float *m_lds = (float *)(smem + C::kOffHead + 576);      // [hb][16] final max
+    float *l_lds = (float *)(smem + C::kOffHead + 832);      // [hb][16] final row sum
+    int32_t *lds_slots = (int32_t *)(smem + C::kOffSlots);
+    int32_t *lds_misc = (int32_t *)(smem + C::kOffMisc);
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int g = lane >> 4, n16 = lane & 15;
+    const bool qk_role = wave < 4;
+    const int rw = wave & 3;       // head block (QK^T wave) or dim group (PV wave)
+
+    // Workgroup id -> (token, split, head group); all workgroups of one token
+    // get the same id mod 8, the XCD the hardware dispatches them to.
+    int bid = blockIdx.x;
+    const int xcd = bid & 7;
+    bid >>= 3;
+    const int hg = bid % p.HB;
+    bid /= p.HB;
+    const int s = bid % p.S;
+    const int t = (bid / p.S) * 8 + xcd;
+    if (t >= p.T)
+        return;
+
+    const int wg_head0 = hg * C::kHeads;
+    const float c2 = p.log2e_scale;
+    const int32_t *topk_row = p.topk + (size_t)t * p.K;
+    const int req = p.slot_in ? 0 : p.req_id[t];
+    const int pos_begin = s * p.split_len;
+    const int pos_end = min(p.K, pos_begin + p.split_len);
+
+    // QK^T waves hold q^T as the B operands: the latent goes through
+    // v_mfma_scale_f32_16x16x128_f8f6f4 on the raw e4m3 K bytes, so q is written
+    // exactly as hi + lo e4m3 terms with a power-of-two scale per head and
+    // 128-column group G: lane (head, g) holds columns 128 G + 32 g .. + 31
+    // (qh, ql, scales qsh, qsl). RoPE: bf16 (qr), k-step ks holds columns
+    // 512 + 32 ks + 8 g .. + 7.
+    // QK^T and online softmax of head block rw on one tile; publishes the P^T
+    // operands of all four scale groups into parity par (and the rescale
+    // factors when the running max moved).
+    auto qk_tile = [&](const uint8_t *buf, int n_tile, int par, auto exact_c, const i32x8 (&qh)[4],
+                       const i32x8 (&ql)[4], const int (&qsh)[4], const int (&qsl)[4], const bf16x8 (&qr)[2],
+                       float &m_run, float &l_part) __attribute__((always_inline)) {
+        constexpr bool exact = decltype(exact_c)::value;
+        const int off_k = n16 * RS;                      // K rows 16 rb + n16
+        const int off_sc = (4 * g) * RS;                 // accumulator rows 16 rb + 4 g + i
+        f32x4 sc[RB][4];        // four group scales of accumulator row 16 rb + 4 g + i
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                sc[rb][i] = *(const f32x4 *)(buf + rb * RBB + off_sc + i * RS + 512);
+        f32x4 acc[RB];
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+            acc[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int G = 0; G < 4; ++G) {
+            i32x8 kf[RB];
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) {
+                const uint4 *src = (const uint4 *)(buf + rb * RBB + off_k + 128 * G + 32 * g);
+                const uint4 a0 = src[0], a1 = src[1];
+                kf[rb] = i32x8{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+            }
+            f32x4 part[RB];
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb)
+                part[rb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                    kf[rb], qh[G], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, qsh[G]);
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb)
+                part[rb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                    kf[rb], ql[G], part[rb], 0, 0, 0, 127, 0, qsl[G]);
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    acc[rb][i] = fmaf(sc[rb][i][G], part[rb][i], acc[rb][i]);
+        }
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) {
+                const bf16x8 rf = *(const bf16x8 *)(buf + rb * RBB + off_k + kRope + 64 * ks + 16 * g);
+                acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(rf, qr[ks], acc[rb], 0, 0, 0);
+            }
+
+        // online softmax in log2 units. The running max moves only when some
+        // row exceeds it by 2^8 (tested on each lane's own rows, moved to the
+        // whole head's max). The scale c2 > 0 is applied to the maximum and
+        // inside the exp2 argument: max(c2 * a) = c2 * max(a).
+        float lmax = -INFINITY;
+        if (n_tile == kTile) {
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    lmax = fmaxf(lmax, acc[rb][i]);
+        } else {
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    acc[rb][i] = 16 * rb + 4 * g + i < n_tile ? acc[rb][i] : -INFINITY;
+                    lmax = fmaxf(lmax, acc[rb][i]);
+                }
+        }
+        lmax *= c2;
+        bool moved = false;
+        float alpha = 1.f;
+        if (__ballot(lmax > m_run + kLazyRescale) != 0) {
+            float mx = fmaxf(lmax, __shfl_xor(lmax, 16));
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            if (mx > m_run + kLazyRescale) {
+                alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - mx);
+                l_part *= alpha;
+                m_run = mx;
+            }
+            moved = true;
+        }
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                acc[rb][i] = __builtin_amdgcn_exp2f(fmaf(acc[rb][i], c2, -m_run));
+                l_part += acc[rb][i];
+            }
+        // P^T operands: the weights for output group G carry that group's row
+        // scales, so the dequantisation adds no rounding
+#pragma unroll
+        for (int G = 0; G < 4; ++G) {
+            f32x4 p0, p1;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                p0[i] = acc[0][i] * sc[0][i][G];
+                p1[i] = acc[1][i] * sc[1][i][G];
+            }
+            const bf16x8 hi = pack_p(p0, p1);
+            p_hi[((par * 4 + rw) * 4 + G) * 64 + lane] = hi;
+            if constexpr (exact)
+                p_lo[((par * 4 + rw) * 4 + G) * 64 + lane] = pack_p_residual(p0, p1, hi);
+        }
+        if (lane == 0)
+            resc_flag[par * 4 + rw] = moved ? 1 : 0;
+        if (moved && g == 0)
+            alpha_lds[(par * 4 + rw) * 16 + n16] = alpha;
+    };
+
+    // ---- compaction of one round of the list (up to kMaxChunk positions):
+    //      converted slots of valid positions into LDS in list order with one
+    //      exchange of per-wave counts; every wave takes part (two barriers)
+    const bool write_phys = p.phys_out != nullptr && hg == 0;   // head group 0 writes the slots
+    auto compact = [&](int chunk0, int (&slotv)[kPer]) __attribute__((always_inline)) {
+        const int chunk_n = min(kMaxChunk, pos_end - chunk0);
+        if (write_phys) {
+#pragma unroll
+            for (int j = 0; j < kPer; ++j) {
+                const int i = tid + C::kThreads * j;
+                if (i < chunk_n)
+                    p.phys_out[(size_t)t * p.K + chunk0 + i] = slotv[j];
+            }
+        }
+        uint64_t masks[kPer];
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) {
+            masks[j] = __ballot(slotv[j] >= 0);
+            if (lane == 0)
+                lds_misc[16 + j * C::kWaves + wave] = __popcll(masks[j]);
+        }
+        __syncthreads();
+        const int my_count = lds_misc[16 + (lane & 31)];
+        int n_valid = 0;
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) {
+#pragma unroll
+            for (int w = 0; w < C::kWaves; ++w) {
+                const int cw = __builtin_amdgcn_readlane(my_count, j * C::kWaves + w);
+                if (w == wave && slotv[j] >= 0)
+                    lds_slots[n_valid + __popcll(masks[j] & ((1ull << lane) - 1ull))] = slotv[j];
+                n_valid += cw;
+            }
+        }
+        __syncthreads();
+        return n_valid;
+    };
+    // slots of a later round of a long list (loaded here, so no load is left in
+    // flight across the tile loop)
+    auto convert_round = [&](int chunk0, int (&slotv)[kPer]) __attribute__((always_inline)) {
+        int idxv[kPer];
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) {
+            const int i = chunk0 + tid + C::kThreads * j;
+            idxv[j] = i < pos_end ? topk_row[i] : -1;
+        }
+#pragma unroll
+        for (int j = 0; j < kPer; ++j)
+            slotv[j] = p.slot_in ? given_slot(idxv[j], p.NB)
+                                 : finish_slot(lookup_block(req, idxv[j], p.bt, p.R, p.MB), req, idxv[j], p.R,
+                                               p.MB, p.NB);
+    };
+
+    // the first round's indices, then their block-table lookups
+    int slotv[kPer];
+    {
+        int idxv[kPer];
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) {
+            const int i = pos_begin + tid + C::kThreads * j;
+            idxv[j] = i < min(pos_end, pos_begin + kMaxChunk) ? topk_row[i] : -1;
+        }
+#pragma unroll
+        for (int j = 0; j < kPer; ++j)
+            slotv[j] = p.slot_in ? 0 : lookup_block(req, idxv[j], p.bt, p.R, p.MB);
+#pragma unroll
+        for (int j = 0; j < kPer; ++j)
+            slotv[j] = p.slot_in ? given_slot(idxv[j], p.NB) : finish_slot(slotv[j], req, idxv[j], p.R, p.MB, p.NB);
+    }
+
+    if (qk_role) {
+        // ================= QK^T waves: head block rw =================
+        i32x8 qh[4], ql[4];
+        int qsh[4], qsl[4];
+        bf16x8 qr[2];
+        float m_run = -INFINITY, l_part = 0.f;   // log2-domain running max (same in a head's 4 lanes), row sum
+        for (int chunk0 = pos_begin; chunk0 < pos_end; chunk0 += kMaxChunk) {
+            if (chunk0 != pos_begin)
+                convert_round(chunk0, slotv);
+            const int n_valid = compact(chunk0, slotv);
+            const bool exact_p = n_valid <= kExactPRows;
+            const int nbuf = exact_p ? C::kNBufExact : C::kNBuf;
+            const int n_tiles = (n_valid + kTile - 1) / kTile;
+            if (chunk0 == pos_begin) {
+                // q, loaded and written exactly as hi + lo e4m3 terms while the
+                // PV waves' first copies are in flight
+                uint4 qraw[18];     // [4 * G + c] latent of group G, [16 + ks] RoPE k-step ks
+                const uint16_t *qrow = p.q + ((size_t)t * p.H + wg_head0 + 16 * rw + n16) * kDqk;
+#pragma unroll
+                for (int G = 0; G < 4; ++G)
+#pragma unroll
+                    for (int c = 0; c < 4; ++c)
+                        qraw[4 * G + c] = ((const uint4 *)(qrow + 128 * G + 32 * g))[c];
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks)
+                    qraw[16 + ks] = *(const uint4 *)(qrow + kDv + 32 * ks + 8 * g);
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks)
+                    qr[ks] = __builtin_bit_cast(bf16x8, qraw[16 + ks]);
+#pragma unroll
+                for (int G = 0; G < 4; ++G) {
+                    float v[32];
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        const uint4 w = qraw[4 * G + c];
+                        const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            v[8 * c + 2 * e] = bf16_lo(ww[e]);
+                            v[8 * c + 2 * e + 1] = bf16_hi(ww[e]);
+                        }
+                    }
+                    float amax = 0.f;
+#pragma unroll
+                    for (int i = 0; i < 32; ++i)
+                        amax = fmaxf(amax, fabsf(v[i]));
+                    // the MFMA applies one B scale per column (head) to all 128 k of
+                    // the group, so the exponent is shared by the head's four lanes
+                    amax = fmaxf(amax, __shfl_xor(amax, 16));
+                    amax = fmaxf(amax, __shfl_xor(amax, 32));
+                    // block exponent: the largest |q| maps into [128, 256), within e4m3's range
+                    const int ex = max((int)((__float_as_uint(amax) >> 23) & 0xFF) - 127 - 7, -120);
+                    const float down = __uint_as_float((uint32_t)(127 - ex) << 23);     // 2^-ex, exact
+                    uint32_t hw[8], lw[8];
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        float x[4];
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            x[e] = v[4 * j + e] * down;
+                        s16x2 h = {0, 0};
+                        h = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(h, x[0], x[1], 1.0f, false);
+                        h = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(h, x[2], x[3], 1.0f, true);
+                        hw[j] = __builtin_bit_cast(uint32_t, h);
+                        // what the hi term misses, exactly, times 16 (its scale is 2^(ex - 4))
+                        const f32x2 b0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(hw[j], 1.0f, false);
+                        const f32x2 b1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(hw[j], 1.0f, true);
+                        s16x2 l = {0, 0};
+                        l = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(l, (x[0] - b0[0]) * 16.f, (x[1] - b0[1]) * 16.f, 1.0f, false);
+                        l = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(l, (x[2] - b1[0]) * 16.f, (x[3] - b1[1]) * 16.f, 1.0f, true);
+                        lw[j] = __builtin_bit_cast(uint32_t, l);
+                    }
+                    qh[G] = i32x8{(int)hw[0], (int)hw[1], (int)hw[2], (int)hw[3], (int)hw[4], (int)hw[5], (int)hw[6], (int)hw[7]};
+                    ql[G] = i32x8{(int)lw[0], (int)lw[1], (int)lw[2], (int)lw[3], (int)lw[4], (int)lw[5], (int)lw[6], (int)lw[7]};
+                    qsh[G] = 127 + ex;
+                    qsl[G] = 127 + ex - 4;
+                }
+            }
+            auto tiles = [&](auto exact_c) __attribute__((always_inline)) {
+                for (int r = 0; r <= n_tiles; ++r) {
+                    // tile r has landed; tile r - 2 is done with its P^T parity
+                    __syncthreads();
+                    if (r < n_tiles)
+                        qk_tile(ring + (r % nbuf) * C::kBufBytes, min(kTile, n_valid - r * kTile), r & 1, exact_c,
+                                qh, ql, qsh, qsl, qr, m_run, l_part);
+                }
+            };
+            if (exact_p)
+                tiles(std::true_type{});
+            else
+                tiles(std::false_type{});
+            __syncthreads();     // ring, P^T and slot list are free for the next round
+        }
+        // (max, row sum) of each head to the PV waves
+        float l = l_part;
+        l += __shfl_xor(l, 16);
+        l += __shfl_xor(l, 32);
+        if (g == 0) {
+            m_lds[rw * 16 + n16] = m_run;
+            l_lds[rw * 16 + n16] = l;
+        }
+        __syncthreads();
+        // lse of this head block (natural log; v_log_f32 is log2, and l >= 1
+        // here: the row that set the max adds >= 1)
+        if (g == 0) {
+            const float lse_v = l > 0.f ? (m_run + __builtin_amdgcn_logf(l)) * 0.69314718055994531f : -INFINITY;
+            if (!p.partials) {
+                if (p.lse != nullptr)
+                    p.lse[(size_t)t * p.H + wg_head0 + 16 * rw + n16] = lse_v;
+            } else {
+                p.part_lse[((size_t)t * p.S + s) * p.H + wg_head0 + 16 * rw + n16] = lse_v;
+            }
+        }
+        __syncthreads();    // the PV waves have staged the output
+    } else {
+        // ================= PV waves: output dims 128 rw .. 128 rw + 127 =================
+        // o[8 * hb + db] holds dims 128 rw + 16 db + 4 g + i of head 16 hb + n16
+        f32x4 o[32];
+#pragma unroll
+        for (int k = 0; k < 32; ++k)
+            o[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+        // V^T (ds_read_b64_tr_b8): source lane n16 = 2k + h reads row k of
+        // {4g..4g+3, 16+4g..16+4g+3}, bytes 8h..8h+7 of a 16-byte column block;
+        // this wave's dims start at byte 128 * rw of the row
+        const int vk = n16 >> 1;
+        const int off_v8 = (vk >> 2) * RBB + (4 * g + (vk & 3)) * RS + 8 * (n16 & 1) + 128 * rw;
+        constexpr int dma_w = C::kDmaPerWave;
+        for (int chunk0 = pos_begin; chunk0 < pos_end; chunk0 += kMaxChunk) {
+            if (chunk0 != pos_begin)
+                convert_round(chunk0, slotv);
+            const int n_valid = compact(chunk0, slotv);
+            const bool exact_p = n_valid <= kExactPRows;
+            const int nbuf = exact_p ? C::kNBufExact : C::kNBuf;
+            const int n_tiles = (n_valid + kTile - 1) / kTile;
+            // the first tiles' copies (every buffer starts free); from here on the
+            // only vector-memory instructions in flight are tile copies
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            // the first two tiles now; the rest of the ring during iteration 0,
+            // while the QK^T waves already work on tile 0 (copies of a cold
+            // start queue behind the whole chip's, and a wave issuing them
+            // stalls)
+            int issued = min(n_tiles, 2);
+            for (int i = 0; i < issued; ++i)
+                issue_tile<C>(p.cache, lds_slots + i * kTile, min(kTile, n_valid - i * kTile),
+                              ring + i * C::kBufBytes, rw, lane);
+            const bool exact_s = __builtin_amdgcn_readfirstlane(exact_p ? 1 : 0) != 0;
+            {
+                for (int r = 0; r <= n_tiles; ++r) {
+                    // this wave's pieces of tile r have landed ...
+                    if (r < n_tiles)
+                        wait_vmcnt(dma_w * (issued - (r + 1)));
+                    // ... and every wave's; P^T of tile r - 1 is published; tile
+                    // r - 2 is done with its buffer
+                    __syncthreads();
+                    // fill the ring: tile nt goes into buffer nt % nbuf once its
+                    // previous tile nt - nbuf is done (< r - 1)
+                    const int hi = min(n_tiles, max(r - 1 + nbuf, nbuf));
+                    for (int nt = issued; nt < hi; ++nt)
+                        issue_tile<C>(p.cache, lds_slots + nt * kTile, min(kTile, n_valid - nt * kTile),
+                                      ring + (nt % nbuf) * C::kBufBytes, rw, lane);
+                    issued = max(issued, hi);
+                    if (r >= 1) {
+                        // ---- O^T += V^T P^T of tile r - 1 over this wave's dims
+                        const int par = (r - 1) & 1;
+                        const uint8_t *buf = ring + ((r - 1) % nbuf) * C::kBufBytes;
+                        uint2 vf[8];
+#pragma unroll
+                        for (int db = 0; db < 8; ++db) {
+                            const i32x2 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                                LDS_PTR(i32x2, buf + off_v8 + 16 * db));
+                            vf[db] = make_uint2((uint32_t)v[0], (uint32_t)v[1]);
+                        }
+#pragma unroll
+                        for (int hb = 0; hb < 4; ++hb) {
+                            // a scalar branch: O is rescaled in place (a lane-divergent
+                            // one would keep a second copy of the accumulators)
+                            if (__builtin_amdgcn_readfirstlane(resc_flag[par * 4 + hb])) {
+                                const float al = alpha_lds[(par * 4 + hb) * 16 + n16];
+#pragma unroll
+                                for (int db = 0; db < 8; ++db)
+                                    o[hb * 8 + db] *= al;
+                            }
+                        }
+                        // V^T converted four blocks at a time, each block feeding the
+                        // four head blocks
+#pragma unroll
+                        for (int half = 0; half < 2; ++half) {
+                            bf16x8 va[4];
+#pragma unroll
+                            for (int d = 0; d < 4; ++d)
+                                va[d] = e4m3x8_to_bf16x8(vf[4 * half + d]);
+#pragma unroll
+                            for (int hb = 0; hb < 4; ++hb) {
+                                const bf16x8 ph = p_hi[((par * 4 + hb) * 4 + rw) * 64 + lane];
+#pragma unroll
+                                for (int d = 0; d < 4; ++d)
+                                    o[hb * 8 + 4 * half + d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                        va[d], ph, o[hb * 8 + 4 * half + d], 0, 0, 0);
+                                if (exact_s) {
+                                    const bf16x8 pl = p_lo[((par * 4 + hb) * 4 + rw) * 64 + lane];
+#pragma unroll
+                                    for (int d = 0; d < 4; ++d)
+                                        o[hb * 8 + 4 * half + d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                            va[d], pl, o[hb * 8 + 4 * half + d], 0, 0, 0);
+                                }
+                            }
+                        }
+                    }
+                }
+            }
+            __syncthreads();     // ring, P^T and slot list are free for the next round
+        }
+        __syncthreads();        // (max, row sum) of every head are in LDS
+        // ---- this wave's slice of the output rows, normalised, staged in LDS
+        //      (rows padded so the 16 heads of one store fall on distinct banks)
+        const int n16_late = late(n16);
+        const int dim0 = 128 * rw;
+#pragma unroll
+        for (int hb = 0; hb < 4; ++hb) {
+            const float l0 = l_lds[hb * 16 + n16];
+            const float inv_l = l0 > 0.f ? 1.f / l0 : 0.f;
+            if (!p.partials) {
+                uint16_t *stage = (uint16_t *)smem;
+#pragma unroll
+                for (int db = 0; db < 8; ++db) {
+                    const f32x4 v = o[hb * 8 + db] * inv_l;
+                    *(uint2 *)(stage + (16 * hb + n16_late) * C::kStageBf16 + dim0 + 16 * db + 4 * g) =
+                        make_uint2(pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3]));
+                }
+            } else {
+                float *stage = (float *)smem;
+#pragma unroll
+                for (int db = 0; db < 8; ++db)
+                    *(f32x4 *)(stage + (16 * hb + n16_late) * C::kStageF32 + dim0 + 16 * db + 4 * g) =
+                        o[hb * 8 + db] * inv_l;
+            }
+        }
+        __syncthreads();
+    }
+
+    // ---- the staged rows written out coalesced. One split: the bf16 rows of
+    //      the result. A top-k split: the fp32 partial O / l, head-major, for
+    //      merge_kernel.
+    if (!p.partials) {
+        const uint16_t *stage = (const uint16_t *)smem;
+        uint16_t *dst = p.out + ((size_t)t * p.H + wg_head0) * kDv;
+        for (int u = tid; u < C::kHeads * kDv / 8; u += C::kThreads) {
+            const int row = u / (kDv / 8), c8 = u % (kDv / 8);
+            *(uint4 *)(dst + 8 * u) = *(const uint4 *)(stage + row * C::kStageBf16 + 8 * c8);
+        }
+    } else {
+        const float *stage = (const float *)smem;
+        float *dst = p.part_o + (((size_t)t * p.S + s) * p.H + wg_head0) * kDv;
+        for (int u = tid; u < C::kHeads * kDv / 4; u += C::kThreads) {
+            const int row = u / (kDv / 4), c4 = u % (kDv / 4);
+            *(f32x4 *)(dst + 4 * u) = *(const f32x4 *)(stage + row * C::kStageF32 + 4 * c4);
+        }
+    }
+}
+
 // Log-sum-exp merge of a token's top-k splits: thread (t, h, c) combines
 // dims 4c .. 4c + 3 of head h over the splits in index order (weights
 // exp(lse_s - max lse), normalised by their sum) and writes the bf16 output
@@ -1240,10 +1791,23 @@ hipError_t launch_one(const KParams &p, hipStream_t stream)
     return hipGetLastError();
 }
 
+hipError_t launch_pc(const KParams &p, hipStream_t stream)
+{
+    const int64_t tq = (p.T + 7) / 8;
+    const dim3 grid((unsigned)(tq * 8 * p.S * p.HB));
+    hipLaunchKernelGGL(attn_pc_kernel, grid, dim3(CfgPC::kThreads), 0, stream, p);
+    return hipGetLastError();
+}
+
 template <int FMT>
 hipError_t launch_fmt(const KParams &p, hipStream_t stream)
 {
     const int heads = p.H / p.HB;     // heads per workgroup: 64, 32 or 16
+    if constexpr (FMT == kCacheFp8) {
+        // fp8 cache, 64 heads per workgroup: QK^T waves and PV waves
+        if (heads == 64)
+            return launch_pc(p, stream);
+    }
     if (heads == 64)
         return launch_one<FMT, 4>(p, stream);
     if (heads == 32)

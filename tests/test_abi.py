@@ -49,15 +49,20 @@ def test_status_strings(lib):
 
 
 def test_plan_fills_the_chip_for_small_decode_batches(lib):
-    # 64 tokens x 64 heads: one workgroup per token -> 4 top-k splits on 256 CUs
+    # 64 tokens x 64 heads: one 64-head workgroup per token -> 4 top-k splits
+    # fill 256 CUs once
     s, ws = smla.smla_plan(64, 64, 2048, 256)
     assert s == 4
     up = lambda v: -(-v // 256) * 256
     rows = 64 * 4 * 64
     o_off = up(rows * 4)                     # the partial lse first, then the partial o
     assert ws == up(o_off + rows * 512 * 4)
-    # two-wave workgroups (h_q <= 32) fit two per CU: 256 tokens x 16 heads -> 2 splits
+    # two-wave workgroups (h_q = 16) fit two per CU: 256 tokens x 16 heads -> 2 splits
     assert smla.smla_plan(256, 16, 2048, 256)[0] == 2
+    # 32-head workgroups fit two per CU: 64 tokens x 32 heads -> 8 splits
+    assert smla.smla_plan(64, 32, 2048, 256)[0] == 8
+    # 128 heads, 32 tokens: two 64-head workgroups per token -> 4 splits
+    assert smla.smla_plan(32, 128, 2048, 256)[0] == 4
     # enough (token, head-block) units already: no split, no workspace
     assert smla.smla_plan(512, 16, 2048, 256) == (1, 0)
     assert smla.smla_plan(16384, 128, 2048, 256) == (1, 0)
