@@ -314,7 +314,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "fp8/bf16",
         "data": "synthetic",
         "config": {
             "workload": "fp8_ds_mla sparse MLA decode: 64 tokens (1 per request), ctx U{4096..8192}, "
@@ -329,9 +329,9 @@ def main():
                              "query_tokens_per_s": roof_tok_s},
         "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved_gbs / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": "attn_kernel", "algorithmic_bytes_per_launch": attn_bytes,
+                     "kernel": "attn_pc_kernel", "algorithmic_bytes_per_launch": attn_bytes,
                      "avg_launch_ms": attn_avg_ms},
-        "kernels_ms_cold": {"attn_kernel": attn_avg_ms, "merge_kernel": float(merge_ms.mean())},
+        "kernels_ms_cold": {"attn_pc_kernel": attn_avg_ms, "merge_kernel": float(merge_ms.mean())},
         "whole_step_hbm_frac": bytes_alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "algorithmic_bytes_per_step": bytes_alg,
         "algorithmic_bytes_breakdown": by,
