@@ -1027,7 +1027,7 @@ struct CfgPC {
     static constexpr int kRowStride = kRowBytes;
     static constexpr int kRowBlockBytes = 16 * kRowStride + 16;
     static constexpr int kInstrPerRow = 1;
-    static constexpr int kRowsPerWave = kTile / 4;                   // copies: the four PV waves
+    static constexpr int kRowsPerWave = kTile / 4;                   // first tiles: the four PV waves
     static constexpr int kDmaPerWave = kRowsPerWave;
     static constexpr int kBufBytes = (kRB * kRowBlockBytes + 1023) / 1024 * 1024;
     static constexpr int kNBuf = 5;                                  // ring buffers
@@ -1050,11 +1050,21 @@ struct CfgPC {
     static_assert(16 + (kMaxChunk / kThreads) * kWaves <= 128, "compaction counts fit");
 };
 
+// Refills (tiles kNBuf and later) are copied by all eight waves, four rows each.
+struct CfgPCRefill : CfgPC {
+    static constexpr int kRowsPerWave = kTile / kWaves;
+    static constexpr int kDmaPerWave = kRowsPerWave;
+};
+
 // The fp8_ds_mla path (a1-a6 and the per-split part of a7). Iteration r of the
 // tile loop, after the barrier (tile r has landed; P^T of tile r - 1 is
 // published; tile r - 2 is done): the QK^T waves process tile r into P^T
-// parity r & 1; the PV waves refill tile r - 2's buffer with tile
-// r - 2 + nbuf and add V^T P^T of tile r - 1 to their slices of O.
+// parity r & 1; the PV waves add V^T P^T of tile r - 1 to their slices of O.
+// At the end of its iteration every wave copies its four rows of the tiles
+// whose buffers the barrier freed (tile r - 2's buffer takes tile
+// r - 2 + nbuf): with eight waves issuing, the copies run at about twice the
+// rate of four, and a wave stalled on one waits where it would otherwise wait
+// at the next barrier.
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_pc_kernel(const KParams p)
 {
@@ -1366,13 +1376,22 @@ void attn_pc_kernel(const KParams p)
                     qsl[G] = 127 + ex - 4;
                 }
             }
+            int issued = min(n_tiles, nbuf);     // tiles whose copies have been issued
             auto tiles = [&](auto exact_c) __attribute__((always_inline)) {
                 for (int r = 0; r <= n_tiles; ++r) {
-                    // tile r has landed; tile r - 2 is done with its P^T parity
+                    // this wave's rows of tile r have landed (it copies refills only) ...
+                    if (r < n_tiles)
+                        wait_vmcnt(CfgPCRefill::kDmaPerWave * max(0, issued - max(nbuf, r + 1)));
+                    // ... and every wave's; tile r - 2 is done with its buffer and P^T parity
                     __syncthreads();
                     if (r < n_tiles)
                         qk_tile(ring + (r % nbuf) * C::kBufBytes, min(kTile, n_valid - r * kTile), r & 1, exact_c,
                                 qh, ql, qsh, qsl, qr, m_run, l_part);
+                    const int hi = min(n_tiles, r - 1 + nbuf);
+                    for (int nt = max(issued, nbuf); nt < hi; ++nt)
+                        issue_tile<CfgPCRefill>(p.cache, lds_slots + nt * kTile, min(kTile, n_valid - nt * kTile),
+                                                ring + (nt % nbuf) * C::kBufBytes, wave, lane);
+                    issued = max(issued, hi);
                 }
             };
             if (exact_p)
@@ -1436,19 +1455,22 @@ void attn_pc_kernel(const KParams p)
             const bool exact_s = __builtin_amdgcn_readfirstlane(exact_p ? 1 : 0) != 0;
             {
                 for (int r = 0; r <= n_tiles; ++r) {
-                    // this wave's pieces of tile r have landed ...
+                    // this wave's rows of tile r have landed (eight per first
+                    // tile, four per refill) ...
                     if (r < n_tiles)
-                        wait_vmcnt(dma_w * (issued - (r + 1)));
+                        wait_vmcnt(dma_w * max(0, min(issued, nbuf) - (r + 1)) +
+                                   CfgPCRefill::kDmaPerWave * max(0, issued - max(nbuf, r + 1)));
                     // ... and every wave's; P^T of tile r - 1 is published; tile
                     // r - 2 is done with its buffer
                     __syncthreads();
-                    // fill the ring: tile nt goes into buffer nt % nbuf once its
-                    // previous tile nt - nbuf is done (< r - 1)
-                    const int hi = min(n_tiles, max(r - 1 + nbuf, nbuf));
-                    for (int nt = issued; nt < hi; ++nt)
-                        issue_tile<C>(p.cache, lds_slots + nt * kTile, min(kTile, n_valid - nt * kTile),
-                                      ring + (nt % nbuf) * C::kBufBytes, rw, lane);
-                    issued = max(issued, hi);
+                    if (r == 0) {
+                        // the rest of the first tiles, while the QK^T waves work on tile 0
+                        const int hi0 = min(n_tiles, nbuf);
+                        for (int nt = issued; nt < hi0; ++nt)
+                            issue_tile<C>(p.cache, lds_slots + nt * kTile, min(kTile, n_valid - nt * kTile),
+                                          ring + nt * C::kBufBytes, rw, lane);
+                        issued = max(issued, hi0);
+                    }
                     if (r >= 1) {
                         // ---- O^T += V^T P^T of tile r - 1 over this wave's dims
                         const int par = (r - 1) & 1;
@@ -1496,6 +1518,12 @@ void attn_pc_kernel(const KParams p)
                             }
                         }
                     }
+                    // refills whose buffers the barrier freed: rows 4 wave .. 4 wave + 3
+                    const int hi = min(n_tiles, r - 1 + nbuf);
+                    for (int nt = max(issued, nbuf); nt < hi; ++nt)
+                        issue_tile<CfgPCRefill>(p.cache, lds_slots + nt * kTile, min(kTile, n_valid - nt * kTile),
+                                                ring + (nt % nbuf) * C::kBufBytes, wave, lane);
+                    issued = max(issued, hi);
                 }
             }
             __syncthreads();     // ring, P^T and slot list are free for the next round
