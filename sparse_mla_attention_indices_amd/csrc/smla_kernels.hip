@@ -1589,9 +1589,15 @@ __global__ __launch_bounds__(256) void merge_kernel(const float *__restrict__ pa
                                                     uint16_t *__restrict__ out, float *__restrict__ lse,
                                                     int T, int H, int S)
 {
-    const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (gid >= (int64_t)T * H * (kDv / 4))
+    // Workgroup id -> (token, pair of heads): the workgroups of token t get id
+    // mod 8 = t mod 8, the XCD whose L2 the attention kernel wrote t's
+    // partials through.
+    const int wpt = H * (kDv / 4) / 256;              // workgroups per token
+    const int bid = blockIdx.x;
+    const int tt = (bid >> 3) / wpt * 8 + (bid & 7);
+    if (tt >= T)
         return;
+    const int64_t gid = ((int64_t)tt * wpt + (bid >> 3) % wpt) * 256 + threadIdx.x;
     const int c = (int)(gid % (kDv / 4));
     const int64_t th = gid / (kDv / 4);           // t * H + h
     const int t = (int)(th / H), h = (int)(th - (int64_t)t * H);
@@ -1897,8 +1903,10 @@ hipError_t launch_cache_write(CacheFormat fmt, const void *k_c, const void *k_pe
 hipError_t launch_merge(const float *part_lse, const float *part_o, void *out, float *lse, int T,
                         int H, int S, hipStream_t stream)
 {
-    const int64_t threads = (int64_t)T * H * (kDv / 4);
-    const dim3 grid((unsigned)((threads + 255) / 256));
+    // whole workgroups per token (h_q * 128 threads, h_q in {16, 32, 64, 128}),
+    // tokens padded to a multiple of 8 for the XCD mapping
+    const int64_t wpt = (int64_t)H * (kDv / 4) / 256;
+    const dim3 grid((unsigned)((T + 7) / 8 * 8 * wpt));
     uint16_t *o = (uint16_t *)out;
     switch (S) {
     case 2: hipLaunchKernelGGL(merge_kernel<2>, grid, dim3(256), 0, stream, part_o, part_lse, o, lse, T, H, S); break;
