@@ -8,7 +8,13 @@
 // fp8_ds_mla row format of the module note, and the multi-query attention with
 // 576-wide keys and 512-wide values that FlashMLASparseImpl.forward runs for
 // both cache formats. How it is computed here is this library's own design for
-// 64-wide wavefronts, MFMA and the 160 KB LDS of a gfx950 compute unit:
+// 64-wide wavefronts, MFMA and the 160 KB LDS of a gfx950 compute unit.
+//
+// attn_pc_kernel (fp8 cache, 64 heads per workgroup, the decode batches) gives
+// each SIMD one QK^T wave (16 heads over all 576 columns: S^T, online softmax,
+// P^T into LDS) and one PV wave (128 output dims of all 64 heads), PV one tile
+// behind QK^T; it is described where it is defined. attn_kernel covers the
+// bf16 cache and 16- or 32-head fp8 workgroups:
 //
 //  * Workgroup = one query token x 16, 32 or 64 heads x one part ("split") of
 //    the token's top-k list. Every wave owns 16 heads and one half of the 576
