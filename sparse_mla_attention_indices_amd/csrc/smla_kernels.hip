@@ -320,20 +320,38 @@ __device__ __forceinline__ void issue_tile(const uint8_t *__restrict__ cache, co
     const int my_slot = slots[ri < n_tile ? ri : 0];
     const uint32_t base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)LDS_PTR(uint8_t, buf) +
                                                          (uint32_t)lds_row<C>(r0));
+    if constexpr (C::kInstrPerRow == 1) {
+        // one instruction per row (fp8): the rows' addresses first, then all the
+        // copies under one lane mask
+        const uint8_t *rowp[C::kRowsPerWave];
+        uint32_t ldsp[C::kRowsPerWave];
 #pragma unroll
-    for (int i = 0; i < C::kRowsPerWave; ++i) {
-        const int r = r0 + i;
-        const int slot = __builtin_amdgcn_readlane(my_slot, i);
-        const uint8_t *row = cache + (size_t)(uint32_t)slot * C::kRowBytes;
-        // lds_row(r) - lds_row(r0): r0 is a multiple of kRowsPerWave, so whether
-        // row r crosses into the next 16-row block is known from i alone when
-        // kRowsPerWave divides 16; otherwise it is computed
-        const uint32_t lds = base + (uint32_t)(lds_row<C>(r) - lds_row<C>(r0));
+        for (int i = 0; i < C::kRowsPerWave; ++i) {
+            const int slot = __builtin_amdgcn_readlane(my_slot, i);
+            rowp[i] = cache + (size_t)(uint32_t)slot * C::kRowBytes + 16 * lane;
+            ldsp[i] = __builtin_amdgcn_readfirstlane(base + (uint32_t)(lds_row<C>(r0 + i) - lds_row<C>(r0)));
+        }
+        if (lane < C::kChunksPerRow) {
 #pragma unroll
-        for (int k = 0; k < C::kInstrPerRow; ++k) {
-            const int chunk = 64 * k + lane;
-            if (chunk < C::kChunksPerRow)
-                dma16(row + 16 * chunk, __builtin_amdgcn_readfirstlane(lds + 1024u * k));
+            for (int i = 0; i < C::kRowsPerWave; ++i)
+                dma16(rowp[i], ldsp[i]);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < C::kRowsPerWave; ++i) {
+            const int r = r0 + i;
+            const int slot = __builtin_amdgcn_readlane(my_slot, i);
+            const uint8_t *row = cache + (size_t)(uint32_t)slot * C::kRowBytes;
+            // lds_row(r) - lds_row(r0): r0 is a multiple of kRowsPerWave, so whether
+            // row r crosses into the next 16-row block is known from i alone when
+            // kRowsPerWave divides 16; otherwise it is computed
+            const uint32_t lds = base + (uint32_t)(lds_row<C>(r) - lds_row<C>(r0));
+#pragma unroll
+            for (int k = 0; k < C::kInstrPerRow; ++k) {
+                const int chunk = 64 * k + lane;
+                if (chunk < C::kChunksPerRow)
+                    dma16(row + 16 * chunk, __builtin_amdgcn_readfirstlane(lds + 1024u * k));
+            }
         }
     }
 }
