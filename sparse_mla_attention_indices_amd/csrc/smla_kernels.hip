@@ -1865,6 +1865,9 @@ hipError_t launch_fmt(const KParams &p, hipStream_t stream)
         // fp8 cache, 64 heads per workgroup: QK^T waves and PV waves
         if (heads == 64)
             return launch_pc(p, stream);
+        if (heads == 32)
+            return launch_one<FMT, 2>(p, stream);
+        return launch_one<FMT, 1>(p, stream);
     }
     if (heads == 64)
         return launch_one<FMT, 4>(p, stream);

@@ -117,6 +117,31 @@ def test_degenerate_rows(fmt):
         assert_parity(w, out, lse, label=f"degenerate {fmt} s{splits}")
 
 
+@pytest.mark.parametrize("h_q", [64, 128])
+def test_valid_counts_across_tile_ring_and_short_list_bounds(h_q):
+    """64-head fp8 workgroups (QK^T and PV waves, a ring of five 32-row tiles, or
+    three for lists of at most 128 valid rows): per-token valid counts of 0, 1,
+    around one tile, around the 128-row short-list bound, and past the ring's
+    wrap; a token with a request id outside the table; unsplit, planned and
+    3-way split calls."""
+    counts = [0, 1, 31, 32, 33, 64, 96, 127, 128, 129, 160, 161, 224, 300, 500, 600]
+    w = small(71 + h_q, "fp8", h_q, 600, n_req=4, tok_per_req=4, ctx=(700, 900), p_invalid=0.0)
+    rng = np.random.default_rng(71 + h_q)
+    for t, n in enumerate(counts):
+        keep = rng.permutation(600)[:n]
+        row = np.full(600, -1, dtype=np.int32)
+        row[keep] = w.topk_indices[t, keep]
+        w.topk_indices[t] = row
+    w.req_id_per_token[3] = w.num_reqs + 2      # request id outside the table: nothing valid
+    dw = DeviceWorkload(w)
+    want = oracle.convert_indices(w.req_id_per_token, w.block_table, w.topk_indices, w.num_blocks)
+    for splits in (1, 0, 3):
+        log(f"[case] ring bounds fp8 h_q={h_q} splits={splits}")
+        out, lse, phys = dw.run(num_splits=splits, with_phys=True)
+        assert np.array_equal(phys.cpu().numpy(), want)
+        assert_parity(w, out, lse, label=f"ring bounds h{h_q} s{splits}")
+
+
 @pytest.mark.parametrize("fmt", ["bf16", "fp8"])
 def test_short_lists_are_exact_up_to_output_rounding(fmt):
     """Tokens with 1..8 valid rows put large weights on few rows, so |o| can reach the
