@@ -1061,6 +1061,11 @@ struct CfgPC {
     static constexpr int kOffP = kNBuf * kBufBytes;
     static constexpr int kOffPLo = kNBufExact * kBufBytes;           // short lists: P^T lo terms
     static constexpr int kOffHead = kOffP + kPBytes;                 // flags, factors, max and sums
+    // q of the four QK^T waves' head blocks (16 rows of 1152 bytes each), held
+    // from the kernel start to the first barrier of the tile loop in space the
+    // loop fills only after it: ring buffers 2.. and P^T
+    static constexpr int kQBlockBytes = 16 * kDqk * 2;
+    static constexpr int kOffQ = 2 * kBufBytes;
     static constexpr int kOffSlots = kOffHead + 1024;
     static constexpr int kOffMisc = kOffSlots + kSlotsBytes;         // compaction counts
     static constexpr int kLdsBytes = kOffMisc + 512;
@@ -1069,6 +1074,8 @@ struct CfgPC {
     static_assert(kChunksPerRow <= 64, "one copy instruction per row");
     static_assert(kOffPLo + kPBytes <= kOffP, "lo terms fit the ring buffers a short list leaves free");
     static_assert(kNBufExact >= 3, "the ring holds tiles r - 1, r and the copy of r + 1");
+    static_assert(kOffQ + 4 * kQBlockBytes <= kOffHead, "q staging stays clear of tiles 0, 1 and the flags");
+    static_assert(kQBlockBytes % 1024 == 0, "q staging in whole-wave copies");
     static_assert(kLdsBytes <= 160 * 1024, "LDS of one gfx950 workgroup");
     static_assert(kHeads * kStageF32 * 4 <= kOffHead, "staging fits the ring and P^T");
     static_assert(16 + (kMaxChunk / kThreads) * kWaves <= 128, "compaction counts fit");
@@ -1305,6 +1312,16 @@ void attn_pc_kernel(const KParams p)
                                                p.MB, p.NB);
     };
 
+    // QK^T waves: q of their 16 heads (contiguous rows) copied into LDS first,
+    // so its round trip overlaps the indices' and the lookups'
+    if (qk_role) {
+        const uint8_t *qsrc = (const uint8_t *)(p.q + ((size_t)t * p.H + wg_head0 + 16 * rw) * kDqk);
+        const uint32_t qdst = __builtin_amdgcn_readfirstlane(
+            (uint32_t)(uintptr_t)LDS_PTR(uint8_t, smem + C::kOffQ + rw * C::kQBlockBytes));
+#pragma unroll
+        for (int k = 0; k < C::kQBlockBytes / 1024; ++k)
+            dma16(qsrc + 1024 * k + 16 * lane, qdst + 1024u * k);
+    }
     // the first round's indices, then their block-table lookups
     int slotv[kPer];
     {
@@ -1339,7 +1356,8 @@ void attn_pc_kernel(const KParams p)
                 // q, loaded and written exactly as hi + lo e4m3 terms while the
                 // PV waves' first copies are in flight
                 uint4 qraw[18];     // [4 * G + c] latent of group G, [16 + ks] RoPE k-step ks
-                const uint16_t *qrow = p.q + ((size_t)t * p.H + wg_head0 + 16 * rw + n16) * kDqk;
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");     // this wave's q copies
+                const uint16_t *qrow = (const uint16_t *)(smem + C::kOffQ + rw * C::kQBlockBytes) + n16 * kDqk;
 #pragma unroll
                 for (int G = 0; G < 4; ++G)
 #pragma unroll
