@@ -80,17 +80,23 @@ def algorithmic_work(w):
 
 def cache_writer_bench(torch, smla, dev, stream, flush, sink, steps: int):
     """The cache writer (smla_concat_and_cache_mla, fp8_ds_mla) on a prefill-sized
-    batch (16384 tokens into random slots of a 1.3 GB pool) and on the decode
-    batch size (64 tokens), cold cache. Algorithmic bytes per token: 1024 latent +
-    128 RoPE + 8 slot read, 656 written."""
+    batch of 16384 tokens into a 1.3 GB pool, with two slot patterns: random slots,
+    and paged slots (256 blocks taken in shuffled order, each filled by 64
+    consecutive tokens, as a prefill request's block table assigns them). Also the
+    decode batch size (64 tokens, random slots). Cold cache. Algorithmic bytes
+    per token: 1024 latent + 128 RoPE + 8 slot read, 656 written."""
     res = {}
     g = torch.Generator(device="cpu").manual_seed(21)
     NB = 32768
     cache = torch.zeros((NB, 64, 656), dtype=torch.uint8, device=dev)
-    for T in (16384, 64):
+    for T, name in ((16384, "tokens_16384"), (16384, "tokens_16384_paged"), (64, "tokens_64")):
         lat = (torch.randn(T, 512, generator=g) * 2).to(torch.bfloat16).to(dev)
         rope = torch.randn(T, 64, generator=g).to(torch.bfloat16).to(dev)
-        slots = torch.randperm(NB * 64, generator=g)[:T].to(torch.int64).to(dev)
+        if name.endswith("paged"):
+            blocks = torch.randperm(NB, generator=g)[:T // 64].to(torch.int64)
+            slots = (blocks[:, None] * 64 + torch.arange(64)).reshape(-1).to(dev)
+        else:
+            slots = torch.randperm(NB * 64, generator=g)[:T].to(torch.int64).to(dev)
         for _ in range(3):
             smla.smla_concat_and_cache_mla(lat, rope, cache, slots, stream=stream)
         e0 = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
@@ -103,7 +109,7 @@ def cache_writer_bench(torch, smla, dev, stream, flush, sink, steps: int):
         torch.cuda.synchronize()
         ms = float(np.mean([a.elapsed_time(b) for a, b in zip(e0, e1)]))
         nbytes = T * (1024 + 128 + 8 + 656)
-        res[f"tokens_{T}"] = {"ms": ms, "tokens_per_s": T / (ms * 1e-3), "algorithmic_bytes": nbytes,
+        res[name] = {"ms": ms, "tokens_per_s": T / (ms * 1e-3), "algorithmic_bytes": nbytes,
                               "achieved_GBps": nbytes / (ms * 1e-3) / 1e9,
                               "frac_of_hbm_peak": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
     del cache

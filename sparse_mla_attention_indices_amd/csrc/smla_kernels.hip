@@ -1811,50 +1811,88 @@ __device__ __forceinline__ uint32_t bf16_of_product(float x, float sc)
 }
 
 // Upconvert [flashmla_sparse.py page, _forward_fp8_kv_separate_prefill_decode:
-// cp_gather_and_upconvert_fp8_kv_cache]: one wave per (request, position);
-// lane l turns latent bytes 8l .. 8l + 7 (scale group l / 16) into 16 bytes of
-// bf16, lanes 0..7 copy the RoPE. A position past the table, or a table entry
-// outside the cache, writes zeros; rows outside the workspace are not written.
+// cp_gather_and_upconvert_fp8_kv_cache]. One wave per R consecutive positions of
+// one request: R divides the cache block size, so the R rows share one
+// block-table entry and lie back to back both in their cache block and in the
+// workspace. The wave reads its three index words once, issues every row load
+// before the first conversion, then lane l turns latent bytes 8l .. 8l + 7
+// (scale group l / 16) of each row into 16 bytes of bf16. The 4R per-128
+// scales come in with one dword load (lane 4r + g holds row r's scale g) and
+// reach their lanes through a cross-lane read; the RoPE bytes are copied as
+// R * 8 16-byte pieces. A position past the table, or a table entry outside
+// the cache, writes zeros; rows outside the workspace are not written.
+constexpr int kUpRows = 4;
+
+template <int R>
 __global__ __launch_bounds__(256) void upconvert_kernel(const uint8_t *__restrict__ cache, int64_t num_blocks,
                                                         const int32_t *__restrict__ bt, int max_blocks,
                                                         const int32_t *__restrict__ seq_lens,
                                                         const int32_t *__restrict__ ws_starts,
                                                         uint16_t *__restrict__ ws, int64_t ws_rows)
 {
+    static_assert(kBlock % R == 0 && R >= 1 && R <= 16, "rows per wave");
+    constexpr int kRope = (R * 8 + 63) / 64;     // 16-byte RoPE pieces per lane
     const int b = blockIdx.y;
-    const int pos = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
-    if (pos >= seq_lens[b])
-        return;
-    const int64_t w = (int64_t)ws_starts[b] + pos;
-    if (w < 0 || w >= ws_rows)
-        return;
-    uint4 *dst = (uint4 *)(ws + w * kDqk);
-    const int blk = pos >> 6;
+    const int p0 = (blockIdx.x * 4 + wave) * R;
+    const int blk = p0 / kBlock;
+    const int len = seq_lens[b];
+    const int64_t w0 = (int64_t)ws_starts[b] + p0;
     const int base = blk < max_blocks ? bt[(size_t)b * max_blocks + blk] : -1;
+    const int n = min(R, len - p0);
+    if (n <= 0)
+        return;
     if (base < 0 || (int64_t)base >= num_blocks) {
-        dst[lane] = make_uint4(0u, 0u, 0u, 0u);
-        if (lane < 8)
-            dst[64 + lane] = make_uint4(0u, 0u, 0u, 0u);
+        for (int r = 0; r < n; ++r) {
+            const int64_t w = w0 + r;
+            if (w >= 0 && w < ws_rows) {
+                uint4 *dst = (uint4 *)(ws + w * kDqk);
+                dst[lane] = make_uint4(0u, 0u, 0u, 0u);
+                if (lane < 8)
+                    dst[64 + lane] = make_uint4(0u, 0u, 0u, 0u);
+            }
+        }
         return;
     }
-    const uint8_t *row = cache + ((int64_t)base * kBlock + (pos & (kBlock - 1))) * kFp8RowBytes;
-    const uint2 v = *(const uint2 *)(row + 8 * lane);
-    const float sc = *(const float *)(row + 512 + 4 * (lane >> 4));
-    uint4 rope = make_uint4(0u, 0u, 0u, 0u);
-    if (lane < 8)
-        rope = *(const uint4 *)(row + 528 + 16 * lane);
-    const f32x2 x[4] = {__builtin_amdgcn_cvt_scalef32_pk_f32_fp8(v.x, 1.0f, false),
-                        __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(v.x, 1.0f, true),
-                        __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(v.y, 1.0f, false),
-                        __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(v.y, 1.0f, true)};
-    uint32_t h[4];
+    // rows n .. R - 1 (the end of the context) re-read row n - 1 and are not stored
+    const uint8_t *rows = cache + ((int64_t)base * kBlock + p0 % kBlock) * kFp8RowBytes;
+    uint2 v[R];
 #pragma unroll
-    for (int k = 0; k < 4; ++k)
-        h[k] = bf16_of_product(x[k][0], sc) | (bf16_of_product(x[k][1], sc) << 16);
-    dst[lane] = make_uint4(h[0], h[1], h[2], h[3]);
-    if (lane < 8)
-        dst[64 + lane] = rope;
+    for (int r = 0; r < R; ++r)
+        v[r] = *(const uint2 *)(rows + (int64_t)min(r, n - 1) * kFp8RowBytes + 8 * lane);
+    float sc_all = 0.f;
+    if (lane < 4 * R)
+        sc_all = *(const float *)(rows + (int64_t)min(lane >> 2, n - 1) * kFp8RowBytes + 512 + 4 * (lane & 3));
+    uint4 rope[kRope];
+#pragma unroll
+    for (int j = 0; j < kRope; ++j) {
+        const int i = min(j * 64 + lane, R * 8 - 1);
+        rope[j] = *(const uint4 *)(rows + (int64_t)min(i >> 3, n - 1) * kFp8RowBytes + 528 + 16 * (i & 7));
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const float sc = __shfl(sc_all, 4 * r + (lane >> 4));
+        const int64_t w = w0 + r;
+        if (r < n && w >= 0 && w < ws_rows) {
+            const f32x2 x[4] = {__builtin_amdgcn_cvt_scalef32_pk_f32_fp8(v[r].x, 1.0f, false),
+                                __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(v[r].x, 1.0f, true),
+                                __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(v[r].y, 1.0f, false),
+                                __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(v[r].y, 1.0f, true)};
+            uint32_t h[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                h[k] = bf16_of_product(x[k][0], sc) | (bf16_of_product(x[k][1], sc) << 16);
+            ((uint4 *)(ws + w * kDqk))[lane] = make_uint4(h[0], h[1], h[2], h[3]);
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < kRope; ++j) {
+        const int i = j * 64 + lane;
+        const int64_t w = w0 + (i >> 3);
+        if (i < R * 8 && (i >> 3) < n && w >= 0 && w < ws_rows)
+            ((uint4 *)(ws + w * kDqk))[64 + (i & 7)] = rope[j];
+    }
 }
 
 template <int FMT, int NHH>
@@ -1926,8 +1964,8 @@ hipError_t launch_upconvert(const void *cache, int64_t num_blocks, const int32_t
                             const int32_t *seq_lens, const int32_t *ws_starts, int batch, int max_seq_len,
                             void *workspace, int64_t workspace_rows, hipStream_t stream)
 {
-    const dim3 grid((unsigned)((max_seq_len + 3) / 4), (unsigned)batch);
-    hipLaunchKernelGGL(upconvert_kernel, grid, dim3(256), 0, stream, (const uint8_t *)cache, num_blocks,
+    const dim3 grid((unsigned)((max_seq_len + 4 * kUpRows - 1) / (4 * kUpRows)), (unsigned)batch);
+    hipLaunchKernelGGL(upconvert_kernel<kUpRows>, grid, dim3(256), 0, stream, (const uint8_t *)cache, num_blocks,
                        block_table, max_blocks, seq_lens, ws_starts, (uint16_t *)workspace, workspace_rows);
     return hipGetLastError();
 }

@@ -52,16 +52,18 @@ def tricky_rows(rng, T):
     return lat
 
 
+@pytest.mark.parametrize("T", [300, 303, 1])
 @pytest.mark.parametrize("fmt", ["fp8_ds_mla", "auto"])
-def test_cache_write_bit_exact(fmt):
+def test_cache_write_bit_exact(fmt, T):
+    """T = 303 ends inside a wave's group of tokens; T = 1 is a lone token."""
     rng = np.random.default_rng(11)
-    T, NB = 300, 16
+    NB = 16
     lat_b = bits_of(tricky_rows(rng, T))
     rope_b = bits_of(rng.normal(0, 2, (T, 64)))
     slots = rng.permutation(NB * 64)[:T].astype(np.int64)
     slots[::17] = -1                      # skipped
-    slots[5] = NB * 64                    # past the cache: skipped
-    slots[6] = NB * 64 + 1000
+    slots[5:6] = NB * 64                  # past the cache: skipped
+    slots[6:7] = NB * 64 + 1000
     f = oracle.FP8_CACHE if fmt == "fp8_ds_mla" else oracle.BF16_CACHE
     if fmt == "fp8_ds_mla":
         init = rng.integers(0, 256, (NB, 64, 656), dtype=np.uint8)

@@ -89,6 +89,27 @@ def test_upconvert_bit_exact(kind):
     assert bad.size == 0, f"rows differ: {bad[:10]}"
 
 
+def test_upconvert_negative_start_and_positions_past_the_table():
+    """A request whose workspace start is negative (its first rows are not
+    written) and whose length runs past its block-table row (those positions
+    write zeros), next to one whose length ends inside a 16-row group."""
+    cache = W.random_fp8_cache(5, 99, 9)
+    lens = np.array([300, 37], dtype=np.int32)
+    bt = np.array([[4, 8, 2, 6], [1, 0, 0, 0]], dtype=np.int32)
+    starts = np.array([-21, 290], dtype=np.int32)
+    rows = 330
+    init = np.full((rows, 576), 0x7E57, dtype=np.uint16)
+    want = oracle.gather_upconvert(cache, bt, lens, starts, rows, workspace=init.copy())
+    assert (want[236:279] == 0).all() and (want[279:290] == 0x7E57).all()
+    ws = bf16_tensor(init)
+    log("[case] upconvert negative start, positions past the table")
+    smla.smla_gather_upconvert_fp8(_dev(cache), _dev(bt), _dev(lens), _dev(starts), int(lens.max()), ws)
+    torch.cuda.synchronize()
+    got = ws.view(torch.int16).cpu().numpy().view(np.uint16)
+    bad = np.nonzero((got != want).any(axis=1))[0]
+    assert bad.size == 0, f"rows differ: {bad[:10]}"
+
+
 def test_upconvert_full_size_prefill_part_sampled():
     """Config 5's prefill contexts (131072 and 65536 positions, 196608 rows) in one
     launch; sampled rows against the oracle, bit-exact."""
