@@ -1517,6 +1517,9 @@ void attn_pc_kernel(const KParams p)
                         // ---- O^T += V^T P^T of tile r - 1 over this wave's dims
                         const int par = (r - 1) & 1;
                         const uint8_t *buf = ring + ((r - 1) % nbuf) * C::kBufBytes;
+                        // every LDS read of the tile issued before the first wait: V^T,
+                        // the four head blocks' rescale flags (one 16-byte read) and
+                        // their P^T hi operands
                         uint2 vf[8];
 #pragma unroll
                         for (int db = 0; db < 8; ++db) {
@@ -1524,15 +1527,23 @@ void attn_pc_kernel(const KParams p)
                                 LDS_PTR(i32x2, buf + off_v8 + 16 * db));
                             vf[db] = make_uint2((uint32_t)v[0], (uint32_t)v[1]);
                         }
+                        const int4 fl = *(const int4 *)(resc_flag + par * 4);
+                        bf16x8 ph[4];
 #pragma unroll
-                        for (int hb = 0; hb < 4; ++hb) {
-                            // a scalar branch: O is rescaled in place (a lane-divergent
-                            // one would keep a second copy of the accumulators)
-                            if (__builtin_amdgcn_readfirstlane(resc_flag[par * 4 + hb])) {
-                                const float al = alpha_lds[(par * 4 + hb) * 16 + n16];
+                        for (int hb = 0; hb < 4; ++hb)
+                            ph[hb] = p_hi[((par * 4 + hb) * 4 + rw) * 64 + lane];
+                        // scalar branches: O is rescaled in place (a lane-divergent one
+                        // would keep a second copy of the accumulators)
+                        if (__builtin_amdgcn_readfirstlane(fl.x | fl.y | fl.z | fl.w)) {
+                            const int fls[4] = {fl.x, fl.y, fl.z, fl.w};
 #pragma unroll
-                                for (int db = 0; db < 8; ++db)
-                                    o[hb * 8 + db] *= al;
+                            for (int hb = 0; hb < 4; ++hb) {
+                                if (__builtin_amdgcn_readfirstlane(fls[hb])) {
+                                    const float al = alpha_lds[(par * 4 + hb) * 16 + n16];
+#pragma unroll
+                                    for (int db = 0; db < 8; ++db)
+                                        o[hb * 8 + db] *= al;
+                                }
                             }
                         }
                         // V^T converted four blocks at a time, each block feeding the
@@ -1545,11 +1556,10 @@ void attn_pc_kernel(const KParams p)
                                 va[d] = e4m3x8_to_bf16x8(vf[4 * half + d]);
 #pragma unroll
                             for (int hb = 0; hb < 4; ++hb) {
-                                const bf16x8 ph = p_hi[((par * 4 + hb) * 4 + rw) * 64 + lane];
 #pragma unroll
                                 for (int d = 0; d < 4; ++d)
                                     o[hb * 8 + 4 * half + d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                                        va[d], ph, o[hb * 8 + 4 * half + d], 0, 0, 0);
+                                        va[d], ph[hb], o[hb * 8 + 4 * half + d], 0, 0, 0);
                                 if (exact_s) {
                                     const bf16x8 pl = p_lo[((par * 4 + hb) * 4 + rw) * 64 + lane];
 #pragma unroll
