@@ -29,10 +29,14 @@ Plan make_plan(int num_tokens, int h_q, int topk, int num_cus, int forced_splits
         // otherwise cut each token's list so the grid covers every workgroup
         // slot once: 64-head workgroups take a CU each, 32- and 16-head ones
         // fit two per CU.
+        // A list of at most kShortList positions is not cut once every CU has a
+        // workgroup: the merge launch then costs more than the second
+        // workgroup per CU gains.
         const int64_t units = (int64_t)num_tokens * p.head_blocks;
         const int64_t slots = (int64_t)num_cus * (h_q >= kHeadsPerGroup ? 1 : 2);
         const int64_t tiles = (topk + kBlock - 1) / kBlock;
-        if (units > 0 && units < slots)
+        constexpr int kShortList = 512;
+        if (units > 0 && units < slots && !(units >= num_cus && topk <= kShortList))
             splits = (int)std::min<int64_t>(std::min<int64_t>(tiles, kMaxSplits), (slots + units - 1) / units);
         splits = std::max(splits, 1);
     }

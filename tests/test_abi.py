@@ -59,6 +59,11 @@ def test_plan_fills_the_chip_for_small_decode_batches(lib):
     assert ws == up(o_off + rows * 512 * 4)
     # two-wave workgroups (h_q = 16) fit two per CU: 256 tokens x 16 heads -> 2 splits
     assert smla.smla_plan(256, 16, 2048, 256)[0] == 2
+    assert smla.smla_plan(256, 16, 1024, 256)[0] == 2
+    # ... unless the list is short (<= 512) and every CU already has a workgroup
+    assert smla.smla_plan(256, 16, 512, 256) == (1, 0)
+    assert smla.smla_plan(255, 16, 512, 256)[0] == 3         # 255 < 256 CUs: split as before
+    assert smla.smla_plan(256, 32, 512, 256) == (1, 0)
     # 32-head workgroups fit two per CU: 64 tokens x 32 heads -> 8 splits
     assert smla.smla_plan(64, 32, 2048, 256)[0] == 8
     # 128 heads, 32 tokens: two 64-head workgroups per token -> 4 splits
