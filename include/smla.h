@@ -243,8 +243,9 @@ smla_status smla_convert_indices_workspace(const int32_t *req_id_per_token, cons
  *   workspace         bf16 [workspace_rows, 576], 16-B aligned; rows outside
  *                     [0, workspace_rows) are never written, rows no request
  *                     covers keep their contents
- * Errors: SMLA_ERR_NULL, SMLA_ERR_SHAPE, SMLA_ERR_ALIGN, SMLA_ERR_HIP. batch == 0
- * or max_seq_len == 0 is a no-op. */
+ * Errors: SMLA_ERR_NULL, SMLA_ERR_SHAPE (also for batch > 65535: cut larger
+ * chunks into several calls), SMLA_ERR_ALIGN, SMLA_ERR_HIP. batch == 0 or
+ * max_seq_len == 0 is a no-op. */
 smla_status smla_gather_upconvert_fp8(const void *kv_cache, int64_t num_blocks, const int32_t *block_table,
                                       int32_t max_blocks_per_req, const int32_t *seq_lens,
                                       const int32_t *workspace_starts, int32_t batch, int32_t max_seq_len,

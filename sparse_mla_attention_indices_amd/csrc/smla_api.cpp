@@ -353,13 +353,16 @@ smla_status smla_convert_indices_workspace(const int32_t *req_id_per_token, cons
                : SMLA_ERR_HIP;
 }
 
+// requests of one upconvert call: the second grid dimension of its launch
+constexpr int32_t kMaxUpconvertBatch = 65535;
+
 smla_status smla_gather_upconvert_fp8(const void *kv_cache, int64_t num_blocks, const int32_t *block_table,
                                       int32_t max_blocks_per_req, const int32_t *seq_lens,
                                       const int32_t *workspace_starts, int32_t batch, int32_t max_seq_len,
                                       void *workspace, int64_t workspace_rows, hipStream_t stream)
 {
-    if (batch < 0 || max_seq_len < 0 || workspace_rows < 0 || max_blocks_per_req < 1 || num_blocks < 1 ||
-        num_blocks > (int64_t)INT32_MAX / smla::kBlock)
+    if (batch < 0 || batch > kMaxUpconvertBatch || max_seq_len < 0 || workspace_rows < 0 ||
+        max_blocks_per_req < 1 || num_blocks < 1 || num_blocks > (int64_t)INT32_MAX / smla::kBlock)
         return SMLA_ERR_SHAPE;
     if (batch == 0 || max_seq_len == 0)
         return SMLA_OK;

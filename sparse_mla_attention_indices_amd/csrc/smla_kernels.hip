@@ -1845,12 +1845,12 @@ __global__ __launch_bounds__(256) void upconvert_kernel(const uint8_t *__restric
     const int b = blockIdx.y;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
-    const int p0 = (blockIdx.x * 4 + wave) * R;
-    const int blk = p0 / kBlock;
+    const int64_t p0 = ((int64_t)blockIdx.x * 4 + wave) * R;
+    const int64_t blk = p0 / kBlock;
     const int len = seq_lens[b];
     const int64_t w0 = (int64_t)ws_starts[b] + p0;
     const int base = blk < max_blocks ? bt[(size_t)b * max_blocks + blk] : -1;
-    const int n = min(R, len - p0);
+    const int n = (int)min((int64_t)R, len - p0);
     if (n <= 0)
         return;
     if (base < 0 || (int64_t)base >= num_blocks) {
@@ -1974,7 +1974,7 @@ hipError_t launch_upconvert(const void *cache, int64_t num_blocks, const int32_t
                             const int32_t *seq_lens, const int32_t *ws_starts, int batch, int max_seq_len,
                             void *workspace, int64_t workspace_rows, hipStream_t stream)
 {
-    const dim3 grid((unsigned)((max_seq_len + 4 * kUpRows - 1) / (4 * kUpRows)), (unsigned)batch);
+    const dim3 grid((unsigned)(((int64_t)max_seq_len + 4 * kUpRows - 1) / (4 * kUpRows)), (unsigned)batch);
     hipLaunchKernelGGL(upconvert_kernel<kUpRows>, grid, dim3(256), 0, stream, (const uint8_t *)cache, num_blocks,
                        block_table, max_blocks, seq_lens, ws_starts, (uint16_t *)workspace, workspace_rows);
     return hipGetLastError();

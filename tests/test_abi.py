@@ -310,7 +310,7 @@ def _upconvert(lib, kv=A16, NB=8, bt=A16, MB=4, sl=A16, st=A16, B=2, L=100, ws=A
 @pytest.mark.parametrize("kw,code", [
     (dict(kv=None), 1), (dict(bt=None), 1), (dict(sl=None), 1), (dict(st=None), 1), (dict(ws=None), 1),
     (dict(B=-1), 2), (dict(L=-1), 2), (dict(rows=-1), 2), (dict(MB=0), 2), (dict(NB=0), 2),
-    (dict(NB=(1 << 31) // 64 + 1), 2),
+    (dict(NB=(1 << 31) // 64 + 1), 2), (dict(B=65536), 2),
     (dict(kv=MIS), 3), (dict(ws=A16B + 8), 3), (dict(bt=A16 + 2), 3), (dict(sl=A16 + 1), 3),
 ])
 def test_upconvert_rejects(lib, kw, code):
