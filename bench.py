@@ -6,9 +6,10 @@ paged cache (656-byte rows, block size 64, shuffled block table), bf16 q. One
 step = the whole hot path over the batch (index conversion, gather + dequant,
 QK^T, softmax, PV, split merge), inputs already resident in HBM: one
 smla_decode_fp8 call (the attention kernel, then the merge kernel). A second
-pass issues the same two kernels as smla_decode_fp8 with partials_only followed
-by smla_merge_partials, with a HIP event between them, to time each kernel; the
-roofline object is the attention kernel's.
+pass issues the same call in its two stages (the attention kernel with the
+merge deferred, then the merge only: together bit-identical to the call), with
+a HIP event between them, to time each kernel; the roofline object is the
+attention kernel's.
 
 Cold-cache timing: before every timed step a 1 GiB buffer is read (outside the
 timed events) so neither L2 nor the 256 MB MALL holds the 95 MB working set; a
@@ -232,10 +233,8 @@ def main():
     lse = torch.empty((w.num_tokens, w.h_q), dtype=torch.float32, device=dev)
     ws_bytes = smla.smla_workspace_size(w.num_tokens, w.h_q, w.topk)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
-    ws_parts = torch.empty(max(smla.smla_workspace_size(w.num_tokens, w.h_q, w.topk, partials_only=True), 1),
-                           dtype=torch.uint8, device=dev)
     props = torch.cuda.get_device_properties(dev)
-    splits, _ = smla.smla_plan(w.num_tokens, w.h_q, w.topk, props.multi_processor_count, partials_only=True)
+    splits, _ = smla.smla_plan(w.num_tokens, w.h_q, w.topk, props.multi_processor_count)
     flush = torch.ones(1 << 28, dtype=torch.int32, device=dev)     # 1 GiB, read to evict caches
     sink = torch.empty((), dtype=torch.int32, device=dev)
 
@@ -244,11 +243,12 @@ def main():
                              stream=stream)
 
     def attention():
-        smla.smla_decode_fp8(q, cache, bt, req, idx, w.sm_scale, workspace=ws_parts, stream=stream,
-                             partials_only=True)
+        smla.smla_decode_fp8(q, cache, bt, req, idx, w.sm_scale, out=out, lse=lse, workspace=ws,
+                             stream=stream, stage="attention")
 
     def merge():
-        smla.smla_merge_partials(ws_parts, w.num_tokens, w.h_q, splits, out=out, lse=lse, stream=stream)
+        smla.smla_decode_fp8(q, cache, bt, req, idx, w.sm_scale, out=out, lse=lse, workspace=ws,
+                             stream=stream, stage="merge")
 
     for i in range(args.warmup):
         torch.amax(flush, 0, out=sink)
@@ -270,7 +270,7 @@ def main():
     t_wall = time.perf_counter() - t_wall
     cold_ms = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
 
-    # per-kernel times: the same kernels issued as two calls with an event between
+    # per-kernel times: the call in its two stages, with an event between
     a0, a1, m1 = events(args.steps), events(args.steps), events(args.steps)
     for i in range(args.steps):
         torch.amax(flush, 0, out=sink)

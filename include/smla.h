@@ -79,7 +79,20 @@ typedef enum smla_status {
        workspace rows of smla_convert_indices_workspace. block_table and
        req_id_per_token are not read and may be NULL; num_reqs and
        max_blocks_per_req are ignored. */
-#define SMLA_FLAG_ALL (SMLA_FLAG_PARTIALS_ONLY | SMLA_FLAG_SLOT_INDICES)
+#define SMLA_FLAG_DEFER_MERGE 0x4u
+    /* A call whose lists are split launches its attention kernel only and
+       leaves the call's own per-part results in the workspace (their form may
+       differ from what SMLA_FLAG_PARTIALS_ONLY writes). The same call repeated
+       with SMLA_FLAG_MERGE_ONLY and the same workspace, out and lse finishes
+       it: together the two write what one ordinary call writes, bit for bit.
+       An unsplit call writes its result at once. */
+#define SMLA_FLAG_MERGE_ONLY 0x8u
+    /* Only the merge of a call made with SMLA_FLAG_DEFER_MERGE and the same
+       arguments (a no-op when the call is not split); it reads the workspace,
+       not the inputs. DEFER_MERGE and MERGE_ONLY together, or either with
+       PARTIALS_ONLY, is SMLA_ERR_ARG. */
+#define SMLA_FLAG_ALL (SMLA_FLAG_PARTIALS_ONLY | SMLA_FLAG_SLOT_INDICES | SMLA_FLAG_DEFER_MERGE | \
+                       SMLA_FLAG_MERGE_ONLY)
 
 /* Tuning options (host struct, may be NULL for defaults). */
 typedef struct smla_options {
@@ -266,8 +279,9 @@ smla_status smla_gather_upconvert_fp8(const void *kv_cache, int64_t num_blocks, 
  *   lse               fp32 [num_tokens, h_q] natural-log LSE of the scaled logits; may be NULL
  *   phys_indices_out  int32 [num_tokens, topk] converted slots (-1 = invalid), bit-identical
  *                     to smla_convert_indices; may be NULL
- *   workspace         device scratch for the per-part results of a top-k split (fp32
- *                     partial outputs and their lse), 256-B aligned; may be NULL when
+ *   workspace         device scratch for the per-part results of a top-k split (partial
+ *                     outputs, their lse and, for a call that merges its own parts, one
+ *                     int32 flag per token and part), 256-B aligned; may be NULL when
  *                     smla_workspace_size reports 0 bytes for these sizes. Its contents
  *                     need not be initialised; they are written before they are read
  *                     within the call. Calls that overlap in time (other streams) must

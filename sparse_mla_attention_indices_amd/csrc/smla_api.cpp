@@ -47,6 +47,10 @@ Plan make_plan(int num_tokens, int h_q, int topk, int num_cus, int forced_splits
         p.part_lse_off = 0;
         p.part_o_off = partials_o_offset(rows);
         p.workspace = align_up(p.part_o_off + rows * kDv * sizeof(float), 256);
+        if (!partials) {
+            p.part_exact_off = p.workspace;
+            p.workspace = align_up(p.part_exact_off + (size_t)num_tokens * p.num_splits * sizeof(int32_t), 256);
+        }
     }
     return p;
 }
@@ -60,6 +64,10 @@ smla_status check_options(const smla_options *o)
     if (o == nullptr)
         return SMLA_OK;
     if (o->num_splits < 0 || (o->flags & ~(uint32_t)SMLA_FLAG_ALL) != 0)
+        return SMLA_ERR_ARG;
+    const uint32_t stages = o->flags & (SMLA_FLAG_DEFER_MERGE | SMLA_FLAG_MERGE_ONLY);
+    if (stages == (SMLA_FLAG_DEFER_MERGE | SMLA_FLAG_MERGE_ONLY) ||
+        (stages != 0 && (o->flags & SMLA_FLAG_PARTIALS_ONLY)))
         return SMLA_ERR_ARG;
     for (int i = 0; i < 6; ++i)
         if (o->reserved[i] != 0)
@@ -170,7 +178,11 @@ smla_status attention_entry(CacheFormat fmt, const void *q, const void *kv_cache
     a.max_blocks = max_blocks_per_req;
     a.num_blocks = num_blocks;
     a.slot_indices = slot_in;
-    return launch_attention(fmt, a, plan, partials_only, stream) == hipSuccess
+    const AttnStage stage = !options                                      ? AttnStage::kBoth
+                            : (options->flags & SMLA_FLAG_DEFER_MERGE) ? AttnStage::kAttentionOnly
+                            : (options->flags & SMLA_FLAG_MERGE_ONLY)  ? AttnStage::kMergeOnly
+                                                                       : AttnStage::kBoth;
+    return launch_attention(fmt, a, plan, partials_only, stage, stream) == hipSuccess
                ? SMLA_OK
                : SMLA_ERR_HIP;
 }
@@ -263,8 +275,8 @@ smla_status smla_merge_partials(const void *partials, size_t partials_bytes, int
     if (partials_bytes < o_off + rows * smla::kDv * sizeof(float))
         return SMLA_ERR_WORKSPACE;
     const float *base = (const float *)partials;
-    return smla::launch_merge(base, (const float *)((const char *)partials + o_off), out, lse, num_tokens,
-                              h_q, num_parts, stream) == hipSuccess
+    return smla::launch_merge(base, (const float *)((const char *)partials + o_off), nullptr, out, lse,
+                              num_tokens, h_q, num_parts, stream) == hipSuccess
                ? SMLA_OK
                : SMLA_ERR_HIP;
 }

@@ -32,8 +32,9 @@ struct Plan {
     int split_len;           // top-k positions per part (the last part may be shorter)
     int head_blocks;         // workgroups per (token, part) along heads
     size_t workspace;        // bytes needed (0 when num_splits == 1)
-    size_t part_lse_off;     // byte offsets inside the workspace: [T][S][H] fp32 lse
-    size_t part_o_off;       // and [T][S][H][512] fp32 partial outputs
+    size_t part_lse_off;     // byte offsets inside the workspace: [T][S][H] fp32 lse,
+    size_t part_o_off;       // [T][S][H][512] fp32 partial outputs (or bf16 rows in them)
+    size_t part_exact_off;   // and, for a call that merges its own splits, [T][S] int32 flags
 };
 
 // Host arithmetic only. partials: the call writes per-part results (workspace
@@ -79,15 +80,20 @@ hipError_t launch_upconvert(const void *cache, int64_t num_blocks, const int32_t
 
 // The attention kernel and, when the plan splits the top-k lists (and
 // partials_only is false), the merge kernel after it on the same stream.
+// Which kernels of a call run: both, the attention kernel only (a split
+// call's merge deferred), or the merge only.
+enum class AttnStage { kBoth, kAttentionOnly, kMergeOnly };
+
 hipError_t launch_attention(CacheFormat fmt, const AttnArgs &a, const Plan &p, bool partials_only,
-                            hipStream_t stream);
+                            AttnStage stage, hipStream_t stream);
 
 // cache_write_kernel: rows of num_tokens tokens into their slots (< num_slots).
 hipError_t launch_cache_write(CacheFormat fmt, const void *k_c, const void *k_pe, const int64_t *slot_mapping,
                              void *cache, int64_t num_tokens, int64_t num_slots, hipStream_t stream);
 
-// merge_kernel alone over a partials buffer of T x S x H entries.
-hipError_t launch_merge(const float *part_lse, const float *part_o, void *out, float *lse, int T,
-                        int H, int S, hipStream_t stream);
+// merge_kernel alone over a partials buffer of T x S x H entries; part_exact
+// null: fp32 partials, else bf16 rows and their flags (attn_pc_kernel's form).
+hipError_t launch_merge(const float *part_lse, const float *part_o, const int32_t *part_exact, void *out,
+                        float *lse, int T, int H, int S, hipStream_t stream);
 
 }  // namespace smla

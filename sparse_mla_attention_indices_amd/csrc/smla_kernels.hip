@@ -157,6 +157,11 @@ struct KParams {
     int32_t *phys_out;
     float *part_o;        // [T][S][H][512] fp32 partial output (O / l) of each split
     float *part_lse;      // [T][S][H] natural-log lse of each split
+    // non-null (attn_pc_kernel inside a split call): each split's O / l goes out
+    // as bf16 rows in the first half of its fp32 slot ((t, s) holds [2][H][512]
+    // bf16), and a split with at most kExactPRows valid rows also writes the
+    // bf16 residual rows (O / l - hi) into the second half and sets its flag
+    int32_t *part_exact;  // [T][S]
     float log2e_scale;    // sm_scale * log2(e): logits are kept in log2 units
     int T, H, K, R, MB;
     int64_t NB;
@@ -1339,6 +1344,9 @@ void attn_pc_kernel(const KParams p)
             slotv[j] = p.slot_in ? given_slot(idxv[j], p.NB) : finish_slot(slotv[j], req, idxv[j], p.R, p.MB, p.NB);
     }
 
+    // split partials in bf16 (hi rows only, unless the split is short enough
+    // for the exact path: then fp32 staging, written out as hi + lo rows)
+    int valid_total = 0;
     if (qk_role) {
         // ================= QK^T waves: head block rw =================
         i32x8 qh[4], ql[4];
@@ -1349,6 +1357,7 @@ void attn_pc_kernel(const KParams p)
             if (chunk0 != pos_begin)
                 convert_round(chunk0, slotv);
             const int n_valid = compact(chunk0, slotv);
+            valid_total += n_valid;
             const bool exact_p = n_valid <= kExactPRows;
             const int nbuf = exact_p ? C::kNBufExact : C::kNBuf;
             const int n_tiles = (n_valid + kTile - 1) / kTile;
@@ -1480,6 +1489,7 @@ void attn_pc_kernel(const KParams p)
             if (chunk0 != pos_begin)
                 convert_round(chunk0, slotv);
             const int n_valid = compact(chunk0, slotv);
+            valid_total += n_valid;
             const bool exact_p = n_valid <= kExactPRows;
             const int nbuf = exact_p ? C::kNBufExact : C::kNBuf;
             const int n_tiles = (n_valid + kTile - 1) / kTile;
@@ -1589,7 +1599,7 @@ void attn_pc_kernel(const KParams p)
         for (int hb = 0; hb < 4; ++hb) {
             const float l0 = l_lds[hb * 16 + n16];
             const float inv_l = l0 > 0.f ? 1.f / l0 : 0.f;
-            if (!p.partials) {
+            if (!p.partials || (p.part_exact != nullptr && valid_total > kExactPRows)) {
                 uint16_t *stage = (uint16_t *)smem;
 #pragma unroll
                 for (int db = 0; db < 8; ++db) {
@@ -1611,12 +1621,30 @@ void attn_pc_kernel(const KParams p)
     // ---- the staged rows written out coalesced. One split: the bf16 rows of
     //      the result. A top-k split: the fp32 partial O / l, head-major, for
     //      merge_kernel.
-    if (!p.partials) {
+    const bool bf16_parts = p.partials && p.part_exact != nullptr;
+    if (bf16_parts && tid == 0 && hg == 0)
+        p.part_exact[(size_t)t * p.S + s] = valid_total <= kExactPRows ? 1 : 0;
+    if (!p.partials || (bf16_parts && valid_total > kExactPRows)) {
         const uint16_t *stage = (const uint16_t *)smem;
-        uint16_t *dst = p.out + ((size_t)t * p.H + wg_head0) * kDv;
+        uint16_t *dst = !p.partials ? p.out + ((size_t)t * p.H + wg_head0) * kDv
+                                    : (uint16_t *)p.part_o + (((size_t)t * p.S + s) * 2 * p.H + wg_head0) * kDv;
         for (int u = tid; u < C::kHeads * kDv / 8; u += C::kThreads) {
             const int row = u / (kDv / 8), c8 = u % (kDv / 8);
             *(uint4 *)(dst + 8 * u) = *(const uint4 *)(stage + row * C::kStageBf16 + 8 * c8);
+        }
+    } else if (bf16_parts) {
+        // a short split: hi rows in the slot's first half, residual rows in its second
+        const float *stage = (const float *)smem;
+        uint16_t *dst = (uint16_t *)p.part_o + (((size_t)t * p.S + s) * 2 * p.H + wg_head0) * kDv;
+        const size_t lo_off = (size_t)p.H * kDv;
+        for (int u = tid; u < C::kHeads * kDv / 4; u += C::kThreads) {
+            const int row = u / (kDv / 4), c4 = u % (kDv / 4);
+            const f32x4 v = *(const f32x4 *)(stage + row * C::kStageF32 + 4 * c4);
+            const uint32_t h01 = pack_bf16(v[0], v[1]), h23 = pack_bf16(v[2], v[3]);
+            *(uint2 *)(dst + 4 * u) = make_uint2(h01, h23);
+            *(uint2 *)(dst + lo_off + 4 * u) =
+                make_uint2(pack_bf16(v[0] - bf16_lo(h01), v[1] - bf16_hi(h01)),
+                           pack_bf16(v[2] - bf16_lo(h23), v[3] - bf16_hi(h23)));
         }
     } else {
         const float *stage = (const float *)smem;
@@ -1634,10 +1662,13 @@ void attn_pc_kernel(const KParams p)
 // and, once per head, the merged natural-log lse. A split with lse = -inf
 // (no valid position) has weight 0; a head with none at all gets 0 and -inf.
 // KS > 0: exactly KS splits, every load issued before the first is used;
-// KS = 0: any count, in batches of 8.
-template <int KS>
+// KS = 0: any count, in batches of 8. BF: the partials are bf16 hi rows (the
+// first half of each split's fp32 slot), plus residual rows (the second half)
+// for the splits part_exact flags, which are loaded only after the flags.
+template <int KS, bool BF>
 __global__ __launch_bounds__(256) void merge_kernel(const float *__restrict__ part_o,
                                                     const float *__restrict__ part_lse,
+                                                    const int32_t *__restrict__ part_exact,
                                                     uint16_t *__restrict__ out, float *__restrict__ lse,
                                                     int T, int H, int S)
 {
@@ -1658,15 +1689,39 @@ __global__ __launch_bounds__(256) void merge_kernel(const float *__restrict__ pa
     const float *pl = part_lse + (size_t)t * S * H + h;
     const f32x4 *po = (const f32x4 *)part_o + ((size_t)t * S * H + h) * (kDv / 4) + c;
     const size_t ostride = (size_t)H * (kDv / 4);
+    // BF: split s2's hi row of head h at 4-dim group c, in uint2 units; its
+    // residual row is ostride / 2 further
+    const uint2 *pb = (const uint2 *)part_o + ((size_t)t * S * 2 * H + h) * (kDv / 4) + c;
+    const int32_t *pe = BF ? part_exact + (size_t)t * S : nullptr;
+    auto load = [&](int s2) __attribute__((always_inline)) -> f32x4 {
+        if constexpr (BF) {
+            const uint2 u = pb[(size_t)s2 * 2 * ostride];
+            return f32x4{bf16_lo(u.x), bf16_hi(u.x), bf16_lo(u.y), bf16_hi(u.y)};
+        } else {
+            return po[(size_t)s2 * ostride];
+        }
+    };
+    auto residual = [&](int s2) __attribute__((always_inline)) -> f32x4 {
+        const uint2 u = pb[(size_t)s2 * 2 * ostride + ostride];
+        return f32x4{bf16_lo(u.x), bf16_hi(u.x), bf16_lo(u.y), bf16_hi(u.y)};
+    };
     float M = -INFINITY, W = 0.f;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     if constexpr (KS > 0) {
         float l[KS];
         f32x4 v[KS];
+        int ex[KS];
 #pragma unroll
         for (int s2 = 0; s2 < KS; ++s2) {
             l[s2] = pl[(size_t)s2 * H];
-            v[s2] = po[s2 * ostride];
+            v[s2] = load(s2);
+            ex[s2] = BF ? pe[s2] : 0;
+        }
+        if constexpr (BF) {
+#pragma unroll
+            for (int s2 = 0; s2 < KS; ++s2)
+                if (ex[s2])
+                    v[s2] += residual(s2);
         }
 #pragma unroll
         for (int s2 = 0; s2 < KS; ++s2)
@@ -1685,7 +1740,13 @@ __global__ __launch_bounds__(256) void merge_kernel(const float *__restrict__ pa
 #pragma unroll
             for (int k = 0; k < 8; ++k)
                 if (s0 + k < S)
-                    v[k] = po[(size_t)(s0 + k) * ostride];
+                    v[k] = load(s0 + k);
+            if constexpr (BF) {
+#pragma unroll
+                for (int k = 0; k < 8; ++k)
+                    if (s0 + k < S && pe[s0 + k])
+                        v[k] += residual(s0 + k);
+            }
 #pragma unroll
             for (int k = 0; k < 8; ++k)
                 if (s0 + k < S) {
@@ -1993,28 +2054,37 @@ hipError_t launch_cache_write(CacheFormat fmt, const void *k_c, const void *k_pe
     return hipGetLastError();
 }
 
-hipError_t launch_merge(const float *part_lse, const float *part_o, void *out, float *lse, int T,
-                        int H, int S, hipStream_t stream)
+template <bool BF>
+void launch_merge_as(const float *part_lse, const float *part_o, const int32_t *part_exact, uint16_t *o,
+                     float *lse, int T, int H, int S, dim3 grid, hipStream_t stream)
+{
+    switch (S) {
+    case 2: hipLaunchKernelGGL((merge_kernel<2, BF>), grid, dim3(256), 0, stream, part_o, part_lse, part_exact, o, lse, T, H, S); break;
+    case 3: hipLaunchKernelGGL((merge_kernel<3, BF>), grid, dim3(256), 0, stream, part_o, part_lse, part_exact, o, lse, T, H, S); break;
+    case 4: hipLaunchKernelGGL((merge_kernel<4, BF>), grid, dim3(256), 0, stream, part_o, part_lse, part_exact, o, lse, T, H, S); break;
+    case 5: hipLaunchKernelGGL((merge_kernel<5, BF>), grid, dim3(256), 0, stream, part_o, part_lse, part_exact, o, lse, T, H, S); break;
+    case 6: hipLaunchKernelGGL((merge_kernel<6, BF>), grid, dim3(256), 0, stream, part_o, part_lse, part_exact, o, lse, T, H, S); break;
+    case 8: hipLaunchKernelGGL((merge_kernel<8, BF>), grid, dim3(256), 0, stream, part_o, part_lse, part_exact, o, lse, T, H, S); break;
+    default: hipLaunchKernelGGL((merge_kernel<0, BF>), grid, dim3(256), 0, stream, part_o, part_lse, part_exact, o, lse, T, H, S); break;
+    }
+}
+
+hipError_t launch_merge(const float *part_lse, const float *part_o, const int32_t *part_exact, void *out,
+                        float *lse, int T, int H, int S, hipStream_t stream)
 {
     // whole workgroups per token (h_q * 128 threads, h_q in {16, 32, 64, 128}),
     // tokens padded to a multiple of 8 for the XCD mapping
     const int64_t wpt = (int64_t)H * (kDv / 4) / 256;
     const dim3 grid((unsigned)((T + 7) / 8 * 8 * wpt));
-    uint16_t *o = (uint16_t *)out;
-    switch (S) {
-    case 2: hipLaunchKernelGGL(merge_kernel<2>, grid, dim3(256), 0, stream, part_o, part_lse, o, lse, T, H, S); break;
-    case 3: hipLaunchKernelGGL(merge_kernel<3>, grid, dim3(256), 0, stream, part_o, part_lse, o, lse, T, H, S); break;
-    case 4: hipLaunchKernelGGL(merge_kernel<4>, grid, dim3(256), 0, stream, part_o, part_lse, o, lse, T, H, S); break;
-    case 5: hipLaunchKernelGGL(merge_kernel<5>, grid, dim3(256), 0, stream, part_o, part_lse, o, lse, T, H, S); break;
-    case 6: hipLaunchKernelGGL(merge_kernel<6>, grid, dim3(256), 0, stream, part_o, part_lse, o, lse, T, H, S); break;
-    case 8: hipLaunchKernelGGL(merge_kernel<8>, grid, dim3(256), 0, stream, part_o, part_lse, o, lse, T, H, S); break;
-    default: hipLaunchKernelGGL(merge_kernel<0>, grid, dim3(256), 0, stream, part_o, part_lse, o, lse, T, H, S); break;
-    }
+    if (part_exact != nullptr)
+        launch_merge_as<true>(part_lse, part_o, part_exact, (uint16_t *)out, lse, T, H, S, grid, stream);
+    else
+        launch_merge_as<false>(part_lse, part_o, part_exact, (uint16_t *)out, lse, T, H, S, grid, stream);
     return hipGetLastError();
 }
 
 hipError_t launch_attention(CacheFormat fmt, const AttnArgs &a, const Plan &pl, bool partials_only,
-                            hipStream_t stream)
+                            AttnStage stage, hipStream_t stream)
 {
     KParams p;
     p.q = (const uint16_t *)a.q;
@@ -2028,6 +2098,10 @@ hipError_t launch_attention(CacheFormat fmt, const AttnArgs &a, const Plan &pl, 
     const bool split = pl.num_splits > 1 || partials_only;
     p.part_o = split ? (float *)((char *)a.workspace + pl.part_o_off) : nullptr;
     p.part_lse = split ? (float *)((char *)a.workspace + pl.part_lse_off) : nullptr;
+    // bf16 split partials: attn_pc_kernel (fp8 cache, 64-head workgroups) in a
+    // call that merges its own splits
+    const bool pc = fmt == kCacheFp8 && a.h_q / pl.head_blocks == 64;
+    p.part_exact = split && !partials_only && pc ? (int32_t *)((char *)a.workspace + pl.part_exact_off) : nullptr;
     p.log2e_scale = a.sm_scale * 1.4426950408889634f;
     p.T = a.num_tokens;
     p.H = a.h_q;
@@ -2040,10 +2114,15 @@ hipError_t launch_attention(CacheFormat fmt, const AttnArgs &a, const Plan &pl, 
     p.HB = pl.head_blocks;
     p.partials = split ? 1 : 0;
     p.slot_in = a.slot_indices ? 1 : 0;
-    const hipError_t err = fmt == kCacheFp8 ? launch_fmt<kCacheFp8>(p, stream) : launch_fmt<kCacheBf16>(p, stream);
-    if (err != hipSuccess || !split || partials_only)
-        return err;
-    return launch_merge(p.part_lse, p.part_o, p.out, p.lse, p.T, p.H, p.S, stream);
+    if (stage == AttnStage::kMergeOnly && (!split || partials_only))
+        return hipSuccess;
+    if (stage != AttnStage::kMergeOnly) {
+        const hipError_t err =
+            fmt == kCacheFp8 ? launch_fmt<kCacheFp8>(p, stream) : launch_fmt<kCacheBf16>(p, stream);
+        if (err != hipSuccess || !split || partials_only || stage == AttnStage::kAttentionOnly)
+            return err;
+    }
+    return launch_merge(p.part_lse, p.part_o, p.part_exact, p.out, p.lse, p.T, p.H, p.S, stream);
 }
 
 }  // namespace smla

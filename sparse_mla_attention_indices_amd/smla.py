@@ -31,6 +31,8 @@ EXPORTS = ("smla_status_string", "smla_abi_version", "smla_plan", "smla_workspac
 CACHE_FORMATS = {"auto": 0, "bf16": 0, "fp8_ds_mla": 1}
 FLAG_PARTIALS_ONLY = 0x1
 FLAG_SLOT_INDICES = 0x2
+FLAG_DEFER_MERGE = 0x4
+FLAG_MERGE_ONLY = 0x8
 
 
 class SmlaError(RuntimeError):
@@ -218,12 +220,18 @@ def smla_convert_indices(req_id_per_token, block_table, topk_indices, num_blocks
 
 def _attention(name: str, q, kv_cache, block_table, req_id_per_token, topk_indices, sm_scale,
                out, lse, phys_indices_out, workspace, num_splits, stream, want_lse, partials_only=False,
-               slot_indices=False):
+               slot_indices=False, stage=None):
     T, H, D = q.shape
     if D != 576:
         raise ValueError("q must be [num_tokens, h_q, 576]")
     K = topk_indices.shape[1]
     flags = (FLAG_PARTIALS_ONLY if partials_only else 0) | (FLAG_SLOT_INDICES if slot_indices else 0)
+    if stage is not None:
+        if stage not in ("attention", "merge"):
+            raise ValueError("stage must be None, 'attention' or 'merge'")
+        if workspace is None:
+            raise ValueError("a staged call needs the caller's workspace (it carries the parts)")
+        flags |= FLAG_DEFER_MERGE if stage == "attention" else FLAG_MERGE_ONLY
     if slot_indices:
         block_table = req_id_per_token = None
     R, MB = (1, 1) if block_table is None else block_table.shape
@@ -256,7 +264,7 @@ def _attention(name: str, q, kv_cache, block_table, req_id_per_token, topk_indic
 
 def smla_prefill_bf16(q, kv_cache, block_table, req_id_per_token, topk_indices, sm_scale,
                       out=None, lse=None, phys_indices_out=None, workspace=None, num_splits=0,
-                      stream=None, want_lse=True, partials_only=False, slot_indices=False):
+                      stream=None, want_lse=True, partials_only=False, slot_indices=False, stage=None):
     """Sparse MLA forward over a bf16 cache [num_blocks, 64, 576]. Returns (out, lse).
 
     workspace: uint8 device tensor of at least smla_workspace_size bytes (contents
@@ -264,17 +272,20 @@ def smla_prefill_bf16(q, kv_cache, block_table, req_id_per_token, topk_indices, 
     partials_only: write the per-part results into `workspace` (required) for
     smla_merge_partials and return (None, None).
     slot_indices: topk_indices already hold cache slots (block_table and
-    req_id_per_token are not used and may be None)."""
+    req_id_per_token are not used and may be None).
+    stage: None (the whole call), "attention" (a split call's attention kernel
+    only, its merge deferred) or "merge" (only the merge of such a call, made
+    with the same arguments and workspace)."""
     if kv_cache.dtype != torch.bfloat16 or kv_cache.shape[1:] != (64, 576):
         raise ValueError("kv_cache must be bf16 [num_blocks, 64, 576]")
     return _attention("smla_prefill_bf16", q, kv_cache, block_table, req_id_per_token, topk_indices,
                       sm_scale, out, lse, phys_indices_out, workspace, num_splits, stream, want_lse,
-                      partials_only, slot_indices)
+                      partials_only, slot_indices, stage)
 
 
 def smla_decode_fp8(q, kv_cache, block_table, req_id_per_token, topk_indices, sm_scale,
                     out=None, lse=None, phys_indices_out=None, workspace=None, num_splits=0,
-                    stream=None, want_lse=True, partials_only=False, slot_indices=False):
+                    stream=None, want_lse=True, partials_only=False, slot_indices=False, stage=None):
     """Sparse MLA forward over an fp8_ds_mla cache uint8 [num_blocks, 64, 656]. Returns (out, lse).
 
     Other arguments as for smla_prefill_bf16."""
@@ -282,7 +293,7 @@ def smla_decode_fp8(q, kv_cache, block_table, req_id_per_token, topk_indices, sm
         raise ValueError("kv_cache must be uint8 [num_blocks, 64, 656]")
     return _attention("smla_decode_fp8", q, kv_cache, block_table, req_id_per_token, topk_indices,
                       sm_scale, out, lse, phys_indices_out, workspace, num_splits, stream, want_lse,
-                      partials_only, slot_indices)
+                      partials_only, slot_indices, stage)
 
 
 # ---- separate-prefill mode of an fp8_ds_mla cache (decode tokens over the fp8

@@ -55,8 +55,8 @@ def test_plan_fills_the_chip_for_small_decode_batches(lib):
     assert s == 4
     up = lambda v: -(-v // 256) * 256
     rows = 64 * 4 * 64
-    o_off = up(rows * 4)                     # the partial lse first, then the partial o
-    assert ws == up(o_off + rows * 512 * 4)
+    o_off = up(rows * 4)                     # the partial lse first, then the partial o,
+    assert ws == up(up(o_off + rows * 512 * 4) + 64 * 4 * 4)     # then a flag per (token, part)
     # two-wave workgroups (h_q = 16) fit two per CU: 256 tokens x 16 heads -> 2 splits
     assert smla.smla_plan(256, 16, 2048, 256)[0] == 2
     assert smla.smla_plan(256, 16, 1024, 256)[0] == 2
@@ -84,10 +84,13 @@ def test_plan_fills_the_chip_for_small_decode_batches(lib):
 
 
 def test_plan_workspace_layout_for_large_batches(lib):
-    # [T][S][H] fp32 lse, then [T][S][H][512] fp32 partial outputs, 256-B aligned
+    # [T][S][H] fp32 lse, then [T][S][H][512] fp32 partial outputs, then [T][S]
+    # int32 flags, 256-B aligned; a partials-only call needs no flags
     up = lambda v: -(-v // 256) * 256
     s, ws = smla.smla_plan(5000, 16, 64, 256, num_splits=2)
     rows = 5000 * 2 * 16
+    assert s == 2 and ws == up(up(up(rows * 4) + rows * 512 * 4) + 5000 * 2 * 4)
+    s, ws = smla.smla_plan(5000, 16, 64, 256, num_splits=2, partials_only=True)
     assert s == 2 and ws == up(up(rows * 4) + rows * 512 * 4)
 
 
@@ -112,9 +115,16 @@ def test_plan_rejects_bad_options(lib):
     o.num_splits = -2
     assert lib.smla_plan(8, 16, 64, 256, ctypes.byref(o), ctypes.byref(s), ctypes.byref(b)) == 6
     o = smla.SmlaOptions()
-    for bit in (0x4, 0x8, 0x80000000):       # unknown flag bits
+    for bit in (0x10, 0x80000000):           # unknown flag bits
         o.flags = bit
         assert lib.smla_plan(8, 16, 64, 256, ctypes.byref(o), ctypes.byref(s), ctypes.byref(b)) == 6
+    # a deferred merge and a merge-only call exclude each other and partials-only
+    for bits in (0xC, 0x5, 0x9):
+        o.flags = bits
+        assert lib.smla_plan(8, 16, 64, 256, ctypes.byref(o), ctypes.byref(s), ctypes.byref(b)) == 6
+    for bits in (0x4, 0x8, 0x6, 0xA):
+        o.flags = bits
+        assert lib.smla_plan(8, 16, 64, 256, ctypes.byref(o), ctypes.byref(s), ctypes.byref(b)) == 0
     o.flags = smla.FLAG_PARTIALS_ONLY
     assert lib.smla_plan(8, 16, 64, 256, ctypes.byref(o), ctypes.byref(s), ctypes.byref(b)) == 0
     assert lib.smla_plan(8, 16, 64, 256, None, None, ctypes.byref(b)) == 1
@@ -198,9 +208,13 @@ def test_plan_partials_only_needs_a_workspace_even_unsplit(lib):
 
 
 def test_partials_layout_matches_the_plan(lib):
+    up = lambda v: -(-v // 256) * 256
     for T, H, K, S in ((64, 64, 2048, 4), (5, 16, 300, 3), (1000, 128, 64, 2)):
-        s, ws = smla.smla_plan(T, H, K, 256, num_splits=S)
+        s, ws = smla.smla_plan(T, H, K, 256, num_splits=S, partials_only=True)
         assert s == S and ws == smla.partials_layout(T, H, S)[1]
+        # a call that merges its own parts also keeps one flag per (token, part)
+        s, ws = smla.smla_plan(T, H, K, 256, num_splits=S)
+        assert s == S and ws == up(smla.partials_layout(T, H, S)[1] + T * S * 4)
 
 
 def _merge(lib, part=A256, pb=1 << 30, T=4, H=16, F=2, out=A16B, lse=A16):
