@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define SMLA_ABI_VERSION 4
+#define SMLA_ABI_VERSION 5
 #define SMLA_BLOCK_SIZE 64
 #define SMLA_HEAD_DIM_QK 576
 #define SMLA_HEAD_DIM_V 512

@@ -40,7 +40,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_abi_version(lib):
-    assert smla.smla_abi_version() == 4
+    assert smla.smla_abi_version() == 5
 
 
 def test_status_strings(lib):
