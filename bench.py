@@ -17,7 +17,15 @@ read leaves no dirty lines behind for the timed call to write back. Each step is
 bracketed by HIP events on the stream the library launches on. Warm-cache
 throughput (back-to-back calls) is reported beside it.
 
-Prints ONE JSON line. `python bench.py --gpus N --steps K --warmup W`.
+The same run also times every other workload of the target, one call per step
+over the whole batch, cold, HIP events around the call (the `configs` key): the
+tiny batch (bf16 and fp8 caches), the bf16 prefill batch (4 x 4096 tokens, h_q
+128), the speculative-decode batch at h_q 16 with top-k 512, 1024 and 2048, and
+the long mixed batch (32 decode + 2 x 2048 prefill tokens, h_q 128, contexts to
+131072), each with its own binding roofline.
+
+Prints ONE JSON line. `python bench.py --gpus N --steps K --warmup W`;
+`--only NAME` times one workload alone (for profiler runs).
 """
 
 from __future__ import annotations
@@ -153,6 +161,117 @@ def upconvert_bench(torch, smla, W, dev, stream, flush, sink, steps: int):
             "workload": "config 5 prefill contexts: 131072 + 65536 positions, shuffled blocks"}
 
 
+def kernels_of_plan(cache_format: str, h_q: int, splits: int):
+    """Names of the kernels one call launches, from the split plan (the same rule the
+    library's launcher applies: 64 heads per workgroup for h_q >= 64)."""
+    heads = 64 if h_q >= 64 else h_q
+    if cache_format == "fp8" and heads == 64:
+        names = ["attn_pc_kernel"]
+    else:
+        names = [f"attn_kernel<{'fp8' if cache_format == 'fp8' else 'bf16'}, {heads // 16}>"]
+    if splits > 1:
+        names.append(f"merge_kernel<{splits}>")
+    return names
+
+
+def upload(torch, w, dev):
+    """A workload's arrays as device tensors (q, cache, block table, request ids, indices)."""
+    q = torch.from_numpy(w.q.view(np.int16)).view(torch.bfloat16).to(dev)
+    if w.cache_format == "bf16":
+        cache = torch.from_numpy(w.cache.view(np.int16)).view(torch.bfloat16).to(dev)
+    else:
+        cache = torch.from_numpy(w.cache).to(dev)
+    return (q, cache, torch.from_numpy(w.block_table).to(dev), torch.from_numpy(w.req_id_per_token).to(dev),
+            torch.from_numpy(w.topk_indices).to(dev))
+
+
+def roofline_of(w, ms: float):
+    """Throughput and the binding roofline (lower of bf16 MFMA peak and HBM peak x
+    arithmetic intensity) of one call over workload w taking ms milliseconds."""
+    bytes_alg, flops, by, n_valid = algorithmic_work(w)
+    ai = flops / bytes_alg
+    roof_tflops = min(BF16_PEAK_TFLOPS, HBM_PEAK_GBS * 1e9 * ai / 1e12)
+    tflops = flops / (ms * 1e-3) / 1e12
+    return {"query_tokens_per_s": w.num_tokens / (ms * 1e-3), "tflops": tflops,
+            "binding_roofline": {"bound": "hbm" if roof_tflops < BF16_PEAK_TFLOPS else "mfma",
+                                 "arith_intensity_flop_per_byte": ai, "tflops": roof_tflops},
+            "pct_of_binding_roofline": 100.0 * tflops / roof_tflops,
+            "algorithmic_GBps": bytes_alg / (ms * 1e-3) / 1e9,
+            "algorithmic_bytes": bytes_alg, "flops": flops, "valid_slots": n_valid}
+
+
+def config_bench(torch, smla, w, dev, stream, flush, sink, steps: int, warmup: int = 2):
+    """One workload through its entry point (smla_prefill_bf16 for a bf16 cache,
+    smla_decode_fp8 for fp8_ds_mla), one call per step over the whole batch, cold
+    cache (the 1 GiB read before each step, outside the events), HIP events on the
+    library's stream around each call."""
+    q, cache, bt, req, idx = upload(torch, w, dev)
+    T, H, K = w.num_tokens, w.h_q, w.topk
+    out = torch.empty((T, H, 512), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((T, H), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(smla.smla_workspace_size(T, H, K), 1), dtype=torch.uint8, device=dev)
+    fn = smla.smla_prefill_bf16 if w.cache_format == "bf16" else smla.smla_decode_fp8
+    props = torch.cuda.get_device_properties(dev)
+    splits, _ = smla.smla_plan(T, H, K, props.multi_processor_count)
+
+    def call():
+        fn(q, cache, bt, req, idx, w.sm_scale, out=out, lse=lse, workspace=ws, stream=stream)
+
+    for _ in range(warmup):
+        torch.amax(flush, 0, out=sink)
+        call()
+    e0 = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    e1 = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    for i in range(steps):
+        torch.amax(flush, 0, out=sink)
+        e0[i].record(stream)
+        call()
+        e1[i].record(stream)
+    torch.cuda.synchronize()
+    t = np.array([a.elapsed_time(b) for a, b in zip(e0, e1)])
+    ms = float(np.median(t))
+    rec = {"workload": w.name, "num_tokens": T, "h_q": H, "topk": K,
+           "cache": "fp8_ds_mla" if w.cache_format == "fp8" else "bf16",
+           "entry_point": "smla_prefill_bf16" if w.cache_format == "bf16" else "smla_decode_fp8",
+           "kernels": kernels_of_plan(w.cache_format, H, splits), "num_splits": splits,
+           "steps": steps, "ms_median": ms, "ms_p10": float(np.percentile(t, 10)),
+           "ms_p90": float(np.percentile(t, 90))}
+    rec.update(roofline_of(w, ms))
+    del q, cache, bt, req, idx, out, lse, ws
+    torch.cuda.empty_cache()
+    return rec
+
+
+# The other workloads of the target, each timed in the default run beside the
+# headline batch: name -> (generator, timed steps).
+def other_configs(W, seed: int):
+    def c4():
+        return W.config4_sweep(seed)
+    return [("c1_tiny_bf16", lambda: [W.config1(seed)], 20),
+            ("c1_tiny_fp8", lambda: [W.config1_fp8(seed)], 20),
+            ("c3_bf16_prefill", lambda: [W.config3(seed)], 5),
+            ("c4_spec_decode", c4, 20),
+            ("c5_long_mixed", lambda: [W.config5(seed)], 5)]
+
+
+def cpu_identity():
+    """Host CPU model and core counts, as the host reports them."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:
+        usable = os.cpu_count()
+    return {"cpu_model": model, "nproc": usable, "os_cpu_count": os.cpu_count()}
+
+
 def cpu_baseline(w, target_s: float = 10.0):
     """The oracle as it stands, on this host's cores: whole passes over the batch's
     tokens (in a fixed shuffled order) until about target_s of CPU work is done."""
@@ -172,10 +291,12 @@ def cpu_baseline(w, target_s: float = 10.0):
             if t_total >= target_s:
                 break
         passes += 1
-    return {"value": done / t_total, "unit": "query-tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{done} token evaluations ({passes} pass(es) over the batch's {w.num_tokens} "
-                      f"tokens, all {w.h_q} heads, top-k {w.topk}), float64 C + OpenMP, "
-                      f"{t_total:.1f} s"}
+    rec = {"value": done / t_total, "unit": "query-tokens/s", "cores": threads, "kind": "oracle",
+           "sample": f"{done} token evaluations ({passes} pass(es) over the batch's {w.num_tokens} "
+                     f"tokens, all {w.h_q} heads, top-k {w.topk}), float64 C + OpenMP, "
+                     f"{t_total:.1f} s"}
+    rec.update(cpu_identity())
+    return rec
 
 
 def traffic_from_profile():
@@ -200,6 +321,12 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calib", action="store_true",
                     help="run only a plain device copy of known size (counter calibration)")
+    ap.add_argument("--only", default=None,
+                    help="time one workload alone and print its record (for profiler runs): "
+                         "c2 (the headline batch, no side measurements), c1_tiny_bf16, c1_tiny_fp8, "
+                         "c3_bf16_prefill, c4_spec_decode (top-k 512, 1024, 2048), c5_long_mixed")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the other workloads (the headline line only)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -223,20 +350,28 @@ def main():
         print(json.dumps({"copy_calib_bytes": src.numel(), "launches": 5}), flush=True)
         return
 
+    flush = torch.ones(1 << 28, dtype=torch.int32, device=dev)     # 1 GiB, read to evict caches
+    sink = torch.empty((), dtype=torch.int32, device=dev)
+    if args.only is not None and args.only != "c2":
+        gens = {name: (gen, steps) for name, gen, steps in other_configs(W, args.seed)}
+        if args.only not in gens:
+            print(f"unknown workload {args.only!r}; choose c2 or one of {sorted(gens)}", file=sys.stderr)
+            sys.exit(2)
+        gen, steps = gens[args.only]
+        for w in gen():
+            print(f"[bench] {w.name}", file=sys.stderr, flush=True)
+            print(json.dumps(config_bench(torch, smla, w, dev, stream, flush, sink, min(steps, args.steps),
+                                          args.warmup)), flush=True)
+        return
+
     w = W.config2(args.seed)
-    q = torch.from_numpy(w.q.view(np.int16)).view(torch.bfloat16).to(dev)
-    cache = torch.from_numpy(w.cache).to(dev)
-    bt = torch.from_numpy(w.block_table).to(dev)
-    req = torch.from_numpy(w.req_id_per_token).to(dev)
-    idx = torch.from_numpy(w.topk_indices).to(dev)
+    q, cache, bt, req, idx = upload(torch, w, dev)
     out = torch.empty((w.num_tokens, w.h_q, 512), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((w.num_tokens, w.h_q), dtype=torch.float32, device=dev)
     ws_bytes = smla.smla_workspace_size(w.num_tokens, w.h_q, w.topk)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     props = torch.cuda.get_device_properties(dev)
     splits, _ = smla.smla_plan(w.num_tokens, w.h_q, w.topk, props.multi_processor_count)
-    flush = torch.ones(1 << 28, dtype=torch.int32, device=dev)     # 1 GiB, read to evict caches
-    sink = torch.empty((), dtype=torch.int32, device=dev)
 
     def step():
         smla.smla_decode_fp8(q, cache, bt, req, idx, w.sm_scale, out=out, lse=lse, workspace=ws,
@@ -353,6 +488,22 @@ def main():
         "kernel_source_hash": kernel_source_hash(),
         "device": props.name,
     }
+    if args.only == "c2":
+        print(json.dumps(rec), flush=True)
+        return
+    del q, cache, bt, req, idx, out, lse, ws
+    torch.cuda.empty_cache()
+    if not args.no_configs:
+        rec["configs"] = {}
+        for name, gen, steps in other_configs(W, args.seed):
+            for wc in gen():
+                print(f"[bench] {wc.name}", file=sys.stderr, flush=True)
+                rec["configs"][wc.name] = config_bench(torch, smla, wc, dev, stream, flush, sink,
+                                                       min(steps, args.steps))
+        rec["configs"][w.name] = {"workload": w.name, "kernels": kernels_of_plan("fp8", w.h_q, splits),
+                                  "num_splits": splits, "ms_median": rec["ms_per_step_median"],
+                                  "note": "the headline batch: see the top-level fields"}
+        rec["configs"][w.name].update(roofline_of(w, rec["ms_per_step_median"]))
     rec["cache_writer"] = cache_writer_bench(torch, smla, dev, stream, flush, sink, min(args.steps, 20))
     rec["separate_prefill_upconvert"] = upconvert_bench(torch, smla, W, dev, stream, flush, sink,
                                                         min(args.steps, 20))

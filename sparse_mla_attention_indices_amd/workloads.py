@@ -276,6 +276,23 @@ def config4(seed: int = 0, topk: int = 2048) -> Workload:
                  p_invalid=0.05, max_blocks_per_req=1024, index_part=10 + topk)
 
 
+def config4_sweep(seed: int = 0):
+    """config4 at top-k 512, 1024 and 2048, generated once: the three workloads
+    share one cache array (the cache, q and block table do not depend on top-k;
+    each index list comes from its own sub-seed), so each equals config4(seed, k)."""
+    base = config4(seed, 2048)
+    out = [base]
+    for k in (512, 1024):
+        u = _rng(seed, 4, 4).uniform(math.log(16384), math.log(65536), size=128)
+        ctx = np.floor(np.exp(u)).astype(np.int64)
+        vis = np.stack([ctx - 1, ctx], axis=1).reshape(-1)
+        idx = draw_indices(_rng(seed, 4, 10 + k), vis, k, 0.05)
+        out.append(Workload(name=f"c4_spec_decode_k{k}", cache_format="fp8", q=base.q, cache=base.cache,
+                            block_table=base.block_table, req_id_per_token=base.req_id_per_token,
+                            topk_indices=idx, sm_scale=base.sm_scale, ctx_lens=base.ctx_lens))
+    return sorted(out, key=lambda w: w.topk)
+
+
 def config5(seed: int = 0) -> Workload:
     """Long mixed: 32 decode tokens (ctx U{8192..106496}) then 2 prefill requests
     (ctx 131072, 65536) whose last 2048 positions are query tokens; h_q 128, top-k 2048."""
