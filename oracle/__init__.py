@@ -285,7 +285,7 @@ def attention(cache_format: int, q_bits, cache, block_table, req_id_per_token, t
 
 def separate_prefill_attention(q_bits, cache, block_table, req_id_per_token, topk_indices, sm_scale: float,
                                num_decode_reqs: int, seq_lens, max_rows: int):
-    """The separate-prefill mode of an fp8_ds_mla cache, end to end [P1,
+    """The separate-prefill mode of an fp8_ds_mla cache, end to end [flashmla_sparse.py page,
     _build_fp8_separate_prefill_decode and _forward_fp8_kv_separate_prefill_decode]:
     requests [0, num_decode_reqs) are decode requests, the rest prefill requests
     (prefill index r = request id - num_decode_reqs) with context length

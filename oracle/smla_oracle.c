@@ -10,10 +10,10 @@
  * computed in double precision, one query token per OpenMP iteration, no
  * tiling, no fusion, no online softmax.
  *
- * Sources (the pages this build follows):
- *   [P2] "vllm/v1/attention/backends/mla/flashmla_sparse.py" (the vLLM
- *        FLASHMLA_SPARSE backend source, as shown in the vllm-cpu-avx512bf16
- *        0.14.0 wheel diff):
+ * Sources (the pages this build follows). Every citation below names the
+ * "flashmla_sparse.py page": the package-diff page of the vllm-cpu-avx512bf16
+ * 0.14.0 wheel that shows vllm/v1/attention/backends/mla/flashmla_sparse.py,
+ * the vLLM FLASHMLA_SPARSE backend source. From it:
  *          - the module note on the fp8_ds_mla cache format (656-byte rows:
  *            512 float8_e4m3, 4 float32 scales per 128 values, 64 bfloat16
  *            RoPE values);
@@ -27,12 +27,11 @@
  *            and the softmax_scale the backend passes to the kernels.
  *   The OCP 8-bit floating point specification (the E4M3FN encoding) for the
  *   value of an e4m3 byte, and its round-to-nearest-even encoding.
- *   [P2] FlashMLASparseImpl.forward: the concat_and_cache_mla call that writes
+ *   flashmla_sparse.py page, FlashMLASparseImpl.forward: the concat_and_cache_mla call that writes
  *   a token's latent (k_c_normed) and RoPE (k_pe) into the cache slot given by
  *   slot_mapping, in the cache's dtype ("auto" = bf16 or "fp8_ds_mla").
- *   [P1] "vllm/v1/attention/backends/mla/flashmla_sparse.py" as changed by the
- *   vllm-xpu-kernels / vLLM pull requests (the separate-prefill mode of an
- *   fp8 cache): _convert_req_index_to_global_index_kernel with HAS_PREFILL
+ *   flashmla_sparse.py page, the separate-prefill mode of an fp8 cache:
+ *   _convert_req_index_to_global_index_kernel with HAS_PREFILL
  *   (a prefill token's index maps to its request's workspace start plus the
  *   index), _build_fp8_separate_prefill_decode (workspace starts are the
  *   running sum of the prefill sequence lengths, cut into chunks that fit the
@@ -114,7 +113,7 @@ double smla_oracle_bf16(uint16_t bits)
     return (double)f;
 }
 
-/* One 656-byte fp8_ds_mla row -> 576 values [P2, cache format note]:
+/* One 656-byte fp8_ds_mla row -> 576 values [flashmla_sparse.py page, cache format note]:
  * bytes 0..511 are e4m3 latent values, bytes 512..527 four little-endian
  * float32 scales (scale i covers latent values 128*i .. 128*i+127), bytes
  * 528..655 sixty-four bfloat16 RoPE values, not quantized. */
@@ -161,7 +160,7 @@ uint8_t smla_oracle_e4m3fn_encode(float x)
     return (uint8_t)(signbit(x) ? (0x80 | best) : best);
 }
 
-/* Write num_tokens token rows into a paged cache [P2, FlashMLASparseImpl.forward:
+/* Write num_tokens token rows into a paged cache [flashmla_sparse.py page, FlashMLASparseImpl.forward:
  * concat_and_cache_mla; cache format note]. k_c: bfloat16 [T][512] latent,
  * k_pe: bfloat16 [T][64] RoPE, slot_mapping: int64 [T] (flat slot = block * 64
  * + offset). cache_format 0: bf16 rows [slots][576] (latent then RoPE, copied);
@@ -202,7 +201,7 @@ void smla_oracle_cache_write(int cache_format, const uint16_t *k_c, const uint16
 
 /* --------------------------------------------------------- index convert */
 
-/* Logical per-request top-k index -> physical cache slot [P2,
+/* Logical per-request top-k index -> physical cache slot [flashmla_sparse.py page,
  * triton_convert_req_index_to_global_index docstring and kernel]:
  *   slot = block_table[req, idx / 64] * 64 + idx % 64,
  * with -1 for a negative index and for a block position outside the table
@@ -239,7 +238,7 @@ void smla_oracle_convert_indices(const int32_t *req_id_per_token, const int32_t 
 
 /* ------------------------------------------------ separate-prefill mode */
 
-/* Index conversion with a prefill workspace [P1,
+/* Index conversion with a prefill workspace [flashmla_sparse.py page,
  * _convert_req_index_to_global_index_kernel with HAS_PREFILL]: a token whose
  * prefill request id r is >= 0 maps a valid index to workspace_starts[r] + idx;
  * other tokens convert as smla_oracle_convert_one. Invalid either way: a
@@ -294,7 +293,7 @@ uint16_t smla_oracle_bf16_rne(double x)
 }
 
 /* Gather and upconvert the context rows of a batch of prefill requests into a
- * bf16 workspace [P1, _forward_fp8_kv_separate_prefill_decode: the
+ * bf16 workspace [flashmla_sparse.py page, _forward_fp8_kv_separate_prefill_decode: the
  * cp_gather_and_upconvert_fp8_kv_cache call]: for request b and position
  * p < seq_lens[b], workspace row workspace_starts[b] + p (when inside
  * [0, workspace_rows)) receives the row at slot block_table[b, p / 64] * 64 +
@@ -328,7 +327,7 @@ void smla_oracle_gather_upconvert(const uint8_t *cache, int64_t num_blocks, cons
 }
 
 /* Cut consecutive prefill requests into chunks whose total sequence length fits
- * max_rows workspace rows [P1, _build_fp8_separate_prefill_decode]: greedy in
+ * max_rows workspace rows [flashmla_sparse.py page, _build_fp8_separate_prefill_decode]: greedy in
  * request order. Writes chunk_ends[c] (one past the chunk's last request) and,
  * for every request, its chunk-local workspace start. Returns the chunk count,
  * or -1 if a single request is longer than max_rows or a length is negative. */
@@ -353,7 +352,7 @@ int64_t smla_oracle_plan_prefill_chunks(const int32_t *seq_lens, int64_t num_pre
 
 /* -------------------------------------------------------------- attention */
 
-/* Sparse MQA-576/512 attention for the listed query tokens [P2,
+/* Sparse MQA-576/512 attention for the listed query tokens [flashmla_sparse.py page,
  * FlashMLASparseImpl.forward and the two kernel wrappers]:
  *   for token t, head h and valid slots j of t's list,
  *     s_j      = sm_scale * <q[t,h,0:576], K_j>

@@ -19,9 +19,7 @@ constexpr int kBf16RowBytes = kDqk * 2;
 enum CacheFormat { kCacheBf16 = 0, kCacheFp8 = 1 };
 
 // Heads one workgroup covers: 64 (eight waves) for h_q >= 64, so h_q = 128 takes
-// two workgroups per token; h_q = 16 / 32 use one two- / four-wave workgroup. A
-// 64-head batch too small to fill the chip is planned as two 32-head
-// workgroups per token instead (two per CU).
+// two workgroups per token; h_q = 16 / 32 use one two- / four-wave workgroup.
 constexpr int kHeadsPerGroup = 64;
 
 // Most top-k parts one token's list is cut into.

@@ -29,8 +29,10 @@
 //    straight into one of a ring of LDS buffers; the next tiles are in flight
 //    while one is used.
 //  * QK^T runs transposed, S^T = K q^T, with q in registers. fp8: the raw e4m3
-//    K bytes feed v_mfma_scale_f32_16x16x128_f8f6f4 against q written exactly as
-//    hi + lo e4m3 terms; each 128-column group's partial sum is multiplied by
+//    K bytes feed v_mfma_scale_f32_16x16x128_f8f6f4 against q written as hi + lo
+//    e4m3 terms (exact for elements within 2^13 of their group's largest, an
+//    absolute error below 2^-21 of it otherwise); each 128-column group's partial
+//    sum is multiplied by
 //    that group's row scales in fp32. bf16: v_mfma_f32_16x16x32_bf16. The two
 //    column halves add their partial S^T through LDS.
 //  * Softmax: the S^T accumulator layout gives a lane one head and four rows
@@ -405,9 +407,11 @@ void attn_kernel(const KParams p)
     // k-step of v_mfma_f32_16x16x32_bf16: latent 256*dh + 32k + 8g (k < 8), RoPE
     // 512 + 32*dh + 8g (k = 8). fp8 cache: the RoPE step is the same (qb[8]); the
     // latent goes through v_mfma_scale_f32_16x16x128_f8f6f4 on the raw e4m3 K
-    // bytes, so q is written exactly as hi + lo e4m3 terms with a power-of-two
-    // scale per head and 128-column group: lane (head, g) holds columns
-    // 128*(2*dh + gi) + 32g .. +31.
+    // bytes, so q is written as hi + lo e4m3 terms with a power-of-two scale per
+    // head and 128-column group (exact for elements within 2^13 of the group's
+    // largest; below that hi and lo fall into e4m3's subnormal steps and the
+    // absolute error stays below 2^-21 of the largest): lane (head, g) holds
+    // columns 128*(2*dh + gi) + 32g .. +31.
     bf16x8 qb[9];
     i32x8 qh[2], ql[2];         // fp8: hi and lo e4m3 terms of the 32 columns
     int qsh[2], qsl[2];         // fp8: their e8m0 block scales (2^(e - 127))
@@ -1148,8 +1152,9 @@ void attn_pc_kernel(const KParams p)
 
     // QK^T waves hold q^T as the B operands: the latent goes through
     // v_mfma_scale_f32_16x16x128_f8f6f4 on the raw e4m3 K bytes, so q is written
-    // exactly as hi + lo e4m3 terms with a power-of-two scale per head and
-    // 128-column group G: lane (head, g) holds columns 128 G + 32 g .. + 31
+    // as hi + lo e4m3 terms with a power-of-two scale per head and 128-column
+    // group G (exact within 2^13 of the group's largest magnitude, absolute error
+    // below 2^-21 of it further down): lane (head, g) holds columns 128 G + 32 g .. + 31
     // (qh, ql, scales qsh, qsl). RoPE: bf16 (qr), k-step ks holds columns
     // 512 + 32 ks + 8 g .. + 7.
     // QK^T and online softmax of head block rw on one tile; publishes the P^T
@@ -1362,7 +1367,7 @@ void attn_pc_kernel(const KParams p)
             const int nbuf = exact_p ? C::kNBufExact : C::kNBuf;
             const int n_tiles = (n_valid + kTile - 1) / kTile;
             if (chunk0 == pos_begin) {
-                // q, loaded and written exactly as hi + lo e4m3 terms while the
+                // q, loaded and written as hi + lo e4m3 terms while the
                 // PV waves' first copies are in flight
                 uint4 qraw[18];     // [4 * G + c] latent of group G, [16 + ks] RoPE k-step ks
                 asm volatile("s_waitcnt vmcnt(0)" ::: "memory");     // this wave's q copies

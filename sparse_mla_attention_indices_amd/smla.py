@@ -19,7 +19,9 @@ import numpy as np
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libsmla.so")
+# SMLA_LIB_PATH names another build of the same library (the sanitizer build of
+# the host code); by default the in-tree libsmla.so.
+LIB_PATH = os.environ.get("SMLA_LIB_PATH") or os.path.join(_PKG, "libsmla.so")
 
 SMLA_OK = 0
 STATUS_NAMES = {0: "SMLA_OK", 1: "SMLA_ERR_NULL", 2: "SMLA_ERR_SHAPE", 3: "SMLA_ERR_ALIGN",
@@ -354,64 +356,98 @@ def smla_gather_upconvert_fp8(kv_cache, block_table, seq_lens, workspace_starts,
     return workspace
 
 
-def smla_forward_fp8_separate_prefill(q, kv_cache, block_table, req_id_per_token, topk_indices, sm_scale,
-                                      num_decode_reqs: int, seq_lens, max_rows: int, out=None, lse=None,
-                                      bf16_workspace=None, stream=None):
-    """The separate-prefill mode end to end. Requests [0, num_decode_reqs) are
-    decode requests, the rest prefill requests; seq_lens (host sequence, one per
-    request) gives each request's context + query length. Decode tokens run
-    smla_decode_fp8 over the cache; prefill requests are cut into chunks of at
-    most max_rows context rows, and for each chunk the rows are upconverted into
-    bf16_workspace (bf16 [>= max_rows rounded up to 64, 576]; allocated when None)
-    and its tokens run smla_prefill_bf16 over it with workspace-row indices.
-    Tokens must be ordered by request. Returns (out, lse)."""
-    T, H, _ = q.shape
-    dev = q.device
-    R = block_table.shape[0]
-    nd = int(num_decode_reqs)
+class SeparatePrefillPlan:
+    """Per-batch metadata of the separate-prefill mode, built once per batch on
+    the host (as the backend's metadata builder does) and reused by every call
+    over that batch: the decode token range, the prefill chunks (request and
+    token ranges, context rows, longest context), and three device arrays
+    uploaded once: per-token prefill request ids (-1 for decode tokens), each
+    prefill request's chunk-local workspace start, and its sequence length."""
+
+    def __init__(self, num_tokens, num_decode_reqs, decode_tokens, chunks, prefill_request_id,
+                 workspace_starts, seq_lens, workspace_rows):
+        self.num_tokens = num_tokens
+        self.num_decode_reqs = num_decode_reqs
+        self.decode_tokens = decode_tokens          # (t0, t1)
+        self.chunks = chunks                        # [(c0, c1, t0, t1, rows, max_seq_len)], c = prefill index
+        self.prefill_request_id = prefill_request_id
+        self.workspace_starts = workspace_starts
+        self.seq_lens = seq_lens
+        self.workspace_rows = workspace_rows
+
+
+def smla_build_separate_prefill_plan(query_start_loc, seq_lens, num_decode_reqs: int, max_rows: int,
+                                     device) -> SeparatePrefillPlan:
+    """Host metadata of a batch for smla_forward_fp8_separate_prefill.
+
+    query_start_loc: host sequence of R + 1 token offsets (request r owns tokens
+    [query_start_loc[r], query_start_loc[r + 1]); decode requests come first).
+    seq_lens: host sequence of R lengths (context + query). Requests
+    [0, num_decode_reqs) are decode requests. The chunk plan is the library's
+    host call smla_plan_prefill_chunks over the prefill lengths."""
+    qsl = np.asarray(query_start_loc, dtype=np.int64).reshape(-1)
     sl = np.asarray(seq_lens, dtype=np.int64).reshape(-1)
-    if sl.shape[0] != R:
-        raise ValueError("seq_lens needs one length per request")
+    R = sl.shape[0]
+    nd = int(num_decode_reqs)
+    if qsl.shape[0] != R + 1 or qsl[0] != 0 or np.any(np.diff(qsl) < 0):
+        raise ValueError("query_start_loc needs R + 1 non-decreasing offsets starting at 0")
+    if not 0 <= nd <= R:
+        raise ValueError("num_decode_reqs outside [0, R]")
+    T = int(qsl[-1])
+    counts = np.diff(qsl)
+    pid = np.repeat(np.concatenate([np.full(nd, -1), np.arange(R - nd)]).astype(np.int32), counts)
+    ends, starts = smla_plan_prefill_chunks(sl[nd:], max_rows)
+    chunks = []
+    c0 = 0
+    for c1 in ends:
+        rows = int(sl[nd + c0:nd + c1].sum())
+        longest = int(sl[nd + c0:nd + c1].max()) if c1 > c0 else 0
+        chunks.append((c0, c1, int(qsl[nd + c0]), int(qsl[nd + c1]), rows, longest))
+        c0 = c1
+    P = R - nd
+    up = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(device)
+    return SeparatePrefillPlan(T, nd, (0, int(qsl[nd])), chunks, up(pid), up(starts) if P else None,
+                               up(sl[nd:]) if P else None, -(-int(max_rows) // 64) * 64)
+
+
+def smla_forward_fp8_separate_prefill(q, kv_cache, block_table, req_id_per_token, topk_indices, sm_scale,
+                                      plan: SeparatePrefillPlan, out=None, lse=None, bf16_workspace=None,
+                                      slots=None, stream=None):
+    """The separate-prefill mode end to end, as library calls only: the
+    workspace index conversion over the whole batch, smla_decode_fp8 over the
+    fp8 cache for the decode tokens, then for each prefill chunk
+    smla_gather_upconvert_fp8 (its requests' context rows into bf16_workspace)
+    and smla_prefill_bf16 over that workspace with workspace-row indices.
+    plan comes from smla_build_separate_prefill_plan. bf16_workspace: bf16
+    [>= plan.workspace_rows, 576]; slots: int32 [T, topk] scratch for the
+    converted indices; out, lse: results. Each is allocated when None. Returns
+    (out, lse)."""
+    T, H, _ = q.shape
+    if plan.num_tokens != T:
+        raise ValueError("the plan was built for another batch")
+    dev = q.device
+    ws_rows = plan.workspace_rows
     if out is None:
         out = torch.empty((T, H, 512), dtype=torch.bfloat16, device=dev)
     if lse is None:
         lse = torch.empty((T, H), dtype=torch.float32, device=dev)
-    ends, starts = smla_plan_prefill_chunks(sl[nd:], max_rows)
-    ws_rows = -(-int(max_rows) // 64) * 64
     if bf16_workspace is None:
         bf16_workspace = torch.empty((ws_rows, 576), dtype=torch.bfloat16, device=dev)
     elif bf16_workspace.shape[0] < ws_rows:
         raise ValueError(f"bf16_workspace needs {ws_rows} rows")
-    req = req_id_per_token
-    with torch.cuda.stream(stream) if stream is not None else torch.cuda.stream(torch.cuda.current_stream()):
-        prefill_id = torch.where(req >= nd, req - nd, torch.full_like(req, -1))
-        starts_d = torch.from_numpy(np.ascontiguousarray(starts, dtype=np.int32)).to(dev)
-        sl_d = torch.from_numpy(sl[nd:].astype(np.int32)).to(dev)
-    slots = smla_convert_indices_workspace(req, block_table, topk_indices, prefill_id,
-                                           starts_d if len(starts) else None, kv_cache.shape[0],
-                                           stream=stream)
-    req_h = req.cpu().numpy()
-    tok_of = [np.nonzero(req_h == r)[0] for r in range(R)]
-    dec = np.concatenate(tok_of[:nd]) if nd else np.zeros(0, dtype=np.int64)
-    if dec.size:
-        d0, d1 = int(dec.min()), int(dec.max()) + 1
-        if d1 - d0 != dec.size:
-            raise ValueError("decode tokens must be contiguous")
+    slots = smla_convert_indices_workspace(req_id_per_token, block_table, topk_indices, plan.prefill_request_id,
+                                           plan.workspace_starts, kv_cache.shape[0], out=slots, stream=stream)
+    d0, d1 = plan.decode_tokens
+    if d1 > d0:
         smla_decode_fp8(q[d0:d1], kv_cache, None, None, slots[d0:d1], sm_scale, out=out[d0:d1],
                         lse=lse[d0:d1], stream=stream, slot_indices=True)
     ws_view = bf16_workspace[:ws_rows].view(ws_rows // 64, 64, 576)
-    c0 = 0
-    for c1 in ends:
-        toks = np.concatenate(tok_of[nd + c0:nd + c1])
-        rows = int(sl[nd + c0:nd + c1].sum())
+    for c0, c1, t0, t1, rows, longest in plan.chunks:
         if rows > 0:
-            smla_gather_upconvert_fp8(kv_cache, block_table[nd + c0:nd + c1], sl_d[c0:c1], starts_d[c0:c1],
-                                      int(sl[nd + c0:nd + c1].max()), bf16_workspace, stream=stream)
-        if toks.size:
-            t0, t1 = int(toks.min()), int(toks.max()) + 1
-            if t1 - t0 != toks.size:
-                raise ValueError("a chunk's tokens must be contiguous")
+            nd = plan.num_decode_reqs
+            smla_gather_upconvert_fp8(kv_cache, block_table[nd + c0:nd + c1], plan.seq_lens[c0:c1],
+                                      plan.workspace_starts[c0:c1], longest, bf16_workspace, stream=stream)
+        if t1 > t0:
             smla_prefill_bf16(q[t0:t1], ws_view, None, None, slots[t0:t1], sm_scale, out=out[t0:t1],
                               lse=lse[t0:t1], stream=stream, slot_indices=True)
-        c0 = c1
     return out, lse

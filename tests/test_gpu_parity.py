@@ -171,6 +171,25 @@ def test_short_lists_are_exact_up_to_output_rounding(fmt):
         np.testing.assert_allclose(lse.cpu().numpy(), lse_ref, rtol=0, atol=2e-3)
 
 
+@pytest.mark.parametrize("h_q", [16, 64, 128])
+def test_wide_range_q_within_a_scale_group(h_q):
+    """q whose magnitudes span 2^-20 .. 2^2 inside every 128-column group. The fp8
+    QK^T writes q as hi + lo e4m3 terms under one power-of-two scale per head and
+    group: elements within 2^13 of the group's largest are exact, smaller ones
+    keep an absolute error below about 2^-21 of it. Results must still meet the
+    fp8 bounds, unsplit and split."""
+    w = small(61 + h_q, "fp8", h_q, 256, n_req=3, tok_per_req=3, ctx=(300, 900), p_invalid=0.1)
+    rng = np.random.default_rng(61 + h_q)
+    mag = np.exp2(rng.uniform(-20.0, 2.0, size=w.q.shape))
+    sign = np.where(rng.random(w.q.shape) < 0.5, -1.0, 1.0)
+    w.q = W.to_bf16_bits((sign * mag).astype(np.float32))
+    dw = DeviceWorkload(w)
+    for splits in (1, 0, 3):
+        log(f"[case] wide-range q h_q={h_q} splits={splits}")
+        out, lse, _ = dw.run(num_splits=splits)
+        assert_parity(w, out, lse, label=f"wide-range q h{h_q} s{splits}")
+
+
 # ------------------------------------------------------------ split merge
 
 @pytest.mark.parametrize("fmt", ["bf16", "fp8"])

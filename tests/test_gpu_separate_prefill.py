@@ -170,8 +170,13 @@ def test_separate_prefill_mode_end_to_end(h_q, topk, max_rows):
     ends, _ = oracle.plan_prefill_chunks(w.ctx_lens[nd:], max_rows)
     log(f"  chunks {ends}")
     q = bf16_tensor(w.q)
+    # the batch's host metadata, built once (tokens are grouped by request, decode first)
+    counts = np.bincount(w.req_id_per_token, minlength=w.num_reqs)
+    qsl = np.concatenate([[0], np.cumsum(counts)])
+    plan = smla.smla_build_separate_prefill_plan(qsl, w.ctx_lens, nd, max_rows, "cuda")
+    assert [c[1] for c in plan.chunks] == list(ends)
     o, l = smla.smla_forward_fp8_separate_prefill(q, _dev(w.cache), _dev(w.block_table), _dev(w.req_id_per_token),
-                                                  _dev(w.topk_indices), w.sm_scale, nd, w.ctx_lens, max_rows)
+                                                  _dev(w.topk_indices), w.sm_scale, plan)
     torch.cuda.synchronize()
     o = o.float().cpu().numpy().astype(np.float64)
     l = l.cpu().numpy().astype(np.float64)
