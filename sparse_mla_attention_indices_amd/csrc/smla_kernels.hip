@@ -307,6 +307,16 @@ __device__ __forceinline__ void dma16(const uint8_t *src, uint32_t lds_base)
                  : "memory", "m0");
 }
 
+// global_load_lds_dword: 4 bytes per active lane from `src` into LDS at
+// lds_base + 4 * lane (inline assembly for the same reason as dma16).
+__device__ __forceinline__ void dma4(const void *src, uint32_t lds_base)
+{
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+                 :
+                 : "v"(src), "s"(lds_base)
+                 : "memory", "m0");
+}
+
 // Copy the rows of one tile, as stored, into an LDS ring buffer in the layout
 // lds_row() describes. Wave w copies rows w * kRowsPerWave ...: one lane reads
 // the slots of those rows from the compacted list, each row's slot is then a
@@ -1075,6 +1085,10 @@ struct CfgPC {
     // loop fills only after it: ring buffers 2.. and P^T
     static constexpr int kQBlockBytes = 16 * kDqk * 2;
     static constexpr int kOffQ = 2 * kBufBytes;
+    // the request's block-table row, copied into ring buffers 0 and 1 (free until
+    // the first tile copies, which start after the first round's compaction), so
+    // its load runs beside the indices' instead of after them
+    static constexpr int kBtLdsMax = kOffQ / 4;                       // entries
     static constexpr int kOffSlots = kOffHead + 1024;
     static constexpr int kOffMisc = kOffSlots + kSlotsBytes;         // compaction counts
     static constexpr int kLdsBytes = kOffMisc + 512;
@@ -1306,48 +1320,85 @@ void attn_pc_kernel(const KParams p)
         __syncthreads();
         return n_valid;
     };
-    // slots of a later round of a long list (loaded here, so no load is left in
-    // flight across the tile loop)
-    auto convert_round = [&](int chunk0, int (&slotv)[kPer]) __attribute__((always_inline)) {
+    // Slots of one round of the list (up to kMaxChunk positions from chunk0),
+    // one round trip: the round's indices (into the slot-list area, which the
+    // compaction fills only after every index has been read) and, beside them,
+    // the request's whole block-table row (into ring buffers 0 and 1, free until
+    // the round's first tile copies) are copied straight into LDS. In the first
+    // round the QK^T waves then copy q of their 16 heads (contiguous rows),
+    // needed only once the first tile has landed. Every load of the kernel is
+    // such an explicit copy with an explicit wait: the compiler sees no vector
+    // memory load, so it places no wait of its own (one would also cover the
+    // copies in flight, in the tile loop too).
+    const int32_t *bt_lds = (const int32_t *)smem;
+    const int32_t *idx_lds = lds_slots;
+    const bool bt_in_lds = !p.slot_in && (unsigned)req < (unsigned)p.R && p.MB <= C::kBtLdsMax;
+    auto fetch_round = [&](int chunk0, int (&slotv)[kPer]) __attribute__((always_inline)) {
+        const int n = min(pos_end, chunk0 + kMaxChunk) - chunk0;
+        // wave w copies entries 64 (8 k + w) .. + 63 of each list; lanes past its
+        // end are inactive
+        const uint32_t idx_base = (uint32_t)(uintptr_t)LDS_PTR(int32_t, lds_slots);
+        for (int e0 = 64 * wave; e0 < n; e0 += C::kThreads) {
+            if (e0 + lane < n)
+                dma4(topk_row + chunk0 + e0 + lane, __builtin_amdgcn_readfirstlane(idx_base + 4u * (uint32_t)e0));
+        }
+        if (bt_in_lds) {
+            const int32_t *bt_row = p.bt + (size_t)req * p.MB;
+            const uint32_t bt_base = (uint32_t)(uintptr_t)LDS_PTR(uint8_t, smem);
+            for (int e0 = 64 * wave; e0 < p.MB; e0 += C::kThreads) {
+                if (e0 + lane < p.MB)
+                    dma4(bt_row + e0 + lane, __builtin_amdgcn_readfirstlane(bt_base + 4u * (uint32_t)e0));
+            }
+        }
+        const bool q_now = qk_role && chunk0 == pos_begin;
+        if (q_now) {
+            const uint8_t *qsrc = (const uint8_t *)(p.q + ((size_t)t * p.H + wg_head0 + 16 * rw) * kDqk);
+            const uint32_t qdst = __builtin_amdgcn_readfirstlane(
+                (uint32_t)(uintptr_t)LDS_PTR(uint8_t, smem + C::kOffQ + rw * C::kQBlockBytes));
+#pragma unroll
+            for (int k = 0; k < C::kQBlockBytes / 1024; ++k)
+                dma16(qsrc + 1024 * k + 16 * lane, qdst + 1024u * k);
+        }
+        // every wave's index and table copies have landed (q's copies, issued
+        // after them, may still be in flight: loads complete in order)
+        wait_vmcnt(q_now ? C::kQBlockBytes / 1024 : 0);
+        __syncthreads();
         int idxv[kPer];
 #pragma unroll
         for (int j = 0; j < kPer; ++j) {
-            const int i = chunk0 + tid + C::kThreads * j;
-            idxv[j] = i < pos_end ? topk_row[i] : -1;
+            const int i = tid + C::kThreads * j;
+            idxv[j] = i < n ? idx_lds[i] : -1;
         }
+        if (p.slot_in) {
 #pragma unroll
-        for (int j = 0; j < kPer; ++j)
-            slotv[j] = p.slot_in ? given_slot(idxv[j], p.NB)
-                                 : finish_slot(lookup_block(req, idxv[j], p.bt, p.R, p.MB), req, idxv[j], p.R,
-                                               p.MB, p.NB);
+            for (int j = 0; j < kPer; ++j)
+                slotv[j] = given_slot(idxv[j], p.NB);
+        } else if (bt_in_lds) {
+#pragma unroll
+            for (int j = 0; j < kPer; ++j)
+                slotv[j] = finish_slot(bt_lds[slot_position_ok(req, idxv[j], p.R, p.MB) ? (idxv[j] >> 6) : 0], req,
+                                       idxv[j], p.R, p.MB, p.NB);
+        } else {
+            // a table row too long for the ring buffers: each thread's entries are
+            // copied from the table itself into words of ring buffer 0 (lane l of
+            // wave w, position j: word 64 (kPer w + j) + l), then read back
+            const uint32_t own_base = (uint32_t)(uintptr_t)LDS_PTR(int32_t, (int32_t *)smem) +
+                                      4u * 64u * (uint32_t)(kPer * wave);
+#pragma unroll
+            for (int j = 0; j < kPer; ++j) {
+                const bool ok = slot_position_ok(req, idxv[j], p.R, p.MB);
+                dma4(p.bt + (ok ? (size_t)req * p.MB + (idxv[j] >> 6) : 0),
+                     __builtin_amdgcn_readfirstlane(own_base + 4u * 64u * (uint32_t)j));
+            }
+            wait_vmcnt(0);
+#pragma unroll
+            for (int j = 0; j < kPer; ++j)
+                slotv[j] = finish_slot(((const int32_t *)smem)[64 * (kPer * wave + j) + lane], req, idxv[j], p.R,
+                                       p.MB, p.NB);
+        }
     };
-
-    // QK^T waves: q of their 16 heads (contiguous rows) copied into LDS first,
-    // so its round trip overlaps the indices' and the lookups'
-    if (qk_role) {
-        const uint8_t *qsrc = (const uint8_t *)(p.q + ((size_t)t * p.H + wg_head0 + 16 * rw) * kDqk);
-        const uint32_t qdst = __builtin_amdgcn_readfirstlane(
-            (uint32_t)(uintptr_t)LDS_PTR(uint8_t, smem + C::kOffQ + rw * C::kQBlockBytes));
-#pragma unroll
-        for (int k = 0; k < C::kQBlockBytes / 1024; ++k)
-            dma16(qsrc + 1024 * k + 16 * lane, qdst + 1024u * k);
-    }
-    // the first round's indices, then their block-table lookups
     int slotv[kPer];
-    {
-        int idxv[kPer];
-#pragma unroll
-        for (int j = 0; j < kPer; ++j) {
-            const int i = pos_begin + tid + C::kThreads * j;
-            idxv[j] = i < min(pos_end, pos_begin + kMaxChunk) ? topk_row[i] : -1;
-        }
-#pragma unroll
-        for (int j = 0; j < kPer; ++j)
-            slotv[j] = p.slot_in ? 0 : lookup_block(req, idxv[j], p.bt, p.R, p.MB);
-#pragma unroll
-        for (int j = 0; j < kPer; ++j)
-            slotv[j] = p.slot_in ? given_slot(idxv[j], p.NB) : finish_slot(slotv[j], req, idxv[j], p.R, p.MB, p.NB);
-    }
+    fetch_round(pos_begin, slotv);
 
     // split partials in bf16 (hi rows only, unless the split is short enough
     // for the exact path: then fp32 staging, written out as hi + lo rows)
@@ -1360,7 +1411,7 @@ void attn_pc_kernel(const KParams p)
         float m_run = -INFINITY, l_part = 0.f;   // log2-domain running max (same in a head's 4 lanes), row sum
         for (int chunk0 = pos_begin; chunk0 < pos_end; chunk0 += kMaxChunk) {
             if (chunk0 != pos_begin)
-                convert_round(chunk0, slotv);
+                fetch_round(chunk0, slotv);
             const int n_valid = compact(chunk0, slotv);
             valid_total += n_valid;
             const bool exact_p = n_valid <= kExactPRows;
@@ -1492,7 +1543,7 @@ void attn_pc_kernel(const KParams p)
         constexpr int dma_w = C::kDmaPerWave;
         for (int chunk0 = pos_begin; chunk0 < pos_end; chunk0 += kMaxChunk) {
             if (chunk0 != pos_begin)
-                convert_round(chunk0, slotv);
+                fetch_round(chunk0, slotv);
             const int n_valid = compact(chunk0, slotv);
             valid_total += n_valid;
             const bool exact_p = n_valid <= kExactPRows;
