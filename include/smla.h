@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define SMLA_ABI_VERSION 5
+#define SMLA_ABI_VERSION 6
 #define SMLA_BLOCK_SIZE 64
 #define SMLA_HEAD_DIM_QK 576
 #define SMLA_HEAD_DIM_V 512
@@ -316,6 +316,34 @@ smla_status smla_decode_fp8(const void *q, const void *kv_cache, const int32_t *
                             void *out, float *lse, int32_t *phys_indices_out,
                             void *workspace, size_t workspace_bytes,
                             const smla_options *options, hipStream_t stream);
+
+/* Split workspace of smla_decode_fp8_noalloc: 64 MiB of device memory that the
+ * library holds on each device it runs on, until the process ends. */
+#define SMLA_STATIC_WORKSPACE_BYTES ((size_t)64 << 20)
+
+/* smla_decode_fp8 for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation.
+ * Same computation, arguments and results as smla_decode_fp8, minus the
+ * workspace: a call whose top-k lists are split keeps its per-part results in a
+ * library-owned array of SMLA_STATIC_WORKSPACE_BYTES on the current device
+ * (found once per device with hipGetSymbolAddress), and the call makes no
+ * allocation of any kind. Nothing in that array needs initialising: each call
+ * writes every entry it later reads. Every call on one device shares the
+ * device's array, so calls that may overlap on one device (other streams,
+ * other host threads) race; order them on one stream or use smla_decode_fp8
+ * with workspaces of their own.
+ * Errors: as smla_decode_fp8; SMLA_ERR_WORKSPACE if the split plan needs more
+ * than SMLA_STATIC_WORKSPACE_BYTES (smla_workspace_size reports the need);
+ * SMLA_ERR_ARG for SMLA_FLAG_PARTIALS_ONLY, SMLA_FLAG_DEFER_MERGE or
+ * SMLA_FLAG_MERGE_ONLY (their parts would live in the shared array);
+ * SMLA_ERR_HIP if the array's address cannot be found. Nothing is launched
+ * or written on an error. */
+smla_status smla_decode_fp8_noalloc(const void *q, const void *kv_cache, const int32_t *block_table,
+                                    const int32_t *req_id_per_token, const int32_t *topk_indices,
+                                    float sm_scale, int32_t num_tokens, int32_t h_q, int32_t topk,
+                                    int32_t num_reqs, int32_t max_blocks_per_req, int64_t num_blocks,
+                                    void *out, float *lse, int32_t *phys_indices_out,
+                                    const smla_options *options, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -13,6 +13,8 @@
 
 namespace smla {
 
+static_assert(SMLA_STATIC_WORKSPACE_BYTES == kStaticWorkspaceBytes, "static workspace size in the header");
+
 static size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 size_t partials_o_offset(size_t rows) { return align_up(rows * sizeof(float), 256); }
@@ -121,11 +123,15 @@ smla_status attention_entry(CacheFormat fmt, const void *q, const void *kv_cache
                             int32_t h_q, int32_t topk, int32_t num_reqs,
                             int32_t max_blocks_per_req, int64_t num_blocks, void *out, float *lse,
                             int32_t *phys_indices_out, void *workspace, size_t workspace_bytes,
-                            const smla_options *options, hipStream_t stream)
+                            const smla_options *options, hipStream_t stream, bool static_ws = false)
 {
     smla_status st = check_options(options);
     if (st != SMLA_OK)
         return st;
+    // the static workspace holds one call's own parts: no staged or parts-only calls
+    if (static_ws && options &&
+        (options->flags & (SMLA_FLAG_PARTIALS_ONLY | SMLA_FLAG_DEFER_MERGE | SMLA_FLAG_MERGE_ONLY)))
+        return SMLA_ERR_ARG;
     if (!(sm_scale > 0.f) || !isfinite(sm_scale))
         return SMLA_ERR_ARG;
     if ((st = check_sizes(num_tokens, h_q, topk)) != SMLA_OK)
@@ -157,6 +163,15 @@ smla_status attention_entry(CacheFormat fmt, const void *q, const void *kv_cache
     if ((st = device_cus(&cus)) != SMLA_OK)
         return st;
     const Plan plan = make_plan(num_tokens, h_q, topk, cus, forced, partials_only);
+    if (static_ws) {
+        // no allocation: the device's static array, or an error if the plan needs more
+        if (plan.workspace > kStaticWorkspaceBytes)
+            return SMLA_ERR_WORKSPACE;
+        workspace = nullptr;
+        if (plan.workspace > 0 && static_workspace(&workspace) != hipSuccess)
+            return SMLA_ERR_HIP;
+        workspace_bytes = plan.workspace;
+    }
     if (plan.workspace > 0 && (workspace == nullptr || workspace_bytes < plan.workspace))
         return SMLA_ERR_WORKSPACE;
 
@@ -439,6 +454,19 @@ smla_status smla_decode_fp8(const void *q, const void *kv_cache, const int32_t *
                                  topk_indices, sm_scale, num_tokens, h_q, topk, num_reqs,
                                  max_blocks_per_req, num_blocks, out, lse, phys_indices_out,
                                  workspace, workspace_bytes, options, stream);
+}
+
+smla_status smla_decode_fp8_noalloc(const void *q, const void *kv_cache, const int32_t *block_table,
+                                    const int32_t *req_id_per_token, const int32_t *topk_indices,
+                                    float sm_scale, int32_t num_tokens, int32_t h_q, int32_t topk,
+                                    int32_t num_reqs, int32_t max_blocks_per_req, int64_t num_blocks,
+                                    void *out, float *lse, int32_t *phys_indices_out,
+                                    const smla_options *options, hipStream_t stream)
+{
+    return smla::attention_entry(smla::kCacheFp8, q, kv_cache, block_table, req_id_per_token,
+                                 topk_indices, sm_scale, num_tokens, h_q, topk, num_reqs,
+                                 max_blocks_per_req, num_blocks, out, lse, phys_indices_out, nullptr, 0,
+                                 options, stream, true);
 }
 
 }  // extern "C"

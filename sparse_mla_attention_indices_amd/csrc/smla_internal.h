@@ -25,6 +25,10 @@ constexpr int kHeadsPerGroup = 64;
 // Most top-k parts one token's list is cut into.
 constexpr int kMaxSplits = 32;
 
+// Bytes of the split workspace that the allocation-free entry point takes from
+// a library-owned device array (one per device, held until the process ends).
+constexpr size_t kStaticWorkspaceBytes = (size_t)64 << 20;
+
 struct Plan {
     int num_splits;          // top-k parts per token
     int split_len;           // top-k positions per part (the last part may be shorter)
@@ -88,6 +92,10 @@ hipError_t launch_attention(CacheFormat fmt, const AttnArgs &a, const Plan &p, b
 // cache_write_kernel: rows of num_tokens tokens into their slots (< num_slots).
 hipError_t launch_cache_write(CacheFormat fmt, const void *k_c, const void *k_pe, const int64_t *slot_mapping,
                              void *cache, int64_t num_tokens, int64_t num_slots, hipStream_t stream);
+
+// Device address of this device's static split workspace (kStaticWorkspaceBytes,
+// 256-byte aligned), looked up once per device; the current device must be set.
+hipError_t static_workspace(void **ptr);
 
 // merge_kernel alone over a partials buffer of T x S x H entries; part_exact
 // null: fp32 partials, else bf16 rows and their flags (attn_pc_kernel's form).

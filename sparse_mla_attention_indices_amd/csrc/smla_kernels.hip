@@ -55,6 +55,7 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "smla_internal.h"
@@ -2060,6 +2061,37 @@ hipError_t launch_fmt(const KParams &p, hipStream_t stream)
 }
 
 }  // namespace
+
+// The split workspace of the allocation-free entry point: each device holds
+// its own copy for the life of the process. In host code the array's name is
+// only a stand-in for the symbol; kernels get the device address that
+// hipGetSymbolAddress returns, never the name.
+static __device__ __align__(256) uint8_t scratch[kStaticWorkspaceBytes];
+
+hipError_t static_workspace(void **ptr)
+{
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void *addr[kMaxDevices] = {};
+    int dev = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess)
+        return err;
+    if (dev < 0 || dev >= kMaxDevices)
+        return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (addr[dev] == nullptr) {
+        void *p = nullptr;
+        err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (err != hipSuccess)
+            return err;
+        if (p == nullptr || ((uintptr_t)p & 255u) != 0)
+            return hipErrorInvalidSymbol;
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    return hipSuccess;
+}
 
 hipError_t launch_convert(const int32_t *req_id, const int32_t *block_table, const int32_t *topk,
                           int32_t *out, int num_tokens, int topk_len, int num_reqs, int max_blocks,

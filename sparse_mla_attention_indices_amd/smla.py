@@ -29,7 +29,8 @@ STATUS_NAMES = {0: "SMLA_OK", 1: "SMLA_ERR_NULL", 2: "SMLA_ERR_SHAPE", 3: "SMLA_
 EXPORTS = ("smla_status_string", "smla_abi_version", "smla_plan", "smla_workspace_size",
            "smla_merge_partials", "smla_concat_and_cache_mla", "smla_convert_indices",
            "smla_prefill_workspace_rows", "smla_plan_prefill_chunks", "smla_convert_indices_workspace",
-           "smla_gather_upconvert_fp8", "smla_prefill_bf16", "smla_decode_fp8")
+           "smla_gather_upconvert_fp8", "smla_prefill_bf16", "smla_decode_fp8", "smla_decode_fp8_noalloc")
+STATIC_WORKSPACE_BYTES = 64 << 20
 CACHE_FORMATS = {"auto": 0, "bf16": 0, "fp8_ds_mla": 1}
 FLAG_PARTIALS_ONLY = 0x1
 FLAG_SLOT_INDICES = 0x2
@@ -88,6 +89,8 @@ def library() -> ctypes.CDLL:
     for name in ("smla_prefill_bf16", "smla_decode_fp8"):
         getattr(lib, name).restype = ctypes.c_int
         getattr(lib, name).argtypes = attn
+    lib.smla_decode_fp8_noalloc.restype = ctypes.c_int
+    lib.smla_decode_fp8_noalloc.argtypes = attn[:15] + attn[17:]
     _lib = lib
     return lib
 
@@ -296,6 +299,33 @@ def smla_decode_fp8(q, kv_cache, block_table, req_id_per_token, topk_indices, sm
     return _attention("smla_decode_fp8", q, kv_cache, block_table, req_id_per_token, topk_indices,
                       sm_scale, out, lse, phys_indices_out, workspace, num_splits, stream, want_lse,
                       partials_only, slot_indices, stage)
+
+
+def smla_decode_fp8_noalloc(q, kv_cache, block_table, req_id_per_token, topk_indices, sm_scale, out,
+                            lse=None, phys_indices_out=None, num_splits=0, stream=None, slot_indices=False):
+    """smla_decode_fp8 with the split workspace in the library's static device
+    array (no allocation by the library or here): out (bf16 [T, h_q, 512]) is
+    required, lse (fp32 [T, h_q]) and phys_indices_out are optional. Calls that
+    may overlap on one device share that array and race. Returns (out, lse)."""
+    if kv_cache.dtype != torch.uint8 or kv_cache.shape[1:] != (64, 656):
+        raise ValueError("kv_cache must be uint8 [num_blocks, 64, 656]")
+    T, H, D = q.shape
+    if D != 576:
+        raise ValueError("q must be [num_tokens, h_q, 576]")
+    K = topk_indices.shape[1]
+    if slot_indices:
+        block_table = req_id_per_token = None
+    R, MB = (1, 1) if block_table is None else block_table.shape
+    _check(library().smla_decode_fp8_noalloc(
+        _dev(q, "q", torch.bfloat16, 3), _dev(kv_cache, "kv_cache"),
+        _dev(block_table, "block_table", torch.int32, 2),
+        _dev(req_id_per_token, "req_id_per_token", torch.int32, 1),
+        _dev(topk_indices, "topk_indices", torch.int32, 2), float(sm_scale), T, H, K, R, MB, kv_cache.shape[0],
+        _dev(out, "out", torch.bfloat16, 3), _dev(lse, "lse", torch.float32, 2),
+        _dev(phys_indices_out, "phys_indices_out", torch.int32, 2),
+        _options(num_splits, FLAG_SLOT_INDICES if slot_indices else 0), _stream(stream)),
+        "smla_decode_fp8_noalloc")
+    return out, lse
 
 
 # ---- separate-prefill mode of an fp8_ds_mla cache (decode tokens over the fp8

@@ -40,7 +40,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_abi_version(lib):
-    assert smla.smla_abi_version() == 5
+    assert smla.smla_abi_version() == 6
 
 
 def test_status_strings(lib):
@@ -168,6 +168,27 @@ def test_attention_rejects_bad_options(lib, name):
 def test_zero_tokens_is_a_noop(lib, name):
     # no pointer is needed and nothing is launched
     assert _attn(lib, name, q=None, kv=None, bt=None, req=None, idx=None, out=None, T=0) == 0
+
+
+def _noalloc(lib, q=A16, kv=A16, bt=A16, req=A16, idx=A16, scale=0.04, T=8, H=16, K=64, R=2, MB=4, NB=8,
+             out=A16B, lse=A16, phys=None, opts=None):
+    return lib.smla_decode_fp8_noalloc(q, kv, bt, req, idx, scale, T, H, K, R, MB, NB, out, lse, phys, opts, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), 1), (dict(out=None), 1), (dict(idx=None), 1), (dict(H=8), 2), (dict(K=0), 2),
+    (dict(q=MIS), 3), (dict(out=MIS), 3), (dict(scale=0.0), 6),
+])
+def test_noalloc_rejects_before_any_hip_call(lib, kw, code):
+    assert _noalloc(lib, **kw) == code
+
+
+def test_noalloc_rejects_staged_and_parts_only_flags(lib):
+    for bits in (smla.FLAG_PARTIALS_ONLY, smla.FLAG_DEFER_MERGE, smla.FLAG_MERGE_ONLY):
+        o = smla.SmlaOptions()
+        o.flags = bits
+        assert _noalloc(lib, opts=ctypes.byref(o)) == 6
+    assert _noalloc(lib, q=None, kv=None, bt=None, req=None, idx=None, out=None, T=0) == 0
 
 
 def test_options_struct_layout():
