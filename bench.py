@@ -163,12 +163,14 @@ def upconvert_bench(torch, smla, W, dev, stream, flush, sink, steps: int):
 
 def kernels_of_plan(cache_format: str, h_q: int, splits: int):
     """Names of the kernels one call launches, from the split plan (the same rule the
-    library's launcher applies: 64 heads per workgroup for h_q >= 64)."""
-    heads = 64 if h_q >= 64 else h_q
-    if cache_format == "fp8" and heads == 64:
+    library's launcher applies: one workgroup covers all h_q heads of a token)."""
+    fmt = "fp8" if cache_format == "fp8" else "bf16"
+    if h_q == 128:
+        names = [f"attn128_kernel<{fmt}>"]
+    elif cache_format == "fp8" and h_q == 64:
         names = ["attn_pc_kernel"]
     else:
-        names = [f"attn_kernel<{'fp8' if cache_format == 'fp8' else 'bf16'}, {heads // 16}>"]
+        names = [f"attn_kernel<{fmt}, {h_q // 16}>"]
     if splits > 1:
         names.append(f"merge_kernel<{splits}>")
     return names

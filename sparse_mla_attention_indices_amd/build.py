@@ -13,17 +13,21 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libsmla.so")
-SOURCES = [os.path.join(CSRC, "smla_api.cpp"), os.path.join(CSRC, "smla_kernels.hip")]
-HEADERS = [os.path.join(ROOT, "include", "smla.h"), os.path.join(CSRC, "smla_internal.h")]
+SOURCES = [os.path.join(CSRC, "smla_api.cpp"), os.path.join(CSRC, "smla_kernels.hip"),
+           os.path.join(CSRC, "smla_attn128.hip")]
+HEADERS = [os.path.join(ROOT, "include", "smla.h"), os.path.join(CSRC, "smla_internal.h"),
+           os.path.join(CSRC, "smla_device.h")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 # Packed-fp32 VALU ops are disabled: the compiler must not emit them.
-# MFMA accumulators are kept in the VGPR form; the 512-register attention waves
-# then place operands in AGPRs without spilling.
-DEVICE_FLAGS = ["--offload-arch=" + ARCH, "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-                "-mllvm", "-amdgpu-mfma-vgpr-form=1"]
+DEVICE_FLAGS = ["--offload-arch=" + ARCH, "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# MFMA results in ordinary registers (VGPR form): the two-wave-per-SIMD kernels
+# then place operands in AGPRs without spilling, and attn128_kernel keeps its S^T
+# accumulator there while O takes every AGPR through its written-out MFMA.
+VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]
+FILE_FLAGS = {"smla_kernels.hip": VGPR_FORM, "smla_attn128.hip": VGPR_FORM}
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-result", "-I", os.path.join(ROOT, "include")]
 
 
@@ -34,7 +38,8 @@ def build(verbose: bool = False) -> str:
     os.makedirs(build_dir, exist_ok=True)
     for src in SOURCES:
         obj = os.path.join(build_dir, os.path.basename(src) + ".o")
-        cmd = [HIPCC, *DEVICE_FLAGS, *COMMON, "-x", "hip", "-c", src, "-o", obj]
+        cmd = [HIPCC, *DEVICE_FLAGS, *FILE_FLAGS.get(os.path.basename(src), []), *COMMON, "-x", "hip", "-c", src,
+               "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         r = subprocess.run(cmd, capture_output=True, text=True)

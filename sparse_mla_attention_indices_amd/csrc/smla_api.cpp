@@ -22,7 +22,9 @@ size_t partials_o_offset(size_t rows) { return align_up(rows * sizeof(float), 25
 Plan make_plan(int num_tokens, int h_q, int topk, int num_cus, int forced_splits, bool partials)
 {
     Plan p{};
-    p.head_blocks = h_q >= kHeadsPerGroup ? h_q / kHeadsPerGroup : 1;
+    // h_q = 128: one workgroup covers every head (attn128_kernel); h_q = 64:
+    // one 64-head workgroup; 16 and 32 heads: one smaller workgroup
+    p.head_blocks = 1;
     int splits = 1;
     if (forced_splits > 0) {
         splits = std::min(std::min(forced_splits, topk), kMaxSplits);

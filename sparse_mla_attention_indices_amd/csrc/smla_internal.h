@@ -18,8 +18,8 @@ constexpr int kBf16RowBytes = kDqk * 2;
 
 enum CacheFormat { kCacheBf16 = 0, kCacheFp8 = 1 };
 
-// Heads one workgroup covers: 64 (eight waves) for h_q >= 64, so h_q = 128 takes
-// two workgroups per token; h_q = 16 / 32 use one two- / four-wave workgroup.
+// Every workgroup covers all h_q heads of its token: 128 (four waves of 32
+// heads), 64 (eight waves), 32 or 16.
 constexpr int kHeadsPerGroup = 64;
 
 // Most top-k parts one token's list is cut into.

@@ -8,7 +8,7 @@ Builds, under _build/sanitize/ (not committed):
   * libsmla.so with its host code (csrc/smla_api.cpp: argument validation, the
     split planner, the workspace contract, the prefill chunk planner) compiled
     by hipcc with AddressSanitizer and UndefinedBehaviorSanitizer on the host
-    side only, and the unchanged GPU kernels object;
+    side only, and the unchanged GPU kernel objects;
 then runs, each in its own process with the matching sanitizer runtime
 preloaded (gcc's for the oracle, clang's for the library; one runtime per
 process):
@@ -54,7 +54,7 @@ def build_oracle() -> str:
 
 def build_library() -> str:
     api_o = os.path.join(OUT, "smla_api.o")
-    kern_o = os.path.join(OUT, "smla_kernels.o")
+    kern_os = [os.path.join(OUT, "smla_kernels.o"), os.path.join(OUT, "smla_attn128.o")]
     lib = os.path.join(OUT, "libsmla.so")
     dev = ["--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
     host_san = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
@@ -62,11 +62,11 @@ def build_library() -> str:
     common = ["-O1", "-g", "-std=c++17", "-fPIC", "-I", os.path.join(ROOT, "include")]
     run([HIPCC, *dev, *common, *host_san, "-x", "hip", "-c",
          os.path.join(PKG, "csrc", "smla_api.cpp"), "-o", api_o])
-    run([HIPCC, *dev, "-O3", "-std=c++17", "-fPIC", "-mllvm", "-amdgpu-mfma-vgpr-form=1", "-I",
-         os.path.join(ROOT, "include"), "-x", "hip", "-c", os.path.join(PKG, "csrc", "smla_kernels.hip"),
-         "-o", kern_o])
-    # host-only link with clang++ (the kernels object carries its own device code)
-    run([CLANGXX, "-shared", "-fPIC", "-fsanitize=address,undefined", "-shared-libsan", api_o, kern_o,
+    for src, obj in zip(("smla_kernels.hip", "smla_attn128.hip"), kern_os):
+        run([HIPCC, *dev, "-O3", "-std=c++17", "-fPIC", "-mllvm", "-amdgpu-mfma-vgpr-form=1", "-I",
+             os.path.join(ROOT, "include"), "-x", "hip", "-c", os.path.join(PKG, "csrc", src), "-o", obj])
+    # host-only link with clang++ (the kernel objects carry their own device code)
+    run([CLANGXX, "-shared", "-fPIC", "-fsanitize=address,undefined", "-shared-libsan", api_o, *kern_os,
          "-L/opt/rocm/lib", "-lamdhip64", "-Wl,-rpath,/opt/rocm/lib", "-o", lib])
     return lib
 

@@ -66,8 +66,8 @@ def test_plan_fills_the_chip_for_small_decode_batches(lib):
     assert smla.smla_plan(256, 32, 512, 256) == (1, 0)
     # 32-head workgroups fit two per CU: 64 tokens x 32 heads -> 8 splits
     assert smla.smla_plan(64, 32, 2048, 256)[0] == 8
-    # 128 heads, 32 tokens: two 64-head workgroups per token -> 4 splits
-    assert smla.smla_plan(32, 128, 2048, 256)[0] == 4
+    # 128 heads, 32 tokens: one 128-head workgroup per token -> 8 splits
+    assert smla.smla_plan(32, 128, 2048, 256)[0] == 8
     # enough (token, head-block) units already: no split, no workspace
     assert smla.smla_plan(512, 16, 2048, 256) == (1, 0)
     assert smla.smla_plan(16384, 128, 2048, 256) == (1, 0)
