@@ -163,11 +163,12 @@ def upconvert_bench(torch, smla, W, dev, stream, flush, sink, steps: int):
 
 def kernels_of_plan(cache_format: str, h_q: int, splits: int):
     """Names of the kernels one call launches, from the split plan (the same rule the
-    library's launcher applies: one workgroup covers all h_q heads of a token)."""
+    library's launcher applies: one workgroup covers all h_q heads of a token, except
+    fp8 with h_q = 128, which takes two 64-head workgroups)."""
     fmt = "fp8" if cache_format == "fp8" else "bf16"
-    if h_q == 128:
-        names = [f"attn128_kernel<{fmt}>"]
-    elif cache_format == "fp8" and h_q == 64:
+    if h_q == 128 and fmt == "bf16":
+        names = ["attn128_kernel"]
+    elif fmt == "fp8" and h_q >= 64:
         names = ["attn_pc_kernel"]
     else:
         names = [f"attn_kernel<{fmt}, {h_q // 16}>"]

@@ -22,21 +22,20 @@ size_t partials_o_offset(size_t rows) { return align_up(rows * sizeof(float), 25
 Plan make_plan(int num_tokens, int h_q, int topk, int num_cus, int forced_splits, bool partials)
 {
     Plan p{};
-    // h_q = 128: one workgroup covers every head (attn128_kernel); h_q = 64:
-    // one 64-head workgroup; 16 and 32 heads: one smaller workgroup
-    p.head_blocks = 1;
     int splits = 1;
     if (forced_splits > 0) {
         splits = std::min(std::min(forced_splits, topk), kMaxSplits);
     } else {
-        // One workgroup per (token, head block) when that fills the chip;
-        // otherwise cut each token's list so the grid covers every workgroup
-        // slot once: 64-head workgroups take a CU each, 32- and 16-head ones
-        // fit two per CU.
+        // One workgroup per token when that fills the chip; otherwise cut each
+        // token's list so the grid covers every workgroup slot once: 64- and
+        // 128-head workgroups take a CU each, 32- and 16-head ones fit two per
+        // CU. (fp8 with h_q = 128 runs two 64-head workgroups per token and
+        // part under the same plan, so the plan and the workspace it sizes do
+        // not depend on the cache format.)
         // A list of at most kShortList positions is not cut once every CU has a
         // workgroup: the merge launch then costs more than the second
         // workgroup per CU gains.
-        const int64_t units = (int64_t)num_tokens * p.head_blocks;
+        const int64_t units = num_tokens;
         const int64_t slots = (int64_t)num_cus * (h_q >= kHeadsPerGroup ? 1 : 2);
         const int64_t tiles = (topk + kBlock - 1) / kBlock;
         constexpr int kShortList = 512;

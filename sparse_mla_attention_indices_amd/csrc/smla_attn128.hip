@@ -1,13 +1,12 @@
-// smla_attn128.hip -- sparse MLA attention with all 128 heads of a token in one
-// workgroup (h_q = 128), for both cache formats.
+// smla_attn128.hip -- sparse MLA attention over the bf16 cache with all 128
+// heads of a token in one workgroup (h_q = 128).
 //
 // What is computed follows the vLLM page "vllm/v1/attention/backends/mla/
 // flashmla_sparse.py" (FLASHMLA_SPARSE backend): the index conversion of
 // triton_convert_req_index_to_global_index, the fp8_ds_mla row format of the
 // module note, and the multi-query attention with 576-wide keys and 512-wide
 // values that FlashMLASparseImpl.forward runs (_bf16_flash_mla_kernel for the
-// bf16 cache, _fp8_flash_mla_kernel for fp8_ds_mla). How it is computed is this
-// library's own design for gfx950:
+// bf16 cache). How it is computed is this library's own design for gfx950:
 //
 //  * Workgroup = one query token x all 128 heads x one part of its top-k list.
 //    Every gathered tile of 32 cache rows is shared by the 128 heads: it is
@@ -21,14 +20,12 @@
 //    k-rows per step are taken in the accumulator's row order; the transposed
 //    V^T reads gather the same rows in that order). No weight goes through LDS.
 //  * O^T of the wave's 32 heads (32 x 512 fp32) lives in the 256 accumulation
-//    registers (AGPRs); q lives in ordinary registers for the whole kernel:
-//    bf16 columns for the bf16 cache; for fp8, the 512 latent columns as hi + lo
-//    e4m3 terms with a power-of-two scale per head and 128-column group (the
-//    scaled MFMA applies it), and the 64 RoPE columns as bf16 in LDS.
-//  * fp8: the raw e4m3 K bytes feed v_mfma_scale_f32_32x32x64_f8f6f4; each
-//    128-column group's partial S is multiplied by its rows' scales; V^T is
-//    converted to bf16 exactly and the weights of each 128-dim output group
-//    carry that group's row scales, so dequantisation adds no rounding.
+//    registers (AGPRs); q (bf16, 144 registers per lane) lives in ordinary
+//    registers for the whole kernel.
+//  * The fp8_ds_mla cache keeps the 64-head kernel at h_q = 128 (two
+//    workgroups per token): there its QK^T and PV waves overlap on each SIMD,
+//    while one wave per SIMD here leaves the fp8 tile's dependency chain
+//    (dequantisation scales, hi + lo q terms) exposed.
 //  * Prologue, gather, compaction and the explicit-wait discipline are those
 //    of the 64-head kernel: the indices and the block-table row come into LDS
 //    in one round trip, valid slots are compacted in list order, each row is
@@ -41,8 +38,6 @@
 #include <math.h>
 #include <stdint.h>
 
-#include <type_traits>
-
 #include "smla_device.h"
 #include "smla_internal.h"
 
@@ -52,48 +47,29 @@ namespace {
 typedef float f32x16 __attribute__((__vector_size__(64)));
 typedef uint32_t u32x4 __attribute__((__vector_size__(16)));
 
-template <int FMT> struct Ring128;
 // bf16 rows: 1152 bytes, stored at a 1168-byte stride (16 consecutive rows fall
 // on distinct banks for the 16-byte K reads and the transposed V reads); four
 // ring buffers.
-template <> struct Ring128<kCacheBf16> {
-    static constexpr int kRowStride = kBf16RowBytes + 16;
-    static constexpr int kBlockGap = 0;
-    static constexpr int kNBuf = 4;
-};
-// fp8_ds_mla rows: 656 bytes at their own stride, rows 16..31 of a tile 16
-// bytes later (the transposed V reads touch rows r and r + 8); six buffers
-// (the RoPE part of q takes the room of a seventh).
-template <> struct Ring128<kCacheFp8> {
-    static constexpr int kRowStride = kFp8RowBytes;
-    static constexpr int kBlockGap = 16;
-    static constexpr int kNBuf = 6;
-};
-
-template <int FMT>
 struct Cfg128 {
     static constexpr int kWaves = 4;
     static constexpr int kThreads = 64 * kWaves;
     static constexpr int kHeads = 128;
-    static constexpr int kRowBytes = RowFmt<FMT>::kBytes;
+    static constexpr int kRowBytes = RowFmt<kCacheBf16>::kBytes;
     static constexpr int kChunksPerRow = kRowBytes / 16;
-    static constexpr int kRowStride = Ring128<FMT>::kRowStride;
-    static constexpr int kRowBlockBytes = 16 * kRowStride + Ring128<FMT>::kBlockGap;
+    static constexpr int kRowStride = kBf16RowBytes + 16;
+    static constexpr int kRowBlockBytes = 16 * kRowStride;
     static constexpr int kInstrPerRow = (kChunksPerRow + 63) / 64;
     static constexpr int kRowsPerWave = kTile / kWaves;
     static constexpr int kDmaPerWave = kRowsPerWave * kInstrPerRow;  // copy instructions per wave and tile
     static constexpr int kBufBytes = (kRB * kRowBlockBytes + 255) / 256 * 256;
-    static constexpr int kNBuf = Ring128<FMT>::kNBuf;
+    static constexpr int kNBuf = 4;
     static constexpr int kOffSlots = kNBuf * kBufBytes;
-    // fp8: the RoPE columns of q (bf16), 16 bytes per lane and k-step, lane-major
-    static constexpr int kOffQRope = kOffSlots + kMaxChunk * 4;
-    static constexpr int kQRopeBytes = FMT == kCacheFp8 ? kWaves * 4 * 64 * 16 : 0;
-    static constexpr int kOffMisc = kOffQRope + kQRopeBytes;
+    static constexpr int kOffMisc = kOffSlots + kMaxChunk * 4;
     static constexpr int kLdsBytes = kOffMisc + 512;
     static constexpr int kStageRow = kDv * 2 + 16;                     // bf16 output staging row
     static constexpr int kBtLdsMax = 2 * kBufBytes / 4;                // table entries in buffers 0, 1
     static_assert(kLdsBytes <= 160 * 1024, "LDS of one gfx950 workgroup");
-    static_assert(kHeads * kStageRow <= kOffQRope, "output staging fits the ring and the slot list");
+    static_assert(kHeads * kStageRow <= kOffMisc, "output staging fits the ring and the slot list");
     static_assert(kTile % kWaves == 0, "whole rows per wave");
     static_assert(kDmaPerWave * (kNBuf - 2) <= 63, "copies in flight within the vmcnt range");
     static_assert(16 + (kMaxChunk / kThreads) * kWaves <= 128, "compaction counts fit");
@@ -138,12 +114,10 @@ __device__ __forceinline__ void o_zero(f32x16 &o)
 // 2^20 rows. Past it, the workgroup redoes the list in two passes.
 constexpr float kRefHeadroom = 64.0f;
 
-template <int FMT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void attn128_kernel(const KParams p)
 {
-    using C = Cfg128<FMT>;
-    constexpr bool kFp8 = FMT == kCacheFp8;
+    using C = Cfg128;
     constexpr int kPer = kMaxChunk / C::kThreads;   // top-k positions per thread per round
 
     __shared__ __attribute__((aligned(1024))) uint8_t smem[C::kLdsBytes];
@@ -172,22 +146,14 @@ void attn128_kernel(const KParams p)
     const int pos_end = min(p.K, pos_begin + p.split_len);
 
     // ---- q of this lane's head, requested first (plain loads; their wait is
-    //      placed where the prologue has already waited for everything)
-    //      bf16: k-step ks (16 columns) holds columns 16 ks + 8 hh .. + 7.
-    //      fp8:  latent k-instruction i (64 columns) holds columns
-    //            64 i + 16 hh + 0..15 and 64 i + 32 + 16 hh + 0..15 (the
-    //            scaled MFMA's operand order); RoPE k-step ks as bf16.
+    //      placed where the prologue has already waited for everything):
+    //      k-step ks (16 columns) holds columns 16 ks + 8 hh .. + 7.
     const uint4 *qrow = (const uint4 *)(p.q + ((size_t)t * p.H + head) * kDqk);
     constexpr int kQ = 36;             // 16-byte pieces of q per lane
     u32x4 qraw[kQ];
 #pragma unroll
     for (int k = 0; k < kQ; ++k) {
-        uint4 w;
-        if constexpr (kFp8)
-            w = k < 32 ? qrow[(k >> 2) * 8 + (k & 2) * 2 + 2 * hh + (k & 1)] : qrow[64 + 2 * (k - 32) + hh];
-        else
-            w = qrow[2 * k + hh];
-        qraw[k] = __builtin_bit_cast(u32x4, w);
+        qraw[k] = __builtin_bit_cast(u32x4, qrow[2 * k + hh]);
     }
 
     // ---- one round of the list: indices and the block-table row into LDS in
@@ -297,74 +263,18 @@ void attn128_kernel(const KParams p)
     for (int k = 0; k < kQ; ++k)
         asm volatile("" : "+v"(qraw[k]));
 
-    // q operands
-    bf16x8 qb[kFp8 ? 1 : 36];          // bf16 cache: k-steps 0..35
-    i32x8 qh[kFp8 ? 8 : 1], ql[kFp8 ? 8 : 1];
-    int qsc[kFp8 ? 4 : 1];             // fp8: e8m0 scale of q per 128-column group (the lo term's extra
-                                       // 2^-4 is the K operand's scale in its MFMA)
-    // fp8: RoPE k-step ks of this lane in LDS (each lane reads back only what it wrote)
-    uint8_t *const qrope = smem + C::kOffQRope + 4096 * wave + 16 * lane;
-    if constexpr (!kFp8) {
+    // q as the B operand of the QK^T MFMAs, k-steps 0..35
+    bf16x8 qb[kQ];
 #pragma unroll
-        for (int k = 0; k < 36; ++k)
-            qb[k] = __builtin_bit_cast(bf16x8, qraw[k]);
-    } else {
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-            *(u32x4 *)(qrope + 1024 * ks) = qraw[32 + ks];
-#pragma unroll
-        for (int G = 0; G < 4; ++G) {
-            // the group's 64 values of this lane are qraw[8 G .. 8 G + 7]; the
-            // largest magnitude compared on the bf16 bits (same order as the values)
-            uint32_t mbits = 0;
-#pragma unroll
-            for (int c = 0; c < 8; ++c) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const uint32_t w = qraw[8 * G + c][e];
-                    mbits = max(mbits, max(w & 0x7FFFu, (w >> 16) & 0x7FFFu));
-                }
-            }
-            mbits = max(mbits, (uint32_t)__shfl_xor((int)mbits, 32));   // the head's other half of the group
-            // block exponent: the largest |q| of the group maps into [128, 256)
-            const int ex = max((int)((mbits >> 7) & 0xFF) - 127 - 7, -120);
-            const float down = __uint_as_float((uint32_t)(127 - ex) << 23);     // 2^-ex, exact
-#pragma unroll
-            for (int ii = 0; ii < 2; ++ii) {
-                uint32_t hw[8], lw[8];
-#pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    // values 32 ii + 4 j .. + 3: two words of qraw[8 G + 4 ii + j / 2]
-                    const u32x4 src = qraw[8 * G + 4 * ii + (j >> 1)];
-                    const uint32_t w0 = src[2 * (j & 1)], w1 = src[2 * (j & 1) + 1];
-                    const float x[4] = {bf16_lo(w0) * down, bf16_hi(w0) * down, bf16_lo(w1) * down,
-                                        bf16_hi(w1) * down};
-                    s16x2 h = {0, 0};
-                    h = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(h, x[0], x[1], 1.0f, false);
-                    h = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(h, x[2], x[3], 1.0f, true);
-                    hw[j] = __builtin_bit_cast(uint32_t, h);
-                    // what the hi term misses, times 16 (the lo term's scale is 2^(ex - 4))
-                    const f32x2 b0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(hw[j], 1.0f, false);
-                    const f32x2 b1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(hw[j], 1.0f, true);
-                    s16x2 l = {0, 0};
-                    l = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(l, (x[0] - b0[0]) * 16.f, (x[1] - b0[1]) * 16.f, 1.0f, false);
-                    l = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(l, (x[2] - b1[0]) * 16.f, (x[3] - b1[1]) * 16.f, 1.0f, true);
-                    lw[j] = __builtin_bit_cast(uint32_t, l);
-                }
-                qh[2 * G + ii] = i32x8{(int)hw[0], (int)hw[1], (int)hw[2], (int)hw[3], (int)hw[4], (int)hw[5], (int)hw[6], (int)hw[7]};
-                ql[2 * G + ii] = i32x8{(int)lw[0], (int)lw[1], (int)lw[2], (int)lw[3], (int)lw[4], (int)lw[5], (int)lw[6], (int)lw[7]};
-            }
-            qsc[G] = 127 + ex;
-        }
-    }
+    for (int k = 0; k < kQ; ++k)
+        qb[k] = __builtin_bit_cast(bf16x8, qraw[k]);
 
     // ---- per-lane LDS offsets inside a tile buffer, derived from the lane id in
     //      every tile (from late(lane): held across the tile loop instead, they and
     //      the row numbers below would take registers that q and O need)
     struct Offs {
-        int k;          // K / RoPE rows for the A operand: row n32, half hh
-        int v[2][2];    // V^T transposed reads: bf16 [k-step][row quad]; fp8 [k-step][0]
-        int sc;         // fp8: scale of accumulator row e, group G at sc + sc_const(e) + 4 G
+        int k;          // K rows for the A operand: row n32, half hh
+        int v[2][2];    // V^T transposed reads: [k-step][row quad]
         int lim_off;    // 4 hh: accumulator rows are 8 j + i + 4 hh
     };
     auto offsets = [&]() __attribute__((always_inline)) {
@@ -375,27 +285,16 @@ void attn128_kernel(const KParams p)
         const int vg = ln >> 4, vj = ln & 15;   // 16-lane group g, lane j in it
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-            if constexpr (kFp8) {
-                // lanes 2k, 2k+1 supply row number k of the operand's 8 rows
-                const int k = vj >> 1;
-                const int row = 16 * ks + 8 * (k >> 2) + 4 * (vg >> 1) + (k & 3);
-                f.v[ks][0] = lds_row<C>(row) + 16 * (vg & 1) + 8 * (vj & 1);
-                f.v[ks][1] = 0;
-            } else {
 #pragma unroll
-                for (int qd = 0; qd < 2; ++qd) {
-                    const int row = 16 * ks + 8 * qd + 4 * (vg >> 1) + (vj >> 2);
-                    f.v[ks][qd] = lds_row<C>(row) + 2 * (16 * (vg & 1) + 4 * (vj & 3));
-                }
+            for (int qd = 0; qd < 2; ++qd) {
+                // lane j of a 16-lane group supplies row j / 4 of the 4-row read
+                const int row = 16 * ks + 8 * qd + 4 * (vg >> 1) + (vj >> 2);
+                f.v[ks][qd] = lds_row<C>(row) + 2 * (16 * (vg & 1) + 4 * (vj & 3));
             }
         }
-        // accumulator rows 8 j + i (+ 4 hh) stay inside their 16-row block, so
-        // only the half's offset varies per lane
-        f.sc = 4 * C::kRowStride * h2 + 512;
         f.lim_off = 4 * h2;
         return f;
     };
-    auto sc_const = [](int e) { return lds_row<C>(8 * (e >> 2) + (e & 3)); };
 
     f32x16 o[16];
 #pragma unroll
@@ -428,9 +327,9 @@ void attn128_kernel(const KParams p)
     auto tile = [&](const uint8_t *buf, int n_tile, bool exact, auto mode_c, int *flag) __attribute__((always_inline)) {
         constexpr int kMode = decltype(mode_c)::value;
         const Offs f = offsets();
-        const int off_k = f.k, off_sc = f.sc;
+        const int off_k = f.k;
         f32x16 acc = {};
-        if constexpr (!kFp8) {
+        {
             constexpr int KG = 6;      // k-steps per stage
             bf16x8 cur[KG], nxt[KG];
 #pragma unroll
@@ -450,46 +349,6 @@ void attn128_kernel(const KParams p)
 #pragma unroll
                 for (int j = 0; j < KG; ++j)
                     cur[j] = nxt[j];
-            }
-        } else {
-            // stage i (k-instruction i, 64 columns of group i / 2): its K fragment
-            // was read one stage ahead; the group's 16 row scales are read at the
-            // start of its second stage and applied after that stage's MFMAs
-            auto load_k = [&](int i) __attribute__((always_inline)) -> i32x8 {
-                const uint4 a0 = *(const uint4 *)(buf + off_k + 64 * i);
-                const uint4 a1 = *(const uint4 *)(buf + off_k + 64 * i + 32);
-                return i32x8{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
-            };
-            i32x8 kc = load_k(0), kn;
-            f32x16 part = {};
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int G = i >> 1;
-                if (i < 7)
-                    kn = load_k(i + 1);
-                float scc[16];
-                if (i & 1) {
-#pragma unroll
-                    for (int e = 0; e < 16; ++e)
-                        scc[e] = *(const float *)(buf + off_sc + sc_const(e) + 4 * G);
-                }
-                part = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kc, qh[i], (i & 1) ? part : f32x16{}, 0, 0, 0,
-                                                                       127, 0, qsc[G]);
-                part = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kc, ql[i], part, 0, 0, 0, 123, 0, qsc[G]);
-                if (i & 1) {
-#pragma unroll
-                    for (int e = 0; e < 16; ++e)
-                        acc[e] = fmaf(scc[e], part[e], acc[e]);
-                }
-                __builtin_amdgcn_sched_barrier(0);
-                if (i < 7)
-                    kc = kn;
-            }
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                const bf16x8 a = *(const bf16x8 *)(buf + off_k + RowFmt<kCacheFp8>::kRope + 32 * ks);
-                const bf16x8 b = *(const bf16x8 *)(smem + C::kOffQRope + 4096 * wave + 16 * late(lane) + 1024 * ks);
-                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
             }
         }
 
@@ -525,22 +384,16 @@ void attn128_kernel(const KParams p)
         // ---- O^T += V^T P^T; k-step ks takes accumulator elements 8 ks .. 8 ks + 7.
         //      Stages of four (dim block, k-step) pairs, the next stage's V^T
         //      fragments read while the current MFMAs run.
-        using VFrag = std::conditional_t<kFp8, uint2, uint4>;
-        auto load_v = [&](int db, int ks) __attribute__((always_inline)) -> VFrag {
-            if constexpr (kFp8) {
-                const i32x2 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32(LDS_PTR(i32x2, buf + f.v[ks][0] + 32 * db));
-                return make_uint2((uint32_t)v[0], (uint32_t)v[1]);
-            } else {
-                const uint2 w0 = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    LDS_PTR(i16x4, buf + f.v[ks][0] + 64 * db)));
-                const uint2 w1 = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    LDS_PTR(i16x4, buf + f.v[ks][1] + 64 * db)));
-                return make_uint4(w0.x, w0.y, w1.x, w1.y);
-            }
+        auto load_v = [&](int db, int ks) __attribute__((always_inline)) -> uint4 {
+            const uint2 w0 = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                LDS_PTR(i16x4, buf + f.v[ks][0] + 64 * db)));
+            const uint2 w1 = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                LDS_PTR(i16x4, buf + f.v[ks][1] + 64 * db)));
+            return make_uint4(w0.x, w0.y, w1.x, w1.y);
         };
         // dim blocks db0 .. db0 + 3, both k-steps: 8 MFMAs with the weights p
         auto pv_group = [&](int db0, const bf16x8 (&pp)[2]) __attribute__((always_inline)) {
-            VFrag vc[4], vn[4];
+            uint4 vc[4], vn[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j)
                 vc[j] = load_v(db0 + (j >> 1), j & 1);
@@ -554,12 +407,7 @@ void attn128_kernel(const KParams p)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int db = db0 + 2 * h2 + (j >> 1), ks = j & 1;
-                    bf16x8 a;
-                    if constexpr (kFp8)
-                        a = e4m3x8_to_bf16x8(vc[j]);
-                    else
-                        a = __builtin_bit_cast(bf16x8, vc[j]);
-                    mfma_o(o[db], a, pp[ks]);
+                    mfma_o(o[db], __builtin_bit_cast(bf16x8, vc[j]), pp[ks]);
                 }
                 __builtin_amdgcn_sched_barrier(0);
                 if (h2 == 0) {
@@ -581,32 +429,14 @@ void attn128_kernel(const KParams p)
             }
         };
         bf16x8 pp[2];
-        if constexpr (!kFp8) {
 #pragma unroll
-            for (int pass = 0; pass < 2; ++pass) {
-                if (pass == 1 && !exact)
-                    break;
-                pack(pw, pass == 1, pp);
+        for (int pass = 0; pass < 2; ++pass) {
+            if (pass == 1 && !exact)
+                break;
+            pack(pw, pass == 1, pp);
 #pragma unroll
-                for (int db0 = 0; db0 < 16; db0 += 4)
-                    pv_group(db0, pp);
-            }
-        } else {
-            // output group G (dims 128 G ..): the weights carry the rows' group-G scales
-#pragma unroll
-            for (int G = 0; G < 4; ++G) {
-                float ws[16];
-#pragma unroll
-                for (int e = 0; e < 16; ++e)
-                    ws[e] = pw[e] * *(const float *)(buf + off_sc + sc_const(e) + 4 * G);
-#pragma unroll
-                for (int pass = 0; pass < 2; ++pass) {
-                    if (pass == 1 && !exact)
-                        break;
-                    pack(ws, pass == 1, pp);
-                    pv_group(4 * G, pp);
-                }
-            }
+            for (int db0 = 0; db0 < 16; db0 += 4)
+                pv_group(db0, pp);
         }
     };
 
@@ -717,14 +547,11 @@ void attn128_kernel(const KParams p)
 
 }  // namespace
 
-hipError_t launch_attn128(CacheFormat fmt, const KParams &p, hipStream_t stream)
+hipError_t launch_attn128(const KParams &p, hipStream_t stream)
 {
     const int64_t tq = (p.T + 7) / 8;
     const dim3 grid((unsigned)(tq * 8 * p.S));
-    if (fmt == kCacheFp8)
-        hipLaunchKernelGGL(attn128_kernel<kCacheFp8>, grid, dim3(Cfg128<kCacheFp8>::kThreads), 0, stream, p);
-    else
-        hipLaunchKernelGGL(attn128_kernel<kCacheBf16>, grid, dim3(Cfg128<kCacheBf16>::kThreads), 0, stream, p);
+    hipLaunchKernelGGL(attn128_kernel, grid, dim3(Cfg128::kThreads), 0, stream, p);
     return hipGetLastError();
 }
 

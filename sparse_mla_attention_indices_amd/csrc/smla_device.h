@@ -38,8 +38,9 @@ struct KParams {
     int slot_in;          // topk holds cache slots: no request id, no block-table lookup
 };
 
-// Attention with all 128 heads of a token in one workgroup (smla_attn128.hip).
-hipError_t launch_attn128(CacheFormat fmt, const KParams &p, hipStream_t stream);
+// bf16-cache attention with all 128 heads of a token in one workgroup
+// (smla_attn128.hip).
+hipError_t launch_attn128(const KParams &p, hipStream_t stream);
 
 namespace {
 

@@ -18,8 +18,9 @@ constexpr int kBf16RowBytes = kDqk * 2;
 
 enum CacheFormat { kCacheBf16 = 0, kCacheFp8 = 1 };
 
-// Every workgroup covers all h_q heads of its token: 128 (four waves of 32
-// heads), 64 (eight waves), 32 or 16.
+// A workgroup covers all h_q heads of its token (128: four waves of 32 heads
+// for the bf16 cache; 64: eight waves; 32 or 16), except fp8 with h_q = 128,
+// which takes two 64-head workgroups per token and part.
 constexpr int kHeadsPerGroup = 64;
 
 // Most top-k parts one token's list is cut into.
@@ -32,7 +33,6 @@ constexpr size_t kStaticWorkspaceBytes = (size_t)64 << 20;
 struct Plan {
     int num_splits;          // top-k parts per token
     int split_len;           // top-k positions per part (the last part may be shorter)
-    int head_blocks;         // workgroups per (token, part) along heads
     size_t workspace;        // bytes needed (0 when num_splits == 1)
     size_t part_lse_off;     // byte offsets inside the workspace: [T][S][H] fp32 lse,
     size_t part_o_off;       // [T][S][H][512] fp32 partial outputs (or bf16 rows in them)

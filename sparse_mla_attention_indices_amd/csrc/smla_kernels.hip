@@ -1788,9 +1788,11 @@ hipError_t launch_pc(const KParams &p, hipStream_t stream)
 template <int FMT>
 hipError_t launch_fmt(const KParams &p, hipStream_t stream)
 {
-    const int heads = p.H / p.HB;     // heads per workgroup: 128, 64, 32 or 16
-    if (heads == 128)
-        return launch_attn128((CacheFormat)FMT, p, stream);
+    const int heads = p.H / p.HB;     // heads per workgroup: 128 (bf16), 64, 32 or 16
+    if constexpr (FMT == kCacheBf16) {
+        if (heads == 128)
+            return launch_attn128(p, stream);
+    }
     if constexpr (FMT == kCacheFp8) {
         // fp8 cache, 64 heads per workgroup: QK^T waves and PV waves
         if (heads == 64)
@@ -1932,9 +1934,12 @@ hipError_t launch_attention(CacheFormat fmt, const AttnArgs &a, const Plan &pl, 
     const bool split = pl.num_splits > 1 || partials_only;
     p.part_o = split ? (float *)((char *)a.workspace + pl.part_o_off) : nullptr;
     p.part_lse = split ? (float *)((char *)a.workspace + pl.part_lse_off) : nullptr;
+    // workgroups per (token, part) along heads: two 64-head attn_pc_kernel
+    // workgroups for fp8 with h_q = 128, else one covering every head
+    const int hb = fmt == kCacheFp8 && a.h_q == 128 ? 2 : 1;
     // bf16 split partials: attn_pc_kernel (fp8 cache, 64-head workgroups) in a
     // call that merges its own splits
-    const bool pc = fmt == kCacheFp8 && a.h_q / pl.head_blocks == 64;
+    const bool pc = fmt == kCacheFp8 && a.h_q / hb == 64;
     p.part_exact = split && !partials_only && pc ? (int32_t *)((char *)a.workspace + pl.part_exact_off) : nullptr;
     p.log2e_scale = a.sm_scale * 1.4426950408889634f;
     p.T = a.num_tokens;
@@ -1945,7 +1950,7 @@ hipError_t launch_attention(CacheFormat fmt, const AttnArgs &a, const Plan &pl, 
     p.NB = a.num_blocks;
     p.S = pl.num_splits;
     p.split_len = pl.split_len;
-    p.HB = pl.head_blocks;
+    p.HB = hb;
     p.partials = split ? 1 : 0;
     p.slot_in = a.slot_indices ? 1 : 0;
     if (stage == AttnStage::kMergeOnly && (!split || partials_only))

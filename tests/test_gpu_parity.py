@@ -100,10 +100,11 @@ def test_long_list_crosses_the_lds_chunk(fmt, h_q):
 
 @pytest.mark.parametrize("fmt", ["bf16", "fp8"])
 def test_logits_rising_past_the_first_tile_reference(fmt):
-    """128-head workgroups weight every row against a reference per head taken from
-    the max of the first tile (32 valid rows); when a later tile's max rises more
-    than 64 log2 units above it, the workgroup redoes its list (exact maxima, then
-    the full pass). Here the first 32 valid rows of every token are zero rows
+    """128-head workgroups (bf16 cache) weight every row against a reference per
+    head taken from the max of the first tile (32 valid rows); when a later tile's
+    max rises more than 64 log2 units above it, the workgroup redoes its list
+    (exact maxima, then the full pass). The fp8 cache's 64-head workgroups rescale
+    online instead and are held to the same bound on the same kind of input. Here the first 32 valid rows of every token are zero rows
     (logit 0) and q is scaled by 12 or 24 per head, so the later rows' maxima rise
     past that headroom for some heads of every token, which is checked on the
     oracle first: the lse of the whole list minus ln(rows) exceeds the lse of its
