@@ -324,7 +324,8 @@ void attn128_kernel(const KParams p)
     // next group's fragments while its own MFMAs run, and a scheduling barrier
     // closes every stage, so no more than two groups of fragments are ever
     // live beside q (144 registers) and the 256 accumulators of O.
-    auto tile = [&](const uint8_t *buf, int n_tile, bool exact, auto mode_c, int *flag) __attribute__((always_inline)) {
+    auto tile = [&](const uint8_t *buf, int n_tile, bool exact, auto mode_c, int *flag, auto &&copy)
+                    __attribute__((always_inline)) {
         constexpr int kMode = decltype(mode_c)::value;
         const Offs f = offsets();
         const int off_k = f.k;
@@ -345,6 +346,10 @@ void attn128_kernel(const KParams p)
 #pragma unroll
                 for (int j = 0; j < KG; ++j)
                     acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur[j], qb[g0 + j], acc, 0, 0, 0);
+                // this stage's share of the refill copies, issued while its MFMAs run
+#pragma unroll
+                for (int k = 3 * (g0 / KG); k < 3 * (g0 / KG) + 3; ++k)
+                    copy(k);
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int j = 0; j < KG; ++j)
@@ -462,23 +467,59 @@ void attn128_kernel(const KParams p)
                                   ring + i * C::kBufBytes, wave, lane);
             }
             bool stop = false;
-            for (int r = 0; r < n_tiles; ++r) {
+            // Iteration r: tile r, and (copy_c) the refill of the buffer tile r - 1
+            // freed with tile r + kNBuf - 1, whose 16 copy instructions of this wave
+            // go out between the QK^T stages (tile() calls copy(k)). The
+            // iterations with and without a refill run as two loops, so no branch
+            // on it sits in the run of MFMAs.
+            auto iteration = [&](int r, auto copy_c) __attribute__((always_inline)) -> bool {
+                constexpr bool kCopy = decltype(copy_c)::value;
                 // this wave's rows of tile r have landed ...
                 wait_vmcnt(C::kDmaPerWave * (issued - r - 1));
                 // ... and every wave's; every wave is done with tile r - 1
                 __syncthreads();
-                if (kMode == 0 && restart_flag[(r + 1) & 1] != 0) {
-                    stop = true;
-                    break;
+                if (kMode == 0 && restart_flag[(r + 1) & 1] != 0)
+                    return true;
+                int rf_slot = 0;
+                uint32_t rf_base = 0;
+                if constexpr (kCopy) {
+                    const int ln = late(lane);
+                    const int ri = C::kRowsPerWave * wave + ln % C::kRowsPerWave;
+                    rf_slot = lds_slots[issued * kTile + (ri < min(kTile, n_valid - issued * kTile) ? ri : 0)];
+                    rf_base = __builtin_amdgcn_readfirstlane(
+                        (uint32_t)(uintptr_t)LDS_PTR(uint8_t, ring + (issued % C::kNBuf) * C::kBufBytes) +
+                        (uint32_t)lds_row<C>(C::kRowsPerWave * wave));
                 }
-                if (issued < n_tiles) {
-                    issue_tile<C>(p.cache, lds_slots + issued * kTile, min(kTile, n_valid - issued * kTile),
-                                  ring + (issued % C::kNBuf) * C::kBufBytes, wave, lane);
-                    ++issued;
-                }
+                // copy k: row k / 2 of this wave's rows, chunks 0..63 (k even) or 64..71
+                auto copy = [&](int k) __attribute__((always_inline)) {
+                    if constexpr (kCopy) {
+                        if (k >= C::kDmaPerWave)
+                            return;
+                        const int i = k >> 1, part = k & 1;
+                        const int ln = late(lane);
+                        const int slot = __builtin_amdgcn_readlane(rf_slot, i);
+                        const uint8_t *src = p.cache + (size_t)(uint32_t)slot * C::kRowBytes + 16 * (64 * part + ln);
+                        const uint32_t dst = __builtin_amdgcn_readfirstlane(
+                            rf_base + (uint32_t)(lds_row<C>(C::kRowsPerWave * wave + i) -
+                                                 lds_row<C>(C::kRowsPerWave * wave)) + 1024u * (uint32_t)part);
+                        if (part == 0)
+                            dma16(src, dst);
+                        else
+                            dma16_lanes(src, dst, (1ull << (C::kChunksPerRow - 64)) - 1ull);
+                    }
+                };
                 tile(ring + (r % C::kNBuf) * C::kBufBytes, min(kTile, n_valid - r * kTile), exact_p, mode_c,
-                     restart_flag + (r & 1));
-            }
+                     restart_flag + (r & 1), copy);
+                if constexpr (kCopy)
+                    ++issued;
+                return false;
+            };
+            const int r_copy = max(0, n_tiles - (C::kNBuf - 1));   // iterations with a refill
+            int r = 0;
+            for (; r < r_copy && !stop; ++r)
+                stop = iteration(r, std::true_type{});
+            for (; r < n_tiles && !stop; ++r)
+                stop = iteration(r, std::false_type{});
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // copies of tiles a stop left unread
             __syncthreads();     // ring and slot list are free for the next round
             if (kMode == 0 && (stop || (restart_flag[0] | restart_flag[1]) != 0))

@@ -215,6 +215,20 @@ __device__ __forceinline__ void dma16(const uint8_t *src, uint32_t lds_base)
                  : "memory", "m0");
 }
 
+// dma16 for the lanes set in `lanes` only, without a branch: the mask goes into
+// EXEC for the one copy and the wave's mask is restored after it, so the copy
+// can sit in a straight run of MFMAs (a divergent branch there splits the
+// accumulators' live ranges and makes the compiler spill them).
+__device__ __forceinline__ void dma16_lanes(const uint8_t *src, uint32_t lds_base, uint64_t lanes)
+{
+    uint64_t saved;
+    asm volatile("s_mov_b64 %0, exec\n\ts_mov_b64 exec, %3\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\t"
+                 "global_load_lds_dwordx4 %1, off\n\ts_mov_b64 exec, %0"
+                 : "=&s"(saved)
+                 : "v"(src), "s"(lds_base), "s"(lanes)
+                 : "memory", "m0");
+}
+
 // global_load_lds_dword: 4 bytes per active lane from `src` into LDS at
 // lds_base + 4 * lane (inline assembly for the same reason as dma16).
 __device__ __forceinline__ void dma4(const void *src, uint32_t lds_base)
