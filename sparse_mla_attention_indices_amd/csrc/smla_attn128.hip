@@ -108,6 +108,20 @@ __device__ __forceinline__ void o_zero(f32x16 &o)
     asm volatile("s_nop 3\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %1, 0" : "=a"(o) : "v"(z));
 }
 
+// x and the value of lane l xor 32, through v_permlane32_swap (no LDS round
+// trip): the swap returns (x of lanes 0..31 twice, x of lanes 32..63 twice), so
+// each lane sees its own value in one result and its partner's in the other.
+__device__ __forceinline__ float xor32_max(float x)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_sum(float x)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // How far (log2 units) a head's logits may rise above the reference its first
 // tile set before the weights exp2(s - reference) risk overflow: 2^64 leaves
 // fp32 and bf16 (same exponent range) far from their limit even summed over
@@ -366,7 +380,7 @@ void attn128_kernel(const KParams p)
                 acc[e] = 8 * (e >> 2) + (e & 3) < n_tile - f.lim_off ? acc[e] : -INFINITY;
             lmax = fmaxf(lmax, acc[e]);
         }
-        lmax = fmaxf(lmax, __shfl_xor(lmax, 32)) * c2;
+        lmax = xor32_max(lmax) * c2;
         if constexpr (kMode == 1) {
             m_ref = fmaxf(m_ref, lmax);
             return;
@@ -545,7 +559,7 @@ void attn128_kernel(const KParams p)
 
     // ---- epilogue: the head's row sum (this lane's rows and the other half's)
     o_settle(o);
-    const float l = l_part + __shfl_xor(l_part, 32);
+    const float l = xor32_sum(l_part);
     const float inv_l = l > 0.f ? 1.f / l : 0.f;
     // natural-log lse (v_log_f32 is log2; l >= 1 here: the row that set the max adds >= 1)
     const float lse_v = l > 0.f ? (m_ref + __builtin_amdgcn_logf(l)) * 0.69314718055994531f : -INFINITY;
