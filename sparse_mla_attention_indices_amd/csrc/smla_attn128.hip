@@ -108,20 +108,6 @@ __device__ __forceinline__ void o_zero(f32x16 &o)
     asm volatile("s_nop 3\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %1, 0" : "=a"(o) : "v"(z));
 }
 
-// x and the value of lane l xor 32, through v_permlane32_swap (no LDS round
-// trip): the swap returns (x of lanes 0..31 twice, x of lanes 32..63 twice), so
-// each lane sees its own value in one result and its partner's in the other.
-__device__ __forceinline__ float xor32_max(float x)
-{
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float xor32_sum(float x)
-{
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
 // How far (log2 units) a head's logits may rise above the reference its first
 // tile set before the weights exp2(s - reference) risk overflow: 2^64 leaves
 // fp32 and bf16 (same exponent range) far from their limit even summed over

@@ -229,6 +229,32 @@ __device__ __forceinline__ void dma16_lanes(const uint8_t *src, uint32_t lds_bas
                  : "memory", "m0");
 }
 
+// Cross-lane max and sum with the lane l xor 16 (same 32-lane half) or l xor 32,
+// through v_permlane16_swap / v_permlane32_swap instead of an LDS round trip
+// (ds_bpermute). Each swap with itself returns, for every lane, its own value
+// in one result and its partner's in the other, so a symmetric op of the two
+// results is the op with the partner.
+__device__ __forceinline__ float xor16_max(float x)
+{
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_max(float x)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor16_sum(float x)
+{
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xor32_sum(float x)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // global_load_lds_dword: 4 bytes per active lane from `src` into LDS at
 // lds_base + 4 * lane (inline assembly for the same reason as dma16).
 __device__ __forceinline__ void dma4(const void *src, uint32_t lds_base)

@@ -360,8 +360,7 @@ void attn_kernel(const KParams p)
         bool moved = false;
         float alpha = 1.f;
         if (__ballot(lmax > m_run + kLazyRescale) != 0) {
-            float mx = fmaxf(lmax, __shfl_xor(lmax, 16));
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            const float mx = xor32_max(xor16_max(lmax));
             if (mx > m_run + kLazyRescale) {
                 alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - mx);
                 l_part *= alpha;
@@ -541,8 +540,7 @@ void attn_kernel(const KParams p)
                         amax = fmaxf(amax, fabsf(v[i]));
                     // the MFMA applies one B scale per column (head) to all 128 k of the
                     // group, so the exponent is shared by the head's four lanes
-                    amax = fmaxf(amax, __shfl_xor(amax, 16));
-                    amax = fmaxf(amax, __shfl_xor(amax, 32));
+                    amax = xor32_max(xor16_max(amax));
                     // block exponent: the largest |q| maps into [128, 256), within e4m3's range
                     const int ex = max((int)((__float_as_uint(amax) >> 23) & 0xFF) - 127 - 7, -120);
                     const float down = __uint_as_float((uint32_t)(127 - ex) << 23);     // 2^-ex, exact
@@ -728,8 +726,7 @@ void attn_kernel(const KParams p)
         //      same in both column halves), handed to every wave through LDS
         {
             float l = l_part;
-            l += __shfl_xor(l, 16);
-            l += __shfl_xor(l, 32);
+            l = xor32_sum(xor16_sum(l));
             // natural-log LSE; v_log_f32 is log2 (l >= 1 here: the row that set m_run adds >= 1)
             const float inv_l = l > 0.f ? 1.f / l : 0.f;
             const float lse_v = l > 0.f ? (m_run + __builtin_amdgcn_logf(l)) * 0.69314718055994531f : -INFINITY;
@@ -991,8 +988,7 @@ void attn_pc_kernel(const KParams p)
         bool moved = false;
         float alpha = 1.f;
         if (__ballot(lmax > m_run + kLazyRescale) != 0) {
-            float mx = fmaxf(lmax, __shfl_xor(lmax, 16));
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            const float mx = xor32_max(xor16_max(lmax));
             if (mx > m_run + kLazyRescale) {
                 alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - mx);
                 l_part *= alpha;
@@ -1198,8 +1194,7 @@ void attn_pc_kernel(const KParams p)
                         amax = fmaxf(amax, fabsf(v[i]));
                     // the MFMA applies one B scale per column (head) to all 128 k of
                     // the group, so the exponent is shared by the head's four lanes
-                    amax = fmaxf(amax, __shfl_xor(amax, 16));
-                    amax = fmaxf(amax, __shfl_xor(amax, 32));
+                    amax = xor32_max(xor16_max(amax));
                     // block exponent: the largest |q| maps into [128, 256), within e4m3's range
                     const int ex = max((int)((__float_as_uint(amax) >> 23) & 0xFF) - 127 - 7, -120);
                     const float down = __uint_as_float((uint32_t)(127 - ex) << 23);     // 2^-ex, exact
@@ -1254,8 +1249,7 @@ void attn_pc_kernel(const KParams p)
         }
         // (max, row sum) of each head to the PV waves
         float l = l_part;
-        l += __shfl_xor(l, 16);
-        l += __shfl_xor(l, 32);
+        l = xor32_sum(xor16_sum(l));
         if (g == 0) {
             m_lds[rw * 16 + n16] = m_run;
             l_lds[rw * 16 + n16] = l;
