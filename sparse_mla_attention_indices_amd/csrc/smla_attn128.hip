@@ -311,7 +311,9 @@ void attn128_kernel(const KParams p)
     // Restart flags, one per tile parity: tile r may set flag[r & 1]; the waves
     // read flag[(r - 1) & 1] after the barrier that opens tile r, which every
     // write made during tile r - 1 precedes, and no wave can be writing it
-    // then (a wave in tile r writes the other one), so all four waves decide alike.
+    // then (a wave in tile r writes the other one), so all four waves decide
+    // alike. They act on it after tile r, so the read's latency is hidden; the
+    // restart discards that tile's work with the rest of the pass.
     int *restart_flag = lds_misc + 2;
     if (tid == 0) {
         restart_flag[0] = 0;                   // published by the compaction's barriers
@@ -321,9 +323,10 @@ void attn128_kernel(const KParams p)
     // One tile. kMode 0: reference from the first tile, headroom check; 1: max
     // only (no PV); 2: fixed reference. exact: P as hi + lo bf16 (two PV sweeps).
     // The LDS fragments are software-pipelined by hand: each stage reads the
-    // next group's fragments while its own MFMAs run, and a scheduling barrier
-    // closes every stage, so no more than two groups of fragments are ever
-    // live beside q (144 registers) and the 256 accumulators of O.
+    // next group's fragments while its own MFMAs run. In QK^T a scheduling
+    // barrier closes every stage, so no more than two groups of K fragments are
+    // ever live beside q (144 registers) and the 256 accumulators of O; the PV
+    // stages are left to the compiler's schedule (measured faster).
     auto tile = [&](const uint8_t *buf, int n_tile, bool exact, auto mode_c, int *flag, auto &&copy)
                     __attribute__((always_inline)) {
         constexpr int kMode = decltype(mode_c)::value;
@@ -414,7 +417,6 @@ void attn128_kernel(const KParams p)
                     const int db = db0 + 2 * h2 + (j >> 1), ks = j & 1;
                     mfma_o(o[db], __builtin_bit_cast(bf16x8, vc[j]), pp[ks]);
                 }
-                __builtin_amdgcn_sched_barrier(0);
                 if (h2 == 0) {
 #pragma unroll
                     for (int j = 0; j < 4; ++j)
@@ -478,8 +480,12 @@ void attn128_kernel(const KParams p)
                 wait_vmcnt(C::kDmaPerWave * (issued - r - 1));
                 // ... and every wave's; every wave is done with tile r - 1
                 __syncthreads();
-                if (kMode == 0 && restart_flag[(r + 1) & 1] != 0)
-                    return true;
+                // the restart flag of tile r - 1 is read now and acted on after tile r
+                // (no wait for the read before the tile's work; a restart discards
+                // that work anyway)
+                int flag_seen = 0;
+                if (kMode == 0)
+                    flag_seen = restart_flag[(r + 1) & 1];
                 int rf_slot = 0;
                 uint32_t rf_base = 0;
                 if constexpr (kCopy) {
@@ -512,7 +518,7 @@ void attn128_kernel(const KParams p)
                      restart_flag + (r & 1), copy);
                 if constexpr (kCopy)
                     ++issued;
-                return false;
+                return kMode == 0 && flag_seen != 0;
             };
             const int r_copy = max(0, n_tiles - (C::kNBuf - 1));   // iterations with a refill
             int r = 0;
