@@ -236,19 +236,12 @@ void attn128_kernel(const KParams p)
         }
         __syncthreads();
         const int my_count = lds_misc[16 + (lane & 31)];
-        int n_valid = 0;
+        int base[kPer];
+        const int n_valid = compaction_bases<kPer, C::kWaves>(my_count, wave, base);
 #pragma unroll
-        for (int j = 0; j < kPer; ++j) {
-#pragma unroll
-            for (int w = 0; w < C::kWaves; ++w) {
-                const int cw = __builtin_amdgcn_readlane(my_count, j * C::kWaves + w);
-                if (w == wave && slotv[j] >= 0)
-                    lds_slots[n_valid + __builtin_amdgcn_mbcnt_hi((uint32_t)(masks[j] >> 32),
-                                                                  __builtin_amdgcn_mbcnt_lo((uint32_t)masks[j], 0u))] =
-                        slotv[j];
-                n_valid += cw;
-            }
-        }
+        for (int j = 0; j < kPer; ++j)
+            if (slotv[j] >= 0)
+                lds_slots[base[j] + lanes_below(masks[j])] = slotv[j];
         __syncthreads();
         return n_valid;
     };

@@ -164,6 +164,37 @@ __device__ __forceinline__ bf16x8 pack_p_residual(const f32x4 &p0, const f32x4 &
                                                  pack_bf16(p1[2] - bf16_lo(w.w), p1[3] - bf16_hi(w.w))));
 }
 
+// The compaction of a round of the top-k list (valid slots into LDS in list
+// order): position tid + kThreads j of the round is thread tid's j-th, so the
+// list order is (j, wave, lane). Each wave has counted its valid positions of
+// part j, and count j * kWaves + w sits in lane j * kWaves + w of my_count.
+// Gives in base[j] the list index of this wave's first valid position of part
+// j and returns the round's total: scalar reads of the counts and selects on
+// a uniform wave index, no branch per count.
+template <int kPer, int kWaves>
+__device__ __forceinline__ int compaction_bases(int my_count, int wave, int (&base)[kPer])
+{
+    static_assert(kPer * kWaves <= 32, "the counts fit lanes 0..31");
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    int run = 0;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j)
+        base[j] = 0;
+#pragma unroll
+    for (int k = 0; k < kPer * kWaves; ++k) {
+        if (k % kWaves == wv)
+            base[k / kWaves] = run;
+        run += __builtin_amdgcn_readlane(my_count, k);
+    }
+    return run;
+}
+
+// Lanes below this one whose bit is set in mask.
+__device__ __forceinline__ int lanes_below(uint64_t mask)
+{
+    return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
 // Wait until at most n of this wave's vector-memory instructions are pending
 // (n is wave-uniform; values above 63, the counter's range, wait for all).
 __device__ __forceinline__ void wait_vmcnt(int n)

@@ -629,17 +629,12 @@ void attn_kernel(const KParams p)
             // all counts in one read (lane i holds count i), then taken as scalars:
             // no chain of dependent LDS round trips
             const int my_count = lds_misc[16 + (lane & 31)];
-            int n_valid = 0;
+            int base[kPer];
+            const int n_valid = compaction_bases<kPer, C::kWaves>(my_count, wave, base);
 #pragma unroll
-            for (int j = 0; j < kPer; ++j) {
-#pragma unroll
-                for (int w = 0; w < C::kWaves; ++w) {
-                    const int cw = __builtin_amdgcn_readlane(my_count, j * C::kWaves + w);
-                    if (w == wave && slotv[j] >= 0)
-                        lds_slots[n_valid + __popcll(masks[j] & ((1ull << lane) - 1ull))] = slotv[j];
-                    n_valid += cw;
-                }
-            }
+            for (int j = 0; j < kPer; ++j)
+                if (slotv[j] >= 0)
+                    lds_slots[base[j] + lanes_below(masks[j])] = slotv[j];
             __syncthreads();
             const bool exact_p = n_valid <= kExactPRows;
             const int n_tiles = (n_valid + kTile - 1) / kTile;
@@ -1047,17 +1042,12 @@ void attn_pc_kernel(const KParams p)
         }
         __syncthreads();
         const int my_count = lds_misc[16 + (lane & 31)];
-        int n_valid = 0;
+        int base[kPer];
+        const int n_valid = compaction_bases<kPer, C::kWaves>(my_count, wave, base);
 #pragma unroll
-        for (int j = 0; j < kPer; ++j) {
-#pragma unroll
-            for (int w = 0; w < C::kWaves; ++w) {
-                const int cw = __builtin_amdgcn_readlane(my_count, j * C::kWaves + w);
-                if (w == wave && slotv[j] >= 0)
-                    lds_slots[n_valid + __popcll(masks[j] & ((1ull << lane) - 1ull))] = slotv[j];
-                n_valid += cw;
-            }
-        }
+        for (int j = 0; j < kPer; ++j)
+            if (slotv[j] >= 0)
+                lds_slots[base[j] + lanes_below(masks[j])] = slotv[j];
         __syncthreads();
         return n_valid;
     };
