@@ -543,24 +543,24 @@ void attn_kernel(const KParams p)
                     amax = xor32_max(xor16_max(amax));
                     // block exponent: the largest |q| maps into [128, 256), within e4m3's range
                     const int ex = max((int)((__float_as_uint(amax) >> 23) & 0xFF) - 127 - 7, -120);
-                    const float down = __uint_as_float((uint32_t)(127 - ex) << 23);     // 2^-ex, exact
+                    // the conversions apply the powers of two themselves (fp8 = x / scale
+                    // rounded, f32 = fp8 x scale; both exact): hi in units of 2^ex, and
+                    // what it misses, exactly, in units of 2^(ex - 4)
+                    const float up_hi = __uint_as_float((uint32_t)(127 + ex) << 23);      // 2^ex
+                    const float up_lo = __uint_as_float((uint32_t)(127 + ex - 4) << 23);  // 2^(ex - 4)
                     uint32_t hw[8], lw[8];
 #pragma unroll
                     for (int j = 0; j < 8; ++j) {
-                        float x[4];
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            x[e] = v[4 * j + e] * down;
+                        const float *x = v + 4 * j;
                         s16x2 h = {0, 0};
-                        h = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(h, x[0], x[1], 1.0f, false);
-                        h = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(h, x[2], x[3], 1.0f, true);
+                        h = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(h, x[0], x[1], up_hi, false);
+                        h = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(h, x[2], x[3], up_hi, true);
                         hw[j] = __builtin_bit_cast(uint32_t, h);
-                        // what the hi term misses, exactly, times 16 (its scale is 2^(ex - 4))
-                        const f32x2 b0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(hw[j], 1.0f, false);
-                        const f32x2 b1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(hw[j], 1.0f, true);
+                        const f32x2 b0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(hw[j], up_hi, false);
+                        const f32x2 b1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(hw[j], up_hi, true);
                         s16x2 l = {0, 0};
-                        l = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(l, (x[0] - b0[0]) * 16.f, (x[1] - b0[1]) * 16.f, 1.0f, false);
-                        l = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(l, (x[2] - b1[0]) * 16.f, (x[3] - b1[1]) * 16.f, 1.0f, true);
+                        l = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(l, x[0] - b0[0], x[1] - b0[1], up_lo, false);
+                        l = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(l, x[2] - b1[0], x[3] - b1[1], up_lo, true);
                         lw[j] = __builtin_bit_cast(uint32_t, l);
                     }
                     qh[gi] = i32x8{(int)hw[0], (int)hw[1], (int)hw[2], (int)hw[3], (int)hw[4], (int)hw[5], (int)hw[6], (int)hw[7]};
@@ -1187,24 +1187,24 @@ void attn_pc_kernel(const KParams p)
                     amax = xor32_max(xor16_max(amax));
                     // block exponent: the largest |q| maps into [128, 256), within e4m3's range
                     const int ex = max((int)((__float_as_uint(amax) >> 23) & 0xFF) - 127 - 7, -120);
-                    const float down = __uint_as_float((uint32_t)(127 - ex) << 23);     // 2^-ex, exact
+                    // the conversions apply the powers of two themselves (fp8 = x / scale
+                    // rounded, f32 = fp8 x scale; both exact): hi in units of 2^ex, and
+                    // what it misses, exactly, in units of 2^(ex - 4)
+                    const float up_hi = __uint_as_float((uint32_t)(127 + ex) << 23);      // 2^ex
+                    const float up_lo = __uint_as_float((uint32_t)(127 + ex - 4) << 23);  // 2^(ex - 4)
                     uint32_t hw[8], lw[8];
 #pragma unroll
                     for (int j = 0; j < 8; ++j) {
-                        float x[4];
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            x[e] = v[4 * j + e] * down;
+                        const float *x = v + 4 * j;
                         s16x2 h = {0, 0};
-                        h = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(h, x[0], x[1], 1.0f, false);
-                        h = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(h, x[2], x[3], 1.0f, true);
+                        h = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(h, x[0], x[1], up_hi, false);
+                        h = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(h, x[2], x[3], up_hi, true);
                         hw[j] = __builtin_bit_cast(uint32_t, h);
-                        // what the hi term misses, exactly, times 16 (its scale is 2^(ex - 4))
-                        const f32x2 b0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(hw[j], 1.0f, false);
-                        const f32x2 b1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(hw[j], 1.0f, true);
+                        const f32x2 b0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(hw[j], up_hi, false);
+                        const f32x2 b1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(hw[j], up_hi, true);
                         s16x2 l = {0, 0};
-                        l = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(l, (x[0] - b0[0]) * 16.f, (x[1] - b0[1]) * 16.f, 1.0f, false);
-                        l = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(l, (x[2] - b1[0]) * 16.f, (x[3] - b1[1]) * 16.f, 1.0f, true);
+                        l = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(l, x[0] - b0[0], x[1] - b0[1], up_lo, false);
+                        l = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(l, x[2] - b1[0], x[3] - b1[1], up_lo, true);
                         lw[j] = __builtin_bit_cast(uint32_t, l);
                     }
                     qh[G] = i32x8{(int)hw[0], (int)hw[1], (int)hw[2], (int)hw[3], (int)hw[4], (int)hw[5], (int)hw[6], (int)hw[7]};
