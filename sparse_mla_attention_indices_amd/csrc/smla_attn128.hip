@@ -45,7 +45,6 @@ namespace smla {
 namespace {
 
 typedef float f32x16 __attribute__((__vector_size__(64)));
-typedef uint32_t u32x4 __attribute__((__vector_size__(16)));
 
 // bf16 rows: 1152 bytes, stored at a 1168-byte stride (16 consecutive rows fall
 // on distinct banks for the 16-byte K reads and the transposed V reads); four

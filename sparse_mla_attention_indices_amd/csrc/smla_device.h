@@ -52,6 +52,7 @@ typedef float f32x4 __attribute__((__vector_size__(16)));
 typedef float f32x2 __attribute__((__vector_size__(8)));
 typedef int i32x8 __attribute__((__vector_size__(32)));
 typedef short s16x2 __attribute__((__vector_size__(4)));
+typedef uint32_t u32x4 __attribute__((__vector_size__(16)));
 
 #define LDS_PTR(T, p) ((__attribute__((address_space(3))) T *)(p))
 

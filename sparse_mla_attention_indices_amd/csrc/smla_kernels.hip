@@ -1415,7 +1415,10 @@ void attn_pc_kernel(const KParams p)
                                     : (uint16_t *)p.part_o + (((size_t)t * p.S + s) * 2 * p.H + wg_head0) * kDv;
         for (int u = tid; u < C::kHeads * kDv / 8; u += C::kThreads) {
             const int row = u / (kDv / 8), c8 = u % (kDv / 8);
-            *(uint4 *)(dst + 8 * u) = *(const uint4 *)(stage + row * C::kStageBf16 + 8 * c8);
+            // streamed past the caches: read once by the merge, or not at all
+            // here (the result); the kernel's end then writes back less
+            const uint4 val = *(const uint4 *)(stage + row * C::kStageBf16 + 8 * c8);
+            __builtin_nontemporal_store(u32x4{val.x, val.y, val.z, val.w}, (u32x4 *)(dst + 8 * u));
         }
     } else if (bf16_parts) {
         // a short split: hi rows in the slot's first half, residual rows in its second
