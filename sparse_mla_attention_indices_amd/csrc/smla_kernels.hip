@@ -1290,6 +1290,10 @@ void attn_pc_kernel(const KParams p)
                 issue_tile<C>(p.cache, lds_slots + i * kTile, min(kTile, n_valid - i * kTile),
                               ring + i * C::kBufBytes, rw, lane);
             const bool exact_s = __builtin_amdgcn_readfirstlane(exact_p ? 1 : 0) != 0;
+            uint2 vf_next[8];     // V^T (e4m3) of the tile the next iteration's PV takes
+#pragma unroll
+            for (int db = 0; db < 8; ++db)
+                vf_next[db] = make_uint2(0u, 0u);
             {
                 for (int r = 0; r <= n_tiles; ++r) {
                     // this wave's rows of tile r have landed (eight per first
@@ -1311,17 +1315,13 @@ void attn_pc_kernel(const KParams p)
                     if (r >= 1) {
                         // ---- O^T += V^T P^T of tile r - 1 over this wave's dims
                         const int par = (r - 1) & 1;
-                        const uint8_t *buf = ring + ((r - 1) % nbuf) * C::kBufBytes;
-                        // every LDS read of the tile issued before the first wait: V^T,
-                        // the four head blocks' rescale flags (one 16-byte read) and
-                        // their P^T hi operands
-                        uint2 vf[8];
+                        // the LDS reads after the barrier, issued before the first
+                        // wait: the four head blocks' rescale flags (one 16-byte read)
+                        // and their P^T hi operands (V^T was read before the barrier)
+                        uint2 vf[8];     // read at the end of the last iteration
 #pragma unroll
-                        for (int db = 0; db < 8; ++db) {
-                            const i32x2 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-                                LDS_PTR(i32x2, buf + off_v8 + 16 * db));
-                            vf[db] = make_uint2((uint32_t)v[0], (uint32_t)v[1]);
-                        }
+                        for (int db = 0; db < 8; ++db)
+                            vf[db] = vf_next[db];
                         const int4 fl = *(const int4 *)(resc_flag + par * 4);
                         bf16x8 ph[4];
 #pragma unroll
@@ -1371,6 +1371,18 @@ void attn_pc_kernel(const KParams p)
                         issue_tile<CfgPCRefill>(p.cache, lds_slots + nt * kTile, min(kTile, n_valid - nt * kTile),
                                                 ring + (nt % nbuf) * C::kBufBytes, wave, lane);
                     issued = max(issued, hi);
+                    // V^T of tile r for the next iteration, read while this wave
+                    // would otherwise wait at the barrier (tile r has landed; its
+                    // buffer is refilled only after the next iteration's PV)
+                    if (r < n_tiles) {
+                        const uint8_t *nbufp = ring + (r % nbuf) * C::kBufBytes;
+#pragma unroll
+                        for (int db = 0; db < 8; ++db) {
+                            const i32x2 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                                LDS_PTR(i32x2, nbufp + off_v8 + 16 * db));
+                            vf_next[db] = make_uint2((uint32_t)v[0], (uint32_t)v[1]);
+                        }
+                    }
                 }
             }
             __syncthreads();     // ring, P^T and slot list are free for the next round
