@@ -10,7 +10,10 @@ over query tokens); this module only marshals numpy arrays. Every function
 follows a passage of the vLLM ``flashmla_sparse.py`` page (FLASHMLA_SPARSE
 backend source): the fp8_ds_mla cache-format note, the
 ``triton_convert_req_index_to_global_index`` docstring, and
-``FlashMLASparseImpl.forward`` with its two kernel wrappers.
+``FlashMLASparseImpl.forward`` with its two kernel wrappers. The nvfp4_ds_mla
+rows (352 bytes) follow the vLLM pull-request page "Support nvfp4_ds_mla on
+FLASHINFER_MLA_SPARSE, with native NVFP4 decode" (row size, exact values in
+native decode) with the layout reading stated in ``smla_oracle.c``.
 """
 
 from __future__ import annotations
@@ -27,6 +30,8 @@ _LIB_PATH = os.path.join(_HERE, "libsmla_oracle.so")
 
 BF16_CACHE = 0
 FP8_CACHE = 1
+NVFP4_CACHE = 2
+NVFP4_ROW_BYTES = 352
 
 _lib = None
 
@@ -65,6 +70,12 @@ def _load():
     lib.smla_oracle_decode_fp8_row.argtypes = [vp, vp]
     lib.smla_oracle_decode_bf16_row.restype = None
     lib.smla_oracle_decode_bf16_row.argtypes = [vp, vp]
+    lib.smla_oracle_e2m1.restype = dbl
+    lib.smla_oracle_e2m1.argtypes = [ctypes.c_uint8]
+    lib.smla_oracle_e2m1_encode.restype = ctypes.c_uint8
+    lib.smla_oracle_e2m1_encode.argtypes = [ctypes.c_float]
+    lib.smla_oracle_decode_nvfp4_row.restype = None
+    lib.smla_oracle_decode_nvfp4_row.argtypes = [vp, vp]
     lib.smla_oracle_convert_one.restype = i32
     lib.smla_oracle_e4m3fn_encode.restype = ctypes.c_uint8
     lib.smla_oracle_e4m3fn_encode.argtypes = [ctypes.c_float]
@@ -131,6 +142,26 @@ def decode_bf16_rows(rows: np.ndarray) -> np.ndarray:
     return out
 
 
+def e2m1(code: int) -> float:
+    """Value of one FP4 E2M1 code (low 4 bits)."""
+    return _load().smla_oracle_e2m1(int(code) & 0xF)
+
+
+def e2m1_encode(x: float) -> int:
+    """float32 value -> E2M1 code, nearest with ties to even, saturating at 6."""
+    return int(_load().smla_oracle_e2m1_encode(float(x)))
+
+
+def decode_nvfp4_rows(rows: np.ndarray) -> np.ndarray:
+    """[n, 352] uint8 nvfp4_ds_mla rows -> [n, 576] float64."""
+    rows = _c(rows, np.uint8).reshape(-1, NVFP4_ROW_BYTES)
+    out = np.empty((rows.shape[0], 576), dtype=np.float64)
+    lib = _load()
+    for i in range(rows.shape[0]):
+        lib.smla_oracle_decode_nvfp4_row(rows[i].ctypes.data, out[i].ctypes.data)
+    return out
+
+
 def e4m3fn_encode(x: float) -> int:
     """float32 value -> E4M3FN byte, nearest with ties to even, saturating at 448."""
     return int(_load().smla_oracle_e4m3fn_encode(float(x)))
@@ -140,8 +171,9 @@ def cache_write(cache_format: int, k_c_bits: np.ndarray, k_pe_bits: np.ndarray,
                 slot_mapping: np.ndarray, cache: np.ndarray) -> np.ndarray:
     """Write token rows into `cache` in place (the page's concat_and_cache_mla).
     k_c_bits uint16 [T, 512] and k_pe_bits uint16 [T, 64] are bf16 bit patterns;
-    slot_mapping int64 [T]; cache uint16 [NB, 64, 576] (format 0, bf16) or uint8
-    [NB, 64, 656] (format 1, fp8_ds_mla). Returns cache."""
+    slot_mapping int64 [T]; cache uint16 [NB, 64, 576] (format 0, bf16), uint8
+    [NB, 64, 656] (format 1, fp8_ds_mla) or uint8 [NB, 64, 352] (format 2,
+    nvfp4_ds_mla). Returns cache."""
     T = int(slot_mapping.shape[0])
     k_c = _c(k_c_bits.reshape(T, 512), np.uint16)
     k_pe = _c(k_pe_bits.reshape(T, 64), np.uint16)
@@ -149,8 +181,10 @@ def cache_write(cache_format: int, k_c_bits: np.ndarray, k_pe_bits: np.ndarray,
     assert cache.flags["C_CONTIGUOUS"]
     want = np.uint16 if cache_format == BF16_CACHE else np.uint8
     assert cache.dtype == want
+    row = {BF16_CACHE: 576, FP8_CACHE: 656, NVFP4_CACHE: NVFP4_ROW_BYTES}[cache_format]
+    assert cache.shape[-1] == row and cache.size % (64 * row) == 0
     _load().smla_oracle_cache_write(int(cache_format), _ptr(k_c), _ptr(k_pe), _ptr(sm), T, _ptr(cache),
-                                    int(cache.shape[0]) * 64)
+                                    cache.size // row)
     return cache
 
 
@@ -237,8 +271,9 @@ def attention(cache_format: int, q_bits, cache, block_table, req_id_per_token, t
               sm_scale: float, tokens=None, want_weights: bool = False):
     """Sparse MLA forward on the CPU.
 
-    q_bits: uint16 bf16 patterns [T, H, 576]. cache: uint16 [NB, 64, 576] (bf16) or
-    uint8 [NB, 64, 656] (fp8_ds_mla). tokens: optional subset of query tokens.
+    q_bits: uint16 bf16 patterns [T, H, 576]. cache: uint16 [NB, 64, 576] (bf16),
+    uint8 [NB, 64, 656] (fp8_ds_mla) or uint8 [NB, 64, 352] (nvfp4_ds_mla).
+    tokens: optional subset of query tokens.
     Returns (o [n, H, 512] float64, lse [n, H] float64[, weights [n, H, K]]).
     """
     q = _c(q_bits, np.uint16)
@@ -255,8 +290,13 @@ def attention(cache_format: int, q_bits, cache, block_table, req_id_per_token, t
         if c.shape[-1] != 656:
             raise ValueError("fp8_ds_mla cache rows must be 656 bytes")
         nb = c.size // (64 * 656)
+    elif cache_format == NVFP4_CACHE:
+        c = cache if (cache.dtype == np.uint8 and cache.flags.c_contiguous) else _c(cache, np.uint8)
+        if c.shape[-1] != NVFP4_ROW_BYTES:
+            raise ValueError("nvfp4_ds_mla cache rows must be 352 bytes")
+        nb = c.size // (64 * NVFP4_ROW_BYTES)
     else:
-        raise ValueError("cache_format must be 0 (bf16) or 1 (fp8_ds_mla)")
+        raise ValueError("cache_format must be 0 (bf16), 1 (fp8_ds_mla) or 2 (nvfp4_ds_mla)")
     bt = _c(block_table, np.int32)
     req = _c(req_id_per_token, np.int32).reshape(-1)
     idx = _c(topk_indices, np.int32)

@@ -30,6 +30,13 @@
  *   flashmla_sparse.py page, FlashMLASparseImpl.forward: the concat_and_cache_mla call that writes
  *   a token's latent (k_c_normed) and RoPE (k_pe) into the cache slot given by
  *   slot_mapping, in the cache's dtype ("auto" = bf16 or "fp8_ds_mla").
+ *   vLLM pull-request page "Support nvfp4_ds_mla on FLASHINFER_MLA_SPARSE, with
+ *   native NVFP4 decode" (its description and design notes): an nvfp4_ds_mla
+ *   row takes 352 bytes per token against 576 for the fp8 cache, and native
+ *   decode attends over the exact dequantised values of the rows as stored
+ *   (no staging copy, no re-rounding to e4m3). The OCP Microscaling (MX)
+ *   specification for the value of an FP4 E2M1 code, and the NVFP4 block
+ *   form: E2M1 values with one E4M3 scale per 16 values.
  *   flashmla_sparse.py page, the separate-prefill mode of an fp8 cache:
  *   _convert_req_index_to_global_index_kernel with HAS_PREFILL
  *   (a prefill token's index maps to its request's workspace start plus the
@@ -56,6 +63,20 @@
  *     group), and each byte is the e4m3 value nearest to x / scale (float32
  *     division), ties to the even code, saturating at +-448; a negative slot,
  *     or one past the cache, writes nothing.
+ *   - nvfp4_ds_mla row (the page gives its size only): 352 = 256 + 32 + 64
+ *     bytes, the one split of that size into standard NVFP4 pieces: bytes
+ *     0..255 hold the 512 latent values as E2M1 codes, two per byte, value 2i
+ *     in the low nibble of byte i and 2i + 1 in the high nibble; bytes
+ *     256..287 hold 32 E4M3FN scales, scale b multiplying latent values
+ *     16b .. 16b + 15; bytes 288..351 hold the 64 RoPE values as E4M3FN bytes.
+ *     A latent value is its E2M1 value times its block's scale; there is no
+ *     per-tensor factor (the page's k_scale belongs to its fp8 staging copy,
+ *     which native decode does not make).
+ *   - nvfp4_ds_mla writer: a block's scale is the E4M3 value nearest to
+ *     amax / 6 (float32 division), ties to even, saturating at 448; each latent
+ *     value becomes the E2M1 code nearest to x / scale (float32 division), ties
+ *     to the even code, saturating at +-6; a block whose scale is zero stores
+ *     zero codes; RoPE values become the nearest E4M3 bytes, saturating.
  *   - separate-prefill mode: the upconverted value of a latent element is the
  *     exact product e4m3 x scale rounded once to the nearest bfloat16, ties to
  *     even (the RoPE part is copied); chunks are formed greedily in request
@@ -77,6 +98,7 @@
 #define ORACLE_DQK 576    /* 512 latent (NoPE) + 64 RoPE                     */
 #define ORACLE_DV 512     /* value width = latent part                       */
 #define ORACLE_FP8_ROW 656
+#define ORACLE_NVFP4_ROW 352
 
 /* Threads an OpenMP parallel region of this library will use. */
 int smla_oracle_num_threads(void)
@@ -137,6 +159,37 @@ void smla_oracle_decode_bf16_row(const uint16_t *row, double *out)
         out[i] = smla_oracle_bf16(row[i]);
 }
 
+/* OCP FP4 E2M1 code (low 4 bits) -> value. Sign bit 3, 2 exponent bits (bias
+ * 1), 1 mantissa bit; exponent field 0 is subnormal (m * 2^-1); there is no
+ * infinity and no NaN. */
+double smla_oracle_e2m1(uint8_t code)
+{
+    int sign = (code >> 3) & 1;
+    int e = (code >> 1) & 0x3;
+    int m = code & 0x1;
+    double v;
+    if (e == 0)
+        v = ldexp((double)m, -1);
+    else
+        v = ldexp(1.0 + (double)m / 2.0, e - 1);
+    return sign ? -v : v;
+}
+
+/* One 352-byte nvfp4_ds_mla row -> 576 values (layout in the readings above):
+ * latent value i is E2M1 code i (low nibble of byte i / 2 for even i, high
+ * nibble for odd i) times the E4M3 scale in byte 256 + i / 16; RoPE value r is
+ * the E4M3 byte 288 + r. */
+void smla_oracle_decode_nvfp4_row(const uint8_t *row, double *out)
+{
+    for (int i = 0; i < ORACLE_DV; ++i) {
+        const uint8_t byte = row[i / 2];
+        const uint8_t code = (i % 2 == 0) ? (uint8_t)(byte & 0xF) : (uint8_t)(byte >> 4);
+        out[i] = smla_oracle_e2m1(code) * smla_oracle_e4m3fn(row[256 + i / 16]);
+    }
+    for (int r = 0; r < 64; ++r)
+        out[ORACLE_DV + r] = smla_oracle_e4m3fn(row[288 + r]);
+}
+
 /* ------------------------------------------------------------ cache write */
 
 /* float -> OCP E4M3FN byte: the finite code whose value is nearest to x, ties
@@ -160,11 +213,32 @@ uint8_t smla_oracle_e4m3fn_encode(float x)
     return (uint8_t)(signbit(x) ? (0x80 | best) : best);
 }
 
+/* float -> FP4 E2M1 code: the code whose value is nearest to x, ties to the
+ * code with an even mantissa bit (RNE); magnitudes beyond 6 take 6; NaN gives
+ * 0. Found by scanning the 8 non-negative codes with the decoder above. */
+uint8_t smla_oracle_e2m1_encode(float x)
+{
+    if (isnan(x))
+        return 0;
+    const double a = fabs((double)x);
+    int best = 0;
+    double best_d = INFINITY;
+    for (int c = 0; c <= 7; ++c) {
+        const double d = fabs(smla_oracle_e2m1((uint8_t)c) - a);
+        if (d < best_d || (d == best_d && (c & 1) == 0)) {
+            best = c;
+            best_d = d;
+        }
+    }
+    return (uint8_t)(signbit(x) ? (0x8 | best) : best);
+}
+
 /* Write num_tokens token rows into a paged cache [flashmla_sparse.py page, FlashMLASparseImpl.forward:
  * concat_and_cache_mla; cache format note]. k_c: bfloat16 [T][512] latent,
  * k_pe: bfloat16 [T][64] RoPE, slot_mapping: int64 [T] (flat slot = block * 64
  * + offset). cache_format 0: bf16 rows [slots][576] (latent then RoPE, copied);
- * 1: fp8_ds_mla rows [slots][656] (see the readings above). num_slots bounds the
+ * 1: fp8_ds_mla rows [slots][656]; 2: nvfp4_ds_mla rows [slots][352] (both as
+ * the readings above state). num_slots bounds the
  * cache; slots outside [0, num_slots) are skipped. */
 void smla_oracle_cache_write(int cache_format, const uint16_t *k_c, const uint16_t *k_pe,
                              const int64_t *slot_mapping, int64_t num_tokens, void *cache,
@@ -180,6 +254,31 @@ void smla_oracle_cache_write(int cache_format, const uint16_t *k_c, const uint16
             uint16_t *row = (uint16_t *)cache + slot * ORACLE_DQK;
             memcpy(row, lat, ORACLE_DV * sizeof(uint16_t));
             memcpy(row + ORACLE_DV, rope, (ORACLE_DQK - ORACLE_DV) * sizeof(uint16_t));
+            continue;
+        }
+        if (cache_format == 2) {
+            uint8_t *row = (uint8_t *)cache + slot * ORACLE_NVFP4_ROW;
+            for (int b = 0; b < 32; ++b) {
+                float amax = 0.0f;
+                for (int i = 16 * b; i < 16 * b + 16; ++i) {
+                    const float v = fabsf((float)smla_oracle_bf16(lat[i]));
+                    if (v > amax)
+                        amax = v;
+                }
+                const uint8_t sc = smla_oracle_e4m3fn_encode(amax / 6.0f);
+                const float scale = (float)smla_oracle_e4m3fn(sc);
+                row[256 + b] = sc;
+                for (int i = 16 * b; i < 16 * b + 16; ++i) {
+                    const uint8_t code =
+                        scale > 0.0f ? smla_oracle_e2m1_encode((float)smla_oracle_bf16(lat[i]) / scale) : 0;
+                    if (i % 2 == 0)
+                        row[i / 2] = code;
+                    else
+                        row[i / 2] = (uint8_t)(row[i / 2] | (code << 4));
+                }
+            }
+            for (int r = 0; r < 64; ++r)
+                row[288 + r] = smla_oracle_e4m3fn_encode((float)smla_oracle_bf16(rope[r]));
             continue;
         }
         uint8_t *row = (uint8_t *)cache + slot * ORACLE_FP8_ROW;
@@ -361,7 +460,8 @@ int64_t smla_oracle_plan_prefill_chunks(const int32_t *seq_lens, int64_t num_pre
  *     o[t,h,:] = sum_j p_j * K_j[0:512]
  *
  * cache_format: 0 = bf16 rows [num_blocks, 64, 576] (uint16 bit patterns),
- *               1 = 656-byte fp8_ds_mla rows [num_blocks, 64, 656].
+ *               1 = 656-byte fp8_ds_mla rows [num_blocks, 64, 656],
+ *               2 = 352-byte nvfp4_ds_mla rows [num_blocks, 64, 352].
  * q: bf16 bit patterns [num_tokens, h_q, 576].
  * tokens: which query tokens to compute (NULL = all, in order); output row i
  *         belongs to token tokens[i].
@@ -376,7 +476,7 @@ int smla_oracle_attention(int cache_format, const uint16_t *q, const void *cache
                           const int64_t *tokens, int64_t n, double *out, double *lse,
                           double *weights)
 {
-    if (cache_format != 0 && cache_format != 1)
+    if (cache_format != 0 && cache_format != 1 && cache_format != 2)
         return -1;
     if (tokens == NULL)
         n = num_tokens;
@@ -406,6 +506,9 @@ int smla_oracle_attention(int cache_format, const uint16_t *q, const void *cache
             if (cache_format == 1)
                 smla_oracle_decode_fp8_row((const uint8_t *)cache + (int64_t)slot[j] * ORACLE_FP8_ROW,
                                            rows + j * ORACLE_DQK);
+            else if (cache_format == 2)
+                smla_oracle_decode_nvfp4_row((const uint8_t *)cache + (int64_t)slot[j] * ORACLE_NVFP4_ROW,
+                                             rows + j * ORACLE_DQK);
             else
                 smla_oracle_decode_bf16_row((const uint16_t *)cache + (int64_t)slot[j] * ORACLE_DQK,
                                             rows + j * ORACLE_DQK);

@@ -7,13 +7,18 @@ attention arithmetic and no logical-to-physical index conversion. It is the one
 module that both the GPU path's tests/benchmark and the CPU oracle's tests read.
 
 Values are produced as raw bit patterns (numpy ``uint16`` for bfloat16,
-``uint8`` for fp8_ds_mla rows) so every consumer sees the same bytes. Rounding
-to bfloat16 and encoding to e4m3 use PyTorch's own CPU casts.
+``uint8`` for fp8_ds_mla and nvfp4_ds_mla rows) so every consumer sees the same
+bytes. Rounding to bfloat16 and encoding to e4m3 use PyTorch's own CPU casts;
+nvfp4_ds_mla rows are drawn as random codes (no quantisation step).
 
 Row formats follow the vLLM ``flashmla_sparse.py`` page (FLASHMLA_SPARSE
 backend): bf16 cache rows are 576 values (512 latent + 64 RoPE); fp8_ds_mla rows
 are 656 bytes = 512 e4m3 latent values, four float32 scales (scale i covers
 latent values 128*i..128*i+127), 64 bfloat16 RoPE values. Block size is 64.
+nvfp4_ds_mla rows are 352 bytes (the size on the vLLM pull-request page "Support
+nvfp4_ds_mla on FLASHINFER_MLA_SPARSE, with native NVFP4 decode"), laid out as
+256 bytes of E2M1 latent codes (two per byte, the even position in the low
+nibble), 32 E4M3 scales (one per 16 latent values), 64 E4M3 RoPE bytes.
 
 Five named configurations (the shapes the pages' serving setups run at):
 
@@ -24,6 +29,10 @@ Five named configurations (the shapes the pages' serving setups run at):
                 5% -1 slots, fp8 cache
   5 long mixed  32 decode tokens + 2 prefill requests x 2048 tokens (ctx 131072 and 65536),
                 h_q 128, top-k 2048, fp8 cache
+
+and config 4's batches over an nvfp4_ds_mla cache (config4_nvfp4): the shape the
+pull-request page runs its native NVFP4 decode at (16 heads, top-k 512, 1024 or
+2048).
 """
 
 from __future__ import annotations
@@ -37,6 +46,7 @@ BLOCK = 64
 D_QK = 576
 D_V = 512
 FP8_ROW_BYTES = 656
+NVFP4_ROW_BYTES = 352
 E4M3_MAX = 448.0
 SM_SCALE_576 = 1.0 / math.sqrt(576.0)
 
@@ -47,9 +57,9 @@ _CHUNK_ROWS = 1 << 18
 @dataclass
 class Workload:
     name: str
-    cache_format: str                 # "bf16" or "fp8"
+    cache_format: str                 # "bf16", "fp8" or "nvfp4"
     q: np.ndarray                     # uint16 [T, H, 576] bf16 bits
-    cache: np.ndarray                 # uint16 [NB, 64, 576] or uint8 [NB, 64, 656]
+    cache: np.ndarray                 # uint16 [NB, 64, 576], uint8 [NB, 64, 656] or [NB, 64, 352]
     block_table: np.ndarray           # int32 [R, MB], padding entries 0
     req_id_per_token: np.ndarray      # int32 [T]
     topk_indices: np.ndarray          # int32 [T, K], logical, -1 = invalid
@@ -165,6 +175,29 @@ def random_fp8_cache(seed: int, cfg: int, num_blocks: int) -> np.ndarray:
     return out.reshape(num_blocks, BLOCK, FP8_ROW_BYTES)
 
 
+def random_nvfp4_rows(gen, n: int) -> np.ndarray:
+    """n random nvfp4_ds_mla rows: every latent code uniform over the 16 E2M1
+    codes (two random nibbles per byte), every block scale the e4m3 cast of
+    U(0.5, 2) / 3 (a 16-value block of N(0, 1) samples has amax about 2, and
+    amax / 6 is the usual NVFP4 scale), RoPE bytes the e4m3 cast of N(0, 1)."""
+    import torch
+    rows = np.empty((n, NVFP4_ROW_BYTES), dtype=np.uint8)
+    rows[:, 0:256] = torch.randint(0, 256, (n, 256), generator=gen, dtype=torch.uint8).numpy()
+    scale = (torch.rand((n, 32), generator=gen) * 1.5 + 0.5) / 3.0
+    rows[:, 256:288] = scale.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    rows[:, 288:352] = torch.randn((n, 64), generator=gen).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    return rows
+
+
+def random_nvfp4_cache(seed: int, cfg: int, num_blocks: int) -> np.ndarray:
+    rows = num_blocks * BLOCK
+    out = np.empty((rows, NVFP4_ROW_BYTES), dtype=np.uint8)
+    for c, s in enumerate(range(0, rows, _CHUNK_ROWS)):
+        e = min(rows, s + _CHUNK_ROWS)
+        out[s:e] = random_nvfp4_rows(_tgen(seed, cfg, 8, c), e - s)
+    return out.reshape(num_blocks, BLOCK, NVFP4_ROW_BYTES)
+
+
 def fp8_from_bf16_cache(cache_bf16: np.ndarray, seed: int, cfg: int) -> np.ndarray:
     """fp8_ds_mla packing of an existing bf16 cache (same latent values and RoPE bits)."""
     nb = cache_bf16.shape[0]
@@ -224,6 +257,8 @@ def build(name: str, cfg: int, seed: int, ctx_lens, token_req, token_visible, h_
         cache = random_bf16_cache(seed, cfg, nb)
     elif cache_format == "fp8":
         cache = random_fp8_cache(seed, cfg, nb)
+    elif cache_format == "nvfp4":
+        cache = random_nvfp4_cache(seed, cfg, nb)
     else:
         raise ValueError(cache_format)
     return Workload(name=name, cache_format=cache_format, q=q, cache=cache, block_table=bt,
@@ -264,7 +299,7 @@ def config3(seed: int = 0, tokens_per_req: int = 4096, num_reqs: int = 4) -> Wor
     return build("c3_bf16_prefill", 3, seed, ctx, req, vis, 128, 2048, "bf16")
 
 
-def config4(seed: int = 0, topk: int = 2048) -> Workload:
+def config4(seed: int = 0, topk: int = 2048, cache_format: str = "fp8") -> Workload:
     """Spec decode at h_q 16: 128 requests x 2 tokens, ctx log-U[16k, 64k], 5% -1."""
     if topk not in (512, 1024, 2048):
         raise ValueError("config 4 sweeps top-k over 512, 1024, 2048")
@@ -272,22 +307,32 @@ def config4(seed: int = 0, topk: int = 2048) -> Workload:
     ctx = np.floor(np.exp(u)).astype(np.int64)
     req = np.repeat(np.arange(128), 2)
     vis = np.stack([ctx - 1, ctx], axis=1).reshape(-1)
-    return build(f"c4_spec_decode_k{topk}", 4, seed, ctx, req, vis, 16, topk, "fp8",
+    tag = "" if cache_format == "fp8" else f"_{cache_format}"
+    return build(f"c4_spec_decode{tag}_k{topk}", 4, seed, ctx, req, vis, 16, topk, cache_format,
                  p_invalid=0.05, max_blocks_per_req=1024, index_part=10 + topk)
 
 
-def config4_sweep(seed: int = 0):
+def config4_nvfp4(seed: int = 0, topk: int = 2048) -> Workload:
+    """Config 4's batch (same block table, q and index lists) over an
+    nvfp4_ds_mla cache."""
+    return config4(seed, topk, "nvfp4")
+
+
+def config4_sweep(seed: int = 0, cache_format: str = "fp8"):
     """config4 at top-k 512, 1024 and 2048, generated once: the three workloads
     share one cache array (the cache, q and block table do not depend on top-k;
-    each index list comes from its own sub-seed), so each equals config4(seed, k)."""
-    base = config4(seed, 2048)
+    each index list comes from its own sub-seed), so each equals
+    config4(seed, k, cache_format)."""
+    base = config4(seed, 2048, cache_format)
     out = [base]
     for k in (512, 1024):
         u = _rng(seed, 4, 4).uniform(math.log(16384), math.log(65536), size=128)
         ctx = np.floor(np.exp(u)).astype(np.int64)
         vis = np.stack([ctx - 1, ctx], axis=1).reshape(-1)
         idx = draw_indices(_rng(seed, 4, 10 + k), vis, k, 0.05)
-        out.append(Workload(name=f"c4_spec_decode_k{k}", cache_format="fp8", q=base.q, cache=base.cache,
+        tag = "" if cache_format == "fp8" else f"_{cache_format}"
+        out.append(Workload(name=f"c4_spec_decode{tag}_k{k}", cache_format=cache_format, q=base.q,
+                            cache=base.cache,
                             block_table=base.block_table, req_id_per_token=base.req_id_per_token,
                             topk_indices=idx, sm_scale=base.sm_scale, ctx_lens=base.ctx_lens))
     return sorted(out, key=lambda w: w.topk)

@@ -29,7 +29,8 @@ MUTANTS = {
     "table_width_off_by_one": ("if (blk >= max_blocks_per_req)", "if (blk > max_blocks_per_req)"),
     "in_block_offset": ("return (int32_t)(base * ORACLE_BLOCK + off);", "return (int32_t)(base * ORACLE_BLOCK + off + 1);"),
     "weights_unnormalised": ("double p = exp(s[j] - lse_th);", "double p = exp(s[j] - m);"),
-    "encode_ties_to_odd": ("(d == best_d && (c & 1) == 0)", "(d == best_d && (c & 1) == 1)"),
+    "encode_ties_to_odd": ("smla_oracle_e4m3fn((uint8_t)c) - a);\n        if (d < best_d || (d == best_d && (c & 1) == 0))",
+                           "smla_oracle_e4m3fn((uint8_t)c) - a);\n        if (d < best_d || (d == best_d && (c & 1) == 1))"),
     "encode_drops_sign": ("return (uint8_t)(signbit(x) ? (0x80 | best) : best);", "return (uint8_t)best;"),
     "writer_scale_447": ("amax > 0.0f ? amax / 448.0f : 1.0f", "amax > 0.0f ? amax / 447.0f : 1.0f"),
     "writer_scales_reversed": ("memcpy(row + 512 + 4 * g, &scale, sizeof scale);",
@@ -46,6 +47,23 @@ MUTANTS = {
                               "memcpy(dst + ORACLE_DV, row + 526, 64 * sizeof(uint16_t));"),
     "upconvert_block_of_32": ("int64_t blk = pos / ORACLE_BLOCK;", "int64_t blk = pos / 32;"),
     "chunks_close_early": ("if (r > 0 && used + seq_lens[r] > max_rows) {", "if (r > 0 && used + seq_lens[r] >= max_rows) {"),
+    "e2m1_bias": ("v = ldexp(1.0 + (double)m / 2.0, e - 1);", "v = ldexp(1.0 + (double)m / 2.0, e - 2);"),
+    "e2m1_subnormal": ("v = ldexp((double)m, -1);", "v = ldexp((double)m, -2);"),
+    "nvfp4_nibbles_swapped": ("(i % 2 == 0) ? (uint8_t)(byte & 0xF) : (uint8_t)(byte >> 4)",
+                              "(i % 2 == 1) ? (uint8_t)(byte & 0xF) : (uint8_t)(byte >> 4)"),
+    "nvfp4_scale_per_32": ("smla_oracle_e4m3fn(row[256 + i / 16])", "smla_oracle_e4m3fn(row[256 + i / 32])"),
+    "nvfp4_rope_offset": ("out[ORACLE_DV + r] = smla_oracle_e4m3fn(row[288 + r]);",
+                          "out[ORACLE_DV + r] = smla_oracle_e4m3fn(row[287 + r]);"),
+    "e2m1_encode_ties_to_odd": ("if (d < best_d || (d == best_d && (c & 1) == 0)) {\n            best = c;\n            best_d = d;\n        }\n    }\n    return (uint8_t)(signbit(x) ? (0x8 | best) : best);",
+                                "if (d < best_d || (d == best_d && (c & 1) == 1)) {\n            best = c;\n            best_d = d;\n        }\n    }\n    return (uint8_t)(signbit(x) ? (0x8 | best) : best);"),
+    "e2m1_encode_drops_sign": ("return (uint8_t)(signbit(x) ? (0x8 | best) : best);", "return (uint8_t)best;"),
+    "nvfp4_writer_scale_amax_over_4": ("smla_oracle_e4m3fn_encode(amax / 6.0f)", "smla_oracle_e4m3fn_encode(amax / 4.0f)"),
+    "nvfp4_writer_high_nibble_first": ("row[i / 2] = (uint8_t)(row[i / 2] | (code << 4));",
+                                       "row[i / 2] = (uint8_t)((row[i / 2] << 4) | code);"),
+    "nvfp4_writer_rope_copied_as_zero": ("row[288 + r] = smla_oracle_e4m3fn_encode((float)smla_oracle_bf16(rope[r]));",
+                                         "row[288 + r] = 0;"),
+    "nvfp4_attention_reads_fp8_rows": ("smla_oracle_decode_nvfp4_row((const uint8_t *)cache + (int64_t)slot[j] * ORACLE_NVFP4_ROW,",
+                                       "smla_oracle_decode_nvfp4_row((const uint8_t *)cache + (int64_t)slot[j] * ORACLE_FP8_ROW,"),
     "chunk_starts_not_reset": ("            chunk_ends[n++] = (int32_t)r;\n            used = 0;",
                                "            chunk_ends[n++] = (int32_t)r;"),
 }

@@ -8,6 +8,12 @@
   round-trip bounds through the decoder, and slot handling;
 - index conversion: hand-worked cases, and a paged-cache writer simulation that
   places tokens by appending (never by dividing by the block size);
+- nvfp4_ds_mla rows: every E2M1 code against the OCP MX definition worked by
+  hand, hand-worked E2M1 encodings (ties, saturation, signed zero), encodings of
+  a sweep against the nearest value of that table, a hand-worked row, one
+  marker per byte position (which output each byte feeds), a hand-worked
+  writer row, writer round-trip bounds, and attention over nvfp4 rows equal to
+  attention over bf16 rows holding the same (exactly representable) values;
 - attention: the dense special case against torch's scaled_dot_product_attention
   and logsumexp in float64, closed forms (one slot, q = 0, duplicates, no slot),
   and the invariants (-1 slots add nothing, order does not matter, weights sum to
@@ -648,3 +654,148 @@ def test_separate_prefill_differs_from_the_fused_path_by_bf16_rounding_only():
     assert np.array_equal(o_s[0], o_f[0]) and np.array_equal(l_s[0], l_f[0])     # the decode token
     rel = np.linalg.norm(o_s - o_f) / np.linalg.norm(o_f)
     assert 0 < rel < 4e-3 and np.abs(l_s - l_f).max() < 1e-2
+
+
+# ------------------------------------------------------------- nvfp4_ds_mla
+
+def _e2m1_table():
+    g = _golden("e2m1_spec_values.json")
+    return {code: v for code, v in g["cases"]}
+
+
+def test_e2m1_every_code_matches_the_spec_table():
+    table = _e2m1_table()
+    assert sorted(table) == list(range(16))
+    for code, want in table.items():
+        got = oracle.e2m1(code)
+        assert got == want, (code, got, want)
+        assert math.copysign(1.0, got) == math.copysign(1.0, want), code
+
+
+def test_e2m1_encode_hand_worked_values():
+    g = _golden("e2m1_encode_cases.json")
+    for x, want in g["cases"]:
+        got = oracle.e2m1_encode(x)
+        assert got == want, (x, got, want)
+
+
+def test_e2m1_encode_is_the_nearest_table_value_on_a_sweep():
+    table = _e2m1_table()
+    mags = np.array([table[c] for c in range(8)])
+    rng = np.random.default_rng(11)
+    xs = np.concatenate([rng.uniform(-8, 8, 4000), rng.uniform(-0.6, 0.6, 1000)]).astype(np.float32)
+    for x in xs:
+        code = oracle.e2m1_encode(float(x))
+        d = np.abs(mags - abs(float(x)))
+        best = np.flatnonzero(d == d.min())
+        want = int(best[0]) if len(best) == 1 else int(best[best % 2 == 0][0])
+        assert code & 7 == want, (x, code)
+        assert (code >> 3) == (1 if np.signbit(x) else 0), (x, code)
+
+
+def test_nvfp4_row_hand_worked():
+    g = _golden("nvfp4_row_example.json")
+    row = np.zeros(352, dtype=np.uint8)
+    for off, b in g["bytes"]:
+        row[off] = b
+    got = oracle.decode_nvfp4_rows(row[None])[0]
+    want = np.zeros(576)
+    for i, v in g["expected"]:
+        want[i] = v
+    assert np.array_equal(got, want)
+
+
+def test_nvfp4_each_byte_feeds_the_outputs_the_layout_names():
+    # a base row with every scale 1.0 (0x38) and every code 1 (0.5): then a
+    # change of one byte shows which outputs that byte feeds
+    base = np.zeros(352, dtype=np.uint8)
+    base[0:256] = 0x11
+    base[256:288] = 0x38
+    base[288:352] = 0x38
+    ref = oracle.decode_nvfp4_rows(base[None])[0]
+    assert np.all(ref[:512] == 0.5) and np.all(ref[512:] == 1.0)
+    for off in range(352):
+        for new in ((0x17, 0x71) if off < 256 else (0x40,)):
+            row = base.copy()
+            row[off] = new
+            changed = np.flatnonzero(oracle.decode_nvfp4_rows(row[None])[0] != ref)
+            if off < 256:
+                want = [2 * off] if new == 0x17 else [2 * off + 1]
+            elif off < 288:
+                want = list(range(16 * (off - 256), 16 * (off - 256) + 16))
+            else:
+                want = [512 + off - 288]
+            assert list(changed) == want, (off, hex(new), changed)
+
+
+def test_cache_write_nvfp4_hand_worked_row():
+    g = _golden("nvfp4_write_example.json")
+    lat = np.zeros((1, 512), dtype=np.float32)
+    rope = np.zeros((1, 64), dtype=np.float32)
+    for i, v in g["latent"]:
+        lat[0, i] = v
+    for i, v in g["rope"]:
+        rope[0, i] = v
+    cache = np.full((1, 64, 352), 0xAB, dtype=np.uint8)
+    oracle.cache_write(oracle.NVFP4_CACHE, W.to_bf16_bits(lat), W.to_bf16_bits(rope),
+                       np.array([5], dtype=np.int64), cache)
+    want = np.zeros(352, dtype=np.uint8)
+    for off, b in g["expected_bytes"]:
+        want[off] = b
+    assert np.array_equal(cache[0, 5], want)
+    untouched = np.delete(cache.reshape(64, 352), 5, axis=0)
+    assert np.all(untouched == 0xAB)
+
+
+def test_cache_write_nvfp4_round_trip():
+    gen = W._tgen(3, 77)
+    T = 64
+    lat = torch.randn((T, 512), generator=gen) * torch.exp(torch.randn((T, 1), generator=gen))
+    lat_bits = W.to_bf16_bits(lat)
+    rope_bits = W.normal_bf16(gen, (T, 64))
+    cache = np.zeros((1, 64, 352), dtype=np.uint8)
+    slots = np.arange(T, dtype=np.int64)
+    oracle.cache_write(oracle.NVFP4_CACHE, lat_bits, rope_bits, slots, cache)
+    rows = cache.reshape(64, 352)
+    dec = oracle.decode_nvfp4_rows(rows)
+    x = W.bf16_bits_to_f32(lat_bits).astype(np.float64)
+    table = _e2m1_table()
+    mags = np.array([table[c] for c in range(8)])
+    for t in range(T):
+        for b in range(32):
+            blk = x[t, 16 * b:16 * b + 16]
+            amax = np.float32(np.abs(blk).max())
+            # the scale byte is torch's RNE e4m3 cast of amax / 6 in float32
+            want_sc = torch.tensor([amax / np.float32(6.0)]).to(torch.float8_e4m3fn).view(torch.uint8).item()
+            assert rows[t, 256 + b] == want_sc, (t, b)
+            scale = oracle.e4m3fn(want_sc)
+            if scale == 0:
+                assert np.all(dec[t, 16 * b:16 * b + 16] == 0)
+                continue
+            # each value is a nearest E2M1 multiple of the scale (or saturated)
+            for i in range(16):
+                r = abs(np.float32(blk[i]) / np.float32(scale))
+                err = abs(abs(dec[t, 16 * b + i]) / scale - r)
+                assert err <= np.abs(mags - min(r, 6.0)).min() + max(0.0, r - 6.0) + 1e-12, (t, b, i)
+    # RoPE: torch's e4m3 cast of the bf16 values
+    rope_ref = torch.from_numpy(W.bf16_bits_to_f32(rope_bits)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(rows[:T, 288:352], rope_ref)
+
+
+def test_nvfp4_attention_equals_bf16_attention_over_the_same_values():
+    # e2m1 (2 significant bits) x e4m3 (4) is exact in bf16 (8), so a bf16 cache
+    # can hold the nvfp4 rows' values exactly; the two attentions then agree
+    rng = W._rng(4, 1)
+    bt, nb = W.allocate_block_table(rng, [300, 200])
+    cache = W.random_nvfp4_cache(4, 9, nb)
+    vals = oracle.decode_nvfp4_rows(cache.reshape(-1, 352))
+    as_f32 = vals.astype(np.float32)
+    bits = W.to_bf16_bits(as_f32)
+    assert np.array_equal(W.bf16_bits_to_f32(bits).astype(np.float64), vals), "values not exact in bf16"
+    bf16_cache = bits.reshape(nb, 64, 576)
+    q = W.normal_bf16(W._tgen(4, 2), (5, 16, 576))
+    req = np.array([0, 0, 1, 1, 1], dtype=np.int32)
+    idx = W.draw_indices(W._rng(4, 3), [300, 250, 200, 120, 7], 64, 0.1)
+    o4, l4 = oracle.attention(oracle.NVFP4_CACHE, q, cache, bt, req, idx, W.SM_SCALE_576)
+    o0, l0 = oracle.attention(oracle.BF16_CACHE, q, bf16_cache, bt, req, idx, W.SM_SCALE_576)
+    assert np.array_equal(o4, o0) and np.array_equal(l4, l0)
