@@ -48,11 +48,12 @@
 extern "C" {
 #endif
 
-#define SMLA_ABI_VERSION 6
+#define SMLA_ABI_VERSION 7
 #define SMLA_BLOCK_SIZE 64
 #define SMLA_HEAD_DIM_QK 576
 #define SMLA_HEAD_DIM_V 512
 #define SMLA_FP8_ROW_BYTES 656
+#define SMLA_NVFP4_ROW_BYTES 352
 #define SMLA_MAX_TOPK (1 << 20)
 
 typedef enum smla_status {
@@ -152,6 +153,7 @@ smla_status smla_merge_partials(const void *partials, size_t partials_bytes, int
 /* Cache formats of smla_concat_and_cache_mla. */
 #define SMLA_CACHE_BF16 0         /* bf16 rows [num_blocks, 64, 576] ("auto" on the page) */
 #define SMLA_CACHE_FP8_DS_MLA 1   /* 656-byte fp8_ds_mla rows [num_blocks, 64, 656]     */
+#define SMLA_CACHE_NVFP4_DS_MLA 2 /* 352-byte nvfp4_ds_mla rows [num_blocks, 64, 352]   */
 
 /* Write tokens' latent and RoPE values into their slots of a paged cache
  * [flashmla_sparse.py page, FlashMLASparseImpl.forward: the concat_and_cache_mla
@@ -170,6 +172,12 @@ smla_status smla_merge_partials(const void *partials, size_t partials_bytes, int
  *                 (fp32 division) rounded to the nearest e4m3 value, ties to
  *                 even. (The page passes a k_scale here as well; the per-group
  *                 scales of this format do not use it.)
+ *                 SMLA_CACHE_NVFP4_DS_MLA: row as at smla_decode_nvfp4. Scale b
+ *                 = the e4m3 value nearest to max |latent[16b .. 16b+15]| / 6
+ *                 (fp32 division, ties to even, at most 448); each code = the
+ *                 E2M1 value nearest to latent / scale (fp32 division, ties to
+ *                 even, saturating at 6), all codes 0 when the scale is 0; RoPE
+ *                 = nearest e4m3 bytes, saturating at 448.
  * Only the rows of the given slots are written. num_tokens == 0 is a no-op.
  * Errors: SMLA_ERR_ARG (format), SMLA_ERR_SHAPE, SMLA_ERR_NULL, SMLA_ERR_ALIGN,
  * SMLA_ERR_HIP. */
@@ -316,6 +324,34 @@ smla_status smla_decode_fp8(const void *q, const void *kv_cache, const int32_t *
                             void *out, float *lse, int32_t *phys_indices_out,
                             void *workspace, size_t workspace_bytes,
                             const smla_options *options, hipStream_t stream);
+
+/* Sparse MLA forward over an nvfp4_ds_mla paged cache, decoded natively: the
+ * rows are read as stored and attended over with their exact values, with no
+ * staging copy and no re-rounding [vLLM pull-request page "Support nvfp4_ds_mla
+ * on FLASHINFER_MLA_SPARSE, with native NVFP4 decode", description and design
+ * notes: 352 bytes per token, native decode at 16 heads and top-k 512, 1024,
+ * 2048].
+ *
+ *   kv_cache  uint8 [num_blocks, 64, 352], 16-B aligned. The page gives the
+ *             row size only; the layout is the split of 352 bytes into NVFP4
+ *             pieces: bytes 0..255 hold the 512 latent values as OCP E2M1
+ *             codes, two per byte, value 2i in the low nibble of byte i and
+ *             2i+1 in the high nibble; bytes 256..287 hold 32 OCP E4M3FN
+ *             scales, scale b multiplying latent values 16b .. 16b+15; bytes
+ *             288..351 hold the 64 RoPE values as E4M3FN bytes. A latent value
+ *             is E2M1 x scale (no per-tensor factor: the page's k_scale belongs
+ *             to its fp8 staging copy, which this call never makes).
+ * Every h_q of smla_prefill_bf16 is accepted; each 16 heads of a token are one
+ * workgroup, which gathers the token's rows itself. Every other argument,
+ * the workspace contract and the errors as for smla_prefill_bf16.
+ */
+smla_status smla_decode_nvfp4(const void *q, const void *kv_cache, const int32_t *block_table,
+                              const int32_t *req_id_per_token, const int32_t *topk_indices,
+                              float sm_scale, int32_t num_tokens, int32_t h_q, int32_t topk,
+                              int32_t num_reqs, int32_t max_blocks_per_req, int64_t num_blocks,
+                              void *out, float *lse, int32_t *phys_indices_out,
+                              void *workspace, size_t workspace_bytes,
+                              const smla_options *options, hipStream_t stream);
 
 /* Split workspace of smla_decode_fp8_noalloc: 64 MiB of device memory that the
  * library holds on each device it runs on, until the process ends. */

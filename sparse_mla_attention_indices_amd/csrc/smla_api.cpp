@@ -301,7 +301,8 @@ smla_status smla_concat_and_cache_mla(const void *k_c_normed, const void *k_pe,
                                       const int64_t *slot_mapping, int32_t num_tokens, void *kv_cache,
                                       int64_t num_blocks, int32_t cache_format, hipStream_t stream)
 {
-    if (cache_format != SMLA_CACHE_BF16 && cache_format != SMLA_CACHE_FP8_DS_MLA)
+    if (cache_format != SMLA_CACHE_BF16 && cache_format != SMLA_CACHE_FP8_DS_MLA &&
+        cache_format != SMLA_CACHE_NVFP4_DS_MLA)
         return SMLA_ERR_ARG;
     if (num_tokens < 0 || num_blocks < 1 || num_blocks > INT64_MAX / (smla::kBlock * smla::kBf16RowBytes))
         return SMLA_ERR_SHAPE;
@@ -312,8 +313,10 @@ smla_status smla_concat_and_cache_mla(const void *k_c_normed, const void *k_pe,
     if (!smla::aligned(k_c_normed, 16) || !smla::aligned(k_pe, 16) || !smla::aligned(slot_mapping, 8) ||
         !smla::aligned(kv_cache, 16))
         return SMLA_ERR_ALIGN;
-    return smla::launch_cache_write(cache_format == SMLA_CACHE_FP8_DS_MLA ? smla::kCacheFp8 : smla::kCacheBf16,
-                                    k_c_normed, k_pe, slot_mapping, kv_cache, num_tokens,
+    const smla::CacheFormat fmt = cache_format == SMLA_CACHE_FP8_DS_MLA     ? smla::kCacheFp8
+                                  : cache_format == SMLA_CACHE_NVFP4_DS_MLA ? smla::kCacheNvfp4
+                                                                            : smla::kCacheBf16;
+    return smla::launch_cache_write(fmt, k_c_normed, k_pe, slot_mapping, kv_cache, num_tokens,
                                     num_blocks * smla::kBlock, stream) == hipSuccess
                ? SMLA_OK
                : SMLA_ERR_HIP;
@@ -452,6 +455,20 @@ smla_status smla_decode_fp8(const void *q, const void *kv_cache, const int32_t *
                             hipStream_t stream)
 {
     return smla::attention_entry(smla::kCacheFp8, q, kv_cache, block_table, req_id_per_token,
+                                 topk_indices, sm_scale, num_tokens, h_q, topk, num_reqs,
+                                 max_blocks_per_req, num_blocks, out, lse, phys_indices_out,
+                                 workspace, workspace_bytes, options, stream);
+}
+
+smla_status smla_decode_nvfp4(const void *q, const void *kv_cache, const int32_t *block_table,
+                              const int32_t *req_id_per_token, const int32_t *topk_indices,
+                              float sm_scale, int32_t num_tokens, int32_t h_q, int32_t topk,
+                              int32_t num_reqs, int32_t max_blocks_per_req, int64_t num_blocks,
+                              void *out, float *lse, int32_t *phys_indices_out, void *workspace,
+                              size_t workspace_bytes, const smla_options *options,
+                              hipStream_t stream)
+{
+    return smla::attention_entry(smla::kCacheNvfp4, q, kv_cache, block_table, req_id_per_token,
                                  topk_indices, sm_scale, num_tokens, h_q, topk, num_reqs,
                                  max_blocks_per_req, num_blocks, out, lse, phys_indices_out,
                                  workspace, workspace_bytes, options, stream);

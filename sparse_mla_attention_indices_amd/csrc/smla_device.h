@@ -71,6 +71,11 @@ template <> struct RowFmt<kCacheBf16> {
     static constexpr int kBytes = kBf16RowBytes;  // 512 x bf16 latent | 64 x bf16 RoPE
     static constexpr int kRope = 1024;
 };
+template <> struct RowFmt<kCacheNvfp4> {
+    static constexpr int kBytes = kNvfp4RowBytes; // 256 B E2M1 latent | 32 x E4M3 scale | 64 x E4M3 RoPE
+    static constexpr int kScales = 256;
+    static constexpr int kRope = 288;
+};
 
 // Byte offset of tile row r in a ring buffer.
 template <class C>

@@ -15,12 +15,14 @@ constexpr int kDqk = 576;         // query/key width: 512 latent + 64 RoPE
 constexpr int kDv = 512;          // value width: the latent part of the row
 constexpr int kFp8RowBytes = 656; // 512 e4m3 + 4 fp32 scales + 64 bf16
 constexpr int kBf16RowBytes = kDqk * 2;
+constexpr int kNvfp4RowBytes = 352;  // 512 E2M1 codes + 32 E4M3 block scales + 64 E4M3 RoPE
 
-enum CacheFormat { kCacheBf16 = 0, kCacheFp8 = 1 };
+enum CacheFormat { kCacheBf16 = 0, kCacheFp8 = 1, kCacheNvfp4 = 2 };
 
 // A workgroup covers all h_q heads of its token (128: four waves of 32 heads
 // for the bf16 cache; 64: eight waves; 32 or 16), except fp8 with h_q = 128,
-// which takes two 64-head workgroups per token and part.
+// which takes two 64-head workgroups per token and part, and nvfp4, which
+// takes one 16-head workgroup per head block.
 constexpr int kHeadsPerGroup = 64;
 
 // Most top-k parts one token's list is cut into.

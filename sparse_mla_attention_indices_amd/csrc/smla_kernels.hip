@@ -73,7 +73,10 @@ namespace {
 // over distinct banks: fp8 rows keep their 656-byte stride (16 consecutive rows
 // fall on distinct banks) and rows 16..31 start 16 bytes later than a plain
 // stride would put them (the transposed V reads touch rows r and r + 16
-// together); bf16 rows get a 1168-byte stride (1152 + 16).
+// together); bf16 rows get a 1168-byte stride (1152 + 16). nvfp4 rows keep
+// their 352-byte stride in the ring and are dequantised, one tile at a time,
+// into a bf16 tile laid out as the bf16 cache's (kOffConv), which the MFMA
+// operands are read from.
 template <int FMT, int NHH>
 struct Cfg {
     static constexpr int kWaves = 2 * NHH;
@@ -81,7 +84,7 @@ struct Cfg {
     static constexpr int kHeads = 16 * NHH;                          // heads per workgroup
     static constexpr int kRowBytes = RowFmt<FMT>::kBytes;            // bytes of a row in HBM
     static constexpr int kChunksPerRow = kRowBytes / 16;             // 16-byte pieces per row
-    static constexpr int kRowStride = FMT == kCacheFp8 ? kRowBytes : kRowBytes + 16;   // in LDS
+    static constexpr int kRowStride = FMT == kCacheBf16 ? kRowBytes + 16 : kRowBytes;  // in LDS
     static constexpr int kBlockGap = FMT == kCacheFp8 ? 16 : 0;
     static constexpr int kRowBlockBytes = 16 * kRowStride + kBlockGap;                 // 16 rows
     // Tile copies: one wave instruction moves 64 16-byte pieces of one row, so
@@ -93,6 +96,8 @@ struct Cfg {
     // 64 heads: one workgroup per CU; fewer heads: two workgroups per CU
     // share the LDS (fp8).
     static constexpr int kNBuf = NHH == 4 ? (FMT == kCacheFp8 ? 4 : 2) : 2;
+    // nvfp4: the bf16 tile the ring's rows are dequantised into
+    static constexpr int kConvBytes = FMT == kCacheNvfp4 ? Cfg<kCacheBf16, NHH>::kBufBytes : 0;
     // PV is split by output dims: wave w owns dims [w * kDimsPerWave, ...) of
     // every head of the workgroup, kDimBlocks blocks of 16 dims.
     static constexpr int kDimsPerWave = kDv / kWaves;
@@ -102,7 +107,8 @@ struct Cfg {
     // P^T operands per (scale group, head block): hi and lo terms, 1 KB each
     static constexpr int kPBytes = NHH > 1 ? 2 * 4 * NHH * 1024 : 0;
     static constexpr int kSlotsBytes = kMaxChunk * 4;
-    static constexpr int kOffXchg = kNBuf * kBufBytes;
+    static constexpr int kOffConv = kNBuf * kBufBytes;
+    static constexpr int kOffXchg = kOffConv + kConvBytes;
     static constexpr int kOffP = kOffXchg + kXchgBytes;
     static constexpr int kOffSlots = kOffP + kPBytes;
     static constexpr int kOffMisc = kOffSlots + kSlotsBytes;         // compaction counts
@@ -120,15 +126,56 @@ struct Cfg {
 
 // ------------------------------------------------------------- attention
 
+// One nvfp4_ds_mla tile, as copied into the ring, into a bf16 tile in the bf16
+// cache's layout [pull-request page "Support nvfp4_ds_mla on
+// FLASHINFER_MLA_SPARSE, with native NVFP4 decode": native decode works on the
+// exact values of the rows as stored]. A thread turns 8 latent codes (4 bytes,
+// half of a 16-value block) into 8 bf16 values: each code to fp32, times the
+// block's E4M3 scale in fp32, then to bf16. E2M1 (2 significant bits) times
+// E4M3 (4) is exact in fp32 and in bf16, so no step rounds. (The scaled
+// conversions are not used for the product: they apply only the exponent of
+// their scale operand, a power-of-two block scale.) RoPE bytes go to bf16
+// exactly as well. Rows past the tile's valid count hold copies of its first
+// row and are converted too.
+template <class C, class CT>
+__device__ __forceinline__ void dequant_nvfp4_tile(const uint8_t *raw, uint8_t *dst, int tid)
+{
+    using F = RowFmt<kCacheNvfp4>;
+    for (int u = tid; u < kTile * 64; u += C::kThreads) {
+        const int r = u >> 6, piece = u & 63;
+        const uint8_t *src = raw + lds_row<C>(r);
+        const uint32_t codes = *(const uint32_t *)(src + 4 * piece);
+        const uint32_t sc_byte = src[F::kScales + (piece >> 1)];
+        const float sc = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(sc_byte, 1.0f, false)[0];
+        const f32x2 f0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 0);
+        const f32x2 f1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 1);
+        const f32x2 f2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 2);
+        const f32x2 f3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 3);
+        const uint4 v = make_uint4(pack_bf16(f0[0] * sc, f0[1] * sc), pack_bf16(f1[0] * sc, f1[1] * sc),
+                                   pack_bf16(f2[0] * sc, f2[1] * sc), pack_bf16(f3[0] * sc, f3[1] * sc));
+        *(uint4 *)(dst + lds_row<CT>(r) + 16 * piece) = v;
+    }
+    for (int u = tid; u < kTile * 8; u += C::kThreads) {
+        const int r = u >> 3, piece = u & 7;
+        const uint2 b = *(const uint2 *)(raw + lds_row<C>(r) + F::kRope + 8 * piece);
+        *(bf16x8 *)(dst + lds_row<CT>(r) + RowFmt<kCacheBf16>::kRope + 16 * piece) = e4m3x8_to_bf16x8(b);
+    }
+}
+
 template <int FMT, int NHH>
 __global__ __launch_bounds__(128 * NHH) __attribute__((amdgpu_waves_per_eu(NHH == 1 ? 1 : 2)))
 void attn_kernel(const KParams p)
 {
     using C = Cfg<FMT, NHH>;
+    // the layout the MFMA operands are read in: nvfp4 tiles are dequantised
+    // into a bf16 tile first and then run the bf16 code
+    constexpr int TF = FMT == kCacheNvfp4 ? kCacheBf16 : FMT;
+    using CT = Cfg<TF, NHH>;
     constexpr int RB = kRB;
-    constexpr int RS = C::kRowStride;
-    constexpr int RBB = C::kRowBlockBytes;
+    constexpr int RS = CT::kRowStride;
+    constexpr int RBB = CT::kRowBlockBytes;
     constexpr int kPer = kMaxChunk / C::kThreads;    // top-k positions per thread per round
+    static_assert(FMT != kCacheNvfp4 || NHH == 1, "nvfp4 runs 16-head workgroups");
 
     __shared__ __attribute__((aligned(1024))) uint8_t smem[C::kLdsBytes];
     uint8_t *ring = smem;
@@ -263,7 +310,7 @@ void attn_kernel(const KParams p)
             bf16x8 rf[RB];
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb)
-                rf[rb] = *(const bf16x8 *)(buf + rb * RBB + off_k + RowFmt<FMT>::kRope + 64 * dh + 16 * g);
+                rf[rb] = *(const bf16x8 *)(buf + rb * RBB + off_k + RowFmt<TF>::kRope + 64 * dh + 16 * g);
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
@@ -315,7 +362,7 @@ void attn_kernel(const KParams p)
                 acc[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int k = 0; k < 9; ++k) {
-                const int col = k < 8 ? 2 * (256 * dh + 32 * k + 8 * g) : RowFmt<FMT>::kRope + 64 * dh + 16 * g;
+                const int col = k < 8 ? 2 * (256 * dh + 32 * k + 8 * g) : RowFmt<TF>::kRope + 64 * dh + 16 * g;
 #pragma unroll
                 for (int rb = 0; rb < RB; ++rb) {
                     const bf16x8 a = *(const bf16x8 *)(buf + rb * RBB + off_k + col);
@@ -696,8 +743,15 @@ void attn_kernel(const KParams p)
                              pv_part(vf8_pend, pvp, gi * (DB / 2), (gi + 1) * (DB / 2));
                          });
                 } else {
-                    tile(ring + (it % C::kNBuf) * C::kBufBytes, min(kTile, n_valid - it * kTile), exact_p,
-                         [](int) {});
+                    const uint8_t *tb = ring + (it % C::kNBuf) * C::kBufBytes;
+                    if constexpr (FMT == kCacheNvfp4) {
+                        // the bf16 tile is free: every wave passed the barrier above
+                        // after its last read of the previous tile
+                        dequant_nvfp4_tile<C, CT>(tb, smem + C::kOffConv, tid);
+                        __syncthreads();
+                        tb = smem + C::kOffConv;
+                    }
+                    tile(tb, min(kTile, n_valid - it * kTile), exact_p, [](int) {});
                 }
             }
             if constexpr (kPipe) {
@@ -1568,8 +1622,12 @@ __global__ __launch_bounds__(256) void merge_kernel(const float *__restrict__ pa
 // lane l holds latent values 8l .. 8l + 7, so each 128-value group is one row of
 // 16 lanes; the group's scale is amax / 448 in float32 (1.0 for an all-zero
 // group) and each byte is x / scale (float32 division) rounded to the nearest
-// e4m3 value, ties to even. bf16: the row is copied. Slots outside
-// [0, num_slots) write nothing. Four tokens per 256-thread block.
+// e4m3 value, ties to even. nvfp4_ds_mla: lane l holds latent values 8l ..
+// 8l + 7, so each 16-value block is a lane pair; the block's scale is the e4m3
+// value nearest to amax / 6 and each code the E2M1 value nearest to x / scale
+// (both float32 divisions, ties to even, saturating); RoPE values are rounded
+// to e4m3. bf16: the row is copied. Slots outside [0, num_slots) write
+// nothing. Four tokens per 256-thread block.
 template <int FMT>
 __global__ __launch_bounds__(256) void cache_write_kernel(const uint16_t *__restrict__ k_c,
                                                           const uint16_t *__restrict__ k_pe,
@@ -1593,6 +1651,60 @@ __global__ __launch_bounds__(256) void cache_write_kernel(const uint16_t *__rest
         ((uint4 *)row)[lane] = lat;
         if (lane < 8)
             ((uint4 *)(row + 2 * kDv))[lane] = rope;
+    } else if constexpr (FMT == kCacheNvfp4) {
+        // lane l: latent 8l .. 8l + 7, half of 16-value block l / 2
+        uint8_t *row = cache + slot * kNvfp4RowBytes;
+        const uint32_t w[4] = {lat.x, lat.y, lat.z, lat.w};
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            v[2 * e] = bf16_lo(w[e]);
+            v[2 * e + 1] = bf16_hi(w[e]);
+        }
+        float amax = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            amax = fmaxf(amax, fabsf(v[i]));
+        amax = fmaxf(amax, __shfl_xor(amax, 1));
+        // the block scale: the e4m3 value nearest to amax / 6 (ties to even,
+        // at most 448); a scale that rounds to zero stores zero codes
+        const float want = fminf(amax / 6.f, 448.f);
+        const uint32_t sc_code =
+            __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(s16x2{0, 0}, want, want, 1.0f, false)) &
+            0xFFu;
+        const float scale = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(sc_code, 1.0f, false)[0];
+        uint32_t codes = 0;
+        if (scale > 0.f) {
+            // each code: the E2M1 value nearest to x / scale (ties to even), at most 6
+            float x[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                x[i] = fminf(fmaxf(v[i] / scale, -6.f), 6.f);
+            codes = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(codes, x[0], x[1], 1.0f, 0);
+            codes = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(codes, x[2], x[3], 1.0f, 1);
+            codes = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(codes, x[4], x[5], 1.0f, 2);
+            codes = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(codes, x[6], x[7], 1.0f, 3);
+        }
+        ((uint32_t *)row)[lane] = codes;
+        if ((lane & 1) == 0)
+            row[RowFmt<kCacheNvfp4>::kScales + (lane >> 1)] = (uint8_t)sc_code;
+        if (lane < 8) {
+            // RoPE: the nearest e4m3 bytes, saturating at 448
+            const uint32_t rw[4] = {rope.x, rope.y, rope.z, rope.w};
+            uint32_t rc[2];
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const float a0 = fminf(fmaxf(bf16_lo(rw[2 * j]), -448.f), 448.f);
+                const float a1 = fminf(fmaxf(bf16_hi(rw[2 * j]), -448.f), 448.f);
+                const float a2 = fminf(fmaxf(bf16_lo(rw[2 * j + 1]), -448.f), 448.f);
+                const float a3 = fminf(fmaxf(bf16_hi(rw[2 * j + 1]), -448.f), 448.f);
+                s16x2 c = {0, 0};
+                c = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(c, a0, a1, 1.0f, false);
+                c = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(c, a2, a3, 1.0f, true);
+                rc[j] = __builtin_bit_cast(uint32_t, c);
+            }
+            ((uint2 *)(row + RowFmt<kCacheNvfp4>::kRope))[lane] = make_uint2(rc[0], rc[1]);
+        }
     } else {
         uint8_t *row = cache + slot * kFp8RowBytes;
         const uint32_t w[4] = {lat.x, lat.y, lat.z, lat.w};
@@ -1787,24 +1899,28 @@ hipError_t launch_pc(const KParams &p, hipStream_t stream)
 template <int FMT>
 hipError_t launch_fmt(const KParams &p, hipStream_t stream)
 {
-    const int heads = p.H / p.HB;     // heads per workgroup: 128 (bf16), 64, 32 or 16
-    if constexpr (FMT == kCacheBf16) {
-        if (heads == 128)
-            return launch_attn128(p, stream);
-    }
-    if constexpr (FMT == kCacheFp8) {
-        // fp8 cache, 64 heads per workgroup: QK^T waves and PV waves
+    if constexpr (FMT == kCacheNvfp4) {
+        return launch_one<FMT, 1>(p, stream);     // 16 heads: one workgroup per head block
+    } else {
+        const int heads = p.H / p.HB;     // heads per workgroup: 128 (bf16), 64, 32 or 16
+        if constexpr (FMT == kCacheBf16) {
+            if (heads == 128)
+                return launch_attn128(p, stream);
+        }
+        if constexpr (FMT == kCacheFp8) {
+            // fp8 cache, 64 heads per workgroup: QK^T waves and PV waves
+            if (heads == 64)
+                return launch_pc(p, stream);
+            if (heads == 32)
+                return launch_one<FMT, 2>(p, stream);
+            return launch_one<FMT, 1>(p, stream);
+        }
         if (heads == 64)
-            return launch_pc(p, stream);
+            return launch_one<FMT, 4>(p, stream);
         if (heads == 32)
             return launch_one<FMT, 2>(p, stream);
         return launch_one<FMT, 1>(p, stream);
     }
-    if (heads == 64)
-        return launch_one<FMT, 4>(p, stream);
-    if (heads == 32)
-        return launch_one<FMT, 2>(p, stream);
-    return launch_one<FMT, 1>(p, stream);
 }
 
 }  // namespace
@@ -1880,7 +1996,10 @@ hipError_t launch_cache_write(CacheFormat fmt, const void *k_c, const void *k_pe
                              void *cache, int64_t num_tokens, int64_t num_slots, hipStream_t stream)
 {
     const dim3 grid((unsigned)((num_tokens + 3) / 4));
-    if (fmt == kCacheFp8)
+    if (fmt == kCacheNvfp4)
+        hipLaunchKernelGGL(cache_write_kernel<kCacheNvfp4>, grid, dim3(256), 0, stream, (const uint16_t *)k_c,
+                           (const uint16_t *)k_pe, slot_mapping, (uint8_t *)cache, num_tokens, num_slots);
+    else if (fmt == kCacheFp8)
         hipLaunchKernelGGL(cache_write_kernel<kCacheFp8>, grid, dim3(256), 0, stream, (const uint16_t *)k_c,
                            (const uint16_t *)k_pe, slot_mapping, (uint8_t *)cache, num_tokens, num_slots);
     else
@@ -1934,8 +2053,9 @@ hipError_t launch_attention(CacheFormat fmt, const AttnArgs &a, const Plan &pl, 
     p.part_o = split ? (float *)((char *)a.workspace + pl.part_o_off) : nullptr;
     p.part_lse = split ? (float *)((char *)a.workspace + pl.part_lse_off) : nullptr;
     // workgroups per (token, part) along heads: two 64-head attn_pc_kernel
-    // workgroups for fp8 with h_q = 128, else one covering every head
-    const int hb = fmt == kCacheFp8 && a.h_q == 128 ? 2 : 1;
+    // workgroups for fp8 with h_q = 128, one 16-head workgroup per head block
+    // for nvfp4, else one covering every head
+    const int hb = fmt == kCacheNvfp4 ? a.h_q / 16 : fmt == kCacheFp8 && a.h_q == 128 ? 2 : 1;
     // bf16 split partials: attn_pc_kernel (fp8 cache, 64-head workgroups) in a
     // call that merges its own splits
     const bool pc = fmt == kCacheFp8 && a.h_q / hb == 64;
@@ -1955,8 +2075,9 @@ hipError_t launch_attention(CacheFormat fmt, const AttnArgs &a, const Plan &pl, 
     if (stage == AttnStage::kMergeOnly && (!split || partials_only))
         return hipSuccess;
     if (stage != AttnStage::kMergeOnly) {
-        const hipError_t err =
-            fmt == kCacheFp8 ? launch_fmt<kCacheFp8>(p, stream) : launch_fmt<kCacheBf16>(p, stream);
+        const hipError_t err = fmt == kCacheFp8     ? launch_fmt<kCacheFp8>(p, stream)
+                               : fmt == kCacheNvfp4 ? launch_fmt<kCacheNvfp4>(p, stream)
+                                                    : launch_fmt<kCacheBf16>(p, stream);
         if (err != hipSuccess || !split || partials_only || stage == AttnStage::kAttentionOnly)
             return err;
     }

@@ -29,9 +29,11 @@ STATUS_NAMES = {0: "SMLA_OK", 1: "SMLA_ERR_NULL", 2: "SMLA_ERR_SHAPE", 3: "SMLA_
 EXPORTS = ("smla_status_string", "smla_abi_version", "smla_plan", "smla_workspace_size",
            "smla_merge_partials", "smla_concat_and_cache_mla", "smla_convert_indices",
            "smla_prefill_workspace_rows", "smla_plan_prefill_chunks", "smla_convert_indices_workspace",
-           "smla_gather_upconvert_fp8", "smla_prefill_bf16", "smla_decode_fp8", "smla_decode_fp8_noalloc")
+           "smla_gather_upconvert_fp8", "smla_prefill_bf16", "smla_decode_fp8", "smla_decode_nvfp4",
+           "smla_decode_fp8_noalloc")
 STATIC_WORKSPACE_BYTES = 64 << 20
-CACHE_FORMATS = {"auto": 0, "bf16": 0, "fp8_ds_mla": 1}
+CACHE_FORMATS = {"auto": 0, "bf16": 0, "fp8_ds_mla": 1, "nvfp4_ds_mla": 2}
+NVFP4_ROW_BYTES = 352
 FLAG_PARTIALS_ONLY = 0x1
 FLAG_SLOT_INDICES = 0x2
 FLAG_DEFER_MERGE = 0x4
@@ -86,7 +88,7 @@ def library() -> ctypes.CDLL:
     lib.smla_gather_upconvert_fp8.restype = ctypes.c_int
     lib.smla_gather_upconvert_fp8.argtypes = [vp, i64, vp, i32, vp, vp, i32, i32, vp, i64, vp]
     attn = [vp, vp, vp, vp, vp, fl, i32, i32, i32, i32, i32, i64, vp, vp, vp, vp, sz, vp, vp]
-    for name in ("smla_prefill_bf16", "smla_decode_fp8"):
+    for name in ("smla_prefill_bf16", "smla_decode_fp8", "smla_decode_nvfp4"):
         getattr(lib, name).restype = ctypes.c_int
         getattr(lib, name).argtypes = attn
     lib.smla_decode_fp8_noalloc.restype = ctypes.c_int
@@ -194,10 +196,13 @@ def smla_concat_and_cache_mla(k_c_normed, k_pe, kv_cache, slot_mapping, kv_cache
                               stream=None):
     """Write each token's latent ([T, 512] bf16) and RoPE ([T, 64] bf16) into its
     slot (int64 [T], block * 64 + offset; negative = skip) of kv_cache: uint8
-    [NB, 64, 656] for "fp8_ds_mla", bf16 [NB, 64, 576] for "auto". Returns kv_cache."""
+    [NB, 64, 656] for "fp8_ds_mla", uint8 [NB, 64, 352] for "nvfp4_ds_mla",
+    bf16 [NB, 64, 576] for "auto". Returns kv_cache."""
     fmt = CACHE_FORMATS[kv_cache_dtype]
     if fmt == 1 and (kv_cache.dtype != torch.uint8 or kv_cache.shape[1:] != (64, 656)):
         raise ValueError("an fp8_ds_mla cache is uint8 [num_blocks, 64, 656]")
+    if fmt == 2 and (kv_cache.dtype != torch.uint8 or kv_cache.shape[1:] != (64, NVFP4_ROW_BYTES)):
+        raise ValueError("an nvfp4_ds_mla cache is uint8 [num_blocks, 64, 352]")
     if fmt == 0 and (kv_cache.dtype != torch.bfloat16 or kv_cache.shape[1:] != (64, 576)):
         raise ValueError("a bf16 cache is bfloat16 [num_blocks, 64, 576]")
     T = slot_mapping.shape[0]
@@ -297,6 +302,20 @@ def smla_decode_fp8(q, kv_cache, block_table, req_id_per_token, topk_indices, sm
     if kv_cache.dtype != torch.uint8 or kv_cache.shape[1:] != (64, 656):
         raise ValueError("kv_cache must be uint8 [num_blocks, 64, 656]")
     return _attention("smla_decode_fp8", q, kv_cache, block_table, req_id_per_token, topk_indices,
+                      sm_scale, out, lse, phys_indices_out, workspace, num_splits, stream, want_lse,
+                      partials_only, slot_indices, stage)
+
+
+def smla_decode_nvfp4(q, kv_cache, block_table, req_id_per_token, topk_indices, sm_scale,
+                      out=None, lse=None, phys_indices_out=None, workspace=None, num_splits=0,
+                      stream=None, want_lse=True, partials_only=False, slot_indices=False, stage=None):
+    """Sparse MLA forward over an nvfp4_ds_mla cache uint8 [num_blocks, 64, 352],
+    decoded natively (exact values, no staging copy). Returns (out, lse).
+
+    Other arguments as for smla_prefill_bf16."""
+    if kv_cache.dtype != torch.uint8 or kv_cache.shape[1:] != (64, NVFP4_ROW_BYTES):
+        raise ValueError("kv_cache must be uint8 [num_blocks, 64, 352]")
+    return _attention("smla_decode_nvfp4", q, kv_cache, block_table, req_id_per_token, topk_indices,
                       sm_scale, out, lse, phys_indices_out, workspace, num_splits, stream, want_lse,
                       partials_only, slot_indices, stage)
 

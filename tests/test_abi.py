@@ -40,7 +40,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_abi_version(lib):
-    assert smla.smla_abi_version() == 6
+    assert smla.smla_abi_version() == 7
 
 
 def test_status_strings(lib):
@@ -136,7 +136,7 @@ def _attn(lib, name="smla_decode_fp8", q=A16, kv=A16, bt=A16, req=A16, idx=A16, 
                               ws, wsb, opts, None)
 
 
-@pytest.mark.parametrize("name", ["smla_decode_fp8", "smla_prefill_bf16"])
+@pytest.mark.parametrize("name", ["smla_decode_fp8", "smla_decode_nvfp4", "smla_prefill_bf16"])
 @pytest.mark.parametrize("kw,code", [
     (dict(q=None), 1), (dict(kv=None), 1), (dict(bt=None), 1), (dict(req=None), 1),
     (dict(idx=None), 1), (dict(out=None), 1),
@@ -151,7 +151,7 @@ def test_attention_rejects_before_any_hip_call(lib, name, kw, code):
     assert _attn(lib, name, **kw) == code
 
 
-@pytest.mark.parametrize("name", ["smla_decode_fp8", "smla_prefill_bf16"])
+@pytest.mark.parametrize("name", ["smla_decode_fp8", "smla_decode_nvfp4", "smla_prefill_bf16"])
 def test_attention_rejects_bad_options(lib, name):
     o = smla.SmlaOptions()
     o.reserved[0] = 5
@@ -164,7 +164,7 @@ def test_attention_rejects_bad_options(lib, name):
     assert _attn(lib, name, opts=ctypes.byref(o)) == 6
 
 
-@pytest.mark.parametrize("name", ["smla_decode_fp8", "smla_prefill_bf16"])
+@pytest.mark.parametrize("name", ["smla_decode_fp8", "smla_decode_nvfp4", "smla_prefill_bf16"])
 def test_zero_tokens_is_a_noop(lib, name):
     # no pointer is needed and nothing is launched
     assert _attn(lib, name, q=None, kv=None, bt=None, req=None, idx=None, out=None, T=0) == 0
@@ -264,7 +264,7 @@ def _cw(lib, kc=A16, kpe=A16B, sm=A256, T=4, kv=A16, NB=8, fmt=1):
     (dict(kc=None), 1), (dict(kpe=None), 1), (dict(sm=None), 1), (dict(kv=None), 1),
     (dict(T=-1), 2), (dict(NB=0), 2),
     (dict(kc=MIS), 3), (dict(kpe=A16 + 8), 3), (dict(sm=A256 + 4), 3), (dict(kv=A16 + 4), 3),
-    (dict(fmt=2), 6), (dict(fmt=-1), 6),
+    (dict(fmt=3), 6), (dict(fmt=-1), 6),
 ])
 def test_cache_write_rejects_before_any_hip_call(lib, kw, code):
     assert _cw(lib, **kw) == code
@@ -276,7 +276,7 @@ def test_cache_write_zero_tokens_is_a_noop(lib):
 
 # ------------------------------------------------------- separate-prefill mode
 
-@pytest.mark.parametrize("name", ["smla_decode_fp8", "smla_prefill_bf16"])
+@pytest.mark.parametrize("name", ["smla_decode_fp8", "smla_decode_nvfp4", "smla_prefill_bf16"])
 def test_slot_indices_need_no_table_or_request_ids(lib, name):
     o = smla.SmlaOptions()
     o.flags = smla.FLAG_SLOT_INDICES

@@ -84,6 +84,65 @@ def test_cache_write_bit_exact(fmt, T):
         raise AssertionError(f"{len(bad)} bytes differ, first at (slot, byte) {bad[:5].tolist()}")
 
 
+def tricky_nvfp4_rows(rng, T):
+    """Latent rows for the nvfp4 writer. Each 16-value block is one kind: E2M1
+    rounding ties under a scale of exactly 1.0 (the block holds 6.0), tiny values
+    whose scale rounds to zero, signed zeros, large values whose amax / 6 passes
+    448, scales on e4m3 rounding ties, or plain normal values."""
+    e2m1 = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+    ties = (e2m1[:-1] + e2m1[1:]) / 2                     # 0.25 .. 5.0, all bf16 values
+    e4m3 = np.array([oracle.e4m3fn(c) for c in range(0x7F)])
+    sc_ties = (e4m3[:-1] + e4m3[1:]) / 2
+    lat = rng.normal(0, 1, (T, 512)).astype(np.float32)
+    for t in range(T):
+        for b in range(32):
+            blk = lat[t, 16 * b:16 * b + 16]
+            kind = (t + b) % 6
+            if kind == 0:
+                blk[:15] = ties[rng.integers(0, len(ties), 15)] * rng.choice([-1, 1], 15)
+                blk[15] = 6.0
+            elif kind == 1:
+                blk[:] *= 1e-5
+            elif kind == 2:
+                blk[:] = 0.0
+                blk[::2] = -0.0
+            elif kind == 3:
+                blk[:] *= 1e4
+            elif kind == 4:
+                # amax / 6 exactly halfway between two e4m3 values (bf16-exact ones)
+                m = sc_ties[rng.integers(40, 100)]
+                blk[:] = rng.uniform(-1, 1, 16) * m * 6
+                blk[0] = m * 6
+    return lat
+
+
+@pytest.mark.parametrize("T", [300, 303, 1])
+def test_cache_write_nvfp4_bit_exact(T):
+    rng = np.random.default_rng(21)
+    NB = 16
+    lat_b = bits_of(tricky_nvfp4_rows(rng, T))
+    rope = rng.normal(0, 2, (T, 64))
+    rope[:, :4] = [600.0, -1000.0, 1e-6, -0.0]             # saturation, a tiny value, a signed zero
+    rope_b = bits_of(rope)
+    slots = rng.permutation(NB * 64)[:T].astype(np.int64)
+    slots[::17] = -1
+    slots[5:6] = NB * 64
+    init = rng.integers(0, 256, (NB, 64, 352), dtype=np.uint8)
+    want = oracle.cache_write(oracle.NVFP4_CACHE, lat_b, rope_b, slots, init.copy())
+    dev_cache = torch.from_numpy(init.copy()).cuda()
+    log(f"[case] cache write nvfp4_ds_mla T={T}")
+    smla.smla_concat_and_cache_mla(torch.from_numpy(lat_b.view(np.int16)).cuda().view(torch.bfloat16),
+                                   torch.from_numpy(rope_b.view(np.int16)).cuda().view(torch.bfloat16),
+                                   dev_cache, torch.from_numpy(slots).cuda(), kv_cache_dtype="nvfp4_ds_mla")
+    torch.cuda.synchronize()
+    got = dev_cache.cpu().numpy()
+    if not np.array_equal(got, want):
+        bad = np.argwhere(got.reshape(NB * 64, -1) != want.reshape(NB * 64, -1))
+        s, b = bad[0]
+        raise AssertionError(f"{len(bad)} bytes differ, first at (slot, byte) {bad[:5].tolist()}: "
+                             f"got {got.reshape(NB * 64, -1)[s, b]:#x} want {want.reshape(NB * 64, -1)[s, b]:#x}")
+
+
 def test_cache_write_prefill_batch_sampled():
     """16384 tokens (a prefill batch) into a 2 GiB-class pool, checked on 512 sampled rows."""
     rng = np.random.default_rng(12)
@@ -106,24 +165,26 @@ def test_cache_write_prefill_batch_sampled():
     assert np.array_equal(got, want.reshape(-1, 656)[:512])
 
 
-def test_attention_over_a_written_cache():
-    """Rows written by smla_concat_and_cache_mla feed smla_decode_fp8; the result
-    matches the oracle's attention over the oracle's bytes (identical by the test
-    above, compared again here)."""
+@pytest.mark.parametrize("fmt", ["fp8", "nvfp4"])
+def test_attention_over_a_written_cache(fmt):
+    """Rows written by smla_concat_and_cache_mla feed smla_decode_fp8 (or
+    smla_decode_nvfp4); the result matches the oracle's attention over the
+    oracle's bytes (identical by the tests above, compared again here)."""
     from tests.test_gpu_parity import small
-    w = small(61, "fp8", 16, 256, n_req=2, tok_per_req=4, ctx=(300, 600), p_invalid=0.1)
+    w = small(61, fmt, 16, 256, n_req=2, tok_per_req=4, ctx=(300, 600), p_invalid=0.1)
     rng = np.random.default_rng(61)
     NB = w.cache.shape[0]
     lat_b = bits_of(rng.normal(0, 1, (NB * 64, 512)))
     rope_b = bits_of(rng.normal(0, 1, (NB * 64, 64)))
     slots = np.arange(NB * 64, dtype=np.int64)
-    w.cache = oracle.cache_write(oracle.FP8_CACHE, lat_b, rope_b, slots, np.zeros_like(w.cache))
+    ofmt = oracle.FP8_CACHE if fmt == "fp8" else oracle.NVFP4_CACHE
+    w.cache = oracle.cache_write(ofmt, lat_b, rope_b, slots, np.zeros_like(w.cache))
     dw = DeviceWorkload(w)
     dw.cache.zero_()
     smla.smla_concat_and_cache_mla(torch.from_numpy(lat_b.view(np.int16)).cuda().view(torch.bfloat16),
                                    torch.from_numpy(rope_b.view(np.int16)).cuda().view(torch.bfloat16),
-                                   dw.cache, torch.from_numpy(slots).cuda(), kv_cache_dtype="fp8_ds_mla")
+                                   dw.cache, torch.from_numpy(slots).cuda(), kv_cache_dtype=fmt + "_ds_mla")
     torch.cuda.synchronize()
     assert np.array_equal(dw.cache.cpu().numpy(), w.cache)
     out, lse, _ = dw.run()
-    assert_parity(w, out, lse, label="attention over written cache")
+    assert_parity(w, out, lse, label=f"attention over written {fmt} cache")

@@ -2,7 +2,8 @@
 
 Index conversion is compared bit for bit. Attention outputs are compared element
 by element with the stated tolerances: bf16 cache max-abs <= 1e-2 and rel-L2 <=
-5e-3, fp8_ds_mla cache max-abs <= 2e-2 and rel-L2 <= 1e-2, for o and for lse.
+5e-3, fp8_ds_mla and nvfp4_ds_mla caches max-abs <= 2e-2 and rel-L2 <= 1e-2, for
+o and for lse.
 Small cases are checked in full; the full-size configurations run exactly as the
 benchmark launches them and are checked on sampled tokens the oracle computes one
 by one.
@@ -19,7 +20,8 @@ import torch
 import oracle
 from sparse_mla_attention_indices_amd import smla
 from sparse_mla_attention_indices_amd import workloads as W
-from tests.gpu_util import DeviceWorkload, assert_parity, assert_parity_up_to_output_rounding, log, oracle_run
+from tests.gpu_util import (DeviceWorkload, assert_parity, assert_parity_up_to_output_rounding, entry_point, log,
+                            oracle_run)
 
 pytestmark = pytest.mark.gpu
 
@@ -72,7 +74,7 @@ def test_convert_random_bit_exact(T, K):
 
 # ------------------------------------------------------------ small matrix
 
-@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+@pytest.mark.parametrize("fmt", ["bf16", "fp8", "nvfp4"])
 @pytest.mark.parametrize("h_q", [16, 32, 64, 128])
 @pytest.mark.parametrize("topk", [1, 37, 64, 100, 200])
 def test_small_parity(fmt, h_q, topk):
@@ -86,7 +88,7 @@ def test_small_parity(fmt, h_q, topk):
         assert_parity(w, out, lse, label=f"small {fmt} h{h_q} k{topk} s{splits}")
 
 
-@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+@pytest.mark.parametrize("fmt", ["bf16", "fp8", "nvfp4"])
 @pytest.mark.parametrize("h_q", [64, 128])
 def test_long_list_crosses_the_lds_chunk(fmt, h_q):
     """topk 5000 > 2048 positions per LDS round, ragged tail, one split and several."""
@@ -98,7 +100,7 @@ def test_long_list_crosses_the_lds_chunk(fmt, h_q):
         assert_parity(w, out, lse, label=f"long {fmt} h{h_q} s{splits}")
 
 
-@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+@pytest.mark.parametrize("fmt", ["bf16", "fp8", "nvfp4"])
 def test_logits_rising_past_the_first_tile_reference(fmt):
     """128-head workgroups (bf16 cache) weight every row against a reference per
     head taken from the max of the first tile (32 valid rows); when a later tile's
@@ -136,7 +138,7 @@ def test_logits_rising_past_the_first_tile_reference(fmt):
                                             weights_rounded=True)
 
 
-@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+@pytest.mark.parametrize("fmt", ["bf16", "fp8", "nvfp4"])
 @pytest.mark.parametrize("h_q", [32, 128])
 def test_degenerate_rows(fmt, h_q):
     """Whole tokens without a valid slot, bad request ids, bad table entries, duplicates."""
@@ -183,7 +185,7 @@ def test_valid_counts_across_tile_ring_and_short_list_bounds(h_q):
         assert_parity(w, out, lse, label=f"ring bounds h{h_q} s{splits}")
 
 
-@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+@pytest.mark.parametrize("fmt", ["bf16", "fp8", "nvfp4"])
 def test_short_lists_are_exact_up_to_output_rounding(fmt):
     """Tokens with 1..8 valid rows put large weights on few rows, so |o| can reach the
     bf16 range where half an ulp (0.0156 above 4) exceeds the stated max-abs bound by
@@ -224,7 +226,7 @@ def test_wide_range_q_within_a_scale_group(h_q):
 
 # ------------------------------------------------------------ split merge
 
-@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+@pytest.mark.parametrize("fmt", ["bf16", "fp8", "nvfp4"])
 @pytest.mark.parametrize("h_q", [16, 64, 128])
 def test_split_merge_with_converted_indices(fmt, h_q):
     """Top-k splits merged by the second kernel, with invalid positions spread over
@@ -240,7 +242,7 @@ def test_split_merge_with_converted_indices(fmt, h_q):
         assert_parity(w, out, lse, label=f"split merge {fmt} h{h_q} s{splits}")
 
 
-@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+@pytest.mark.parametrize("fmt", ["bf16", "fp8", "nvfp4"])
 def test_workspace_reused_across_batch_sizes(fmt):
     """One workspace, filled with garbage once, then calls of changing token counts
     that share it: every call writes what it reads, so results depend neither on
@@ -255,7 +257,7 @@ def test_workspace_reused_across_batch_sizes(fmt):
         assert_parity(w, out, lse, tokens=np.arange(T), label=f"reused ws {fmt} T{T}")
 
 
-@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+@pytest.mark.parametrize("fmt", ["bf16", "fp8", "nvfp4"])
 def test_uninitialised_workspace(fmt):
     """A workspace full of 0xFF bytes (NaN patterns) gives the same results."""
     w = small(43, fmt, 64, 200, n_req=2, tok_per_req=4)
@@ -268,18 +270,18 @@ def test_uninitialised_workspace(fmt):
         assert_parity(w, out, lse, label=f"garbage ws {fmt}")
 
 
-@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+@pytest.mark.parametrize("fmt", ["bf16", "fp8", "nvfp4"])
 def test_partials_only_then_merge_equals_the_call(fmt):
     """A call with partials_only followed by smla_merge_partials runs the same
     kernels as one ordinary call. The lse is bit-identical. So is the output for
-    the bf16 cache and for an unsplit list (one part). A split fp8 call of
+    the bf16 and nvfp4 caches and for an unsplit list (one part). A split fp8 call of
     64-head workgroups keeps each part's O / l as bf16 rows (plus residual rows
     for a part of at most 128 valid rows), so there the output may differ from
     the fp32 parts' merge by one bf16 rounding of the largest part value plus
     one output ulp, and the call itself meets the oracle bounds."""
     w = small(51, fmt, 64, 300, n_req=3, tok_per_req=5, ctx=(200, 900), p_invalid=0.1)
     dw = DeviceWorkload(w)
-    fn = smla.smla_prefill_bf16 if fmt == "bf16" else smla.smla_decode_fp8
+    fn = entry_point(fmt)
     T, H, K = w.num_tokens, 64, 300
     for splits in (1, 3, 0):
         log(f"[case] partials then merge {fmt} splits={splits}")
@@ -292,7 +294,7 @@ def test_partials_only_then_merge_equals_the_call(fmt):
         out, lse = smla.smla_merge_partials(ws, T, H, S)
         torch.cuda.synchronize()
         assert torch.equal(lse, ref_lse)
-        if fmt == "bf16" or S == 1:
+        if fmt != "fp8" or S == 1:
             assert torch.equal(out, ref_out)
         else:
             o_off, _ = smla.partials_layout(T, H, S)
@@ -303,14 +305,14 @@ def test_partials_only_then_merge_equals_the_call(fmt):
             assert_parity(w, ref_out, ref_lse, label=f"split call {fmt} splits={splits}")
 
 
-@pytest.mark.parametrize("fmt,h_q", [("fp8", 64), ("fp8", 16), ("bf16", 64)])
+@pytest.mark.parametrize("fmt,h_q", [("fp8", 64), ("fp8", 16), ("bf16", 64), ("nvfp4", 16), ("nvfp4", 64)])
 def test_deferred_merge_then_merge_only_equals_the_call(fmt, h_q):
     """The attention stage of a call (merge deferred) and then its merge stage,
     with the same arguments and workspace, write what one ordinary call writes,
     bit for bit: split, unsplit and planner-chosen."""
     w = small(52, fmt, h_q, 300, n_req=3, tok_per_req=5, ctx=(200, 900), p_invalid=0.1)
     dw = DeviceWorkload(w)
-    fn = smla.smla_prefill_bf16 if fmt == "bf16" else smla.smla_decode_fp8
+    fn = entry_point(fmt)
     T, H, K = w.num_tokens, h_q, 300
     for splits in (1, 3, 0):
         log(f"[case] deferred merge {fmt} h{h_q} splits={splits}")
@@ -326,14 +328,14 @@ def test_deferred_merge_then_merge_only_equals_the_call(fmt, h_q):
         assert torch.equal(out, ref_out) and torch.equal(lse, ref_lse)
 
 
-@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+@pytest.mark.parametrize("fmt", ["bf16", "fp8", "nvfp4"])
 def test_parts_of_a_list_merged_like_context_parallel(fmt):
     """Each token's top-k list cut in two halves, each half computed by its own
     call (as two devices would), the two parts stacked into one partials buffer
     and merged: the result is the attention over the whole list."""
     w = small(53, fmt, 32, 400, n_req=4, tok_per_req=4, ctx=(300, 1500), p_invalid=0.1)
     dw = DeviceWorkload(w)
-    fn = smla.smla_prefill_bf16 if fmt == "bf16" else smla.smla_decode_fp8
+    fn = entry_point(fmt)
     T, H, K = w.num_tokens, 32, 400
     halves = ((0, 160), (160, K))          # uneven cut
     o_off, total = smla.partials_layout(T, H, len(halves))
@@ -425,6 +427,21 @@ def test_config4_spec_decode(topk):
     out, lse, _ = dw.run()
     tokens = None if topk == 512 else _sample_tokens(w.num_tokens, np.random.default_rng(topk), [0, 1, 255])
     assert_parity(w, out, lse, tokens=tokens, label=f"config4 (256 tok, h16, k{topk}, fp8)")
+
+
+@pytest.mark.parametrize("topk", [512, 1024, 2048])
+def test_config4_nvfp4_native_decode(topk):
+    """Config 4's batch over an nvfp4_ds_mla cache: 16 heads and top-k 512, 1024
+    or 2048, the shape the pull-request page runs native NVFP4 decode at, in the
+    benchmark's launch configuration."""
+    w = W.config4_nvfp4(topk=topk)
+    dw = DeviceWorkload(w)
+    log(f"[case] config4 nvfp4 topk={topk}")
+    out, lse, phys = dw.run(with_phys=True)
+    want = oracle.convert_indices(w.req_id_per_token, w.block_table, w.topk_indices, w.num_blocks)
+    assert np.array_equal(phys.cpu().numpy(), want)
+    tokens = None if topk == 512 else _sample_tokens(w.num_tokens, np.random.default_rng(topk), [0, 1, 255])
+    assert_parity(w, out, lse, tokens=tokens, label=f"config4 nvfp4 (256 tok, h16, k{topk})")
 
 
 def test_config5_long_mixed_sampled():
