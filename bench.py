@@ -71,7 +71,7 @@ def algorithmic_work(w):
     valid = idx >= 0
     n_valid = int(valid.sum())
     pairs = np.unique((w.req_id_per_token[:, None].astype(np.int64) << 32 | idx.astype(np.int64))[valid])
-    row_bytes = 656 if w.cache_format == "fp8" else 1152
+    row_bytes = {"fp8": 656, "nvfp4": 352, "bf16": 1152}[w.cache_format]
     T, H, K = w.num_tokens, w.h_q, w.topk
     reqs = np.unique(w.req_id_per_token)
     by = {
@@ -164,9 +164,12 @@ def upconvert_bench(torch, smla, W, dev, stream, flush, sink, steps: int):
 def kernels_of_plan(cache_format: str, h_q: int, splits: int):
     """Names of the kernels one call launches, from the split plan (the same rule the
     library's launcher applies: one workgroup covers all h_q heads of a token, except
-    fp8 with h_q = 128, which takes two 64-head workgroups)."""
-    fmt = "fp8" if cache_format == "fp8" else "bf16"
-    if h_q == 128 and fmt == "bf16":
+    fp8 with h_q = 128, which takes two 64-head workgroups, and nvfp4, which takes
+    one 16-head workgroup per 16 heads)."""
+    fmt = cache_format
+    if fmt == "nvfp4":
+        names = ["attn_kernel<nvfp4, 1>"]
+    elif h_q == 128 and fmt == "bf16":
         names = ["attn128_kernel"]
     elif fmt == "fp8" and h_q >= 64:
         names = ["attn_pc_kernel"]
@@ -205,7 +208,8 @@ def roofline_of(w, ms: float):
 
 def config_bench(torch, smla, w, dev, stream, flush, sink, steps: int, warmup: int = 2):
     """One workload through its entry point (smla_prefill_bf16 for a bf16 cache,
-    smla_decode_fp8 for fp8_ds_mla), one call per step over the whole batch, cold
+    smla_decode_fp8 for fp8_ds_mla, smla_decode_nvfp4 for nvfp4_ds_mla), one call
+    per step over the whole batch, cold
     cache (the 1 GiB read before each step, outside the events), HIP events on the
     library's stream around each call."""
     q, cache, bt, req, idx = upload(torch, w, dev)
@@ -213,7 +217,8 @@ def config_bench(torch, smla, w, dev, stream, flush, sink, steps: int, warmup: i
     out = torch.empty((T, H, 512), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((T, H), dtype=torch.float32, device=dev)
     ws = torch.empty(max(smla.smla_workspace_size(T, H, K), 1), dtype=torch.uint8, device=dev)
-    fn = smla.smla_prefill_bf16 if w.cache_format == "bf16" else smla.smla_decode_fp8
+    entry = {"bf16": "smla_prefill_bf16", "fp8": "smla_decode_fp8", "nvfp4": "smla_decode_nvfp4"}[w.cache_format]
+    fn = getattr(smla, entry)
     props = torch.cuda.get_device_properties(dev)
     splits, _ = smla.smla_plan(T, H, K, props.multi_processor_count)
 
@@ -234,8 +239,8 @@ def config_bench(torch, smla, w, dev, stream, flush, sink, steps: int, warmup: i
     t = np.array([a.elapsed_time(b) for a, b in zip(e0, e1)])
     ms = float(np.median(t))
     rec = {"workload": w.name, "num_tokens": T, "h_q": H, "topk": K,
-           "cache": "fp8_ds_mla" if w.cache_format == "fp8" else "bf16",
-           "entry_point": "smla_prefill_bf16" if w.cache_format == "bf16" else "smla_decode_fp8",
+           "cache": {"bf16": "bf16", "fp8": "fp8_ds_mla", "nvfp4": "nvfp4_ds_mla"}[w.cache_format],
+           "entry_point": entry,
            "kernels": kernels_of_plan(w.cache_format, H, splits), "num_splits": splits,
            "steps": steps, "ms_median": ms, "ms_p10": float(np.percentile(t, 10)),
            "ms_p90": float(np.percentile(t, 90))}
@@ -250,10 +255,14 @@ def config_bench(torch, smla, w, dev, stream, flush, sink, steps: int, warmup: i
 def other_configs(W, seed: int):
     def c4():
         return W.config4_sweep(seed)
+
+    def c4_nvfp4():
+        return W.config4_sweep(seed, "nvfp4")
     return [("c1_tiny_bf16", lambda: [W.config1(seed)], 20),
             ("c1_tiny_fp8", lambda: [W.config1_fp8(seed)], 20),
             ("c3_bf16_prefill", lambda: [W.config3(seed)], 5),
             ("c4_spec_decode", c4, 20),
+            ("c4_spec_decode_nvfp4", c4_nvfp4, 20),
             ("c5_long_mixed", lambda: [W.config5(seed)], 5)]
 
 
@@ -327,7 +336,8 @@ def main():
     ap.add_argument("--only", default=None,
                     help="time one workload alone and print its record (for profiler runs): "
                          "c2 (the headline batch, no side measurements), c1_tiny_bf16, c1_tiny_fp8, "
-                         "c3_bf16_prefill, c4_spec_decode (top-k 512, 1024, 2048), c5_long_mixed")
+                         "c3_bf16_prefill, c4_spec_decode (top-k 512, 1024, 2048), c4_spec_decode_nvfp4 "
+                         "(the same over an nvfp4_ds_mla cache), c5_long_mixed")
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the other workloads (the headline line only)")
     args = ap.parse_args()

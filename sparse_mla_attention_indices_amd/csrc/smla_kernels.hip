@@ -74,9 +74,9 @@ namespace {
 // fall on distinct banks) and rows 16..31 start 16 bytes later than a plain
 // stride would put them (the transposed V reads touch rows r and r + 16
 // together); bf16 rows get a 1168-byte stride (1152 + 16). nvfp4 rows keep
-// their 352-byte stride in the ring and are dequantised, one tile at a time,
-// into a bf16 tile laid out as the bf16 cache's (kOffConv), which the MFMA
-// operands are read from.
+// their 352-byte stride in the ring; their latent values, dequantised to bf16
+// as QK^T reads them, are stored in a tile laid out as the bf16 cache's
+// (kOffConv), which PV reads V^T from.
 template <int FMT, int NHH>
 struct Cfg {
     static constexpr int kWaves = 2 * NHH;
@@ -96,7 +96,7 @@ struct Cfg {
     // 64 heads: one workgroup per CU; fewer heads: two workgroups per CU
     // share the LDS (fp8).
     static constexpr int kNBuf = NHH == 4 ? (FMT == kCacheFp8 ? 4 : 2) : 2;
-    // nvfp4: the bf16 tile the ring's rows are dequantised into
+    // nvfp4: the bf16 tile the latent values are stored into for PV
     static constexpr int kConvBytes = FMT == kCacheNvfp4 ? Cfg<kCacheBf16, NHH>::kBufBytes : 0;
     // PV is split by output dims: wave w owns dims [w * kDimsPerWave, ...) of
     // every head of the workgroup, kDimBlocks blocks of 16 dims.
@@ -126,49 +126,13 @@ struct Cfg {
 
 // ------------------------------------------------------------- attention
 
-// One nvfp4_ds_mla tile, as copied into the ring, into a bf16 tile in the bf16
-// cache's layout [pull-request page "Support nvfp4_ds_mla on
-// FLASHINFER_MLA_SPARSE, with native NVFP4 decode": native decode works on the
-// exact values of the rows as stored]. A thread turns 8 latent codes (4 bytes,
-// half of a 16-value block) into 8 bf16 values: each code to fp32, times the
-// block's E4M3 scale in fp32, then to bf16. E2M1 (2 significant bits) times
-// E4M3 (4) is exact in fp32 and in bf16, so no step rounds. (The scaled
-// conversions are not used for the product: they apply only the exponent of
-// their scale operand, a power-of-two block scale.) RoPE bytes go to bf16
-// exactly as well. Rows past the tile's valid count hold copies of its first
-// row and are converted too.
-template <class C, class CT>
-__device__ __forceinline__ void dequant_nvfp4_tile(const uint8_t *raw, uint8_t *dst, int tid)
-{
-    using F = RowFmt<kCacheNvfp4>;
-    for (int u = tid; u < kTile * 64; u += C::kThreads) {
-        const int r = u >> 6, piece = u & 63;
-        const uint8_t *src = raw + lds_row<C>(r);
-        const uint32_t codes = *(const uint32_t *)(src + 4 * piece);
-        const uint32_t sc_byte = src[F::kScales + (piece >> 1)];
-        const float sc = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(sc_byte, 1.0f, false)[0];
-        const f32x2 f0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 0);
-        const f32x2 f1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 1);
-        const f32x2 f2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 2);
-        const f32x2 f3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 3);
-        const uint4 v = make_uint4(pack_bf16(f0[0] * sc, f0[1] * sc), pack_bf16(f1[0] * sc, f1[1] * sc),
-                                   pack_bf16(f2[0] * sc, f2[1] * sc), pack_bf16(f3[0] * sc, f3[1] * sc));
-        *(uint4 *)(dst + lds_row<CT>(r) + 16 * piece) = v;
-    }
-    for (int u = tid; u < kTile * 8; u += C::kThreads) {
-        const int r = u >> 3, piece = u & 7;
-        const uint2 b = *(const uint2 *)(raw + lds_row<C>(r) + F::kRope + 8 * piece);
-        *(bf16x8 *)(dst + lds_row<CT>(r) + RowFmt<kCacheBf16>::kRope + 16 * piece) = e4m3x8_to_bf16x8(b);
-    }
-}
-
 template <int FMT, int NHH>
 __global__ __launch_bounds__(128 * NHH) __attribute__((amdgpu_waves_per_eu(NHH == 1 ? 1 : 2)))
 void attn_kernel(const KParams p)
 {
     using C = Cfg<FMT, NHH>;
-    // the layout the MFMA operands are read in: nvfp4 tiles are dequantised
-    // into a bf16 tile first and then run the bf16 code
+    // the layout the MFMA operands are read in: nvfp4 latent values are
+    // dequantised to bf16 as QK^T reads them and stored in that layout for PV
     constexpr int TF = FMT == kCacheNvfp4 ? kCacheBf16 : FMT;
     using CT = Cfg<TF, NHH>;
     constexpr int RB = kRB;
@@ -290,6 +254,9 @@ void attn_kernel(const KParams p)
     // the QK^T MFMAs of column group gi are issued (fp8), so independent work
     // (the pending PV) can fill the wait for their results.
     auto tile = [&](const uint8_t *buf, int n_tile, bool exact, auto &&mid) __attribute__((always_inline)) {
+        // V^T is read from the tile itself, or for nvfp4 from the bf16 values
+        // this wave stored while converting its K fragments (same layout)
+        const uint8_t *vbuf = FMT == kCacheNvfp4 ? smem + C::kOffConv : buf;
         // per-lane LDS offsets inside the tile buffer
         const int off_k = n16 * RS;                      // K rows 16*rb + n16 (+ rb * RBB)
         const int off_sc = (4 * g) * RS;                 // accumulator rows 16*rb + 4g + i
@@ -355,6 +322,52 @@ void attn_kernel(const KParams p)
                 const i32x2 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
                     LDS_PTR(i32x2, buf + off_v8 + dim0 + 16 * db));
                 vf8[db] = make_uint2((uint32_t)v[0], (uint32_t)v[1]);
+            }
+        } else if constexpr (FMT == kCacheNvfp4) {
+            // raw rows (ring layout C). Lane (n16, g) turns the 8 latent codes of
+            // row 16*rb + n16, columns 256*dh + 32*k + 8*g .. + 7, into bf16: each
+            // code to fp32, times its 16-value block's E4M3 scale, to bf16 (exact at
+            // every step: E2M1 x E4M3 has at most 6 significant bits; the scaled
+            // conversions would apply only the scale's exponent). The fragment
+            // feeds the MFMA and is stored where the bf16 layout puts it, so this
+            // wave's PV reads V^T of its own dims from there: no other wave
+            // touches those columns, and the next tile's stores follow this
+            // tile's reads in the wave's program order.
+            using F = RowFmt<kCacheNvfp4>;
+            const uint8_t *row_b[RB];
+            uint4 scw[RB];          // the row's scales 16*dh .. 16*dh + 15 (this half's blocks)
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) {
+                row_b[rb] = buf + lds_row<C>(16 * rb + n16);
+                scw[rb] = *(const uint4 *)(row_b[rb] + F::kScales + 16 * dh);
+                acc[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+            const bool odd_blk = (g >> 1) != 0;     // columns 8g.. of a 32-column step: block 2k + (g >> 1)
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb) {
+                    const uint32_t codes = *(const uint32_t *)(row_b[rb] + 128 * dh + 16 * k + 4 * g);
+                    const uint32_t sw = k < 2 ? scw[rb].x : k < 4 ? scw[rb].y : k < 6 ? scw[rb].z : scw[rb].w;
+                    const f32x2 s2 = (k & 1) ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(sw, 1.0f, true)
+                                             : __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(sw, 1.0f, false);
+                    const float scl = odd_blk ? s2[1] : s2[0];
+                    const f32x2 f0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 0);
+                    const f32x2 f1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 1);
+                    const f32x2 f2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 2);
+                    const f32x2 f3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 3);
+                    const uint4 w = make_uint4(pack_bf16(f0[0] * scl, f0[1] * scl), pack_bf16(f1[0] * scl, f1[1] * scl),
+                                               pack_bf16(f2[0] * scl, f2[1] * scl), pack_bf16(f3[0] * scl, f3[1] * scl));
+                    *(uint4 *)(smem + C::kOffConv + rb * RBB + off_k + 2 * (256 * dh + 32 * k + 8 * g)) = w;
+                    acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, w), qb[k],
+                                                                      acc[rb], 0, 0, 0);
+                }
+            }
+            // RoPE: 8 E4M3 bytes per lane, exact in bf16
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) {
+                const uint2 rp = *(const uint2 *)(row_b[rb] + F::kRope + 32 * dh + 8 * g);
+                acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_to_bf16x8(rp), qb[8], acc[rb], 0, 0, 0);
             }
         } else {
 #pragma unroll
@@ -455,9 +468,9 @@ void attn_kernel(const KParams p)
                 } else {
                     const int colb = 2 * (dim0 + 16 * db);
                     const uint2 w0 = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        LDS_PTR(i16x4, buf + off_v16 + colb)));
+                        LDS_PTR(i16x4, vbuf + off_v16 + colb)));
                     const uint2 w1 = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        LDS_PTR(i16x4, buf + RBB + off_v16 + colb)));
+                        LDS_PTR(i16x4, vbuf + RBB + off_v16 + colb)));
                     a = __builtin_bit_cast(bf16x8, make_uint4(w0.x, w0.y, w1.x, w1.y));
                 }
                 o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pbh[gi], o[db], 0, 0, 0);
@@ -509,9 +522,9 @@ void attn_kernel(const KParams p)
                 } else {
                     const int colb = 2 * (dim0 + 16 * db);
                     const uint2 w0 = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        LDS_PTR(i16x4, buf + off_v16 + colb)));
+                        LDS_PTR(i16x4, vbuf + off_v16 + colb)));
                     const uint2 w1 = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        LDS_PTR(i16x4, buf + RBB + off_v16 + colb)));
+                        LDS_PTR(i16x4, vbuf + RBB + off_v16 + colb)));
                     a = __builtin_bit_cast(bf16x8, make_uint4(w0.x, w0.y, w1.x, w1.y));
                 }
 #pragma unroll
@@ -743,15 +756,8 @@ void attn_kernel(const KParams p)
                              pv_part(vf8_pend, pvp, gi * (DB / 2), (gi + 1) * (DB / 2));
                          });
                 } else {
-                    const uint8_t *tb = ring + (it % C::kNBuf) * C::kBufBytes;
-                    if constexpr (FMT == kCacheNvfp4) {
-                        // the bf16 tile is free: every wave passed the barrier above
-                        // after its last read of the previous tile
-                        dequant_nvfp4_tile<C, CT>(tb, smem + C::kOffConv, tid);
-                        __syncthreads();
-                        tb = smem + C::kOffConv;
-                    }
-                    tile(tb, min(kTile, n_valid - it * kTile), exact_p, [](int) {});
+                    tile(ring + (it % C::kNBuf) * C::kBufBytes, min(kTile, n_valid - it * kTile), exact_p,
+                         [](int) {});
                 }
             }
             if constexpr (kPipe) {
