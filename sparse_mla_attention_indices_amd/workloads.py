@@ -284,6 +284,15 @@ def config1_fp8(seed: int = 0) -> Workload:
     return w
 
 
+def config1_nvfp4(seed: int = 0) -> Workload:
+    """Config 1's block table, q and indices over an nvfp4_ds_mla cache."""
+    w = config1(seed)
+    w.cache = random_nvfp4_cache(seed, 1, w.cache.shape[0])
+    w.cache_format = "nvfp4"
+    w.name = "c1_tiny_nvfp4"
+    return w
+
+
 def config2(seed: int = 0) -> Workload:
     """FP8 decode: 64 requests x 1 token, ctx U{4096..8192}, h_q 64, top-k 2048."""
     ctx = _rng(seed, 2, 4).integers(4096, 8192, size=64, endpoint=True)

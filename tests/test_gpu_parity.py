@@ -375,7 +375,7 @@ def test_repeat_calls_are_bit_identical():
 
 # ------------------------------------------------------------ named configs
 
-@pytest.mark.parametrize("maker", [W.config1, W.config1_fp8])
+@pytest.mark.parametrize("maker", [W.config1, W.config1_fp8, W.config1_nvfp4])
 def test_config1(maker):
     w = maker()
     dw = DeviceWorkload(w)
