@@ -343,11 +343,24 @@ void attn_kernel(const KParams p)
                 acc[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
             }
             const bool odd_blk = (g >> 1) != 0;     // columns 8g.. of a 32-column step: block 2k + (g >> 1)
+            // every code word and the RoPE bytes first: the stores below go to
+            // another LDS region, which the compiler cannot tell, so a read
+            // after a store would wait for it
+            uint32_t code_w[8][RB];
+            uint2 rope_w[RB];
+#pragma unroll
+            for (int k = 0; k < 8; ++k)
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb)
+                    code_w[k][rb] = *(const uint32_t *)(row_b[rb] + 128 * dh + 16 * k + 4 * g);
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb)
+                rope_w[rb] = *(const uint2 *)(row_b[rb] + F::kRope + 32 * dh + 8 * g);
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
 #pragma unroll
                 for (int rb = 0; rb < RB; ++rb) {
-                    const uint32_t codes = *(const uint32_t *)(row_b[rb] + 128 * dh + 16 * k + 4 * g);
+                    const uint32_t codes = code_w[k][rb];
                     const uint32_t sw = k < 2 ? scw[rb].x : k < 4 ? scw[rb].y : k < 6 ? scw[rb].z : scw[rb].w;
                     const f32x2 s2 = (k & 1) ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(sw, 1.0f, true)
                                              : __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(sw, 1.0f, false);
@@ -365,10 +378,8 @@ void attn_kernel(const KParams p)
             }
             // RoPE: 8 E4M3 bytes per lane, exact in bf16
 #pragma unroll
-            for (int rb = 0; rb < RB; ++rb) {
-                const uint2 rp = *(const uint2 *)(row_b[rb] + F::kRope + 32 * dh + 8 * g);
-                acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_to_bf16x8(rp), qb[8], acc[rb], 0, 0, 0);
-            }
+            for (int rb = 0; rb < RB; ++rb)
+                acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_to_bf16x8(rope_w[rb]), qb[8], acc[rb], 0, 0, 0);
         } else {
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb)
