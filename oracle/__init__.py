@@ -90,6 +90,8 @@ def _load():
     lib.smla_oracle_bf16_rne.argtypes = [dbl]
     lib.smla_oracle_gather_upconvert.restype = None
     lib.smla_oracle_gather_upconvert.argtypes = [vp, i64, vp, i64, vp, vp, i64, vp, i64]
+    lib.smla_oracle_gather_upconvert_nvfp4.restype = None
+    lib.smla_oracle_gather_upconvert_nvfp4.argtypes = [vp, i64, vp, i64, vp, vp, i64, vp, i64]
     lib.smla_oracle_plan_prefill_chunks.restype = i64
     lib.smla_oracle_plan_prefill_chunks.argtypes = [vp, i64, i64, vp, vp]
     lib.smla_oracle_attention.restype = ctypes.c_int
@@ -230,15 +232,17 @@ def bf16_rne(x: float) -> int:
 
 
 def gather_upconvert(cache, block_table, seq_lens, workspace_starts, workspace_rows: int,
-                     workspace=None) -> np.ndarray:
+                     workspace=None, cache_format: int = FP8_CACHE) -> np.ndarray:
     """Upconvert the context rows of prefill requests from an fp8_ds_mla cache
-    (uint8 [NB, 64, 656]) into a bf16 workspace (uint16 bit patterns
+    (uint8 [NB, 64, 656]) or an nvfp4_ds_mla cache (uint8 [NB, 64, 352],
+    cache_format NVFP4_CACHE) into a bf16 workspace (uint16 bit patterns
     [workspace_rows, 576]); block_table [B, MB] holds the requests' rows, seq_lens
     and workspace_starts [B]. Rows no request covers keep their contents (zeros
     for a new workspace). Returns the workspace."""
     c = cache if (cache.dtype == np.uint8 and cache.flags.c_contiguous) else _c(cache, np.uint8)
-    if c.shape[-1] != 656:
-        raise ValueError("fp8_ds_mla cache rows must be 656 bytes")
+    row = {FP8_CACHE: 656, NVFP4_CACHE: NVFP4_ROW_BYTES}[cache_format]
+    if c.shape[-1] != row:
+        raise ValueError(f"cache rows must be {row} bytes for this format")
     bt = _c(block_table, np.int32)
     sl = _c(seq_lens, np.int32).reshape(-1)
     st = _c(workspace_starts, np.int32).reshape(-1)
@@ -247,9 +251,10 @@ def gather_upconvert(cache, block_table, seq_lens, workspace_starts, workspace_r
     if workspace is None:
         workspace = np.zeros((workspace_rows, 576), dtype=np.uint16)
     assert workspace.dtype == np.uint16 and workspace.flags.c_contiguous
-    _load().smla_oracle_gather_upconvert(c.ctypes.data, c.size // (64 * 656), bt.ctypes.data, bt.shape[1],
-                                         sl.ctypes.data, st.ctypes.data, sl.shape[0],
-                                         workspace.ctypes.data, int(workspace_rows))
+    fn = _load().smla_oracle_gather_upconvert if cache_format == FP8_CACHE else \
+        _load().smla_oracle_gather_upconvert_nvfp4
+    fn(c.ctypes.data, c.size // (64 * row), bt.ctypes.data, bt.shape[1], sl.ctypes.data, st.ctypes.data,
+       sl.shape[0], workspace.ctypes.data, int(workspace_rows))
     return workspace
 
 
@@ -324,9 +329,11 @@ def attention(cache_format: int, q_bits, cache, block_table, req_id_per_token, t
 
 
 def separate_prefill_attention(q_bits, cache, block_table, req_id_per_token, topk_indices, sm_scale: float,
-                               num_decode_reqs: int, seq_lens, max_rows: int):
+                               num_decode_reqs: int, seq_lens, max_rows: int, cache_format: int = FP8_CACHE):
     """The separate-prefill mode of an fp8_ds_mla cache, end to end [flashmla_sparse.py page,
-    _build_fp8_separate_prefill_decode and _forward_fp8_kv_separate_prefill_decode]:
+    _build_fp8_separate_prefill_decode and _forward_fp8_kv_separate_prefill_decode]
+    (or of an nvfp4_ds_mla cache with cache_format NVFP4_CACHE, whose prefill the
+    native-decode pull-request page stages through the same kind of gather):
     requests [0, num_decode_reqs) are decode requests, the rest prefill requests
     (prefill index r = request id - num_decode_reqs) with context length
     seq_lens[request]. Decode tokens attend over the fp8 cache; prefill tokens
@@ -339,7 +346,7 @@ def separate_prefill_attention(q_bits, cache, block_table, req_id_per_token, top
     req = _c(req_id_per_token, np.int32).reshape(-1)
     idx = _c(topk_indices, np.int32)
     sl = _c(seq_lens, np.int32).reshape(-1)
-    nb = cache.size // (64 * 656)
+    nb = cache.size // (64 * {FP8_CACHE: 656, NVFP4_CACHE: NVFP4_ROW_BYTES}[cache_format])
     R = bt.shape[0]
     nd = int(num_decode_reqs)
     prefill_id = np.where(req >= nd, req - nd, -1).astype(np.int32)
@@ -349,14 +356,14 @@ def separate_prefill_attention(q_bits, cache, block_table, req_id_per_token, top
     lse = np.full((T, H), -np.inf)
     dec = np.nonzero(prefill_id < 0)[0]
     if dec.size:
-        od, ld = attention(FP8_CACHE, q, cache, bt, req, idx, sm_scale, tokens=dec)
+        od, ld = attention(cache_format, q, cache, bt, req, idx, sm_scale, tokens=dec)
         o[dec], lse[dec] = od, ld
     c0 = 0
     for c1 in ends:
         rows = int(sl[nd + c0:nd + c1].sum())
         nbw = max(1, -(-rows // 64))
         ws = gather_upconvert(cache, bt[nd + c0:nd + c1], sl[nd + c0:nd + c1], starts[c0:c1], rows,
-                              workspace=np.zeros((nbw * 64, 576), dtype=np.uint16))
+                              workspace=np.zeros((nbw * 64, 576), dtype=np.uint16), cache_format=cache_format)
         toks = np.nonzero((prefill_id >= c0) & (prefill_id < c1))[0]
         if toks.size:
             # workspace row w = block w // 64, offset w % 64 of a one-request table

@@ -392,17 +392,25 @@ uint16_t smla_oracle_bf16_rne(double x)
 }
 
 /* Gather and upconvert the context rows of a batch of prefill requests into a
- * bf16 workspace [flashmla_sparse.py page, _forward_fp8_kv_separate_prefill_decode: the
- * cp_gather_and_upconvert_fp8_kv_cache call]: for request b and position
- * p < seq_lens[b], workspace row workspace_starts[b] + p (when inside
- * [0, workspace_rows)) receives the row at slot block_table[b, p / 64] * 64 +
- * p % 64 of the fp8_ds_mla cache, each latent value e4m3 x scale rounded to
- * bfloat16, the RoPE values copied. */
-void smla_oracle_gather_upconvert(const uint8_t *cache, int64_t num_blocks, const int32_t *block_table,
-                                  int64_t max_blocks_per_req, const int32_t *seq_lens,
-                                  const int32_t *workspace_starts, int64_t batch, uint16_t *workspace,
-                                  int64_t workspace_rows)
+ * bf16 workspace: for request b and position p < seq_lens[b], workspace row
+ * workspace_starts[b] + p (when inside [0, workspace_rows)) receives the row at
+ * slot block_table[b, p / 64] * 64 + p % 64 of the cache; a position whose
+ * block lies outside the table, or whose table entry lies outside the cache,
+ * gets a row of zeros.
+ * - fp8_ds_mla (cache_format 1) [flashmla_sparse.py page,
+ *   _forward_fp8_kv_separate_prefill_decode: the cp_gather_and_upconvert_fp8_kv_cache
+ *   call]: each latent value e4m3 x scale rounded to bfloat16, the RoPE values copied.
+ * - nvfp4_ds_mla (cache_format 2) [pull-request page "Support nvfp4_ds_mla on
+ *   FLASHINFER_MLA_SPARSE, with native NVFP4 decode": prefill is staged through a
+ *   context gather per request and chunk]: every value is its exact decoded
+ *   value, which bfloat16 holds exactly (E2M1 x E4M3 has at most 6 significant
+ *   bits; E4M3 RoPE values 4). */
+static void gather_upconvert(int cache_format, const uint8_t *cache, int64_t num_blocks,
+                             const int32_t *block_table, int64_t max_blocks_per_req, const int32_t *seq_lens,
+                             const int32_t *workspace_starts, int64_t batch, uint16_t *workspace,
+                             int64_t workspace_rows)
 {
+    const int64_t row_bytes = cache_format == 1 ? ORACLE_FP8_ROW : ORACLE_NVFP4_ROW;
     for (int64_t b = 0; b < batch; ++b) {
         for (int64_t pos = 0; pos < seq_lens[b]; ++pos) {
             int64_t w = (int64_t)workspace_starts[b] + pos;
@@ -415,14 +423,38 @@ void smla_oracle_gather_upconvert(const uint8_t *cache, int64_t num_blocks, cons
                 memset(dst, 0, ORACLE_DQK * sizeof(uint16_t));
                 continue;
             }
-            const uint8_t *row = cache + (base * ORACLE_BLOCK + pos % ORACLE_BLOCK) * ORACLE_FP8_ROW;
+            const uint8_t *row = cache + (base * ORACLE_BLOCK + pos % ORACLE_BLOCK) * row_bytes;
             double v[ORACLE_DQK];
-            smla_oracle_decode_fp8_row(row, v);
-            for (int i = 0; i < ORACLE_DV; ++i)
-                dst[i] = smla_oracle_bf16_rne(v[i]);
-            memcpy(dst + ORACLE_DV, row + 528, 64 * sizeof(uint16_t));
+            if (cache_format == 1) {
+                smla_oracle_decode_fp8_row(row, v);
+                for (int i = 0; i < ORACLE_DV; ++i)
+                    dst[i] = smla_oracle_bf16_rne(v[i]);
+                memcpy(dst + ORACLE_DV, row + 528, 64 * sizeof(uint16_t));
+            } else {
+                smla_oracle_decode_nvfp4_row(row, v);
+                for (int i = 0; i < ORACLE_DQK; ++i)
+                    dst[i] = smla_oracle_bf16_rne(v[i]);
+            }
         }
     }
+}
+
+void smla_oracle_gather_upconvert(const uint8_t *cache, int64_t num_blocks, const int32_t *block_table,
+                                  int64_t max_blocks_per_req, const int32_t *seq_lens,
+                                  const int32_t *workspace_starts, int64_t batch, uint16_t *workspace,
+                                  int64_t workspace_rows)
+{
+    gather_upconvert(1, cache, num_blocks, block_table, max_blocks_per_req, seq_lens, workspace_starts, batch,
+                     workspace, workspace_rows);
+}
+
+void smla_oracle_gather_upconvert_nvfp4(const uint8_t *cache, int64_t num_blocks, const int32_t *block_table,
+                                        int64_t max_blocks_per_req, const int32_t *seq_lens,
+                                        const int32_t *workspace_starts, int64_t batch, uint16_t *workspace,
+                                        int64_t workspace_rows)
+{
+    gather_upconvert(2, cache, num_blocks, block_table, max_blocks_per_req, seq_lens, workspace_starts, batch,
+                     workspace, workspace_rows);
 }
 
 /* Cut consecutive prefill requests into chunks whose total sequence length fits

@@ -64,6 +64,10 @@ MUTANTS = {
                                          "row[288 + r] = 0;"),
     "nvfp4_attention_reads_fp8_rows": ("smla_oracle_decode_nvfp4_row((const uint8_t *)cache + (int64_t)slot[j] * ORACLE_NVFP4_ROW,",
                                        "smla_oracle_decode_nvfp4_row((const uint8_t *)cache + (int64_t)slot[j] * ORACLE_FP8_ROW,"),
+    "nvfp4_upconvert_fp8_stride": ("const int64_t row_bytes = cache_format == 1 ? ORACLE_FP8_ROW : ORACLE_NVFP4_ROW;",
+                                   "const int64_t row_bytes = ORACLE_FP8_ROW;"),
+    "nvfp4_upconvert_drops_rope": ("for (int i = 0; i < ORACLE_DQK; ++i)\n                    dst[i] = smla_oracle_bf16_rne(v[i]);",
+                                   "for (int i = 0; i < ORACLE_DV; ++i)\n                    dst[i] = smla_oracle_bf16_rne(v[i]);"),
     "chunk_starts_not_reset": ("            chunk_ends[n++] = (int32_t)r;\n            used = 0;",
                                "            chunk_ends[n++] = (int32_t)r;"),
 }

@@ -799,3 +799,48 @@ def test_nvfp4_attention_equals_bf16_attention_over_the_same_values():
     o4, l4 = oracle.attention(oracle.NVFP4_CACHE, q, cache, bt, req, idx, W.SM_SCALE_576)
     o0, l0 = oracle.attention(oracle.BF16_CACHE, q, bf16_cache, bt, req, idx, W.SM_SCALE_576)
     assert np.array_equal(o4, o0) and np.array_equal(l4, l0)
+
+
+def test_nvfp4_upconvert_holds_the_exact_decoded_values():
+    cache = W.random_nvfp4_cache(5, 99, 2)
+    bt = np.array([[1, 0]], dtype=np.int32)
+    ws = oracle.gather_upconvert(cache, bt, [128], [0], 128, cache_format=oracle.NVFP4_CACHE)
+    flat = cache.reshape(128, 352)
+    want = oracle.decode_nvfp4_rows(np.concatenate([flat[64:], flat[:64]]))
+    assert np.array_equal(W.bf16_bits_to_f32(ws).astype(np.float64), want)
+
+
+def test_nvfp4_upconvert_places_each_request_position_at_its_workspace_row():
+    # rows written by a paged-cache simulation; three RoPE bytes carry (request,
+    # position // 64, position % 64) as E4M3 codes 1..65 (distinct finite values)
+    from tests.paged_writer import PagedCache
+    rng = np.random.default_rng(19)
+    lens = [70, 5, 130]
+    pc = PagedCache(rng, lens, extra_blocks=2)
+    cache = np.zeros((pc.num_blocks, 64, 352), dtype=np.uint8)
+    for (r, pos), (blk, off) in pc.where.items():
+        cache[blk, off, 288] = r + 1
+        cache[blk, off, 289] = pos // 64 + 1
+        cache[blk, off, 290] = pos % 64 + 1
+    starts = np.array([3, 80, 90], dtype=np.int32)
+    ws = oracle.gather_upconvert(cache, pc.block_table, lens, starts, 230, cache_format=oracle.NVFP4_CACHE)
+    code_of = {W.to_bf16_bits(np.float32(oracle.e4m3fn(c))).item(): c for c in range(1, 0x78)}
+    for r, n in enumerate(lens):
+        for pos in range(n):
+            row = ws[starts[r] + pos]
+            got = [code_of[int(row[512 + i])] for i in range(3)]
+            assert got == [r + 1, pos // 64 + 1, pos % 64 + 1], (r, pos, got)
+    assert (ws[:3] == 0).all() and (ws[73:80] == 0).all() and (ws[220:] == 0).all()
+
+
+def test_nvfp4_separate_prefill_equals_the_native_path():
+    # the staged rows hold the exact values, so staging changes nothing
+    for seed, max_rows in ((1, 300), (2, 1000)):
+        w = W.mixed_batch(seed, 16, 96, decode_ctx=[150, 300], prefill_ctx=[200, 90, 260],
+                          prefill_queries=[5, 3, 4], p_invalid=0.1, cache_format="nvfp4")
+        o_f, l_f = oracle.attention(oracle.NVFP4_CACHE, w.q, w.cache, w.block_table, w.req_id_per_token,
+                                    w.topk_indices, w.sm_scale)
+        o_s, l_s = oracle.separate_prefill_attention(w.q, w.cache, w.block_table, w.req_id_per_token,
+                                                     w.topk_indices, w.sm_scale, 2, w.ctx_lens, max_rows,
+                                                     cache_format=oracle.NVFP4_CACHE)
+        assert np.array_equal(o_s, o_f) and np.array_equal(l_s, l_f)
