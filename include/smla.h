@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define SMLA_ABI_VERSION 7
+#define SMLA_ABI_VERSION 8
 #define SMLA_BLOCK_SIZE 64
 #define SMLA_HEAD_DIM_QK 576
 #define SMLA_HEAD_DIM_V 512
@@ -271,6 +271,23 @@ smla_status smla_gather_upconvert_fp8(const void *kv_cache, int64_t num_blocks, 
                                       int32_t max_blocks_per_req, const int32_t *seq_lens,
                                       const int32_t *workspace_starts, int32_t batch, int32_t max_seq_len,
                                       void *workspace, int64_t workspace_rows, hipStream_t stream);
+
+/* The same gather over an nvfp4_ds_mla cache (rows as at smla_decode_nvfp4)
+ * [pull-request page "Support nvfp4_ds_mla on FLASHINFER_MLA_SPARSE, with native
+ * NVFP4 decode": prefill is staged through a context gather per request and
+ * chunk]. Every staged value is exact: latent value i is its E2M1 code times its
+ * block's E4M3 scale, and the 64 RoPE values are their E4M3 values; bf16 holds
+ * all of them exactly. So the separate-prefill mode over an nvfp4 cache (this
+ * call, smla_convert_indices_workspace and smla_prefill_bf16 with
+ * SMLA_FLAG_SLOT_INDICES, decode tokens through smla_decode_nvfp4) gives what
+ * smla_decode_nvfp4 gives over the whole batch, up to the kernels' own rounding.
+ *   kv_cache  uint8 [num_blocks, 64, 352], 16-B aligned
+ * Every other argument, the zero rows and the errors as for
+ * smla_gather_upconvert_fp8. */
+smla_status smla_gather_upconvert_nvfp4(const void *kv_cache, int64_t num_blocks, const int32_t *block_table,
+                                        int32_t max_blocks_per_req, const int32_t *seq_lens,
+                                        const int32_t *workspace_starts, int32_t batch, int32_t max_seq_len,
+                                        void *workspace, int64_t workspace_rows, hipStream_t stream);
 
 /* Sparse MLA forward over a bf16 paged cache [flashmla_sparse.py page,
  * _bf16_flash_mla_kernel / flash_mla_sparse_prefill].

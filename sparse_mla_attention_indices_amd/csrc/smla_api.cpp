@@ -387,26 +387,50 @@ smla_status smla_convert_indices_workspace(const int32_t *req_id_per_token, cons
 // requests of one upconvert call: the second grid dimension of its launch
 constexpr int32_t kMaxUpconvertBatch = 65535;
 
-smla_status smla_gather_upconvert_fp8(const void *kv_cache, int64_t num_blocks, const int32_t *block_table,
-                                      int32_t max_blocks_per_req, const int32_t *seq_lens,
-                                      const int32_t *workspace_starts, int32_t batch, int32_t max_seq_len,
-                                      void *workspace, int64_t workspace_rows, hipStream_t stream)
+namespace smla {
+namespace {
+
+smla_status gather_upconvert(CacheFormat fmt, const void *kv_cache, int64_t num_blocks, const int32_t *block_table,
+                             int32_t max_blocks_per_req, const int32_t *seq_lens, const int32_t *workspace_starts,
+                             int32_t batch, int32_t max_seq_len, void *workspace, int64_t workspace_rows,
+                             hipStream_t stream)
 {
     if (batch < 0 || batch > kMaxUpconvertBatch || max_seq_len < 0 || workspace_rows < 0 ||
-        max_blocks_per_req < 1 || num_blocks < 1 || num_blocks > (int64_t)INT32_MAX / smla::kBlock)
+        max_blocks_per_req < 1 || num_blocks < 1 || num_blocks > (int64_t)INT32_MAX / kBlock)
         return SMLA_ERR_SHAPE;
     if (batch == 0 || max_seq_len == 0)
         return SMLA_OK;
     if (!kv_cache || !block_table || !seq_lens || !workspace_starts || !workspace)
         return SMLA_ERR_NULL;
-    if (!smla::aligned(kv_cache, 16) || !smla::aligned(workspace, 16) || !smla::aligned(block_table, 4) ||
-        !smla::aligned(seq_lens, 4) || !smla::aligned(workspace_starts, 4))
+    if (!aligned(kv_cache, 16) || !aligned(workspace, 16) || !aligned(block_table, 4) ||
+        !aligned(seq_lens, 4) || !aligned(workspace_starts, 4))
         return SMLA_ERR_ALIGN;
-    return smla::launch_upconvert(kv_cache, num_blocks, block_table, max_blocks_per_req, seq_lens,
-                                  workspace_starts, batch, max_seq_len, workspace, workspace_rows,
-                                  stream) == hipSuccess
+    return launch_upconvert(fmt, kv_cache, num_blocks, block_table, max_blocks_per_req, seq_lens,
+                            workspace_starts, batch, max_seq_len, workspace, workspace_rows, stream) == hipSuccess
                ? SMLA_OK
                : SMLA_ERR_HIP;
+}
+
+}  // namespace
+}  // namespace smla
+
+smla_status smla_gather_upconvert_fp8(const void *kv_cache, int64_t num_blocks, const int32_t *block_table,
+                                      int32_t max_blocks_per_req, const int32_t *seq_lens,
+                                      const int32_t *workspace_starts, int32_t batch, int32_t max_seq_len,
+                                      void *workspace, int64_t workspace_rows, hipStream_t stream)
+{
+    return smla::gather_upconvert(smla::kCacheFp8, kv_cache, num_blocks, block_table, max_blocks_per_req, seq_lens,
+                                  workspace_starts, batch, max_seq_len, workspace, workspace_rows, stream);
+}
+
+smla_status smla_gather_upconvert_nvfp4(const void *kv_cache, int64_t num_blocks, const int32_t *block_table,
+                                        int32_t max_blocks_per_req, const int32_t *seq_lens,
+                                        const int32_t *workspace_starts, int32_t batch, int32_t max_seq_len,
+                                        void *workspace, int64_t workspace_rows, hipStream_t stream)
+{
+    return smla::gather_upconvert(smla::kCacheNvfp4, kv_cache, num_blocks, block_table, max_blocks_per_req,
+                                  seq_lens, workspace_starts, batch, max_seq_len, workspace, workspace_rows,
+                                  stream);
 }
 
 smla_status smla_convert_indices(const int32_t *req_id_per_token, const int32_t *block_table,

@@ -76,11 +76,11 @@ hipError_t launch_convert_ws(const int32_t *req_id, const int32_t *block_table, 
                              int num_tokens, int topk_len, int num_reqs, int max_blocks, int64_t num_blocks,
                              int num_prefills, hipStream_t stream);
 
-// upconvert_kernel: context rows of `batch` prefill requests from an fp8_ds_mla
-// cache into a bf16 workspace.
-hipError_t launch_upconvert(const void *cache, int64_t num_blocks, const int32_t *block_table, int max_blocks,
-                            const int32_t *seq_lens, const int32_t *ws_starts, int batch, int max_seq_len,
-                            void *workspace, int64_t workspace_rows, hipStream_t stream);
+// upconvert_kernel / upconvert_nvfp4_kernel: context rows of `batch` prefill
+// requests from an fp8_ds_mla or nvfp4_ds_mla cache into a bf16 workspace.
+hipError_t launch_upconvert(CacheFormat fmt, const void *cache, int64_t num_blocks, const int32_t *block_table,
+                            int max_blocks, const int32_t *seq_lens, const int32_t *ws_starts, int batch,
+                            int max_seq_len, void *workspace, int64_t workspace_rows, hipStream_t stream);
 
 // The attention kernel and, when the plan splits the top-k lists (and
 // partials_only is false), the merge kernel after it on the same stream.

@@ -1895,6 +1895,76 @@ __global__ __launch_bounds__(256) void upconvert_kernel(const uint8_t *__restric
     }
 }
 
+// The same gather over an nvfp4_ds_mla cache [pull-request page "Support
+// nvfp4_ds_mla on FLASHINFER_MLA_SPARSE, with native NVFP4 decode": prefill is
+// staged through a context gather per request and chunk]. The staged rows hold
+// the exact values: lane l turns latent codes 8l .. 8l + 7 (one dword, block
+// l / 2) into fp32, multiplies by the block's E4M3 scale and packs to bf16, and
+// lanes 0..7 turn 8 E4M3 RoPE bytes each into bf16; no step rounds (E2M1 x E4M3
+// has at most 6 significant bits). Wave layout, the zero rows of a bad block and
+// the workspace bounds as upconvert_kernel; every load is issued before the
+// first conversion.
+template <int R>
+__global__ __launch_bounds__(256) void upconvert_nvfp4_kernel(const uint8_t *__restrict__ cache, int64_t num_blocks,
+                                                              const int32_t *__restrict__ bt, int max_blocks,
+                                                              const int32_t *__restrict__ seq_lens,
+                                                              const int32_t *__restrict__ ws_starts,
+                                                              uint16_t *__restrict__ ws, int64_t ws_rows)
+{
+    static_assert(kBlock % R == 0 && R >= 1 && R <= 16, "rows per wave");
+    using F = RowFmt<kCacheNvfp4>;
+    const int b = blockIdx.y;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int64_t p0 = ((int64_t)blockIdx.x * 4 + wave) * R;
+    const int64_t blk = p0 / kBlock;
+    const int len = seq_lens[b];
+    const int64_t w0 = (int64_t)ws_starts[b] + p0;
+    const int base = blk < max_blocks ? bt[(size_t)b * max_blocks + blk] : -1;
+    const int n = (int)min((int64_t)R, len - p0);
+    if (n <= 0)
+        return;
+    if (base < 0 || (int64_t)base >= num_blocks) {
+        for (int r = 0; r < n; ++r) {
+            const int64_t w = w0 + r;
+            if (w >= 0 && w < ws_rows) {
+                uint4 *dst = (uint4 *)(ws + w * kDqk);
+                dst[lane] = make_uint4(0u, 0u, 0u, 0u);
+                if (lane < 8)
+                    dst[64 + lane] = make_uint4(0u, 0u, 0u, 0u);
+            }
+        }
+        return;
+    }
+    // rows n .. R - 1 (the end of the context) re-read row n - 1 and are not stored
+    const uint8_t *rows = cache + ((int64_t)base * kBlock + p0 % kBlock) * kNvfp4RowBytes;
+    uint32_t codes[R], sc_byte[R];
+    uint2 rope[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const uint8_t *row = rows + (int64_t)min(r, n - 1) * kNvfp4RowBytes;
+        codes[r] = *(const uint32_t *)(row + 4 * lane);
+        sc_byte[r] = row[F::kScales + (lane >> 1)];
+        rope[r] = *(const uint2 *)(row + F::kRope + 8 * (lane & 7));
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int64_t w = w0 + r;
+        if (r < n && w >= 0 && w < ws_rows) {
+            const float sc = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(sc_byte[r], 1.0f, false)[0];
+            const f32x2 f0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes[r], 1.0f, 0);
+            const f32x2 f1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes[r], 1.0f, 1);
+            const f32x2 f2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes[r], 1.0f, 2);
+            const f32x2 f3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes[r], 1.0f, 3);
+            uint4 *dst = (uint4 *)(ws + w * kDqk);
+            dst[lane] = make_uint4(pack_bf16(f0[0] * sc, f0[1] * sc), pack_bf16(f1[0] * sc, f1[1] * sc),
+                                   pack_bf16(f2[0] * sc, f2[1] * sc), pack_bf16(f3[0] * sc, f3[1] * sc));
+            if (lane < 8)
+                dst[64 + lane] = __builtin_bit_cast(uint4, e4m3x8_to_bf16x8(rope[r]));
+        }
+    }
+}
+
 template <int FMT, int NHH>
 hipError_t launch_one(const KParams &p, hipStream_t stream)
 {
@@ -1999,13 +2069,19 @@ hipError_t launch_convert_ws(const int32_t *req_id, const int32_t *block_table, 
     return hipGetLastError();
 }
 
-hipError_t launch_upconvert(const void *cache, int64_t num_blocks, const int32_t *block_table, int max_blocks,
-                            const int32_t *seq_lens, const int32_t *ws_starts, int batch, int max_seq_len,
-                            void *workspace, int64_t workspace_rows, hipStream_t stream)
+hipError_t launch_upconvert(CacheFormat fmt, const void *cache, int64_t num_blocks, const int32_t *block_table,
+                            int max_blocks, const int32_t *seq_lens, const int32_t *ws_starts, int batch,
+                            int max_seq_len, void *workspace, int64_t workspace_rows, hipStream_t stream)
 {
     const dim3 grid((unsigned)(((int64_t)max_seq_len + 4 * kUpRows - 1) / (4 * kUpRows)), (unsigned)batch);
-    hipLaunchKernelGGL(upconvert_kernel<kUpRows>, grid, dim3(256), 0, stream, (const uint8_t *)cache, num_blocks,
-                       block_table, max_blocks, seq_lens, ws_starts, (uint16_t *)workspace, workspace_rows);
+    if (fmt == kCacheNvfp4)
+        hipLaunchKernelGGL(upconvert_nvfp4_kernel<kUpRows>, grid, dim3(256), 0, stream, (const uint8_t *)cache,
+                           num_blocks, block_table, max_blocks, seq_lens, ws_starts, (uint16_t *)workspace,
+                           workspace_rows);
+    else
+        hipLaunchKernelGGL(upconvert_kernel<kUpRows>, grid, dim3(256), 0, stream, (const uint8_t *)cache,
+                           num_blocks, block_table, max_blocks, seq_lens, ws_starts, (uint16_t *)workspace,
+                           workspace_rows);
     return hipGetLastError();
 }
 

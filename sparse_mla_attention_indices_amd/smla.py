@@ -29,7 +29,8 @@ STATUS_NAMES = {0: "SMLA_OK", 1: "SMLA_ERR_NULL", 2: "SMLA_ERR_SHAPE", 3: "SMLA_
 EXPORTS = ("smla_status_string", "smla_abi_version", "smla_plan", "smla_workspace_size",
            "smla_merge_partials", "smla_concat_and_cache_mla", "smla_convert_indices",
            "smla_prefill_workspace_rows", "smla_plan_prefill_chunks", "smla_convert_indices_workspace",
-           "smla_gather_upconvert_fp8", "smla_prefill_bf16", "smla_decode_fp8", "smla_decode_nvfp4",
+           "smla_gather_upconvert_fp8", "smla_gather_upconvert_nvfp4", "smla_prefill_bf16", "smla_decode_fp8",
+           "smla_decode_nvfp4",
            "smla_decode_fp8_noalloc")
 STATIC_WORKSPACE_BYTES = 64 << 20
 CACHE_FORMATS = {"auto": 0, "bf16": 0, "fp8_ds_mla": 1, "nvfp4_ds_mla": 2}
@@ -85,8 +86,9 @@ def library() -> ctypes.CDLL:
     lib.smla_plan_prefill_chunks.argtypes = [vp, i32, i64, vp, vp, ctypes.POINTER(i32)]
     lib.smla_convert_indices_workspace.restype = ctypes.c_int
     lib.smla_convert_indices_workspace.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i64, i32, vp]
-    lib.smla_gather_upconvert_fp8.restype = ctypes.c_int
-    lib.smla_gather_upconvert_fp8.argtypes = [vp, i64, vp, i32, vp, vp, i32, i32, vp, i64, vp]
+    for name in ("smla_gather_upconvert_fp8", "smla_gather_upconvert_nvfp4"):
+        getattr(lib, name).restype = ctypes.c_int
+        getattr(lib, name).argtypes = [vp, i64, vp, i32, vp, vp, i32, i32, vp, i64, vp]
     attn = [vp, vp, vp, vp, vp, fl, i32, i32, i32, i32, i32, i64, vp, vp, vp, vp, sz, vp, vp]
     for name in ("smla_prefill_bf16", "smla_decode_fp8", "smla_decode_nvfp4"):
         getattr(lib, name).restype = ctypes.c_int
@@ -347,8 +349,9 @@ def smla_decode_fp8_noalloc(q, kv_cache, block_table, req_id_per_token, topk_ind
     return out, lse
 
 
-# ---- separate-prefill mode of an fp8_ds_mla cache (decode tokens over the fp8
-# cache, prefill requests chunk by chunk over an upconverted bf16 workspace)
+# ---- separate-prefill mode of an fp8_ds_mla or nvfp4_ds_mla cache (decode
+# tokens over the cache, prefill requests chunk by chunk over an upconverted
+# bf16 workspace)
 
 def smla_prefill_workspace_rows(max_model_len: int) -> int:
     """bf16 workspace rows reserved for a model (5 x max_model_len)."""
@@ -387,22 +390,36 @@ def smla_convert_indices_workspace(req_id_per_token, block_table, topk_indices, 
     return out
 
 
+def _gather_upconvert(name, row_bytes, kv_cache, block_table, seq_lens, workspace_starts, max_seq_len, workspace,
+                      stream):
+    if kv_cache.dtype != torch.uint8 or kv_cache.shape[1:] != (64, row_bytes):
+        raise ValueError(f"kv_cache must be uint8 [num_blocks, 64, {row_bytes}]")
+    if workspace.dtype != torch.bfloat16 or workspace.dim() != 2 or workspace.shape[1] != 576:
+        raise ValueError("workspace must be bf16 [rows, 576]")
+    B = seq_lens.shape[0]
+    _check(getattr(library(), name)(
+        _dev(kv_cache, "kv_cache"), kv_cache.shape[0], _dev(block_table, "block_table", torch.int32, 2),
+        block_table.shape[1], _dev(seq_lens, "seq_lens", torch.int32, 1),
+        _dev(workspace_starts, "workspace_starts", torch.int32, 1), B, int(max_seq_len),
+        _dev(workspace, "workspace"), workspace.shape[0], _stream(stream)), name)
+    return workspace
+
+
 def smla_gather_upconvert_fp8(kv_cache, block_table, seq_lens, workspace_starts, max_seq_len: int,
                               workspace, stream=None):
     """Upconvert the context rows of a chunk of prefill requests (block_table rows,
     seq_lens, workspace_starts: device int32) from an fp8_ds_mla cache into the
     bf16 workspace [rows, 576]. Returns workspace."""
-    if kv_cache.dtype != torch.uint8 or kv_cache.shape[1:] != (64, 656):
-        raise ValueError("kv_cache must be uint8 [num_blocks, 64, 656]")
-    if workspace.dtype != torch.bfloat16 or workspace.dim() != 2 or workspace.shape[1] != 576:
-        raise ValueError("workspace must be bf16 [rows, 576]")
-    B = seq_lens.shape[0]
-    _check(library().smla_gather_upconvert_fp8(
-        _dev(kv_cache, "kv_cache"), kv_cache.shape[0], _dev(block_table, "block_table", torch.int32, 2),
-        block_table.shape[1], _dev(seq_lens, "seq_lens", torch.int32, 1),
-        _dev(workspace_starts, "workspace_starts", torch.int32, 1), B, int(max_seq_len),
-        _dev(workspace, "workspace"), workspace.shape[0], _stream(stream)), "smla_gather_upconvert_fp8")
-    return workspace
+    return _gather_upconvert("smla_gather_upconvert_fp8", 656, kv_cache, block_table, seq_lens, workspace_starts,
+                             max_seq_len, workspace, stream)
+
+
+def smla_gather_upconvert_nvfp4(kv_cache, block_table, seq_lens, workspace_starts, max_seq_len: int,
+                                workspace, stream=None):
+    """smla_gather_upconvert_fp8 over an nvfp4_ds_mla cache uint8 [num_blocks, 64,
+    352]: the staged rows hold the exact values. Returns workspace."""
+    return _gather_upconvert("smla_gather_upconvert_nvfp4", NVFP4_ROW_BYTES, kv_cache, block_table, seq_lens,
+                             workspace_starts, max_seq_len, workspace, stream)
 
 
 class SeparatePrefillPlan:
@@ -471,6 +488,26 @@ def smla_forward_fp8_separate_prefill(q, kv_cache, block_table, req_id_per_token
     [>= plan.workspace_rows, 576]; slots: int32 [T, topk] scratch for the
     converted indices; out, lse: results. Each is allocated when None. Returns
     (out, lse)."""
+    return _forward_separate_prefill(smla_decode_fp8, smla_gather_upconvert_fp8, q, kv_cache, block_table,
+                                     req_id_per_token, topk_indices, sm_scale, plan, out, lse, bf16_workspace,
+                                     slots, stream)
+
+
+def smla_forward_nvfp4_separate_prefill(q, kv_cache, block_table, req_id_per_token, topk_indices, sm_scale,
+                                        plan: SeparatePrefillPlan, out=None, lse=None, bf16_workspace=None,
+                                        slots=None, stream=None):
+    """smla_forward_fp8_separate_prefill over an nvfp4_ds_mla cache: decode
+    tokens through smla_decode_nvfp4, prefill chunks staged by
+    smla_gather_upconvert_nvfp4 (exact values) and run by smla_prefill_bf16."""
+    return _forward_separate_prefill(smla_decode_nvfp4, smla_gather_upconvert_nvfp4, q, kv_cache, block_table,
+                                     req_id_per_token, topk_indices, sm_scale, plan, out, lse, bf16_workspace,
+                                     slots, stream)
+
+
+def _forward_separate_prefill(decode, upconvert, q, kv_cache, block_table, req_id_per_token, topk_indices,
+                              sm_scale, plan, out, lse, bf16_workspace, slots, stream):
+    """The steps of both separate-prefill entries; decode and upconvert are the
+    format's library calls."""
     T, H, _ = q.shape
     if plan.num_tokens != T:
         raise ValueError("the plan was built for another batch")
@@ -488,14 +525,14 @@ def smla_forward_fp8_separate_prefill(q, kv_cache, block_table, req_id_per_token
                                            plan.workspace_starts, kv_cache.shape[0], out=slots, stream=stream)
     d0, d1 = plan.decode_tokens
     if d1 > d0:
-        smla_decode_fp8(q[d0:d1], kv_cache, None, None, slots[d0:d1], sm_scale, out=out[d0:d1],
-                        lse=lse[d0:d1], stream=stream, slot_indices=True)
+        decode(q[d0:d1], kv_cache, None, None, slots[d0:d1], sm_scale, out=out[d0:d1],
+               lse=lse[d0:d1], stream=stream, slot_indices=True)
     ws_view = bf16_workspace[:ws_rows].view(ws_rows // 64, 64, 576)
     for c0, c1, t0, t1, rows, longest in plan.chunks:
         if rows > 0:
             nd = plan.num_decode_reqs
-            smla_gather_upconvert_fp8(kv_cache, block_table[nd + c0:nd + c1], plan.seq_lens[c0:c1],
-                                      plan.workspace_starts[c0:c1], longest, bf16_workspace, stream=stream)
+            upconvert(kv_cache, block_table[nd + c0:nd + c1], plan.seq_lens[c0:c1],
+                      plan.workspace_starts[c0:c1], longest, bf16_workspace, stream=stream)
         if t1 > t0:
             smla_prefill_bf16(q[t0:t1], ws_view, None, None, slots[t0:t1], sm_scale, out=out[t0:t1],
                               lse=lse[t0:t1], stream=stream, slot_indices=True)

@@ -40,7 +40,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_abi_version(lib):
-    assert smla.smla_abi_version() == 7
+    assert smla.smla_abi_version() == 8
 
 
 def test_status_strings(lib):
@@ -338,8 +338,9 @@ def test_convert_workspace_zero_tokens_and_no_prefills(lib):
     assert _convert_ws(lib, st=None, P=0, idx=None) == 1
 
 
-def _upconvert(lib, kv=A16, NB=8, bt=A16, MB=4, sl=A16, st=A16, B=2, L=100, ws=A16B, rows=256):
-    return lib.smla_gather_upconvert_fp8(kv, NB, bt, MB, sl, st, B, L, ws, rows, None)
+def _upconvert(lib, kv=A16, NB=8, bt=A16, MB=4, sl=A16, st=A16, B=2, L=100, ws=A16B, rows=256,
+               name="smla_gather_upconvert_fp8"):
+    return getattr(lib, name)(kv, NB, bt, MB, sl, st, B, L, ws, rows, None)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -348,10 +349,12 @@ def _upconvert(lib, kv=A16, NB=8, bt=A16, MB=4, sl=A16, st=A16, B=2, L=100, ws=A
     (dict(NB=(1 << 31) // 64 + 1), 2), (dict(B=65536), 2),
     (dict(kv=MIS), 3), (dict(ws=A16B + 8), 3), (dict(bt=A16 + 2), 3), (dict(sl=A16 + 1), 3),
 ])
-def test_upconvert_rejects(lib, kw, code):
-    assert _upconvert(lib, **kw) == code
+@pytest.mark.parametrize("name", ["smla_gather_upconvert_fp8", "smla_gather_upconvert_nvfp4"])
+def test_upconvert_rejects(lib, kw, code, name):
+    assert _upconvert(lib, name=name, **kw) == code
 
 
-def test_upconvert_empty_batch_is_a_noop(lib):
-    assert _upconvert(lib, kv=None, bt=None, sl=None, st=None, ws=None, B=0) == 0
-    assert _upconvert(lib, kv=None, bt=None, sl=None, st=None, ws=None, L=0) == 0
+@pytest.mark.parametrize("name", ["smla_gather_upconvert_fp8", "smla_gather_upconvert_nvfp4"])
+def test_upconvert_empty_batch_is_a_noop(lib, name):
+    assert _upconvert(lib, kv=None, bt=None, sl=None, st=None, ws=None, B=0, name=name) == 0
+    assert _upconvert(lib, kv=None, bt=None, sl=None, st=None, ws=None, L=0, name=name) == 0

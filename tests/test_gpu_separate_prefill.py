@@ -3,7 +3,9 @@ flashmla_sparse.py page as changed for this mode): index conversion to
 workspace rows (bit-exact), the gather-and-upconvert of prefill context rows
 into a bf16 workspace (bit-exact, ties included), attention over cache slots
 given directly (bit-identical to the logical path), and the mode end to end
-against the oracle."""
+against the oracle. The same mode over an nvfp4_ds_mla cache (the staged
+prefill of the native-decode pull-request page): the exact upconvert bit for
+bit, and the mode end to end."""
 
 import numpy as np
 import pytest
@@ -134,14 +136,36 @@ def test_upconvert_full_size_prefill_part_sampled():
             assert np.array_equal(got, one[0]), (r, p)
 
 
+def test_upconvert_nvfp4_bit_exact():
+    """The nvfp4 gather: every staged value is exact, so the bf16 rows equal the
+    oracle's bit for bit; a bad block writes zeros, rows past the workspace and
+    rows no request covers are left alone."""
+    cache = W.random_nvfp4_cache(5, 97, 12)
+    NB = cache.shape[0]
+    lens = np.array([150, 1, 64, 200], dtype=np.int32)
+    bt = np.array([[3, 7, 1, 0], [5, 0, 0, 0], [11, 0, 0, 0], [2, 4, 6, NB + 5]], dtype=np.int32)  # last: bad
+    starts = np.array([10, 0, 170, 300], dtype=np.int32)
+    rows = 480
+    init = np.full((rows, 576), 0x7E57, dtype=np.uint16)
+    want = oracle.gather_upconvert(cache, bt, lens, starts, rows, workspace=init.copy(),
+                                   cache_format=oracle.NVFP4_CACHE)
+    ws = bf16_tensor(init)
+    log("[case] upconvert nvfp4")
+    smla.smla_gather_upconvert_nvfp4(_dev(cache), _dev(bt), _dev(lens), _dev(starts), int(lens.max()), ws)
+    torch.cuda.synchronize()
+    got = ws.view(torch.int16).cpu().numpy().view(np.uint16)
+    bad = np.nonzero((got != want).any(axis=1))[0]
+    assert bad.size == 0, f"rows differ: {bad[:10]}"
+
+
 # ------------------------------------------------------------- slot indices
 
-@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+@pytest.mark.parametrize("fmt", ["bf16", "fp8", "nvfp4"])
 def test_slot_indices_match_the_logical_path(fmt):
     w = W.build(f"slots_{fmt}", 1201, 3, [300, 700, 90], np.repeat([0, 1, 2], 4), np.repeat([300, 700, 90], 4),
                 64, 160, fmt, p_invalid=0.2, max_blocks_per_req=13)
     dw = DeviceWorkload(w)
-    fn = smla.smla_prefill_bf16 if fmt == "bf16" else smla.smla_decode_fp8
+    fn = {"bf16": smla.smla_prefill_bf16, "fp8": smla.smla_decode_fp8, "nvfp4": smla.smla_decode_nvfp4}[fmt]
     for splits in (1, 3):
         log(f"[case] slot indices {fmt} splits={splits}")
         slots = smla.smla_convert_indices(dw.req, dw.bt, dw.idx, w.num_blocks)
@@ -159,14 +183,18 @@ def test_slot_indices_match_the_logical_path(fmt):
 
 # ---------------------------------------------------------------- end to end
 
-@pytest.mark.parametrize("h_q,topk,max_rows", [(16, 96, 300), (64, 128, 520), (128, 64, 1000)])
-def test_separate_prefill_mode_end_to_end(h_q, topk, max_rows):
+@pytest.mark.parametrize("h_q,topk,max_rows,fmt", [(16, 96, 300, "fp8"), (64, 128, 520, "fp8"),
+                                                   (128, 64, 1000, "fp8"), (16, 96, 300, "nvfp4"),
+                                                   (128, 64, 1000, "nvfp4")])
+def test_separate_prefill_mode_end_to_end(h_q, topk, max_rows, fmt):
     w = W.mixed_batch(7 + h_q, h_q, topk, decode_ctx=[150, 300, 77], prefill_ctx=[200, 90, 260, 140],
-                      prefill_queries=[5, 3, 4, 6], p_invalid=0.1)
+                      prefill_queries=[5, 3, 4, 6], p_invalid=0.1, cache_format=fmt)
     nd = 3
-    log(f"[case] separate prefill h_q={h_q} topk={topk} max_rows={max_rows}")
+    log(f"[case] separate prefill {fmt} h_q={h_q} topk={topk} max_rows={max_rows}")
+    ofmt = oracle.FP8_CACHE if fmt == "fp8" else oracle.NVFP4_CACHE
     o_ref, l_ref = oracle.separate_prefill_attention(w.q, w.cache, w.block_table, w.req_id_per_token,
-                                                     w.topk_indices, w.sm_scale, nd, w.ctx_lens, max_rows)
+                                                     w.topk_indices, w.sm_scale, nd, w.ctx_lens, max_rows,
+                                                     cache_format=ofmt)
     ends, _ = oracle.plan_prefill_chunks(w.ctx_lens[nd:], max_rows)
     log(f"  chunks {ends}")
     q = bf16_tensor(w.q)
@@ -175,17 +203,18 @@ def test_separate_prefill_mode_end_to_end(h_q, topk, max_rows):
     qsl = np.concatenate([[0], np.cumsum(counts)])
     plan = smla.smla_build_separate_prefill_plan(qsl, w.ctx_lens, nd, max_rows, "cuda")
     assert [c[1] for c in plan.chunks] == list(ends)
-    o, l = smla.smla_forward_fp8_separate_prefill(q, _dev(w.cache), _dev(w.block_table), _dev(w.req_id_per_token),
-                                                  _dev(w.topk_indices), w.sm_scale, plan)
+    forward = smla.smla_forward_fp8_separate_prefill if fmt == "fp8" else smla.smla_forward_nvfp4_separate_prefill
+    o, l = forward(q, _dev(w.cache), _dev(w.block_table), _dev(w.req_id_per_token), _dev(w.topk_indices),
+                   w.sm_scale, plan)
     torch.cuda.synchronize()
     o = o.float().cpu().numpy().astype(np.float64)
     l = l.cpu().numpy().astype(np.float64)
     dec = w.req_id_per_token < nd
-    for sel, fmt in ((dec, "fp8"), (~dec, "bf16")):
+    for sel, tfmt in ((dec, fmt), (~dec, "bf16")):
         om, orl = errors(o[sel], o_ref[sel])
         fin = np.isfinite(l_ref[sel])
         assert np.array_equal(fin, np.isfinite(l[sel]))
         lm, lrl = errors(l[sel][fin], l_ref[sel][fin])
-        log(f"[parity] separate prefill {fmt} tokens: o max_abs={om:.3e} rel_l2={orl:.3e} lse max_abs={lm:.3e}")
-        assert om <= TOL[fmt]["max_abs"] and orl <= TOL[fmt]["rel_l2"]
-        assert lm <= TOL[fmt]["max_abs"] and lrl <= TOL[fmt]["rel_l2"]
+        log(f"[parity] separate prefill {tfmt} tokens: o max_abs={om:.3e} rel_l2={orl:.3e} lse max_abs={lm:.3e}")
+        assert om <= TOL[tfmt]["max_abs"] and orl <= TOL[tfmt]["rel_l2"]
+        assert lm <= TOL[tfmt]["max_abs"] and lrl <= TOL[tfmt]["rel_l2"]
