@@ -161,6 +161,58 @@ def upconvert_bench(torch, smla, W, dev, stream, flush, sink, steps: int):
             "workload": "config 5 prefill contexts: 131072 + 65536 positions, shuffled blocks"}
 
 
+def nvfp4_prefill_bench(torch, smla, W, dev, stream, flush, sink, steps: int, seed: int):
+    """Config 5's prefill part (2 x 2048 query tokens, h_q 128, top-k 2048,
+    contexts 131072 and 65536) over an nvfp4_ds_mla cache, both ways the library
+    offers, cold cache, HIP events around each call: native decode
+    (smla_decode_nvfp4: one 16-head workgroup per head block, each gathering the
+    token's rows) and the staged separate-prefill mode
+    (smla_forward_nvfp4_separate_prefill: the workspace index conversion, the
+    exact upconvert of both contexts into one bf16 workspace, then the 128-head
+    bf16 kernel over it; its host plan is built once, outside the events)."""
+    w = W.config5_prefill(seed, "nvfp4")
+    q, cache, bt, req, idx = upload(torch, w, dev)
+    T, H, K = w.num_tokens, w.h_q, w.topk
+    out = torch.empty((T, H, 512), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((T, H), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(smla.smla_workspace_size(T, H, K), 1), dtype=torch.uint8, device=dev)
+    counts = np.bincount(w.req_id_per_token, minlength=w.num_reqs)
+    qsl = np.concatenate([[0], np.cumsum(counts)])
+    rows = int(w.ctx_lens.sum())
+    plan = smla.smla_build_separate_prefill_plan(qsl, w.ctx_lens, 0, rows, dev)
+    bf16_ws = torch.empty((plan.workspace_rows, 576), dtype=torch.bfloat16, device=dev)
+    slots = torch.empty_like(idx)
+
+    def native():
+        smla.smla_decode_nvfp4(q, cache, bt, req, idx, w.sm_scale, out=out, lse=lse, workspace=ws, stream=stream)
+
+    def staged():
+        smla.smla_forward_nvfp4_separate_prefill(q, cache, bt, req, idx, w.sm_scale, plan, out=out, lse=lse,
+                                                 bf16_workspace=bf16_ws, slots=slots, stream=stream)
+
+    res = {"workload": w.name + ": 2 x 2048 query tokens, h_q 128, top-k 2048, contexts 131072 + 65536",
+           "num_tokens": T}
+    for name, fn in (("native_decode", native), ("staged_prefill", staged)):
+        for _ in range(2):
+            torch.amax(flush, 0, out=sink)
+            fn()
+        e0 = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+        e1 = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+        for i in range(steps):
+            torch.amax(flush, 0, out=sink)
+            e0[i].record(stream)
+            fn()
+            e1[i].record(stream)
+        torch.cuda.synchronize()
+        ms = float(np.median([a.elapsed_time(b) for a, b in zip(e0, e1)]))
+        r = {"ms_median": ms}
+        r.update(roofline_of(w, ms))
+        res[name] = r
+    del q, cache, bt, req, idx, out, lse, ws, bf16_ws, slots
+    torch.cuda.empty_cache()
+    return res
+
+
 def kernels_of_plan(cache_format: str, h_q: int, splits: int):
     """Names of the kernels one call launches, from the split plan (the same rule the
     library's launcher applies: one workgroup covers all h_q heads of a token, except
@@ -520,6 +572,9 @@ def main():
     rec["cache_writer"] = cache_writer_bench(torch, smla, dev, stream, flush, sink, min(args.steps, 20))
     rec["separate_prefill_upconvert"] = upconvert_bench(torch, smla, W, dev, stream, flush, sink,
                                                         min(args.steps, 20))
+    if not args.no_configs:
+        rec["nvfp4_prefill"] = nvfp4_prefill_bench(torch, smla, W, dev, stream, flush, sink, min(args.steps, 5),
+                                                   args.seed)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(rec), flush=True)

@@ -382,17 +382,19 @@ def mixed_batch(seed: int, h_q: int, topk: int, decode_ctx, prefill_ctx, prefill
     return build("mixed", 6, seed, ctx, req, vis, h_q, topk, cache_format, p_invalid=p_invalid)
 
 
-def config5_prefill(seed: int = 0) -> Workload:
+def config5_prefill(seed: int = 0, cache_format: str = "fp8") -> Workload:
     """Config 5's two prefill requests alone (ctx 131072 and 65536; query tokens are
-    their last 2048 positions), h_q 128, top-k 2048, fp8 cache: the part the
-    separate-prefill mode upconverts."""
+    their last 2048 positions), h_q 128, top-k 2048, fp8 cache (or another
+    format): the part the separate-prefill mode upconverts."""
     pre_ctx = np.array([131072, 65536])
     req, vis = [], []
     for r, c in enumerate(pre_ctx):
         for pos in range(int(c) - 2048, int(c)):
             req.append(r)
             vis.append(pos + 1)
-    return build("c5_prefill_part", 7, seed, pre_ctx, req, vis, 128, 2048, "fp8", max_blocks_per_req=2048)
+    tag = "" if cache_format == "fp8" else f"_{cache_format}"
+    return build(f"c5_prefill_part{tag}", 7, seed, pre_ctx, req, vis, 128, 2048, cache_format,
+                 max_blocks_per_req=2048)
 
 
 CONFIGS = {1: config1, 2: config2, 3: config3, 4: config4, 5: config5}

@@ -218,3 +218,34 @@ def test_separate_prefill_mode_end_to_end(h_q, topk, max_rows, fmt):
         log(f"[parity] separate prefill {tfmt} tokens: o max_abs={om:.3e} rel_l2={orl:.3e} lse max_abs={lm:.3e}")
         assert om <= TOL[tfmt]["max_abs"] and orl <= TOL[tfmt]["rel_l2"]
         assert lm <= TOL[tfmt]["max_abs"] and lrl <= TOL[tfmt]["rel_l2"]
+
+
+def test_config5_prefill_part_over_nvfp4_both_paths_sampled():
+    """Config 5's prefill part (2 x 2048 query tokens, h_q 128, top-k 2048,
+    contexts 131072 and 65536) over an nvfp4 cache, as the benchmark runs it:
+    native decode and the staged mode, sampled tokens against the oracle."""
+    w = W.config5_prefill(0, "nvfp4")
+    dw = DeviceWorkload(w)
+    counts = np.bincount(w.req_id_per_token, minlength=w.num_reqs)
+    qsl = np.concatenate([[0], np.cumsum(counts)])
+    plan = smla.smla_build_separate_prefill_plan(qsl, w.ctx_lens, 0, int(w.ctx_lens.sum()), "cuda")
+    rng = np.random.default_rng(55)
+    tokens = np.unique(np.concatenate([[0, 1, 2047, 2048, 4095], rng.choice(w.num_tokens, 19, replace=False)]))
+    o_ref, l_ref = oracle.attention(oracle.NVFP4_CACHE, w.q, w.cache, w.block_table, w.req_id_per_token,
+                                    w.topk_indices, w.sm_scale, tokens=tokens)
+    for name in ("native", "staged"):
+        log(f"[case] config 5 prefill part nvfp4 {name}")
+        if name == "native":
+            o, l = smla.smla_decode_nvfp4(dw.q, dw.cache, dw.bt, dw.req, dw.idx, w.sm_scale)
+        else:
+            o, l = smla.smla_forward_nvfp4_separate_prefill(dw.q, dw.cache, dw.bt, dw.req, dw.idx, w.sm_scale,
+                                                            plan)
+        torch.cuda.synchronize()
+        sel = torch.from_numpy(tokens).cuda()
+        og = o[sel].float().cpu().numpy().astype(np.float64)
+        lg = l[sel].cpu().numpy().astype(np.float64)
+        om, orl = errors(og, o_ref)
+        lm, lrl = errors(lg, l_ref)
+        log(f"[parity] config 5 prefill nvfp4 {name}: o max_abs={om:.3e} rel_l2={orl:.3e} lse max_abs={lm:.3e}")
+        assert om <= TOL["nvfp4"]["max_abs"] and orl <= TOL["nvfp4"]["rel_l2"]
+        assert lm <= TOL["nvfp4"]["max_abs"] and lrl <= TOL["nvfp4"]["rel_l2"]
