@@ -881,11 +881,15 @@ struct CfgPC {
     static constexpr int kRowsPerWave = kTile / 4;                   // first tiles: the four PV waves
     static constexpr int kDmaPerWave = kRowsPerWave;
     static constexpr int kBufBytes = (kRB * kRowBlockBytes + 1023) / 1024 * 1024;
-    static constexpr int kNBuf = 5;                                  // ring buffers
+    // ring buffers of a long list: four measured faster than five (c2 43.0 ->
+    // 42.0 us, config 5 2.93 -> 2.86 ms) and three slower (c2 50 us)
+    static constexpr int kNBuf = 4;
     static constexpr int kNBufExact = 3;                             // ring buffers of a short list
+    // ring space: five buffers, so a short list's P^T lo terms fit past its three
+    static constexpr int kRingBytes = 5 * kBufBytes;
     static constexpr int kPBytes = 2 * 4 * 4 * 1024;                 // [parity][head block][group] P^T hi
     static constexpr int kSlotsBytes = kMaxChunk * 4;
-    static constexpr int kOffP = kNBuf * kBufBytes;
+    static constexpr int kOffP = kRingBytes;
     static constexpr int kOffPLo = kNBufExact * kBufBytes;           // short lists: P^T lo terms
     static constexpr int kOffHead = kOffP + kPBytes;                 // flags, factors, max and sums
     // q of the four QK^T waves' head blocks (16 rows of 1152 bytes each), held
@@ -904,6 +908,7 @@ struct CfgPC {
     static constexpr int kStageF32 = kDv + 4;
     static_assert(kChunksPerRow <= 64, "one copy instruction per row");
     static_assert(kOffPLo + kPBytes <= kOffP, "lo terms fit the ring buffers a short list leaves free");
+    static_assert(kNBuf * kBufBytes <= kRingBytes, "a long list's ring fits the ring space");
     static_assert(kNBufExact >= 3, "the ring holds tiles r - 1, r and the copy of r + 1");
     static_assert(kOffQ + 4 * kQBlockBytes <= kOffHead, "q staging stays clear of tiles 0, 1 and the flags");
     static_assert(kQBlockBytes % 1024 == 0, "q staging in whole-wave copies");
