@@ -113,7 +113,8 @@ struct Cfg {
     static constexpr int kOffSlots = kOffP + kPBytes;
     static constexpr int kOffMisc = kOffSlots + kSlotsBytes;         // compaction counts
     static constexpr int kOffHead = kOffMisc + 512;                  // per-head factors, rescale flags
-    static constexpr int kLdsBytes = kOffHead + 1024;
+    // (64 heads: the fp32 output staging needs more than the loop's regions)
+    static constexpr int kLdsBytes = kOffHead + 1024 > kHeads * (kDv + 4) * 4 ? kOffHead + 1024 : kHeads * (kDv + 4) * 4;
     static_assert(kRowBlockBytes % 16 == 0, "row blocks are whole 16-byte slots");
     static_assert(kRB * kRowBlockBytes <= kBufBytes, "a tile fits its ring buffer");
     static_assert(kTile % kWaves == 0 && kRowsPerWave <= 64, "whole rows per wave");

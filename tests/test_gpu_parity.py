@@ -91,7 +91,8 @@ def test_small_parity(fmt, h_q, topk):
 @pytest.mark.parametrize("fmt", ["bf16", "fp8", "nvfp4"])
 @pytest.mark.parametrize("h_q", [64, 128])
 def test_long_list_crosses_the_lds_chunk(fmt, h_q):
-    """topk 5000 > 2048 positions per LDS round, ragged tail, one split and several."""
+    """topk 5000: several rounds of LDS compaction per list, a ragged tail, one
+    split and several."""
     w = small(7, fmt, h_q, 5000, n_req=2, tok_per_req=2, ctx=(6000, 9000), p_invalid=0.1)
     dw = DeviceWorkload(w)
     for splits in (1, 2, 0):
