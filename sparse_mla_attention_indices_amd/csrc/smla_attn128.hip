@@ -66,7 +66,9 @@ struct Cfg128 {
     static constexpr int kBufBytes = (kRB * kRowBlockBytes + 255) / 256 * 256;
     static constexpr int kNBuf = 2;                                  // ring buffers of the tile loop
     static constexpr int kOffSlots = 4 * kBufBytes;                  // the ring, or the output staging
-    static constexpr int kOffMisc = kOffSlots + kMaxChunk * 4;
+    // top-k positions compacted into LDS per round (512 and 1024 measured alike)
+    static constexpr int kChunk = 512;
+    static constexpr int kOffMisc = kOffSlots + kChunk * 4;
     static constexpr int kLdsBytes = kOffMisc + 512;
     static constexpr int kStageRow = kDv * 2 + 16;                     // bf16 output staging row
     static constexpr int kBtLdsMax = 2 * kBufBytes / 4;                // table entries in buffers 0, 1
@@ -74,7 +76,7 @@ struct Cfg128 {
     static_assert(kHeads * kStageRow <= kOffMisc, "output staging fits the ring and the slot list");
     static_assert(kTile % kWaves == 0, "whole rows per wave");
     static_assert(kDmaPerWave * (kNBuf - 2) <= 63, "copies in flight within the vmcnt range");
-    static_assert(16 + (kMaxChunk / kThreads) * kWaves <= 128, "compaction counts fit");
+    static_assert(16 + (kChunk / kThreads) * kWaves <= 128, "compaction counts fit");
 };
 
 // O^T += A B with O held in accumulation registers (AGPRs). O of a wave's 32
@@ -120,7 +122,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void attn128_kernel(const KParams p)
 {
     using C = Cfg128;
-    constexpr int kPer = kMaxChunk / C::kThreads;   // top-k positions per thread per round
+    constexpr int kPer = C::kChunk / C::kThreads;   // top-k positions per thread per round
 
     __shared__ __attribute__((aligned(1024))) uint8_t smem[C::kLdsBytes];
     uint8_t *ring = smem;
@@ -167,7 +169,7 @@ void attn128_kernel(const KParams p)
     // rebuilt every round instead of being held across the tile loop.
     auto fetch_round = [&](int chunk0, int (&slotv)[kPer]) __attribute__((always_inline)) {
         const int lane = late(tid & 63), tid = 64 * wave + lane;
-        const int n = min(pos_end, chunk0 + kMaxChunk) - chunk0;
+        const int n = min(pos_end, chunk0 + C::kChunk) - chunk0;
         const uint32_t idx_base = (uint32_t)(uintptr_t)LDS_PTR(int32_t, lds_slots);
         for (int e0 = 64 * wave; e0 < n; e0 += C::kThreads) {
             if (e0 + lane < n)
@@ -220,7 +222,7 @@ void attn128_kernel(const KParams p)
     // valid slots of the round into LDS in list order (two barriers)
     auto compact = [&](int chunk0, int (&slotv)[kPer]) __attribute__((always_inline)) {
         const int lane = late(tid & 63), tid = 64 * wave + lane;
-        const int chunk_n = min(kMaxChunk, pos_end - chunk0);
+        const int chunk_n = min(C::kChunk, pos_end - chunk0);
         if (p.phys_out != nullptr) {
 #pragma unroll
             for (int j = 0; j < kPer; ++j) {
@@ -442,7 +444,7 @@ void attn128_kernel(const KParams p)
         }
     };
 
-    // ---- the list, one round of up to kMaxChunk positions at a time. Returns
+    // ---- the list, one round of up to kChunk positions at a time. Returns
     //      true when mode 0 found a head past its headroom (the tile loop stops
     //      at the next barrier, with every copy landed).
     auto run = [&](auto mode_c, bool first_fetched) __attribute__((always_inline)) -> bool {
@@ -525,7 +527,7 @@ void attn128_kernel(const KParams p)
             __syncthreads();     // ring and slot list are free for the next round
             if (kMode == 0 && (stop || (restart_flag[0] | restart_flag[1]) != 0))
                 return true;
-            chunk0 += kMaxChunk;
+            chunk0 += C::kChunk;
             if (chunk0 < pos_end)
                 fetch_round(chunk0, slotv);
         }

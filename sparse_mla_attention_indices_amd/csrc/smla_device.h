@@ -58,12 +58,12 @@ typedef uint32_t u32x4 __attribute__((__vector_size__(16)));
 
 constexpr int kTile = 32;             // cache rows per tile
 constexpr int kRB = kTile / 16;       // 16-row MFMA blocks per tile
-// top-k positions compacted into LDS per round. 1024 measured faster than 2048
-// on every batch shape (the 16-head decode at top-k 512 and 1024 by 5 %; the
+// Each kernel compacts a list into LDS in rounds of kChunk positions (its
+// configuration's constant). Smaller rounds measured faster on most batch
+// shapes (2048 -> 1024: the 16-head decode at top-k 512 and 1024 by 5 %, the
 // headline decode, 128-head prefill and mixed batches by 1-3 %): each thread
-// handles half as many positions, and a second round costs less than that
-// saves.
-constexpr int kMaxChunk = 1024;
+// handles fewer positions, and a long list's extra rounds cost less than that
+// saves, except where a round boundary drains a shallow ring.
 constexpr int kExactPRows = 128;      // lists this short feed P to PV as hi + lo bf16
 constexpr float kLazyRescale = 8.0f;  // log2 headroom before the running max moves
 

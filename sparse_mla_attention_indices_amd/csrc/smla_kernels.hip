@@ -106,7 +106,10 @@ struct Cfg {
     static constexpr int kXchgBytes = kWaves * kRB * 1024;           // partial S^T exchange
     // P^T operands per (scale group, head block): hi and lo terms, 1 KB each
     static constexpr int kPBytes = NHH > 1 ? 2 * 4 * NHH * 1024 : 0;
-    static constexpr int kSlotsBytes = kMaxChunk * 4;
+    // top-k positions compacted into LDS per round (1024: halving it cost the
+    // 16-head decode 4-5 % at top-k 2048, whose parts then take two rounds)
+    static constexpr int kChunk = 1024;
+    static constexpr int kSlotsBytes = kChunk * 4;
     static constexpr int kOffConv = kNBuf * kBufBytes;
     static constexpr int kOffXchg = kOffConv + kConvBytes;
     static constexpr int kOffP = kOffXchg + kXchgBytes;
@@ -121,7 +124,7 @@ struct Cfg {
     static_assert(kLdsBytes <= 160 * 1024, "LDS of one gfx950 workgroup");
     static_assert(kHeads * kDv * 2 <= kLdsBytes, "bf16 output staging fits");
     static_assert(kHeads * (kDv + 4) * 4 <= kLdsBytes, "fp32 partial staging fits");
-    static_assert(16 + (kMaxChunk / kThreads) * kWaves <= 128, "compaction counts fit");
+    static_assert(16 + (kChunk / kThreads) * kWaves <= 128, "compaction counts fit");
 };
 
 
@@ -139,7 +142,7 @@ void attn_kernel(const KParams p)
     constexpr int RB = kRB;
     constexpr int RS = CT::kRowStride;
     constexpr int RBB = CT::kRowBlockBytes;
-    constexpr int kPer = kMaxChunk / C::kThreads;    // top-k positions per thread per round
+    constexpr int kPer = C::kChunk / C::kThreads;    // top-k positions per thread per round
     static_assert(FMT != kCacheNvfp4 || NHH == 1, "nvfp4 runs 16-head workgroups");
 
     __shared__ __attribute__((aligned(1024))) uint8_t smem[C::kLdsBytes];
@@ -560,7 +563,7 @@ void attn_kernel(const KParams p)
 #pragma unroll
         for (int j = 0; j < kPer; ++j) {
             const int i = pos_begin + tid + C::kThreads * j;
-            idxv[j] = i < min(pos_end, pos_begin + kMaxChunk) ? topk_row[i] : -1;
+            idxv[j] = i < min(pos_end, pos_begin + C::kChunk) ? topk_row[i] : -1;
         }
         // q's raw bytes are loaded now and worked on once the first round's
         // block-table lookups are in flight.
@@ -663,8 +666,8 @@ void attn_kernel(const KParams p)
         const bool write_phys = p.phys_out != nullptr && hb_wg == 0;
 
 
-        for (int chunk0 = pos_begin; chunk0 < pos_end; chunk0 += kMaxChunk) {
-            const int chunk_n = min(kMaxChunk, pos_end - chunk0);
+        for (int chunk0 = pos_begin; chunk0 < pos_end; chunk0 += C::kChunk) {
+            const int chunk_n = min(C::kChunk, pos_end - chunk0);
 
             // ---- convert (all lookups in flight together), then compact the valid
             //      slots in list order with one exchange of per-wave counts
@@ -889,7 +892,10 @@ struct CfgPC {
     // ring space: five buffers, so a short list's P^T lo terms fit past its three
     static constexpr int kRingBytes = 5 * kBufBytes;
     static constexpr int kPBytes = 2 * 4 * 4 * 1024;                 // [parity][head block][group] P^T hi
-    static constexpr int kSlotsBytes = kMaxChunk * 4;
+    // top-k positions compacted into LDS per round: one per thread (512
+    // measured faster than 1024: c2 by 1 %, config 5 by 3 %)
+    static constexpr int kChunk = 512;
+    static constexpr int kSlotsBytes = kChunk * 4;
     static constexpr int kOffP = kRingBytes;
     static constexpr int kOffPLo = kNBufExact * kBufBytes;           // short lists: P^T lo terms
     static constexpr int kOffHead = kOffP + kPBytes;                 // flags, factors, max and sums
@@ -915,7 +921,7 @@ struct CfgPC {
     static_assert(kQBlockBytes % 1024 == 0, "q staging in whole-wave copies");
     static_assert(kLdsBytes <= 160 * 1024, "LDS of one gfx950 workgroup");
     static_assert(kHeads * kStageF32 * 4 <= kOffHead, "staging fits the ring and P^T");
-    static_assert(16 + (kMaxChunk / kThreads) * kWaves <= 128, "compaction counts fit");
+    static_assert(16 + (kChunk / kThreads) * kWaves <= 128, "compaction counts fit");
 };
 
 // Refills (tiles kNBuf and later) are copied by all eight waves, four rows each.
@@ -940,7 +946,7 @@ void attn_pc_kernel(const KParams p)
     constexpr int RB = kRB;
     constexpr int RS = C::kRowStride;
     constexpr int RBB = C::kRowBlockBytes;
-    constexpr int kPer = kMaxChunk / C::kThreads;    // top-k positions per thread per round
+    constexpr int kPer = C::kChunk / C::kThreads;    // top-k positions per thread per round
     constexpr int kRope = RowFmt<kCacheFp8>::kRope;
 
     __shared__ __attribute__((aligned(1024))) uint8_t smem[C::kLdsBytes];
@@ -1096,12 +1102,12 @@ void attn_pc_kernel(const KParams p)
             alpha_lds[(par * 4 + rw) * 16 + n16] = alpha;
     };
 
-    // ---- compaction of one round of the list (up to kMaxChunk positions):
+    // ---- compaction of one round of the list (up to kChunk positions):
     //      converted slots of valid positions into LDS in list order with one
     //      exchange of per-wave counts; every wave takes part (two barriers)
     const bool write_phys = p.phys_out != nullptr && hg == 0;   // head group 0 writes the slots
     auto compact = [&](int chunk0, int (&slotv)[kPer]) __attribute__((always_inline)) {
-        const int chunk_n = min(kMaxChunk, pos_end - chunk0);
+        const int chunk_n = min(C::kChunk, pos_end - chunk0);
         if (write_phys) {
 #pragma unroll
             for (int j = 0; j < kPer; ++j) {
@@ -1128,7 +1134,7 @@ void attn_pc_kernel(const KParams p)
         __syncthreads();
         return n_valid;
     };
-    // Slots of one round of the list (up to kMaxChunk positions from chunk0),
+    // Slots of one round of the list (up to kChunk positions from chunk0),
     // one round trip: the round's indices (into the slot-list area, which the
     // compaction fills only after every index has been read) and, beside them,
     // the request's whole block-table row (into ring buffers 0 and 1, free until
@@ -1142,7 +1148,7 @@ void attn_pc_kernel(const KParams p)
     const int32_t *idx_lds = lds_slots;
     const bool bt_in_lds = !p.slot_in && (unsigned)req < (unsigned)p.R && p.MB <= C::kBtLdsMax;
     auto fetch_round = [&](int chunk0, int (&slotv)[kPer]) __attribute__((always_inline)) {
-        const int n = min(pos_end, chunk0 + kMaxChunk) - chunk0;
+        const int n = min(pos_end, chunk0 + C::kChunk) - chunk0;
         // wave w copies entries 64 (8 k + w) .. + 63 of each list; lanes past its
         // end are inactive
         const uint32_t idx_base = (uint32_t)(uintptr_t)LDS_PTR(int32_t, lds_slots);
@@ -1217,7 +1223,7 @@ void attn_pc_kernel(const KParams p)
         int qsh[4], qsl[4];
         bf16x8 qr[2];
         float m_run = -INFINITY, l_part = 0.f;   // log2-domain running max (same in a head's 4 lanes), row sum
-        for (int chunk0 = pos_begin; chunk0 < pos_end; chunk0 += kMaxChunk) {
+        for (int chunk0 = pos_begin; chunk0 < pos_end; chunk0 += C::kChunk) {
             if (chunk0 != pos_begin)
                 fetch_round(chunk0, slotv);
             const int n_valid = compact(chunk0, slotv);
@@ -1347,7 +1353,7 @@ void attn_pc_kernel(const KParams p)
         const int vk = n16 >> 1;
         const int off_v8 = (vk >> 2) * RBB + (4 * g + (vk & 3)) * RS + 8 * (n16 & 1) + 128 * rw;
         constexpr int dma_w = C::kDmaPerWave;
-        for (int chunk0 = pos_begin; chunk0 < pos_end; chunk0 += kMaxChunk) {
+        for (int chunk0 = pos_begin; chunk0 < pos_end; chunk0 += C::kChunk) {
             if (chunk0 != pos_begin)
                 fetch_round(chunk0, slotv);
             const int n_valid = compact(chunk0, slotv);
