@@ -11,17 +11,21 @@
 //  * Workgroup = one query token x all 128 heads x one part of its top-k list.
 //    Every gathered tile of 32 cache rows is shared by the 128 heads: it is
 //    copied into LDS once and read by four waves, one per SIMD.
-//  * Wave w owns heads 32 w .. 32 w + 31 whole: S^T = K q^T, the online softmax
-//    and O^T += V^T P^T, with 32x32 MFMAs. One MFMA covers 32 rows x 32 heads,
-//    so a K fragment read from LDS feeds all 32 heads of the wave. The S^T
-//    accumulator gives lane l head l mod 32 and 16 of the tile's rows (the other
-//    16 are in lane l xor 32), so the head's max and sum need one cross-lane
-//    step, and the weights are already the B operand of the PV MFMA (its 16
-//    k-rows per step are taken in the accumulator's row order; the transposed
-//    V^T reads gather the same rows in that order). No weight goes through LDS.
-//  * O^T of the wave's 32 heads (32 x 512 fp32) lives in the 256 accumulation
-//    registers (AGPRs); q (bf16, 144 registers per lane) lives in ordinary
-//    registers for the whole kernel.
+//  * Wave w computes S^T = K q^T and the online softmax for heads 32 w .. 32 w
+//    + 31, with 32x32 MFMAs: one MFMA covers 32 rows x 32 heads, so a K fragment
+//    read from LDS feeds all 32 heads of the wave. The S^T accumulator gives
+//    lane l head l mod 32 and 16 of the tile's rows (the other 16 are in lane l
+//    xor 32), so the head's max and sum need one cross-lane step, and the
+//    weights are already in the B-operand layout of the PV MFMA (its 16 k-rows
+//    per step are taken in the accumulator's row order; the transposed V^T
+//    reads gather the same rows in that order).
+//  * PV is split by output dims: each wave publishes its head block's weights
+//    in LDS, and after a second barrier adds O^T += V^T P^T for output dims
+//    128 w .. 128 w + 127 of all 128 heads, so each V^T fragment is read by one
+//    wave instead of four.
+//  * O^T of the wave's dims (128 dims x 128 heads, fp32) lives in the 256
+//    accumulation registers (AGPRs); q (bf16, 144 registers per lane) lives in
+//    ordinary registers for the whole kernel.
 //  * The fp8_ds_mla cache keeps the 64-head kernel at h_q = 128 (two
 //    workgroups per token): there its QK^T and PV waves overlap on each SIMD,
 //    while one wave per SIMD here leaves the fp8 tile's dependency chain
@@ -69,10 +73,15 @@ struct Cfg128 {
     // top-k positions compacted into LDS per round (512 and 1024 measured alike)
     static constexpr int kChunk = 512;
     static constexpr int kOffMisc = kOffSlots + kChunk * 4;
-    static constexpr int kLdsBytes = kOffMisc + 512;
+    // P^T operands of the four head blocks, hi and lo terms ([pass][head block]
+    // [k-step][lane], 16 KB), in ring space the two-buffer loop leaves free
+    static constexpr int kOffP = 2 * kBufBytes;
+    static constexpr int kOffHeadF = kOffMisc + 512;                   // 1 / l of the 128 heads
+    static constexpr int kLdsBytes = kOffHeadF + 512;
     static constexpr int kStageRow = kDv * 2 + 16;                     // bf16 output staging row
     static constexpr int kBtLdsMax = 2 * kBufBytes / 4;                // table entries in buffers 0, 1
     static_assert(kLdsBytes <= 160 * 1024, "LDS of one gfx950 workgroup");
+    static_assert(kOffP + 2 * 4 * 2 * 1024 <= kOffSlots, "P^T fits the ring space past the loop's buffers");
     static_assert(kHeads * kStageRow <= kOffMisc, "output staging fits the ring and the slot list");
     static_assert(kTile % kWaves == 0, "whole rows per wave");
     static_assert(kDmaPerWave * (kNBuf - 2) <= 63, "copies in flight within the vmcnt range");
@@ -387,39 +396,12 @@ void attn128_kernel(const KParams p)
         }
 
         // ---- O^T += V^T P^T; k-step ks takes accumulator elements 8 ks .. 8 ks + 7.
-        //      Stages of four (dim block, k-step) pairs, the next stage's V^T
-        //      fragments read while the current MFMAs run.
         auto load_v = [&](int db, int ks) __attribute__((always_inline)) -> uint4 {
             const uint2 w0 = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                 LDS_PTR(i16x4, buf + f.v[ks][0] + 64 * db)));
             const uint2 w1 = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                 LDS_PTR(i16x4, buf + f.v[ks][1] + 64 * db)));
             return make_uint4(w0.x, w0.y, w1.x, w1.y);
-        };
-        // dim blocks db0 .. db0 + 3, both k-steps: 8 MFMAs with the weights p
-        auto pv_group = [&](int db0, const bf16x8 (&pp)[2]) __attribute__((always_inline)) {
-            uint4 vc[4], vn[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                vc[j] = load_v(db0 + (j >> 1), j & 1);
-#pragma unroll
-            for (int h2 = 0; h2 < 2; ++h2) {
-                if (h2 == 0) {
-#pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        vn[j] = load_v(db0 + 2 + (j >> 1), j & 1);
-                }
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int db = db0 + 2 * h2 + (j >> 1), ks = j & 1;
-                    mfma_o(o[db], __builtin_bit_cast(bf16x8, vc[j]), pp[ks]);
-                }
-                if (h2 == 0) {
-#pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        vc[j] = vn[j];
-                }
-            }
         };
         // weights w as bf16 B operands: hi terms, or (lo) what hi misses
         auto pack = [&](const float (&w)[16], bool lo, bf16x8 (&pp)[2]) __attribute__((always_inline)) {
@@ -432,15 +414,40 @@ void attn128_kernel(const KParams p)
                     pp[ks] = pack_p_residual(p0, p1, pp[ks]);
             }
         };
-        bf16x8 pp[2];
+        // publish this wave's P^T operands (head block `wave`), then PV over this
+        // wave's output dims 128 wave .. 128 wave + 127 for all four head blocks:
+        // each V^T fragment is read by one wave instead of four
+        bf16x8 *p_x = (bf16x8 *)(smem + C::kOffP);
 #pragma unroll
         for (int pass = 0; pass < 2; ++pass) {
             if (pass == 1 && !exact)
                 break;
+            bf16x8 pp[2];
             pack(pw, pass == 1, pp);
 #pragma unroll
-            for (int db0 = 0; db0 < 16; db0 += 4)
-                pv_group(db0, pp);
+            for (int ks = 0; ks < 2; ++ks)
+                p_x[((pass * 4 + wave) * 2 + ks) * 64 + lane] = pp[ks];
+        }
+        __syncthreads();     // every head block's P^T is published
+#pragma unroll
+        for (int pass = 0; pass < 2; ++pass) {
+            if (pass == 1 && !exact)
+                break;
+            bf16x8 pv[4][2];
+#pragma unroll
+            for (int hb = 0; hb < 4; ++hb)
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks)
+                    pv[hb][ks] = p_x[((pass * 4 + hb) * 2 + ks) * 64 + lane];
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                const uint4 v0 = load_v(4 * wave + d, 0), v1 = load_v(4 * wave + d, 1);
+#pragma unroll
+                for (int hb = 0; hb < 4; ++hb) {
+                    mfma_o(o[4 * hb + d], __builtin_bit_cast(bf16x8, v0), pv[hb][0]);
+                    mfma_o(o[4 * hb + d], __builtin_bit_cast(bf16x8, v1), pv[hb][1]);
+                }
+            }
         }
     };
 
@@ -546,23 +553,37 @@ void attn128_kernel(const KParams p)
         run(std::integral_constant<int, 2>{}, false);
     }
 
-    // ---- epilogue: the head's row sum (this lane's rows and the other half's)
+    // ---- epilogue: the head's row sum (this lane's rows and the other half's);
+    //      o[4 hb + d] holds dims 128 wave + 32 d + 8 j + 4 hh + i of head
+    //      32 hb + n32, so every wave needs 1 / l of all 128 heads
     o_settle(o);
     const float l = xor32_sum(l_part);
     const float inv_l = l > 0.f ? 1.f / l : 0.f;
     // natural-log lse (v_log_f32 is log2; l >= 1 here: the row that set the max adds >= 1)
     const float lse_v = l > 0.f ? (m_ref + __builtin_amdgcn_logf(l)) * 0.69314718055994531f : -INFINITY;
+    float *head_f = (float *)(smem + C::kOffHeadF);
+    if (hh == 0)
+        head_f[head] = inv_l;
+    __syncthreads();        // every head's factor is published; the ring and P^T are free
+    float inv_hb[4];
+#pragma unroll
+    for (int hb = 0; hb < 4; ++hb)
+        inv_hb[hb] = head_f[32 * hb + n32];
     if (!p.partials) {
-        // bf16 rows staged in LDS (ring free), then written out coalesced
+        // bf16 rows staged in LDS, then written out coalesced
         uint8_t *stage = smem;
 #pragma unroll
-        for (int db = 0; db < 16; ++db) {
+        for (int hb = 0; hb < 4; ++hb) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const float v0 = o[db][4 * j] * inv_l, v1 = o[db][4 * j + 1] * inv_l;
-                const float v2 = o[db][4 * j + 2] * inv_l, v3 = o[db][4 * j + 3] * inv_l;
-                *(uint2 *)(stage + head * C::kStageRow + 2 * (32 * db + 8 * j + 4 * hh)) =
-                    make_uint2(pack_bf16(v0, v1), pack_bf16(v2, v3));
+            for (int d = 0; d < 4; ++d) {
+                const f32x16 &ob = o[4 * hb + d];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const float v0 = ob[4 * j] * inv_hb[hb], v1 = ob[4 * j + 1] * inv_hb[hb];
+                    const float v2 = ob[4 * j + 2] * inv_hb[hb], v3 = ob[4 * j + 3] * inv_hb[hb];
+                    *(uint2 *)(stage + (32 * hb + n32) * C::kStageRow + 2 * (128 * wave + 32 * d + 8 * j + 4 * hh)) =
+                        make_uint2(pack_bf16(v0, v1), pack_bf16(v2, v3));
+                }
             }
         }
         if (hh == 0 && p.lse != nullptr)
@@ -575,14 +596,17 @@ void attn128_kernel(const KParams p)
         }
     } else {
         // fp32 O / l of this part and its lse, for merge_kernel
-        float *po = p.part_o + (((size_t)t * p.S + s) * p.H + head) * kDv;
 #pragma unroll
-        for (int db = 0; db < 16; ++db) {
+        for (int hb = 0; hb < 4; ++hb) {
+            float *po = p.part_o + (((size_t)t * p.S + s) * p.H + 32 * hb + n32) * kDv + 128 * wave;
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                *(f32x4 *)(po + 32 * db + 8 * j + 4 * hh) =
-                    f32x4{o[db][4 * j] * inv_l, o[db][4 * j + 1] * inv_l, o[db][4 * j + 2] * inv_l,
-                          o[db][4 * j + 3] * inv_l};
+            for (int d = 0; d < 4; ++d) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    *(f32x4 *)(po + 32 * d + 8 * j + 4 * hh) =
+                        f32x4{o[4 * hb + d][4 * j] * inv_hb[hb], o[4 * hb + d][4 * j + 1] * inv_hb[hb],
+                              o[4 * hb + d][4 * j + 2] * inv_hb[hb], o[4 * hb + d][4 * j + 3] * inv_hb[hb]};
+            }
         }
         if (hh == 0)
             p.part_lse[((size_t)t * p.S + s) * p.H + head] = lse_v;
