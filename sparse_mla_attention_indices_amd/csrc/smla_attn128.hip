@@ -428,6 +428,12 @@ void attn128_kernel(const KParams p)
             for (int ks = 0; ks < 2; ++ks)
                 p_x[((pass * 4 + wave) * 2 + ks) * 64 + lane] = pp[ks];
         }
+        // the first dim block's V^T fragments before the barrier: tile r landed
+        // at the previous one, and nothing writes it during the tile
+        uint4 v_pre[1][2];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+            v_pre[0][ks] = load_v(4 * wave, ks);
         __syncthreads();     // every head block's P^T is published
 #pragma unroll
         for (int pass = 0; pass < 2; ++pass) {
@@ -441,7 +447,8 @@ void attn128_kernel(const KParams p)
                     pv[hb][ks] = p_x[((pass * 4 + hb) * 2 + ks) * 64 + lane];
 #pragma unroll
             for (int d = 0; d < 4; ++d) {
-                const uint4 v0 = load_v(4 * wave + d, 0), v1 = load_v(4 * wave + d, 1);
+                const uint4 v0 = d < 1 ? v_pre[0][0] : load_v(4 * wave + d, 0);
+                const uint4 v1 = d < 1 ? v_pre[0][1] : load_v(4 * wave + d, 1);
 #pragma unroll
                 for (int hb = 0; hb < 4; ++hb) {
                     mfma_o(o[4 * hb + d], __builtin_bit_cast(bf16x8, v0), pv[hb][0]);
