@@ -1540,14 +1540,20 @@ void attn_pc_kernel(const KParams p)
 }
 
 // Log-sum-exp merge of a token's top-k splits: thread (t, h, c) combines
-// dims 4c .. 4c + 3 of head h over the splits in index order (weights
-// exp(lse_s - max lse), normalised by their sum) and writes the bf16 output
-// and, once per head, the merged natural-log lse. A split with lse = -inf
-// (no valid position) has weight 0; a head with none at all gets 0 and -inf.
-// KS > 0: exactly KS splits, every load issued before the first is used;
-// KS = 0: any count, in batches of 8. BF: the partials are bf16 hi rows (the
-// first half of each split's fp32 slot), plus residual rows (the second half)
-// for the splits part_exact flags, which are loaded only after the flags.
+// kDpt consecutive dims (group c) of head h over the splits in index order
+// (weights exp(lse_s - max lse), normalised by their sum) and writes the bf16
+// output and, once per head, the merged natural-log lse. A split with
+// lse = -inf (no valid position) has weight 0; a head with none at all gets 0
+// and -inf. KS > 0: exactly KS splits, every load issued before the first is
+// used; KS = 0: any count, in batches of 8. BF: the partials are bf16 hi rows
+// (the first half of each split's fp32 slot), plus residual rows (the second
+// half) for the splits part_exact flags, which are loaded only after the
+// flags; a thread then takes 8 dims, one 16-byte load per row. fp32 partials:
+// 4 dims, also one 16-byte load per row.
+template <bool BF> struct MergeVec;
+template <> struct MergeVec<false> { typedef float type __attribute__((__vector_size__(16))); };
+template <> struct MergeVec<true> { typedef float type __attribute__((__vector_size__(32))); };
+
 template <int KS, bool BF>
 __global__ __launch_bounds__(256) void merge_kernel(const float *__restrict__ part_o,
                                                     const float *__restrict__ part_lse,
@@ -1555,44 +1561,52 @@ __global__ __launch_bounds__(256) void merge_kernel(const float *__restrict__ pa
                                                     uint16_t *__restrict__ out, float *__restrict__ lse,
                                                     int T, int H, int S)
 {
-    // Workgroup id -> (token, pair of heads): the workgroups of token t get id
+    constexpr int kDpt = BF ? 8 : 4;                  // dims per thread
+    constexpr int kGroups = kDv / kDpt;               // threads per (token, head)
+    typedef typename MergeVec<BF>::type vec;
+    // Workgroup id -> (token, run of heads): the workgroups of token t get id
     // mod 8 = t mod 8, the XCD whose L2 the attention kernel wrote t's
     // partials through.
-    const int wpt = H * (kDv / 4) / 256;              // workgroups per token
+    const int wpt = H * kGroups / 256;                // workgroups per token
     const int bid = blockIdx.x;
     const int tt = (bid >> 3) / wpt * 8 + (bid & 7);
     if (tt >= T)
         return;
     const int64_t gid = ((int64_t)tt * wpt + (bid >> 3) % wpt) * 256 + threadIdx.x;
-    const int c = (int)(gid % (kDv / 4));
-    const int64_t th = gid / (kDv / 4);           // t * H + h
+    const int c = (int)(gid % kGroups);
+    const int64_t th = gid / kGroups;                 // t * H + h
     const int t = (int)(th / H), h = (int)(th - (int64_t)t * H);
     if constexpr (KS > 0)
         S = KS;
     const float *pl = part_lse + (size_t)t * S * H + h;
-    const f32x4 *po = (const f32x4 *)part_o + ((size_t)t * S * H + h) * (kDv / 4) + c;
-    const size_t ostride = (size_t)H * (kDv / 4);
-    // BF: split s2's hi row of head h at 4-dim group c, in uint2 units; its
-    // residual row is ostride / 2 further
-    const uint2 *pb = (const uint2 *)part_o + ((size_t)t * S * 2 * H + h) * (kDv / 4) + c;
+    // one split's rows of all heads, in 16-byte units: fp32 rows (fp32), or
+    // the hi rows, with the residual rows right after them (BF)
+    const size_t ostride = (size_t)H * kGroups;
+    const f32x4 *po = (const f32x4 *)part_o + ((size_t)t * S * H + h) * kGroups + c;
+    const uint4 *pb = (const uint4 *)part_o + ((size_t)t * S * 2 * H + h) * kGroups + c;
     const int32_t *pe = BF ? part_exact + (size_t)t * S : nullptr;
-    auto load = [&](int s2) __attribute__((always_inline)) -> f32x4 {
+    auto unpack = [](uint4 u) __attribute__((always_inline)) -> vec {
+        vec v;
         if constexpr (BF) {
-            const uint2 u = pb[(size_t)s2 * 2 * ostride];
-            return f32x4{bf16_lo(u.x), bf16_hi(u.x), bf16_lo(u.y), bf16_hi(u.y)};
-        } else {
-            return po[(size_t)s2 * ostride];
+            v[0] = bf16_lo(u.x); v[1] = bf16_hi(u.x); v[2] = bf16_lo(u.y); v[3] = bf16_hi(u.y);
+            v[4] = bf16_lo(u.z); v[5] = bf16_hi(u.z); v[6] = bf16_lo(u.w); v[7] = bf16_hi(u.w);
         }
+        return v;
     };
-    auto residual = [&](int s2) __attribute__((always_inline)) -> f32x4 {
-        const uint2 u = pb[(size_t)s2 * 2 * ostride + ostride];
-        return f32x4{bf16_lo(u.x), bf16_hi(u.x), bf16_lo(u.y), bf16_hi(u.y)};
+    auto load = [&](int s2) __attribute__((always_inline)) -> vec {
+        if constexpr (BF)
+            return unpack(pb[(size_t)s2 * 2 * ostride]);
+        else
+            return po[(size_t)s2 * ostride];
+    };
+    auto residual = [&](int s2) __attribute__((always_inline)) -> vec {
+        return unpack(pb[(size_t)s2 * 2 * ostride + ostride]);
     };
     float M = -INFINITY, W = 0.f;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    vec acc = {};
     if constexpr (KS > 0) {
         float l[KS];
-        f32x4 v[KS];
+        vec v[KS];
         int ex[KS];
 #pragma unroll
         for (int s2 = 0; s2 < KS; ++s2) {
@@ -1619,7 +1633,7 @@ __global__ __launch_bounds__(256) void merge_kernel(const float *__restrict__ pa
         for (int s2 = 0; s2 < S; ++s2)
             M = fmaxf(M, pl[(size_t)s2 * H]);
         for (int s0 = 0; s0 < S; s0 += 8) {
-            f32x4 v[8];
+            vec v[8];
 #pragma unroll
             for (int k = 0; k < 8; ++k)
                 if (s0 + k < S)
@@ -1639,8 +1653,12 @@ __global__ __launch_bounds__(256) void merge_kernel(const float *__restrict__ pa
                 }
         }
     }
-    const f32x4 o = acc * (W > 0.f ? 1.f / W : 0.f);
-    *(uint2 *)(out + th * kDv + 4 * c) = make_uint2(pack_bf16(o[0], o[1]), pack_bf16(o[2], o[3]));
+    const vec o = acc * (W > 0.f ? 1.f / W : 0.f);
+    if constexpr (BF)
+        *(uint4 *)(out + th * kDv + kDpt * c) = make_uint4(pack_bf16(o[0], o[1]), pack_bf16(o[2], o[3]),
+                                                           pack_bf16(o[4], o[5]), pack_bf16(o[6], o[7]));
+    else
+        *(uint2 *)(out + th * kDv + kDpt * c) = make_uint2(pack_bf16(o[0], o[1]), pack_bf16(o[2], o[3]));
     if (c == 0 && lse != nullptr)
         lse[th] = W > 0.f ? M + logf(W) : -INFINITY;
 }
@@ -2131,11 +2149,13 @@ void launch_merge_as(const float *part_lse, const float *part_o, const int32_t *
 hipError_t launch_merge(const float *part_lse, const float *part_o, const int32_t *part_exact, void *out,
                         float *lse, int T, int H, int S, hipStream_t stream)
 {
-    // whole workgroups per token (h_q * 128 threads, h_q in {16, 32, 64, 128}),
-    // tokens padded to a multiple of 8 for the XCD mapping
-    const int64_t wpt = (int64_t)H * (kDv / 4) / 256;
+    // whole workgroups per token (h_q * 64 threads for bf16 partials, h_q * 128
+    // for fp32, h_q in {16, 32, 64, 128}), tokens padded to a multiple of 8 for
+    // the XCD mapping
+    const bool bf = part_exact != nullptr;
+    const int64_t wpt = (int64_t)H * (kDv / (bf ? 8 : 4)) / 256;
     const dim3 grid((unsigned)((T + 7) / 8 * 8 * wpt));
-    if (part_exact != nullptr)
+    if (bf)
         launch_merge_as<true>(part_lse, part_o, part_exact, (uint16_t *)out, lse, T, H, S, grid, stream);
     else
         launch_merge_as<false>(part_lse, part_o, part_exact, (uint16_t *)out, lse, T, H, S, grid, stream);
