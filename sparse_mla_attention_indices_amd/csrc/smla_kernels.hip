@@ -1585,8 +1585,9 @@ __global__ __launch_bounds__(256) void merge_kernel(const float *__restrict__ pa
     const f32x4 *po = (const f32x4 *)part_o + ((size_t)t * S * H + h) * kGroups + c;
     const uint4 *pb = (const uint4 *)part_o + ((size_t)t * S * 2 * H + h) * kGroups + c;
     const int32_t *pe = BF ? part_exact + (size_t)t * S : nullptr;
+    // 8 bf16 values to fp32 (used only with BF)
     auto unpack = [](uint4 u) __attribute__((always_inline)) -> vec {
-        vec v;
+        vec v = {};
         if constexpr (BF) {
             v[0] = bf16_lo(u.x); v[1] = bf16_hi(u.x); v[2] = bf16_lo(u.y); v[3] = bf16_hi(u.y);
             v[4] = bf16_lo(u.z); v[5] = bf16_hi(u.z); v[6] = bf16_lo(u.w); v[7] = bf16_hi(u.w);
